@@ -1,0 +1,330 @@
+// api_device.hip - C-ABI entry points that enqueue GPU work.  Every argument
+// is validated on the host before the first launch; nothing is allocated and
+// nothing synchronises.
+#include <math.h>
+
+#include "attn.h"
+#include "i4d_internal.h"
+#include "lmhead.h"
+#include "proj.h"
+
+using namespace i4d;
+
+namespace {
+
+#define I4D_TRY(expr)                \
+  do {                               \
+    i4d_status st_ = (expr);         \
+    if (st_ != I4D_OK) return st_;   \
+  } while (0)
+
+i4d_status need(const void* p, const char* what) {
+  if (!p) return fail(I4D_ERR_NULL, "%s is NULL", what);
+  if (!aligned16(p)) return fail(I4D_ERR_ALIGN, "%s is not 16-byte aligned", what);
+  return ok();
+}
+
+i4d_status check_rows(int M) {
+  if (M < 1 || M > I4D_MAX_ROWS) return fail(I4D_ERR_RANGE, "M=%d outside [1, %d]", M, I4D_MAX_ROWS);
+  return ok();
+}
+
+i4d_status check_layer(const i4d_layer* L) {
+  if (!L) return fail(I4D_ERR_NULL, "layer is NULL");
+  I4D_TRY(check_shape(&L->shape));
+  I4D_TRY(need(L->qkv_codes, "qkv_codes"));
+  I4D_TRY(need(L->qkv_scales, "qkv_scales"));
+  I4D_TRY(need(L->o_codes, "o_codes"));
+  I4D_TRY(need(L->o_scales, "o_scales"));
+  I4D_TRY(need(L->gu_codes, "gu_codes"));
+  I4D_TRY(need(L->gu_scales, "gu_scales"));
+  I4D_TRY(need(L->down_codes, "down_codes"));
+  I4D_TRY(need(L->down_scales, "down_scales"));
+  return ok();
+}
+
+i4d_status check_cache(const i4d_kv_cache* c, const i4d_layer_shape* s, int M) {
+  if (!c) return fail(I4D_ERR_NULL, "cache is NULL");
+  I4D_TRY(need(c->k_codes, "cache k_codes"));
+  I4D_TRY(need(c->v_codes, "cache v_codes"));
+  I4D_TRY(need(c->k_scales, "cache k_scales"));
+  I4D_TRY(need(c->v_scales, "cache v_scales"));
+  if (!c->row_base) return fail(I4D_ERR_NULL, "cache row_base is NULL");
+  if (((uintptr_t)c->row_base & 7u) != 0) return fail(I4D_ERR_ALIGN, "row_base not 8-byte aligned");
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(I4D_ERR_UNSUPPORTED, "cache head_dim %d", c->head_dim);
+  if (c->n_kv_heads <= 0) return fail(I4D_ERR_SHAPE, "cache n_kv_heads %d", c->n_kv_heads);
+  if (c->total_capacity <= 0 || c->total_capacity % kVBlock)
+    return fail(I4D_ERR_SHAPE, "cache capacity %lld must be a positive multiple of 32",
+                (long long)c->total_capacity);
+  if (s && (c->head_dim != s->head_dim || c->n_kv_heads != s->n_kv_heads))
+    return fail(I4D_ERR_SHAPE, "cache (n_kv %d, hd %d) does not match the layer (n_kv %d, hd %d)",
+                c->n_kv_heads, c->head_dim, s->n_kv_heads, s->head_dim);
+  if (M > c->n_rows) return fail(I4D_ERR_SHAPE, "M=%d exceeds cache rows %d", M, c->n_rows);
+  return ok();
+}
+
+KvArgs kv_args(const i4d_kv_cache* c) {
+  KvArgs k;
+  k.k_codes = (uint8_t*)c->k_codes;
+  k.v_codes = (uint32_t*)c->v_codes;
+  k.k_scales = c->k_scales;
+  k.v_scales = c->v_scales;
+  k.row_base = c->row_base;
+  k.n_rows = c->n_rows;
+  k.n_kv = c->n_kv_heads;
+  k.hd = c->head_dim;
+  k.err_word = c->err_word;
+  return k;
+}
+
+ProjArgs proj_args(const void* codes, const uint16_t* scales, const uint16_t* x, int Np, int K,
+                   int M, float eps) {
+  ProjArgs a = {};
+  a.codes = (const uint8_t*)codes;
+  a.scales = scales;
+  a.x = x;
+  a.Np = Np;
+  a.K = K;
+  a.G = groups_of(K);
+  a.G8 = g8_of(K);
+  a.M = M;
+  a.eps = eps;
+  return a;
+}
+
+i4d_status do_qkv(const i4d_layer* L, const uint16_t* x, const int32_t* ctx_len, int M, float* q,
+                  uint16_t* k, uint16_t* v, hipStream_t st) {
+  const i4d_layer_shape& s = L->shape;
+  ProjArgs a = proj_args(L->qkv_codes, L->qkv_scales, x,
+                         (s.n_q_heads + 2 * s.n_kv_heads) * s.head_dim, s.d_model, M, s.rms_eps);
+  a.q_out = q;
+  a.k_out = k;
+  a.v_out = v;
+  a.ctx_len = ctx_len;
+  a.n_q = s.n_q_heads;
+  a.n_kv = s.n_kv_heads;
+  a.hd = s.head_dim;
+  a.theta = s.rope_theta;
+  return launch_projection(EPI_QKV, a, st);
+}
+
+i4d_status do_attention(const i4d_kv_cache* c, const i4d_layer_shape& s, const float* q,
+                        const int32_t* ctx_len, int M, int max_ctx_len, int num_splits, void* ws,
+                        float* attn_f32, uint16_t* attn_bf16, hipStream_t st) {
+  AttnArgs a;
+  a.kv = kv_args(c);
+  a.q = q;
+  a.ctx_len = ctx_len;
+  a.M = M;
+  a.n_q = s.n_q_heads;
+  a.G = s.n_q_heads / s.n_kv_heads;
+  a.S = choose_splits(&s, M, max_ctx_len, num_splits);
+  a.score_scale = (float)(1.4426950408889634 / ((double)s.head_dim * sqrt((double)s.head_dim)));
+  AttnWs w = attn_ws_layout(&s, M, a.S);
+  a.part_ml = (float*)((char*)ws + w.ml);
+  a.part_o = (float*)((char*)ws + w.o);
+  a.attn_f32 = attn_f32;
+  a.attn_bf16 = attn_bf16;
+  return launch_attention(a, st);
+}
+
+i4d_status do_o(const i4d_layer* L, const uint16_t* attn, const uint16_t* x, int M, float* h,
+                uint16_t* hb, hipStream_t st) {
+  const i4d_layer_shape& s = L->shape;
+  ProjArgs a = proj_args(L->o_codes, L->o_scales, attn, s.d_model, s.n_q_heads * s.head_dim, M,
+                         s.rms_eps);
+  a.resid_bf16 = x;
+  a.h_f32 = h;
+  a.h_bf16 = hb;
+  return launch_projection(EPI_O, a, st);
+}
+
+i4d_status do_gu(const i4d_layer* L, const uint16_t* hb, int M, uint16_t* out, hipStream_t st) {
+  const i4d_layer_shape& s = L->shape;
+  ProjArgs a = proj_args(L->gu_codes, L->gu_scales, hb, 2 * s.d_ffn, s.d_model, M, s.rms_eps);
+  a.a_out = out;
+  return launch_projection(EPI_GU, a, st);
+}
+
+i4d_status do_down(const i4d_layer* L, const uint16_t* act, const float* h, int M, uint16_t* out,
+                   hipStream_t st) {
+  const i4d_layer_shape& s = L->shape;
+  ProjArgs a = proj_args(L->down_codes, L->down_scales, act, s.d_model, s.d_ffn, M, s.rms_eps);
+  a.resid_f32 = h;
+  a.out_bf16 = out;
+  return launch_projection(EPI_DOWN, a, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+i4d_status i4d_attn_qkv(const i4d_layer* layer, const uint16_t* x, const int32_t* ctx_len, int M,
+                        float* q_out, uint16_t* k_out, uint16_t* v_out, void* stream) {
+  I4D_TRY(check_layer(layer));
+  I4D_TRY(check_rows(M));
+  I4D_TRY(need(x, "x"));
+  I4D_TRY(need(ctx_len, "ctx_len"));
+  I4D_TRY(need(q_out, "q_out"));
+  I4D_TRY(need(k_out, "k_out"));
+  I4D_TRY(need(v_out, "v_out"));
+  return do_qkv(layer, x, ctx_len, M, q_out, k_out, v_out, (hipStream_t)stream);
+}
+
+i4d_status i4d_kv_append(const i4d_kv_cache* cache, const uint16_t* k, const uint16_t* v,
+                         const int32_t* row_idx, const int32_t* pos, int T, void* stream) {
+  I4D_TRY(check_cache(cache, nullptr, 0));
+  if (T < 0) return fail(I4D_ERR_RANGE, "T=%d must be >= 0", T);
+  if (T == 0) return ok();
+  I4D_TRY(need(k, "k"));
+  I4D_TRY(need(v, "v"));
+  I4D_TRY(need(pos, "pos"));
+  if (row_idx && !aligned16(row_idx)) return fail(I4D_ERR_ALIGN, "row_idx not 16-byte aligned");
+  if (!row_idx && T > cache->n_rows)
+    return fail(I4D_ERR_SHAPE, "T=%d tokens without row_idx need T <= n_rows (%d)", T, cache->n_rows);
+  AppendArgs a;
+  a.kv = kv_args(cache);
+  a.k = k;
+  a.v = v;
+  a.row_idx = row_idx;
+  a.pos = pos;
+  a.len = nullptr;
+  a.T = T;
+  return launch_kv_append(a, (hipStream_t)stream);
+}
+
+i4d_status i4d_attention(const i4d_kv_cache* cache, const i4d_layer_shape* shape, const float* q,
+                         const int32_t* ctx_len, int M, int max_ctx_len, int num_splits,
+                         void* workspace, size_t workspace_bytes, float* attn_f32,
+                         uint16_t* attn_bf16, void* stream) {
+  I4D_TRY(check_shape(shape));
+  I4D_TRY(check_rows(M));
+  I4D_TRY(check_cache(cache, shape, M));
+  I4D_TRY(need(q, "q"));
+  I4D_TRY(need(ctx_len, "ctx_len"));
+  I4D_TRY(need(attn_bf16, "attn_bf16"));
+  I4D_TRY(need(workspace, "workspace"));
+  if (attn_f32 && !aligned16(attn_f32)) return fail(I4D_ERR_ALIGN, "attn_f32 not 16-byte aligned");
+  if (max_ctx_len < 1 || max_ctx_len > cache->total_capacity)
+    return fail(I4D_ERR_RANGE, "max_ctx_len %d outside [1, capacity]", max_ctx_len);
+  size_t need_ws;
+  I4D_TRY(i4d_attention_workspace_bytes(shape, M, max_ctx_len, num_splits, &need_ws));
+  if (workspace_bytes < need_ws)
+    return fail(I4D_ERR_WORKSPACE, "attention workspace %zu < %zu bytes", workspace_bytes, need_ws);
+  return do_attention(cache, *shape, q, ctx_len, M, max_ctx_len, num_splits, workspace, attn_f32,
+                      attn_bf16, (hipStream_t)stream);
+}
+
+i4d_status i4d_attn_out_proj(const i4d_layer* layer, const uint16_t* attn_bf16, const uint16_t* x,
+                             int M, float* h_f32, uint16_t* h_bf16, void* stream) {
+  I4D_TRY(check_layer(layer));
+  I4D_TRY(check_rows(M));
+  I4D_TRY(need(attn_bf16, "attn_bf16"));
+  I4D_TRY(need(x, "x"));
+  I4D_TRY(need(h_f32, "h_f32"));
+  I4D_TRY(need(h_bf16, "h_bf16"));
+  return do_o(layer, attn_bf16, x, M, h_f32, h_bf16, (hipStream_t)stream);
+}
+
+i4d_status i4d_ffn_gate_up(const i4d_layer* layer, const uint16_t* h_bf16, int M, uint16_t* a_out,
+                           void* stream) {
+  I4D_TRY(check_layer(layer));
+  I4D_TRY(check_rows(M));
+  I4D_TRY(need(h_bf16, "h_bf16"));
+  I4D_TRY(need(a_out, "a_out"));
+  return do_gu(layer, h_bf16, M, a_out, (hipStream_t)stream);
+}
+
+i4d_status i4d_ffn_down(const i4d_layer* layer, const uint16_t* a, const float* h, int M,
+                        uint16_t* x_out, void* stream) {
+  I4D_TRY(check_layer(layer));
+  I4D_TRY(check_rows(M));
+  I4D_TRY(need(a, "a"));
+  I4D_TRY(need(h, "h"));
+  I4D_TRY(need(x_out, "x_out"));
+  return do_down(layer, a, h, M, x_out, (hipStream_t)stream);
+}
+
+i4d_status i4d_decode_block_step(const i4d_layer* layer, const i4d_kv_cache* cache,
+                                 const uint16_t* x_in, uint16_t* x_out, const int32_t* ctx_len,
+                                 int M, int max_ctx_len, int num_splits, void* workspace,
+                                 size_t workspace_bytes, float* attn_f32, void* stream) {
+  I4D_TRY(check_layer(layer));
+  I4D_TRY(check_rows(M));
+  I4D_TRY(check_cache(cache, &layer->shape, M));
+  I4D_TRY(need(x_in, "x_in"));
+  I4D_TRY(need(x_out, "x_out"));
+  I4D_TRY(need(ctx_len, "ctx_len"));
+  I4D_TRY(need(workspace, "workspace"));
+  if (attn_f32 && !aligned16(attn_f32)) return fail(I4D_ERR_ALIGN, "attn_f32 not 16-byte aligned");
+  if (x_in == x_out) return fail(I4D_ERR_RANGE, "x_in and x_out must not alias");
+  if (max_ctx_len < 1 || max_ctx_len > cache->total_capacity)
+    return fail(I4D_ERR_RANGE, "max_ctx_len %d outside [1, capacity]", max_ctx_len);
+  i4d_workspace_layout wl;
+  I4D_TRY(i4d_workspace_layout_of(&layer->shape, M, max_ctx_len, num_splits, &wl));
+  if (workspace_bytes < wl.total)
+    return fail(I4D_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, wl.total);
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  float* q = (float*)(ws + wl.q);
+  uint16_t* k = (uint16_t*)(ws + wl.k);
+  uint16_t* v = (uint16_t*)(ws + wl.v);
+  uint16_t* attn = (uint16_t*)(ws + wl.attn);
+  float* h = (float*)(ws + wl.h);
+  uint16_t* hb = (uint16_t*)(ws + wl.h_bf16);
+  uint16_t* act = (uint16_t*)(ws + wl.a);
+  const i4d_layer_shape& s = layer->shape;
+
+  I4D_TRY(do_qkv(layer, x_in, ctx_len, M, q, k, v, st));
+  // the new token of row m goes to position ctx_len[m] - 1 of cache row m
+  AppendArgs ap;
+  ap.kv = kv_args(cache);
+  ap.k = k;
+  ap.v = v;
+  ap.row_idx = nullptr;
+  ap.pos = nullptr;
+  ap.len = nullptr;
+  ap.T = M;
+  I4D_TRY(launch_kv_append_at_len(ap, ctx_len, st));
+  I4D_TRY(do_attention(cache, s, q, ctx_len, M, max_ctx_len, num_splits, ws + wl.attn_ws, attn_f32,
+                       attn, st));
+  I4D_TRY(do_o(layer, attn, x_in, M, h, hb, st));
+  I4D_TRY(do_gu(layer, hb, M, act, st));
+  I4D_TRY(do_down(layer, act, h, M, x_out, st));
+  return ok();
+}
+
+i4d_status i4d_lm_head_argmax(const uint16_t* w_lm, int V, int d, const uint16_t* h, int M,
+                              float rms_eps, float* logits_out, int32_t* token_out,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  I4D_TRY(check_rows(M));
+  I4D_TRY(need(w_lm, "w_lm"));
+  I4D_TRY(need(h, "h"));
+  I4D_TRY(need(token_out, "token_out"));
+  I4D_TRY(need(workspace, "workspace"));
+  if (logits_out && !aligned16(logits_out)) return fail(I4D_ERR_ALIGN, "logits not aligned");
+  if (V <= 0 || V % kStrip || d <= 0 || d % kGroup)
+    return fail(I4D_ERR_SHAPE, "LM head V=%d (multiple of 16), d=%d (multiple of 128)", V, d);
+  if (!(rms_eps > 0.f)) return fail(I4D_ERR_RANGE, "rms_eps must be > 0");
+  size_t need_ws;
+  I4D_TRY(i4d_lm_head_workspace_bytes(V, M, &need_ws));
+  if (workspace_bytes < need_ws)
+    return fail(I4D_ERR_WORKSPACE, "LM head workspace %zu < %zu", workspace_bytes, need_ws);
+  LmWs w = lm_ws_layout(V, M);
+  LmArgs a;
+  a.w = w_lm;
+  a.h = h;
+  a.V = V;
+  a.d = d;
+  a.M = M;
+  a.nwaves = w.nwaves;
+  a.eps = rms_eps;
+  a.logits = logits_out;
+  a.part_val = (float*)((char*)workspace + w.val);
+  a.part_idx = (int32_t*)((char*)workspace + w.idx);
+  a.token = token_out;
+  return launch_lm_head(a, (hipStream_t)stream);
+}
+
+}  // extern "C"

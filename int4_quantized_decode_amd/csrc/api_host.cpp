@@ -1,0 +1,388 @@
+// api_host.cpp - host-only part of the C ABI: errors, sizes, weight packing,
+// cache decoding for tests, workspace layouts.  No GPU calls here.
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "i4d_internal.h"
+
+namespace i4d {
+
+static thread_local std::string g_err;
+
+i4d_status fail(i4d_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+i4d_status ok() { return I4D_OK; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+i4d_status check_shape(const i4d_layer_shape* s) {
+  if (!s) return fail(I4D_ERR_NULL, "layer shape is NULL");
+  if (s->head_dim != 64 && s->head_dim != 128)
+    return fail(I4D_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", s->head_dim);
+  if (s->hadamard_block != s->head_dim)
+    return fail(I4D_ERR_UNSUPPORTED, "hadamard_block %d must equal head_dim %d", s->hadamard_block,
+                s->head_dim);
+  if (s->group != kGroup) return fail(I4D_ERR_UNSUPPORTED, "group %d must be 128", s->group);
+  if (s->n_q_heads <= 0 || s->n_kv_heads <= 0 || s->n_q_heads % s->n_kv_heads)
+    return fail(I4D_ERR_SHAPE, "n_q_heads %d must be a positive multiple of n_kv_heads %d",
+                s->n_q_heads, s->n_kv_heads);
+  int G = s->n_q_heads / s->n_kv_heads;
+  if (G > 8 || (G & (G - 1)))
+    return fail(I4D_ERR_UNSUPPORTED, "GQA group %d must be a power of two <= 8", G);
+  int dims[3] = {s->d_model, s->n_q_heads * s->head_dim, s->d_ffn};
+  for (int d : dims)
+    if (d <= 0 || d % kGroup)
+      return fail(I4D_ERR_SHAPE, "dimension %d must be a positive multiple of 128", d);
+  if (!(s->rms_eps > 0.f) || !(s->rope_theta > 1.f))
+    return fail(I4D_ERR_RANGE, "rms_eps must be > 0 and rope_theta > 1");
+  return ok();
+}
+
+int choose_splits(const i4d_layer_shape* s, int M, int max_ctx_len, int num_splits) {
+  int nblk = (max_ctx_len + kVBlock - 1) / kVBlock;
+  if (num_splits > 0) return std::min(num_splits, I4D_MAX_SPLITS);
+  // aim for about two 32-token blocks per wave and at most ~4096 waves
+  long units = (long)M * s->n_kv_heads;
+  long waves_wanted = std::min<long>(4096, std::max<long>(1, units * nblk / 2));
+  long S = (waves_wanted + units * kAttnWaves - 1) / (units * kAttnWaves);
+  S = std::max<long>(1, std::min<long>(S, std::min(nblk, I4D_MAX_SPLITS)));
+  return (int)S;
+}
+
+AttnWs attn_ws_layout(const i4d_layer_shape* s, int M, int S) {
+  AttnWs w;
+  size_t n = (size_t)M * s->n_q_heads * S;
+  w.ml = 0;
+  w.o = align256(n * 2 * sizeof(float));
+  w.total = w.o + align256(n * s->head_dim * sizeof(float));
+  return w;
+}
+
+LmWs lm_ws_layout(int V, int M) {
+  LmWs w;
+  int strips = V / kStrip;
+  w.nwaves = (strips + kLmStripsPerWave - 1) / kLmStripsPerWave;
+  w.val = 0;
+  w.idx = align256((size_t)w.nwaves * M * sizeof(float));
+  w.total = w.idx + align256((size_t)w.nwaves * M * sizeof(int32_t));
+  return w;
+}
+
+// ---------------------------------------------------------------------------
+// fp16 / bf16 conversions (host)
+// ---------------------------------------------------------------------------
+
+static inline uint16_t f32_to_f16_sat(float f) {
+  _Float16 h = (_Float16)f;  // IEEE round-to-nearest-even
+  uint16_t b;
+  memcpy(&b, &h, 2);
+  if ((b & 0x7fffu) == 0x7c00u && isfinite(f)) b = (uint16_t)((b & 0x8000u) | 0x7bffu);
+  return b;
+}
+
+static inline float f16_to_f32(uint16_t b) {
+  _Float16 h;
+  memcpy(&h, &b, 2);
+  return (float)h;
+}
+
+static inline uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// symmetric INT4 RTN of one 128-wide group: scale fp16(absmax/7), codes in [-8, 7]
+static inline uint16_t quantize_group(const float* w, int8_t* q) {
+  float a = 0.f;
+  for (int k = 0; k < kGroup; ++k) a = std::max(a, fabsf(w[k]));
+  uint16_t s16 = f32_to_f16_sat(a / 7.0f);
+  float sf = f16_to_f32(s16);
+  for (int k = 0; k < kGroup; ++k) {
+    if (sf == 0.f) {
+      q[k] = 0;
+    } else {
+      float r = rintf(w[k] / sf);
+      r = std::min(7.f, std::max(-8.f, r));
+      q[k] = (int8_t)r;
+    }
+  }
+  return s16;
+}
+
+template <typename F>
+static void parallel_for(long n, int threads, F&& fn) {
+  if (threads <= 0) threads = (int)std::max(1u, std::thread::hardware_concurrency());
+  threads = (int)std::min<long>(threads, std::max<long>(1, n));
+  if (threads == 1) {
+    fn(0L, n);
+    return;
+  }
+  std::vector<std::thread> pool;
+  long chunk = (n + threads - 1) / threads;
+  for (int t = 0; t < threads; ++t) {
+    long lo = t * chunk, hi = std::min(n, lo + chunk);
+    if (lo >= hi) break;
+    pool.emplace_back([&fn, lo, hi] { fn(lo, hi); });
+  }
+  for (auto& th : pool) th.join();
+}
+
+static i4d_status check_pack_args(i4d_proj_kind kind, int N, int K, int head_dim) {
+  if (N <= 0 || K <= 0 || K % kGroup)
+    return fail(I4D_ERR_SHAPE, "K=%d must be a positive multiple of 128 (N=%d)", K, N);
+  if (N % kStrip) return fail(I4D_ERR_SHAPE, "N=%d must be a multiple of 16", N);
+  if (kind == I4D_PROJ_QKV) {
+    if (head_dim != 64 && head_dim != 128)
+      return fail(I4D_ERR_UNSUPPORTED, "QKV head_dim %d must be 64 or 128", head_dim);
+    if (N % head_dim) return fail(I4D_ERR_SHAPE, "QKV N=%d not a multiple of head_dim", N);
+  } else if (kind == I4D_PROJ_GATE_UP) {
+    if (N % 8) return fail(I4D_ERR_SHAPE, "gate/up N=%d must be a multiple of 8", N);
+  } else if (kind != I4D_PROJ_PLAIN) {
+    return fail(I4D_ERR_RANGE, "unknown projection kind %d", (int)kind);
+  }
+  return ok();
+}
+
+static inline int packed_rows(i4d_proj_kind kind, int N) {
+  return kind == I4D_PROJ_GATE_UP ? 2 * N : N;
+}
+
+// packed row p -> (matrix 0/1, logical row)
+static inline void source_row(i4d_proj_kind kind, int p, int head_dim, int* mat, int* row) {
+  if (kind == I4D_PROJ_QKV) {
+    *mat = 0;
+    *row = qkv_logical_row(p, head_dim);
+  } else if (kind == I4D_PROJ_GATE_UP) {
+    int t = p / kStrip, i = p % kStrip;
+    *mat = i < 8 ? 0 : 1;
+    *row = 8 * t + (i & 7);
+  } else {
+    *mat = 0;
+    *row = p;
+  }
+}
+
+}  // namespace i4d
+
+using namespace i4d;
+
+extern "C" {
+
+const char* i4d_last_error(void) { return g_err.c_str(); }
+
+const char* i4d_version(void) { return "i4d 0.1 (gfx950)"; }
+
+i4d_status i4d_packed_sizes(i4d_proj_kind kind, int N, int K, int head_dim, size_t* code_bytes,
+                            size_t* scale_bytes) {
+  if (!code_bytes || !scale_bytes) return fail(I4D_ERR_NULL, "output pointer is NULL");
+  i4d_status st = check_pack_args(kind, N, K, head_dim);
+  if (st) return st;
+  int Np = packed_rows(kind, N);
+  *code_bytes = packed_code_bytes(Np, K);
+  *scale_bytes = packed_scale_elems(Np, K) * sizeof(uint16_t);
+  return ok();
+}
+
+i4d_status i4d_pack_weights(i4d_proj_kind kind, const float* W0, const float* W1,
+                            const float* gamma, int N, int K, int head_dim, void* codes_out,
+                            uint16_t* scales_out, int threads) {
+  i4d_status st = check_pack_args(kind, N, K, head_dim);
+  if (st) return st;
+  if (!W0 || !codes_out || !scales_out) return fail(I4D_ERR_NULL, "W0/codes_out/scales_out NULL");
+  if (kind == I4D_PROJ_GATE_UP && !W1) return fail(I4D_ERR_NULL, "gate/up needs W1 (up)");
+  if (kind == I4D_PROJ_PLAIN && gamma)
+    return fail(I4D_ERR_RANGE, "PLAIN projections take no gain (gamma must be NULL)");
+  const int Np = packed_rows(kind, N);
+  const int G = groups_of(K), G8 = g8_of(K);
+  uint8_t* codes = (uint8_t*)codes_out;
+  memset(scales_out, 0, packed_scale_elems(Np, K) * sizeof(uint16_t));
+  parallel_for(Np / kStrip, threads, [&](long t0, long t1) {
+    std::vector<float> w(kGroup);
+    int8_t q[kGroup];
+    for (long t = t0; t < t1; ++t) {
+      uint8_t* atom_base = codes + (size_t)t * G * kAtomBytes;
+      memset(atom_base, 0, (size_t)G * kAtomBytes);
+      for (int r = 0; r < kStrip; ++r) {
+        int p = (int)t * kStrip + r, mat, row;
+        source_row(kind, p, head_dim, &mat, &row);
+        const float* src = (mat ? W1 : W0) + (size_t)row * K;
+        for (int g = 0; g < G; ++g) {
+          for (int k = 0; k < kGroup; ++k) {
+            float v = src[g * kGroup + k];
+            w[k] = gamma ? gamma[g * kGroup + k] * v : v;  // one fp32 product
+          }
+          uint16_t s16 = quantize_group(w.data(), q);
+          scales_out[(((size_t)t * G8 + g / 8) * 16 + r) * 8 + (g % 8)] = s16;
+          uint8_t* atom = atom_base + (size_t)g * kAtomBytes;
+          for (int kk = 0; kk < kGroup; ++kk) {
+            int kb = kk / 32, j = (kk % 32) / 8, e = kk % 8;
+            int slot = nibble_slot(e);
+            uint8_t u = (uint8_t)(q[kk] + 8);
+            uint8_t* byte = atom + (16 * j + r) * 16 + kb * 4 + slot / 2;
+            *byte |= (slot & 1) ? (uint8_t)(u << 4) : u;
+          }
+        }
+      }
+    }
+  });
+  (void)G8;
+  return ok();
+}
+
+i4d_status i4d_unpack_weights(i4d_proj_kind kind, const void* codes, const uint16_t* scales, int N,
+                              int K, int head_dim, int8_t* q_out, uint16_t* s_out) {
+  i4d_status st = check_pack_args(kind, N, K, head_dim);
+  if (st) return st;
+  if (!codes || !scales || !q_out || !s_out) return fail(I4D_ERR_NULL, "NULL pointer");
+  const int Np = packed_rows(kind, N);
+  const int G = groups_of(K);
+  const uint8_t* c = (const uint8_t*)codes;
+  for (int p = 0; p < Np; ++p) {
+    int mat, row;
+    source_row(kind, p, head_dim, &mat, &row);
+    int out_row = mat * N + row;
+    for (int k = 0; k < K; ++k) {
+      int hi;
+      size_t off = code_byte_offset(p, k, K, &hi);
+      int u = hi ? (c[off] >> 4) : (c[off] & 15);
+      q_out[(size_t)out_row * K + k] = (int8_t)(u - 8);
+    }
+    for (int g = 0; g < G; ++g) s_out[(size_t)out_row * G + g] = scales[scale_index(p, g, K)];
+  }
+  return ok();
+}
+
+i4d_status i4d_pack_lm_head(const float* W, const float* gamma, int V, int d, uint16_t* out_bf16,
+                            int threads) {
+  if (!W || !out_bf16) return fail(I4D_ERR_NULL, "W/out NULL");
+  if (V <= 0 || d <= 0 || V % kStrip || d % kGroup)
+    return fail(I4D_ERR_SHAPE, "LM head V=%d must be a multiple of 16, d=%d of 128", V, d);
+  parallel_for(V, threads, [&](long v0, long v1) {
+    for (long v = v0; v < v1; ++v)
+      for (int k = 0; k < d; ++k) {
+        float w = W[(size_t)v * d + k];
+        out_bf16[(size_t)v * d + k] = f32_to_bf16_rne(gamma ? gamma[k] * w : w);
+      }
+  });
+  return ok();
+}
+
+i4d_status i4d_kv_cache_bytes(int n_kv_heads, int head_dim, int64_t total_capacity,
+                              size_t* k_code_bytes, size_t* v_code_bytes, size_t* k_scale_bytes,
+                              size_t* v_scale_bytes) {
+  if (!k_code_bytes || !v_code_bytes || !k_scale_bytes || !v_scale_bytes)
+    return fail(I4D_ERR_NULL, "output pointer NULL");
+  if (head_dim != 64 && head_dim != 128) return fail(I4D_ERR_UNSUPPORTED, "head_dim %d", head_dim);
+  if (n_kv_heads <= 0 || total_capacity < 0 || total_capacity % kVBlock)
+    return fail(I4D_ERR_SHAPE, "capacity %lld must be a non-negative multiple of 32",
+                (long long)total_capacity);
+  size_t slots = (size_t)total_capacity * n_kv_heads;
+  *k_code_bytes = *v_code_bytes = slots * head_dim / 2;
+  *k_scale_bytes = *v_scale_bytes = slots * sizeof(uint16_t);
+  return ok();
+}
+
+i4d_status i4d_kv_unpack_host(const i4d_kv_cache* hc, const int64_t* row_base_host, int row,
+                              int t0, int t1, int8_t* k_out, int8_t* v_out, uint16_t* ks_out,
+                              uint16_t* vs_out) {
+  if (!hc || !row_base_host || !k_out || !v_out || !ks_out || !vs_out)
+    return fail(I4D_ERR_NULL, "NULL pointer");
+  if (row < 0 || row >= hc->n_rows) return fail(I4D_ERR_RANGE, "row %d out of range", row);
+  const int hd = hc->head_dim, nkv = hc->n_kv_heads;
+  const int64_t base = row_base_host[row], cap = row_base_host[row + 1] - base;
+  if (t0 < 0 || t1 > cap || t0 > t1) return fail(I4D_ERR_RANGE, "token range out of capacity");
+  const uint8_t* kc = (const uint8_t*)hc->k_codes;
+  const uint32_t* vc = (const uint32_t*)hc->v_codes;
+  for (int t = t0; t < t1; ++t)
+    for (int j = 0; j < nkv; ++j) {
+      int64_t region = base * nkv + (int64_t)j * cap;  // first slot of (row, head)
+      int64_t slot = region + t;
+      size_t o = (size_t)(t - t0) * nkv + j;
+      ks_out[o] = hc->k_scales[slot];
+      vs_out[o] = hc->v_scales[slot];
+      for (int c = 0; c < hd; ++c) {
+        int hi;
+        int b = key_byte_in_slot(c, hd, &hi);
+        uint8_t byte = kc[(size_t)slot * (hd / 2) + b];
+        k_out[o * hd + c] = (int8_t)((hi ? byte >> 4 : byte & 15) - 8);
+        int ns;
+        int dw = value_dword_in_block(t % kVBlock, c, hd, &ns);
+        size_t blk = (size_t)(region / kVBlock + t / kVBlock);
+        uint32_t word = vc[blk * 4 * hd + dw];
+        v_out[o * hd + c] = (int8_t)(((word >> (4 * ns)) & 15) - 8);
+      }
+    }
+  return ok();
+}
+
+i4d_status i4d_attention_workspace_bytes(const i4d_layer_shape* shape, int M, int max_ctx_len,
+                                         int num_splits, size_t* bytes) {
+  i4d_status st = check_shape(shape);
+  if (st) return st;
+  if (!bytes) return fail(I4D_ERR_NULL, "bytes NULL");
+  if (M < 1 || M > I4D_MAX_ROWS) return fail(I4D_ERR_RANGE, "M=%d outside [1, 32]", M);
+  if (max_ctx_len < 1) return fail(I4D_ERR_RANGE, "max_ctx_len must be >= 1");
+  if (num_splits < 0 || num_splits > I4D_MAX_SPLITS)
+    return fail(I4D_ERR_RANGE, "num_splits %d outside [0, %d]", num_splits, I4D_MAX_SPLITS);
+  int S = choose_splits(shape, M, max_ctx_len, num_splits);
+  *bytes = attn_ws_layout(shape, M, S).total;
+  return ok();
+}
+
+i4d_status i4d_workspace_layout_of(const i4d_layer_shape* s, int M, int max_ctx_len,
+                                   int num_splits, i4d_workspace_layout* out) {
+  if (!out) return fail(I4D_ERR_NULL, "layout NULL");
+  size_t attn_bytes;
+  i4d_status st = i4d_attention_workspace_bytes(s, M, max_ctx_len, num_splits, &attn_bytes);
+  if (st) return st;
+  size_t nq = (size_t)M * s->n_q_heads * s->head_dim;
+  size_t nk = (size_t)M * s->n_kv_heads * s->head_dim;
+  size_t off = 0;
+  out->q = off;       off += align256(nq * 4);
+  out->k = off;       off += align256(nk * 2);
+  out->v = off;       off += align256(nk * 2);
+  out->attn = off;    off += align256(nq * 2);
+  out->h = off;       off += align256((size_t)M * s->d_model * 4);
+  out->h_bf16 = off;  off += align256((size_t)M * s->d_model * 2);
+  out->a = off;       off += align256((size_t)M * s->d_ffn * 2);
+  out->attn_ws = off; off += align256(attn_bytes);
+  out->total = off;
+  return ok();
+}
+
+i4d_status i4d_workspace_bytes(const i4d_layer_shape* shape, int M, int max_ctx_len,
+                               int num_splits, size_t* bytes) {
+  if (!bytes) return fail(I4D_ERR_NULL, "bytes NULL");
+  i4d_workspace_layout l;
+  i4d_status st = i4d_workspace_layout_of(shape, M, max_ctx_len, num_splits, &l);
+  if (st) return st;
+  *bytes = l.total;
+  return ok();
+}
+
+i4d_status i4d_lm_head_workspace_bytes(int V, int M, size_t* bytes) {
+  if (!bytes) return fail(I4D_ERR_NULL, "bytes NULL");
+  if (V <= 0 || V % kStrip) return fail(I4D_ERR_SHAPE, "V=%d must be a multiple of 16", V);
+  if (M < 1 || M > I4D_MAX_ROWS) return fail(I4D_ERR_RANGE, "M=%d outside [1, 32]", M);
+  *bytes = lm_ws_layout(V, M).total;
+  return ok();
+}
+
+}  // extern "C"

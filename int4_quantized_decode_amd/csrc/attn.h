@@ -1,0 +1,47 @@
+// attn.h - internal interface of the KV-append and attention kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "i4d_internal.h"
+
+namespace i4d {
+
+struct KvArgs {
+  uint8_t* k_codes;
+  uint32_t* v_codes;
+  uint16_t* k_scales;
+  uint16_t* v_scales;
+  const int64_t* row_base;
+  int n_rows, n_kv, hd;
+  int32_t* err_word;
+};
+
+struct AppendArgs {
+  KvArgs kv;
+  const uint16_t* k;  // bf16 [T][n_kv][hd]
+  const uint16_t* v;
+  const int32_t* row_idx;  // NULL = identity
+  const int32_t* pos;      // position per token, or NULL when len is given
+  const int32_t* len;      // if non-NULL: position = len[t] - 1 (decode step)
+  int T;
+};
+
+struct AttnArgs {
+  KvArgs kv;
+  const float* q;          // fp32 [M][n_q][hd], not rotated
+  const int32_t* ctx_len;  // [M]
+  int M, n_q, G, S;
+  float score_scale;       // log2(e) / (hd * sqrt(hd))
+  float* part_ml;          // [M][n_q][S][2]
+  float* part_o;           // [M][n_q][S][hd]
+  float* attn_f32;         // optional [M][n_q*hd]
+  uint16_t* attn_bf16;     // [M][n_q*hd]
+};
+
+i4d_status launch_kv_append(const AppendArgs& a, hipStream_t st);
+// decode step: token t of row t goes to position ctx_len[t] - 1
+i4d_status launch_kv_append_at_len(AppendArgs a, const int32_t* ctx_len, hipStream_t st);
+i4d_status launch_attention(const AttnArgs& a, hipStream_t st);
+
+}  // namespace i4d

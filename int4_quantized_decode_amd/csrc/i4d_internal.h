@@ -1,0 +1,46 @@
+// i4d_internal.h - host-side helpers shared by the C-ABI translation units.
+#pragma once
+#include <stdarg.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/i4d.h"
+#include "i4d_layout.h"
+
+namespace i4d {
+
+// records the message for i4d_last_error() and returns `st`
+i4d_status fail(i4d_status st, const char* fmt, ...);
+i4d_status ok();
+
+bool aligned16(const void* p);
+
+// validates a layer shape (returns I4D_OK or the error, message set)
+i4d_status check_shape(const i4d_layer_shape* s);
+
+// number of KV splits used for the attention launch
+int choose_splits(const i4d_layer_shape* s, int M, int max_ctx_len, int num_splits);
+
+// waves per attention workgroup
+constexpr int kAttnWaves = 8;
+
+struct AttnWs {
+  size_t ml;      // fp32 [M][n_q][S][2]   (running max in log2 units, sum)
+  size_t o;       // fp32 [M][n_q][S][hd]  unnormalised rotated output
+  size_t total;
+};
+AttnWs attn_ws_layout(const i4d_layer_shape* s, int M, int S);
+
+struct LmWs {
+  size_t val;   // fp32 [nwaves][M]
+  size_t idx;   // int32 [nwaves][M]
+  size_t total;
+  int nwaves;
+};
+constexpr int kLmStripsPerWave = 2;
+constexpr int kLmWavesPerBlock = 4;
+LmWs lm_ws_layout(int V, int M);
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace i4d

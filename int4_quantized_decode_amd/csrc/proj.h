@@ -1,0 +1,38 @@
+// proj.h - internal interface of the INT4 projection kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "i4d_internal.h"
+
+namespace i4d {
+
+enum Epi { EPI_QKV = 0, EPI_O = 1, EPI_GU = 2, EPI_DOWN = 3 };
+
+struct ProjArgs {
+  const uint8_t* codes;    // packed atoms [Np/16][K/128][64][16]
+  const uint16_t* scales;  // fp16 [Np/16][G8][16][8]
+  const uint16_t* x;       // bf16 input [M][K]
+  int Np, K, G, G8, M;
+  float eps;
+  // QKV epilogue
+  float* q_out;
+  uint16_t* k_out;
+  uint16_t* v_out;
+  const int32_t* ctx_len;
+  int n_q, n_kv, hd;
+  float theta;
+  // O epilogue
+  const uint16_t* resid_bf16;
+  float* h_f32;
+  uint16_t* h_bf16;
+  // gate/up epilogue
+  uint16_t* a_out;
+  // down epilogue
+  const float* resid_f32;
+  uint16_t* out_bf16;
+};
+
+i4d_status launch_projection(int epi, const ProjArgs& a, hipStream_t st);
+
+}  // namespace i4d

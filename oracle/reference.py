@@ -361,6 +361,69 @@ class BlockResult:
     v_scales_new: np.ndarray
 
 
+def qkv_stage(shape, W_qkv_hat, x, lengths):
+    """rho1 -> x . W'qkv^T (gain folded) -> RoPE on q and k at position L-1.
+
+    x fp64 [M, d]; returns q [M, n_q, hd], k and v [M, n_kv, hd] (fp64, k/v not
+    yet rounded to bf16).  [P1 how-it-works; R3, R4]
+    """
+    d, hd = shape.d_model, shape.head_dim
+    nq, nkv = shape.n_q_heads, shape.n_kv_heads
+    M = x.shape[0]
+    rho1 = rms_factor(x, shape.rms_eps)
+    qkv = rho1[:, None] * (x @ W_qkv_hat.T)
+    q = qkv[:, : nq * hd].reshape(M, nq, hd)
+    k = qkv[:, nq * hd: (nq + nkv) * hd].reshape(M, nkv, hd)
+    v = qkv[:, (nq + nkv) * hd:].reshape(M, nkv, hd)
+    pos = np.asarray(lengths, dtype=np.float64) - 1.0
+    return rope(q, pos[:, None], shape.rope_theta), rope(k, pos[:, None], shape.rope_theta), v
+
+
+def attention_stage(shape, cache: List[RowCache], q, lengths):
+    """Rotated query against each row's INT4 cache, unsplit softmax, inverse
+    rotation; returns the attention output [M, n_q * hd].  [P1 how-it-differs; R5, R7, R8]"""
+    M = q.shape[0]
+    q_rot = fwht(q)
+    out = np.empty((M,) + q.shape[1:])
+    for r in range(M):
+        c = cache[r]
+        out[r] = attention_one_row(q_rot[r], c.k_codes, c.k_scales, c.v_codes, c.v_scales,
+                                   int(lengths[r]), shape.head_dim)
+    return out.reshape(M, -1)
+
+
+def o_stage(W_o_hat, x, attn):
+    """h = x + attn . Wo^T (no gain: the input is not normalised)."""
+    return x + attn @ W_o_hat.T
+
+
+def gate_up_stage(shape, W_gate_hat, W_up_hat, h):
+    """rho2 -> gate, up (gain folded) -> a = silu(gate) * up.  [P1 how-it-works; R3, R9]"""
+    rho2 = rms_factor(h, shape.rms_eps)
+    g = rho2[:, None] * (h @ W_gate_hat.T)
+    u = rho2[:, None] * (h @ W_up_hat.T)
+    return silu(g) * u
+
+
+def down_stage(W_down_hat, h, a):
+    """out = h + a . Wdown^T."""
+    return h + a @ W_down_hat.T
+
+
+def append_stage(cache: List[RowCache], k, v, lengths):
+    """Round the new k, v to bf16 (R10), encode them (R6) and store them at
+    position L-1 of each row.  Returns the bf16 values and the codes."""
+    k_b = round_to_bf16(k)
+    v_b = round_to_bf16(v)
+    kq, ks = quantize_kv(k_b)
+    vq, vs = quantize_kv(v_b)
+    for r in range(len(lengths)):
+        p = int(lengths[r]) - 1
+        cache[r].k_codes[p], cache[r].k_scales[p] = kq[r], ks[r]
+        cache[r].v_codes[p], cache[r].v_scales[p] = vq[r], vs[r]
+    return k_b, v_b, kq, ks, vq, vs
+
+
 def decode_block(shape, ql: QuantLayer, cache: List[RowCache], x_bits, lengths,
                  dense_cache: Optional[dict] = None) -> BlockResult:
     """One decode step of the block for M rows (row r attends L_r tokens).
@@ -374,10 +437,6 @@ def decode_block(shape, ql: QuantLayer, cache: List[RowCache], x_bits, lengths,
     ``cache`` is updated in place with the appended token.
     ``dense_cache`` (optional dict) memoises the dequantized fp64 weights.
     """
-    d, hd = shape.d_model, shape.head_dim
-    nq, nkv = shape.n_q_heads, shape.n_kv_heads
-    b = hd
-    eps = shape.rms_eps
     lengths = [int(L) for L in lengths]
     M = len(lengths)
 
@@ -388,40 +447,13 @@ def decode_block(shape, ql: QuantLayer, cache: List[RowCache], x_bits, lengths,
             return dense_cache[name]
         return dense(getattr(ql, name))
 
-    x = _bf16_bits_to_values(np.asarray(x_bits).reshape(M, d)).astype(np.float64)
-
-    rho1 = rms_factor(x, eps)
-    qkv = rho1[:, None] * (x @ W("qkv").T)
-    q = qkv[:, : nq * hd].reshape(M, nq, hd)
-    k = qkv[:, nq * hd: (nq + nkv) * hd].reshape(M, nkv, hd)
-    v = qkv[:, (nq + nkv) * hd:].reshape(M, nkv, hd)
-    pos = np.array(lengths, dtype=np.float64) - 1.0
-    q = rope(q, pos[:, None], shape.rope_theta)
-    k = rope(k, pos[:, None], shape.rope_theta)
-
-    k_b = round_to_bf16(k)
-    v_b = round_to_bf16(v)
-    kq, ks = quantize_kv(k_b)
-    vq, vs = quantize_kv(v_b)
-    for r in range(M):
-        p = lengths[r] - 1
-        cache[r].k_codes[p], cache[r].k_scales[p] = kq[r], ks[r]
-        cache[r].v_codes[p], cache[r].v_scales[p] = vq[r], vs[r]
-
-    q_rot = fwht(q)
-    attn = np.empty((M, nq, hd))
-    for r in range(M):
-        c = cache[r]
-        attn[r] = attention_one_row(q_rot[r], c.k_codes, c.k_scales, c.v_codes, c.v_scales,
-                                    lengths[r], b)
-    attn = attn.reshape(M, nq * hd)
-
-    h = x + attn @ W("o").T
-    rho2 = rms_factor(h, eps)
-    g = rho2[:, None] * (h @ W("gate").T)
-    u = rho2[:, None] * (h @ W("up").T)
-    a = silu(g) * u
-    out = h + a @ W("down").T
+    x = _bf16_bits_to_values(np.asarray(x_bits).reshape(M, shape.d_model)).astype(np.float64)
+    q, k, v = qkv_stage(shape, W("qkv"), x, lengths)
+    k_b, v_b, kq, ks, vq, vs = append_stage(cache, k, v, lengths)
+    attn = attention_stage(shape, cache, q, lengths)
+    h = o_stage(W("o"), x, attn)
+    a = gate_up_stage(shape, W("gate"), W("up"), h)
+    out = down_stage(W("down"), h, a)
     return BlockResult(out, attn, h, q, k_b, v_b, kq, ks, vq, vs)
 
 

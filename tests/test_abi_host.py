@@ -1,0 +1,285 @@
+"""Host-side checks of the C ABI (no GPU work is enqueued by any test here).
+
+* the library loads and exports every function include/i4d.h declares;
+* argument validation rejects bad calls before anything reaches the GPU;
+* the host packer is bit-exact against the oracle's quantizer, and the
+  packed bytes sit where the documented device layout says;
+* the KV-cache decoder reads the documented cache layout.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+from int4_quantized_decode_amd import binding as B
+from int4_quantized_decode_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "i4d.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(i4d_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = B.lib()
+    names = declared_functions()
+    assert len(names) >= 20
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in include/i4d.h but not exported"
+    assert sorted(B.exported_names()) == names
+    assert "gfx950" in B.i4d_version()
+
+
+# ---------------------------------------------------------------------------
+# validation (every call below fails in host checks, before any HIP call)
+# ---------------------------------------------------------------------------
+
+def _shape(**kw):
+    s = B.make_shape(synth.SHAPE_TINY)
+    for k, v in kw.items():
+        setattr(s, k, v)
+    return s
+
+
+FAKE = 1 << 20  # never dereferenced: each call fails validation first
+
+
+def _layer(shape=None, **ptrs):
+    f = dict(qkv_codes=FAKE, qkv_scales=FAKE, o_codes=FAKE, o_scales=FAKE, gu_codes=FAKE,
+             gu_scales=FAKE, down_codes=FAKE, down_scales=FAKE)
+    f.update(ptrs)
+    return B.i4d_layer(shape or _shape(), **f)
+
+
+def _cache(**kw):
+    c = B.i4d_kv_cache(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 64, 256, None)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def _status(fn):
+    with pytest.raises(B.I4DError) as e:
+        fn()
+    return e.value.status
+
+
+def test_shape_validation():
+    assert _status(lambda: B.i4d_workspace_bytes(_shape(head_dim=96, hadamard_block=96), 1, 16)) == -3
+    assert _status(lambda: B.i4d_workspace_bytes(_shape(hadamard_block=32), 1, 16)) == -3
+    assert _status(lambda: B.i4d_workspace_bytes(_shape(group=64), 1, 16)) == -3
+    assert _status(lambda: B.i4d_workspace_bytes(_shape(n_kv_heads=3), 1, 16)) == -2
+    assert _status(lambda: B.i4d_workspace_bytes(_shape(d_model=200), 1, 16)) == -2
+    assert _status(lambda: B.i4d_workspace_bytes(_shape(n_q_heads=24, n_kv_heads=2), 1, 16)) == -3
+    assert _status(lambda: B.i4d_workspace_bytes(_shape(), 0, 16)) == -6
+    assert _status(lambda: B.i4d_workspace_bytes(_shape(), 33, 16)) == -6
+    assert _status(lambda: B.i4d_workspace_bytes(_shape(), 1, 0)) == -6
+    assert _status(lambda: B.i4d_workspace_bytes(_shape(), 1, 16, 257)) == -6
+    assert B.i4d_workspace_bytes(_shape(), 32, 4096) > 0
+
+
+def test_device_entry_points_reject_bad_arguments_before_launch():
+    lay, ws = _layer(), FAKE
+    big = 1 << 40
+    # NULL layer / pointers
+    assert B.lib().i4d_decode_block_step(None, ctypes.byref(_cache()), FAKE, FAKE + 16, FAKE, 1, 16, 0,
+                                         ws, big, None, None) == -1
+    assert _status(lambda: B.i4d_decode_block_step(_layer(o_codes=0), _cache(), FAKE, FAKE + 16, FAKE, 1,
+                                                   16, 0, ws, big)) == -1
+    # misaligned pointers
+    assert _status(lambda: B.i4d_decode_block_step(_layer(gu_scales=FAKE + 2), _cache(), FAKE, FAKE + 16,
+                                                   FAKE, 1, 16, 0, ws, big)) == -4
+    assert _status(lambda: B.i4d_decode_block_step(lay, _cache(), FAKE + 8, FAKE + 16, FAKE, 1, 16, 0,
+                                                   ws, big)) == -4
+    # rows out of range / more rows than the cache
+    assert _status(lambda: B.i4d_decode_block_step(lay, _cache(), FAKE, FAKE + 16, FAKE, 0, 16, 0, ws, big)) == -6
+    assert _status(lambda: B.i4d_decode_block_step(lay, _cache(), FAKE, FAKE + 16, FAKE, 5, 16, 0, ws, big)) == -2
+    # cache/layer mismatch, bad capacity
+    assert _status(lambda: B.i4d_decode_block_step(lay, _cache(head_dim=128), FAKE, FAKE + 16, FAKE, 1, 16,
+                                                   0, ws, big)) == -2
+    assert _status(lambda: B.i4d_decode_block_step(lay, _cache(total_capacity=100), FAKE, FAKE + 16, FAKE,
+                                                   1, 16, 0, ws, big)) == -2
+    # max_ctx_len beyond capacity, aliasing, workspace too small
+    assert _status(lambda: B.i4d_decode_block_step(lay, _cache(), FAKE, FAKE + 16, FAKE, 1, 257, 0, ws,
+                                                   big)) == -6
+    assert _status(lambda: B.i4d_decode_block_step(lay, _cache(), FAKE, FAKE, FAKE, 1, 16, 0, ws, big)) == -6
+    assert _status(lambda: B.i4d_decode_block_step(lay, _cache(), FAKE, FAKE + 16, FAKE, 1, 16, 0, ws, 64)) == -5
+    # stage entry points
+    assert _status(lambda: B.i4d_attn_qkv(lay, None, FAKE, 1, FAKE, FAKE, FAKE, 0)) == -1
+    assert _status(lambda: B.i4d_ffn_gate_up(lay, FAKE, 40, FAKE, 0)) == -6
+    assert _status(lambda: B.i4d_ffn_down(_layer(shape=_shape(head_dim=80)), FAKE, FAKE, 1, FAKE, 0)) == -3
+    assert _status(lambda: B.i4d_attention(_cache(), _shape(), FAKE, FAKE, 1, 16, 0, ws, 16, None, FAKE, 0)) == -5
+    assert _status(lambda: B.i4d_kv_append(_cache(), FAKE, FAKE, None, FAKE, 9, 0)) == -2
+    assert _status(lambda: B.i4d_kv_append(_cache(), FAKE, FAKE, None, FAKE, -1, 0)) == -6
+    assert _status(lambda: B.i4d_lm_head_argmax(FAKE, 100, 128, FAKE, 1, 1e-5, None, FAKE, ws, big, 0)) == -2
+    assert _status(lambda: B.i4d_lm_head_argmax(FAKE, 128, 128, FAKE, 1, 0.0, None, FAKE, ws, big, 0)) == -6
+    assert "epsilon" in B.i4d_last_error() or "rms_eps" in B.i4d_last_error()
+
+
+def test_pack_argument_errors():
+    W = np.zeros((16, 100), np.float32)
+    assert _status(lambda: B.i4d_pack_weights(B.I4D_PROJ_PLAIN, W)) == -2
+    W = np.zeros((20, 128), np.float32)
+    assert _status(lambda: B.i4d_pack_weights(B.I4D_PROJ_PLAIN, W)) == -2
+    W = np.zeros((64, 128), np.float32)
+    assert _status(lambda: B.i4d_pack_weights(B.I4D_PROJ_GATE_UP, W)) == -1
+    assert _status(lambda: B.i4d_pack_weights(B.I4D_PROJ_QKV, W, head_dim=96)) == -3
+    assert _status(lambda: B.i4d_pack_weights(B.I4D_PROJ_PLAIN, W, gamma=np.ones(128, np.float32))) == -6
+
+
+# ---------------------------------------------------------------------------
+# packer: bit-exact codes and scales
+# ---------------------------------------------------------------------------
+
+def _check_pack(kind, W0, W1, gamma, hd=0):
+    codes, scales = B.i4d_pack_weights(kind, W0, W1, gamma, hd)
+    q, s = B.i4d_unpack_weights(kind, codes, scales, W0.shape[0], W0.shape[1], hd)
+    rq, rs = O.quantize_weight(W0, gamma)
+    if kind == B.I4D_PROJ_GATE_UP:
+        rq2, rs2 = O.quantize_weight(W1, gamma)
+        rq, rs = np.concatenate([rq, rq2]), np.concatenate([rs, rs2])
+    np.testing.assert_array_equal(q, rq)
+    np.testing.assert_array_equal(s, rs.view(np.uint16))
+    return codes, scales
+
+
+@pytest.mark.parametrize("shape", [synth.SHAPE_TINY, synth.SHAPE_1B], ids=["tiny", "1b"])
+def test_packer_bit_exact_full_layer(shape):
+    lw = synth.make_layer(shape, 5 if shape is synth.SHAPE_TINY else 0)
+    _check_pack(B.I4D_PROJ_QKV, lw.w_qkv, None, lw.gamma_attn, shape.head_dim)
+    _check_pack(B.I4D_PROJ_PLAIN, lw.w_o, None, None)
+    _check_pack(B.I4D_PROJ_GATE_UP, lw.w_gate, lw.w_up, lw.gamma_ffn)
+    _check_pack(B.I4D_PROJ_PLAIN, lw.w_down, None, None)
+
+
+def test_packer_bit_exact_sampled_8b_rows():
+    # 8B-shape distributions on a row sample (every K of the 8B layer)
+    rng = np.random.default_rng(1)
+    for K in (4096, 14336):
+        W = (rng.standard_normal((256, K)) * 0.02).astype(np.float32)
+        g = rng.uniform(0.5, 1.5, K).astype(np.float32)
+        _check_pack(B.I4D_PROJ_PLAIN, W, None, None)
+        _check_pack(B.I4D_PROJ_GATE_UP, W[:128], W[128:], g)
+    W = (rng.standard_normal((6 * 128, 4096)) * 0.02).astype(np.float32)
+    _check_pack(B.I4D_PROJ_QKV, W, None, rng.uniform(0.5, 1.5, 4096).astype(np.float32), 128)
+
+
+def test_packer_edge_values():
+    # ties, zero groups, scale overflow (saturates), scale underflow (s = 0), tiny and huge values
+    W = np.zeros((32, 1024), np.float32)
+    W[0, :7] = [2.5, 3.5, -2.5, 0.5, 7.0, -1.5, -0.5]       # s = 1 exactly, ties to even
+    W[1, 128:131] = [0.7, -0.35, 0.05]                       # fp16-rounded scale example
+    W[2, 256] = 1e6                                          # absmax/7 > 65504 -> scale saturates
+    W[3, 384] = 1e-9                                         # scale rounds to 0 -> codes 0
+    W[4, 512:640] = np.linspace(-3e-5, 3e-5, 128)            # subnormal fp16 scale
+    W[5, 640:768] = -np.float32(3.0)                         # all equal negative
+    rng = np.random.default_rng(3)
+    W[8:] = (rng.standard_normal((24, 1024)) * np.exp(rng.uniform(-8, 8, (24, 1))).astype(np.float32))
+    _check_pack(B.I4D_PROJ_PLAIN, W, None, None)
+    q, s = O.quantize_weight(W)
+    assert s[2, 2] == np.float16(65504) and s[3, 3] == 0 and np.all(q[3] == 0)
+
+
+def test_packed_bytes_follow_documented_layout():
+    """Place one code per group and find its nibble where the layout says."""
+    N, K = 32, 256
+    W = np.zeros((N, K), np.float32)
+    rng = np.random.default_rng(4)
+    pos = {}
+    for n in range(N):
+        for g in range(K // 128):
+            k = 128 * g + int(rng.integers(0, 128))
+            W[n, k] = 7.0 * (n + 1)                           # code +7 -> nibble 15, others nibble 8
+            pos[(n, g)] = k
+    codes, scales = B.i4d_pack_weights(B.I4D_PROJ_PLAIN, W)
+    G = K // 128
+    for (n, g), k in pos.items():
+        t, r, kk = n // 16, n % 16, k % 128
+        kb, j, e = kk // 32, (kk % 32) // 8, kk % 8
+        slot = 4 * (e & 1) + (e >> 1)                         # nibble slots hold e = 0,2,4,6,1,3,5,7
+        byte = ((t * G + g) * 64 + 16 * j + r) * 16 + kb * 4 + slot // 2
+        nib = (codes[byte] >> 4) if slot & 1 else (codes[byte] & 15)
+        assert nib == 15
+        # scale layout [strip][g/8][row][g%8]
+        g8 = (G + 7) // 8
+        assert scales[((t * g8 + g // 8) * 16 + r) * 8 + g % 8] == np.float16(n + 1).view(np.uint16)
+    # every other nibble encodes code 0
+    assert np.count_nonzero(codes == 0x88) == codes.size - len(pos)
+
+
+def test_qkv_and_gate_up_strip_interleave():
+    hd, N, K = 64, 3 * 64, 128
+    W = np.zeros((N, K), np.float32)
+    for n in range(N):
+        W[n, 0] = 7.0 * (n + 1)
+    codes, scales = B.i4d_pack_weights(B.I4D_PROJ_QKV, W, None, None, hd)
+    sc = scales.view(np.float16).reshape(N // 16, 1, 16, 8)[:, 0, :, 0]
+    for t in range(N // 16):
+        head, sp = t // (hd // 16), t % (hd // 16)
+        want = [head * hd + 8 * sp + i for i in range(8)] + [head * hd + hd // 2 + 8 * sp + i for i in range(8)]
+        np.testing.assert_array_equal(sc[t], np.array(want, np.float32) + 1)
+    F = 32
+    Wg = np.zeros((F, K), np.float32)
+    Wu = np.zeros((F, K), np.float32)
+    Wg[:, 0] = 7.0 * (np.arange(F) + 1)
+    Wu[:, 0] = -7.0 * (np.arange(F) + 101)
+    codes, scales = B.i4d_pack_weights(B.I4D_PROJ_GATE_UP, Wg, Wu)
+    sc = scales.view(np.float16).reshape(2 * F // 16, 1, 16, 8)[:, 0, :, 0]
+    for t in range(2 * F // 16):
+        np.testing.assert_array_equal(sc[t, :8], np.arange(8 * t, 8 * t + 8) + 1)
+        np.testing.assert_array_equal(sc[t, 8:], np.arange(8 * t, 8 * t + 8) + 101)
+
+
+def test_lm_head_pack_matches_oracle_bf16():
+    rng = np.random.default_rng(6)
+    W = (rng.standard_normal((64, 256)) * 0.02).astype(np.float32)
+    g = rng.uniform(0.5, 1.5, 256).astype(np.float32)
+    out = B.i4d_pack_lm_head(W, g)
+    ref = O.lm_head_weight_bf16(W, g)
+    np.testing.assert_array_equal(synth.bf16_bits_to_f32(out).astype(np.float64), ref)
+
+
+# ---------------------------------------------------------------------------
+# KV cache layout decoder
+# ---------------------------------------------------------------------------
+
+def test_kv_unpack_reads_documented_layout():
+    """Build a cache by hand from the documented layout; the library decodes it."""
+    nkv, hd = 2, 128
+    caps = [64, 32]
+    rb = np.array([0, 64, 96], np.int64)
+    total = 96
+    rng = np.random.default_rng(8)
+    codes_k = rng.integers(-8, 8, (total * nkv, hd)).astype(np.int8)   # per slot, logical channels
+    codes_v = rng.integers(-8, 8, (total * nkv, hd)).astype(np.int8)
+    sk = rng.integers(0, 1 << 15, total * nkv).astype(np.uint16)
+    sv = rng.integers(0, 1 << 15, total * nkv).astype(np.uint16)
+    kbuf = np.zeros(total * nkv * hd // 2, np.uint8)
+    vbuf = np.zeros(total * nkv * hd // 8, np.uint32)
+    for slot in range(total * nkv):
+        for c in range(hd):
+            kb, jj, e = c // 32, (c % 32) // 8, c % 8
+            ns = 4 * (e & 1) + (e >> 1)
+            byte = slot * hd // 2 + jj * 16 + kb * 4 + ns // 2
+            kbuf[byte] |= (int(codes_k[slot, c]) + 8) << (4 * (ns & 1))
+            w = slot % 32
+            jv, ev = (w // 4, w % 4) if w < 16 else ((w - 16) // 4, 4 + (w - 16) % 4)
+            nsv = 4 * (ev & 1) + (ev >> 1)
+            dw = (slot // 32) * 4 * hd + jv * hd + (c % 16) * (hd // 16) + c // 16
+            vbuf[dw] |= np.uint32((int(codes_v[slot, c]) + 8) << (4 * nsv))
+    hc = B.i4d_kv_cache(kbuf.ctypes.data, vbuf.ctypes.data, sk.ctypes.data, sv.ctypes.data, rb.ctypes.data,
+                        2, nkv, hd, total, None)
+    for row, cap in enumerate(caps):
+        k, v, ks, vs = B.i4d_kv_unpack_host(hc, rb, row, 0, cap)
+        for j in range(nkv):
+            slots = rb[row] * nkv + j * cap + np.arange(cap)
+            np.testing.assert_array_equal(k[:, j], codes_k[slots])
+            np.testing.assert_array_equal(v[:, j], codes_v[slots])
+            np.testing.assert_array_equal(ks[:, j], sk[slots])
+            np.testing.assert_array_equal(vs[:, j], sv[slots])

@@ -1,0 +1,295 @@
+"""GPU parity of each stage of the decode step against the CPU oracle.
+
+Every test calls the HIP library through the C ABI on seeded synthetic inputs
+and compares element by element with the oracle on the same inputs:
+
+* kv_append: codes and fp16 scales bit-exact (the encoding is exact);
+* attention: max |gpu - oracle| / rms(oracle) <= 2e-2 (the stated bound for
+  the attention output);
+* projections and the block: relative RMS error <= 1e-2 (the stated bound
+  for block outputs), on the oracle's fp64 result on the same INT4 grid.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+from int4_quantized_decode_amd import synth
+from tests.gpu_helpers import (bf16_values, norm_maxabs, oracle_cache_from_tokens, random_bf16, rel_rms,
+                               say)
+
+pytestmark = pytest.mark.gpu
+
+REL_TOL = 1e-2
+ATT_TOL = 2e-2
+
+
+@pytest.fixture(scope="module")
+def gpu():
+    import torch
+    from int4_quantized_decode_amd import binding as B
+    from int4_quantized_decode_amd import device as D
+    assert torch.cuda.is_available()
+    B.lib()
+    return torch, B, D
+
+
+# ---------------------------------------------------------------------------
+# kv_append: bit-exact encoding
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("hd", [64, 128])
+def test_kv_append_bit_exact(gpu, hd):
+    torch, B, D = gpu
+    shape = synth.LayerShape(256, 4, 2, hd, 512)
+    rng = np.random.default_rng(hd)
+    lengths = [5, 64, 37, 1]
+    k_rows = [random_bf16(rng, (L, 2, hd), 1.0, hd // 16) for L in lengths]
+    v_rows = [random_bf16(rng, (L, 2, hd), 1.0, hd // 16) for L in lengths]
+    # special vectors: zero, constant, tiny (subnormal fp16 scale), huge (saturating scale)
+    k_rows[1][0] = 0
+    k_rows[1][1] = synth.f32_to_bf16_bits(np.full((2, hd), -3.0, np.float32))
+    k_rows[1][2] = synth.f32_to_bf16_bits(rng.standard_normal((2, hd)).astype(np.float32) * np.float32(1e-7))
+    v_rows[1][3] = synth.f32_to_bf16_bits(rng.standard_normal((2, hd)).astype(np.float32) * np.float32(1e6))
+    v_rows[1][4] = synth.f32_to_bf16_bits(rng.standard_normal((2, hd)).astype(np.float32) * np.float32(1e-9))
+    cache = D.DeviceCache(shape, lengths)
+    say(f"kv_append hd={hd} lengths={lengths}")
+    cache.prefill(synth.CachePrefill(k_rows, v_rows))
+    torch.cuda.synchronize()
+    assert cache.errors() == 0
+    for r, L in enumerate(lengths):
+        k, v, ks, vs = cache.read_codes(r, 0, L)
+        rk, rks = O.quantize_kv(synth.bf16_bits_to_f32(k_rows[r]))
+        rv, rvs = O.quantize_kv(synth.bf16_bits_to_f32(v_rows[r]))
+        np.testing.assert_array_equal(k, rk)
+        np.testing.assert_array_equal(ks, rks.view(np.uint16))
+        np.testing.assert_array_equal(v, rv)
+        np.testing.assert_array_equal(vs, rvs.view(np.uint16))
+
+
+def test_kv_append_rejects_out_of_range_positions(gpu):
+    torch, B, D = gpu
+    shape = synth.SHAPE_TINY
+    cache = D.DeviceCache(shape, [32, 32])
+    k = D.to_device_u16(np.zeros((3, 2, 64), np.uint16))
+    rows = torch.tensor([0, 1, 5], dtype=torch.int32, device="cuda")      # row 5 does not exist
+    pos = torch.tensor([40, 3, 0], dtype=torch.int32, device="cuda")      # 40 >= capacity 32
+    say("kv_append invalid device positions")
+    B.i4d_kv_append(cache.struct, k, k, rows, pos, 3)
+    torch.cuda.synchronize()
+    assert cache.errors() & B.I4D_DEVERR_APPEND_POS
+    kk, vv, ks, vs = cache.read_codes(0, 0, 32)
+    assert np.all(ks == 0)            # the invalid entry of row 0 was skipped
+    _, _, ks1, _ = cache.read_codes(1, 3, 4)
+    assert np.all(ks1 == 0)           # zero vector -> scale 0 written at the valid slot
+
+
+# ---------------------------------------------------------------------------
+# attention
+# ---------------------------------------------------------------------------
+
+ATTN_CASES = [
+    # hd, n_q, n_kv, lengths, num_splits
+    (64, 8, 2, [1, 2, 31, 32, 33, 100], 0),
+    (128, 8, 2, [1, 2, 31, 32, 33, 517], 0),
+    (128, 16, 2, [517, 64, 3], 0),          # G = 8
+    (128, 8, 2, [300, 45], 1),
+    (128, 8, 2, [300, 45], 3),
+    (64, 8, 2, [300, 45], 16),
+    (128, 8, 2, [70, 45], 64),              # more splits than blocks: empty splits
+    (128, 32, 8, [2048], 0),                # 8B head layout
+]
+
+
+@pytest.mark.parametrize("hd,n_q,n_kv,lengths,S", ATTN_CASES)
+def test_attention_parity(gpu, hd, n_q, n_kv, lengths, S):
+    torch, B, D = gpu
+    shape = synth.LayerShape(n_q * hd, n_q, n_kv, hd, 512)
+    rng = np.random.default_rng(sum(lengths) + S)
+    M = len(lengths)
+    k_rows = [random_bf16(rng, (L, n_kv, hd), 1.0, hd // 16) for L in lengths]
+    v_rows = [random_bf16(rng, (L, n_kv, hd), 1.0, hd // 16) for L in lengths]
+    q = (rng.standard_normal((M, n_q, hd)) * 1.3).astype(np.float32)
+    cache = D.DeviceCache(shape, lengths)
+    cache.prefill(synth.CachePrefill(k_rows, v_rows))
+    maxL = max(lengths)
+    cshape = B.make_shape(shape)
+    nbytes = B.i4d_attention_workspace_bytes(cshape, M, maxL, S)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    qd = torch.from_numpy(q).cuda()
+    ctx = torch.tensor(lengths, dtype=torch.int32, device="cuda")
+    out32 = torch.empty((M, n_q * hd), dtype=torch.float32, device="cuda")
+    out16 = torch.empty((M, n_q * hd), dtype=torch.int16, device="cuda")
+    say(f"attention hd={hd} n_q={n_q} n_kv={n_kv} lengths={lengths} S={S}")
+    B.i4d_attention(cache.struct, cshape, qd, ctx, M, maxL, S, ws, nbytes, out32, out16)
+    torch.cuda.synchronize()
+    assert cache.errors() == 0
+    ref = O.attention_stage(shape, oracle_cache_from_tokens(shape, k_rows, v_rows), q.astype(np.float64), lengths)
+    got = out32.cpu().numpy()
+    err = norm_maxabs(got, ref)
+    say(f"  normalised max-abs error {err:.3e}")
+    assert err <= ATT_TOL
+    # the bf16 copy is the rounded fp32 output
+    np.testing.assert_array_equal(D.to_host_u16(out16), synth.f32_to_bf16_bits(got))
+
+
+# ---------------------------------------------------------------------------
+# projections
+# ---------------------------------------------------------------------------
+
+SHAPES = {"tiny": synth.SHAPE_TINY, "small128": synth.SHAPE_SMALL128}
+
+
+@pytest.fixture(scope="module")
+def layers(gpu):
+    torch, B, D = gpu
+    out = {}
+    for name, shape in SHAPES.items():
+        lw = synth.make_layer(shape, 77)
+        ql = O.quantize_layer(lw)
+        dense = {n: O.dense(getattr(ql, n)) for n in ("qkv", "o", "gate", "up", "down")}
+        out[name] = (shape, D.DeviceLayer(shape, lw), dense)
+    return out
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+@pytest.mark.parametrize("M", [1, 2, 5, 16, 17, 32])
+def test_projection_stages(gpu, layers, name, M):
+    torch, B, D = gpu
+    shape, layer, W = layers[name]
+    rng = np.random.default_rng(M)
+    d, F, nq, nkv, hd = shape.d_model, shape.d_ffn, shape.n_q_heads, shape.n_kv_heads, shape.head_dim
+    lengths = rng.integers(1, 5000, M).astype(np.int32)
+    x = random_bf16(rng, (M, d))
+    attn = random_bf16(rng, (M, nq * hd), 0.5)
+    hb = random_bf16(rng, (M, d))
+    a = random_bf16(rng, (M, F), 0.3)
+    hf = rng.standard_normal((M, d)).astype(np.float32)
+    dev = lambda u: D.to_device_u16(u)
+    ctx = torch.from_numpy(lengths).cuda()
+    q = torch.empty((M, nq, hd), dtype=torch.float32, device="cuda")
+    k = torch.empty((M, nkv, hd), dtype=torch.int16, device="cuda")
+    v = torch.empty_like(k)
+    h32 = torch.empty((M, d), dtype=torch.float32, device="cuda")
+    h16 = torch.empty((M, d), dtype=torch.int16, device="cuda")
+    act = torch.empty((M, F), dtype=torch.int16, device="cuda")
+    out = torch.empty((M, d), dtype=torch.int16, device="cuda")
+    say(f"projections {name} M={M}")
+    B.i4d_attn_qkv(layer.struct, dev(x), ctx, M, q, k, v)
+    B.i4d_attn_out_proj(layer.struct, dev(attn), dev(x), M, h32, h16)
+    B.i4d_ffn_gate_up(layer.struct, dev(hb), M, act)
+    B.i4d_ffn_down(layer.struct, dev(a), torch.from_numpy(hf).cuda(), M, out)
+    torch.cuda.synchronize()
+
+    rq, rk, rv = O.qkv_stage(shape, W["qkv"], bf16_values(x), lengths)
+    errs = {
+        "q": rel_rms(q.cpu().numpy(), rq),
+        "k": rel_rms(D.bf16_tensor_to_f32(k), rk),
+        "v": rel_rms(D.bf16_tensor_to_f32(v), rv),
+        "h": rel_rms(h32.cpu().numpy(), O.o_stage(W["o"], bf16_values(x), bf16_values(attn))),
+        "a": rel_rms(D.bf16_tensor_to_f32(act), O.gate_up_stage(shape, W["gate"], W["up"], bf16_values(hb))),
+        "out": rel_rms(D.bf16_tensor_to_f32(out),
+                       O.down_stage(W["down"], hf.astype(np.float64), bf16_values(a))),
+    }
+    say("  rel-RMS " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    for key, e in errs.items():
+        assert e <= REL_TOL, (key, e)
+    # the bf16 copy of h is the rounding of the fp32 h
+    np.testing.assert_array_equal(D.to_host_u16(h16), synth.f32_to_bf16_bits(h32.cpu().numpy()))
+
+
+# ---------------------------------------------------------------------------
+# whole block, small shapes
+# ---------------------------------------------------------------------------
+
+def run_block(gpu, shape, seed, lengths, num_splits=0, dense_cache=None, lw=None):
+    torch, B, D = gpu
+    lengths = np.asarray(lengths, np.int32)
+    M = len(lengths)
+    lw = lw or synth.make_layer(shape, seed)
+    pre = synth.make_cache_prefill(shape, lengths, seed)
+    xb = synth.make_x(shape, M, seed)
+    layer = D.DeviceLayer(shape, lw)
+    cache = D.DeviceCache(shape, lengths)
+    cache.prefill(pre)
+    maxL = int(lengths.max())
+    ws = D.Workspace(shape, M, maxL, num_splits)
+    x_in = D.to_device_u16(xb)
+    x_out = torch.empty_like(x_in)
+    ctx = torch.from_numpy(lengths).cuda()
+    attn = torch.empty((M, shape.n_q_heads * shape.head_dim), dtype=torch.float32, device="cuda")
+    say(f"block d={shape.d_model} hd={shape.head_dim} M={M} maxL={maxL} S={num_splits}")
+    B.i4d_decode_block_step(layer.struct, cache.struct, x_in, x_out, ctx, M, maxL, num_splits, ws.buf,
+                            ws.nbytes, attn)
+    torch.cuda.synchronize()
+    ocache = O.build_cache(shape, lengths, pre)
+    ref = O.decode_block(shape, O.quantize_layer(lw), ocache, xb, lengths, dense_cache)
+    res = dict(out=D.bf16_tensor_to_f32(x_out), attn=attn.cpu().numpy(), ref=ref, cache=cache,
+               layer=layer, x_in=x_in, x_out=x_out, ws=ws, ctx=ctx, lengths=lengths)
+    return res
+
+
+def check_block(res, label=""):
+    ref = res["ref"]
+    e_out = rel_rms(res["out"], ref.out)
+    e_att = norm_maxabs(res["attn"], ref.attn)
+    # codes appended for the new token (differences only if k/v bf16 rounding differs)
+    mism = 0
+    for r, L in enumerate(res["lengths"]):
+        k, v, ks, vs = res["cache"].read_codes(r, int(L) - 1, int(L))
+        mism += int(np.sum(k[0] != ref.k_codes_new[r]) + np.sum(v[0] != ref.v_codes_new[r]))
+    say(f"  {label} out rel-RMS {e_out:.3e}  attn max-abs/rms {e_att:.3e}  new-token code mismatches {mism}")
+    assert res["cache"].errors() == 0
+    assert e_out <= REL_TOL
+    assert e_att <= ATT_TOL
+    return e_out, e_att, mism
+
+
+@pytest.mark.parametrize("shape,lengths", [
+    (synth.SHAPE_TINY, [1, 2, 5, 67]),
+    (synth.SHAPE_SMALL128, [1, 33, 300]),
+    (synth.SHAPE_SMALL128, [4096] * 2 + [1000] * 15),   # M = 17: second MFMA tile
+])
+def test_block_small(gpu, shape, lengths):
+    check_block(run_block(gpu, shape, 11, lengths))
+
+
+def test_block_deterministic(gpu):
+    torch, B, D = gpu
+    res = run_block(gpu, synth.SHAPE_SMALL128, 12, [100, 700, 33])
+    first = res["x_out"].clone()
+    a = res
+    B.i4d_decode_block_step(a["layer"].struct, a["cache"].struct, a["x_in"], a["x_out"], a["ctx"], 3,
+                            int(a["lengths"].max()), 0, a["ws"].buf, a["ws"].nbytes, None)
+    torch.cuda.synchronize()
+    assert torch.equal(first, a["x_out"])
+
+
+# ---------------------------------------------------------------------------
+# LM head
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M", [1, 3, 17])
+def test_lm_head_parity(gpu, M):
+    torch, B, D = gpu
+    V, d = 2048, 512
+    rng = np.random.default_rng(M)
+    W = (rng.standard_normal((V, d)) * 0.02).astype(np.float32)
+    g = rng.uniform(0.5, 1.5, d).astype(np.float32)
+    h = random_bf16(rng, (M, d))
+    w16 = B.i4d_pack_lm_head(W, g)
+    nbytes = B.i4d_lm_head_workspace_bytes(V, M)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    logits = torch.empty((M, V), dtype=torch.float32, device="cuda")
+    tok = torch.empty(M, dtype=torch.int32, device="cuda")
+    say(f"lm head V={V} d={d} M={M}")
+    B.i4d_lm_head_argmax(D.to_device_u16(w16), V, d, D.to_device_u16(h), M, 1e-5, logits, tok, ws, nbytes)
+    torch.cuda.synchronize()
+    rl, rt = O.lm_head_argmax(bf16_values(h), O.lm_head_weight_bf16(W, g), 1e-5)
+    gl = logits.cpu().numpy()
+    assert rel_rms(gl, rl) <= 1e-4
+    gt = tok.cpu().numpy()
+    for m in range(M):
+        if gt[m] != rt[m]:
+            # only a near-tie may differ: the two logits agree within the logit error
+            assert abs(rl[m, gt[m]] - rl[m, rt[m]]) <= 4 * np.abs(gl[m] - rl[m]).max()
+        assert gt[m] == int(np.argmax(gl[m]))   # argmax of the GPU's own logits, lowest index on ties
