@@ -1,0 +1,208 @@
+"""Benchmark of the INT4 decode block step on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--M m]
+
+One step = one decode_block_step (QKV + rho1 + RoPE, KV append through the
+Hadamard rotation, split-KV GQA attention + combine + inverse rotation, O +
+residual, gate/up + SwiGLU, down + residual) for one batch of decode rows.
+Inputs are resident in HBM before timing.  Steps rotate over C independent
+copies of the layer (same bytes at different addresses, each with its own
+KV cache) so that the 256 MB Infinity Cache cannot serve the weights from
+one step to the next; the K timed steps are one captured HIP graph replayed
+between two events on the launch stream.
+
+Printed: one JSON line with the time per step, the achieved HBM bandwidth
+(algorithmic bytes / time), the roofline entry of the dominant kernel (the
+gate/up projection, timed live with HIP events over back-to-back launches
+of that kernel) and the CPU oracle timed on a bounded sample.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+
+
+def algorithmic_bytes(shape, lengths):
+    """INT4 codes (0.5 B/weight) + fp16 group scales + INT4 KV codes and
+    per-token-per-head fp16 scales read by one step."""
+    d, F, hd, nq, nkv = shape.d_model, shape.d_ffn, shape.head_dim, shape.n_q_heads, shape.n_kv_heads
+    weights = (shape.n_qkv * d + d * nq * hd + 2 * F * d + d * F)
+    w_bytes = weights // 2 + (weights // 128) * 2
+    kv_bytes = int(np.sum(lengths)) * nkv * 2 * (hd // 2 + 2)
+    return w_bytes + kv_bytes, w_bytes, kv_bytes
+
+
+def gate_up_bytes(shape):
+    n = 2 * shape.d_ffn * shape.d_model
+    return n // 2 + (n // 128) * 2
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--workload", default="8b_m1_ctx4096")
+    ap.add_argument("--M", type=int, default=0, help="override the batch (70B shape sweep)")
+    ap.add_argument("--copies", type=int, default=8)
+    ap.add_argument("--splits", type=int, default=-1)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-steps", type=int, default=3)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on one GPU only; --gpus must be 1 (the multi-GPU layout is "
+              "described in DESIGN.md, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from int4_quantized_decode_amd import binding as B
+    from int4_quantized_decode_amd import device as D
+    from int4_quantized_decode_amd import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    B.lib()
+    wl = synth.WORKLOADS[args.workload]
+    shape = wl.shape
+    M = args.M or wl.M
+    lengths = synth.make_lengths(wl, M)
+    maxL = int(lengths.max())
+    splits = wl.num_splits if args.splits < 0 else args.splits
+    C = args.copies
+
+    t0 = time.time()
+    lw = synth.make_layer(shape, wl.seed)
+    pre = synth.make_cache_prefill(shape, lengths, wl.seed)
+    xb = synth.make_x(shape, M, wl.seed)
+    base_layer = D.DeviceLayer(shape, lw)
+    base_cache = D.DeviceCache(shape, lengths)
+    base_cache.prefill(pre)
+    layers = [base_layer] + [base_layer.clone() for _ in range(C - 1)]
+    caches = [base_cache]
+    for _ in range(C - 1):
+        c = D.DeviceCache(shape, lengths)
+        for name in ("k_codes", "v_codes", "k_scales", "v_scales"):
+            getattr(c, name).copy_(getattr(base_cache, name))
+        caches.append(c)
+    ws = D.Workspace(shape, M, maxL, splits)
+    x_in = D.to_device_u16(xb)
+    x_out = torch.empty_like(x_in)
+    ctx = torch.from_numpy(lengths).cuda()
+    setup_s = time.time() - t0
+
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        B.i4d_decode_block_step(layers[i % C].struct, caches[i % C].struct, x_in, x_out, ctx, M, maxL,
+                                splits, ws.buf, ws.nbytes, None)
+
+    # eager check that the step runs, then graphs
+    step(0)
+    torch.cuda.synchronize()
+
+    def capture(n, fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                fn(i)
+        return g
+
+    g_warm = capture(max(args.warmup, 1), step)
+    g_main = capture(args.steps, step)
+    g_warm.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    g_main.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = e0.elapsed_time(e1)
+    ms_step = ms_total / args.steps
+    us_step = ms_step * 1e3
+    total_b, w_b, kv_b = algorithmic_bytes(shape, lengths)
+    gbps = total_b / (us_step * 1e-6) / 1e9
+
+    # dominant kernel: gate/up projection, back-to-back launches over the copies
+    a_buf = torch.empty((M, shape.d_ffn), dtype=torch.int16, device="cuda")
+    hb = ws.view("h_bf16", torch.int16, M * shape.d_model)
+    R = 8 * C
+
+    def gu(i):
+        B.i4d_ffn_gate_up(layers[i % C].struct, hb, M, a_buf)
+
+    g_gu = capture(R, gu)
+    g_gu.replay()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    g_gu.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    gu_us = e0.elapsed_time(e1) * 1e3 / R
+    gu_gbps = gate_up_bytes(shape) / (gu_us * 1e-6) / 1e9
+
+    result = {
+        "metric": "us per INT4 decode block step (+ achieved HBM GB/s)",
+        "value": round(us_step, 3),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": max(args.warmup, 1),
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4 x bf16/fp16 -> f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "d_model": shape.d_model, "n_q_heads": shape.n_q_heads,
+                   "n_kv_heads": shape.n_kv_heads, "head_dim": shape.head_dim, "d_ffn": shape.d_ffn,
+                   "M": M, "ctx_total": int(lengths.sum()), "ctx_max": maxL, "num_splits": splits,
+                   "layer_copies": C, "timing": "hip graph of K steps, events on the launch stream"},
+        "hbm_GBps": round(gbps, 1),
+        "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "bytes_per_step": {"total": total_b, "weights": w_b, "kv": kv_b},
+        "roofline": {"kernel": "gate/up + SwiGLU projection", "bound": "hbm",
+                     "achieved": round(gu_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gu_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "avg_launch_us": round(gu_us, 3), "bytes_per_launch": gate_up_bytes(shape)},
+        "setup_s": round(setup_s, 1),
+    }
+
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(shape, lw, lengths, pre, xb, args.cpu_steps, args.workload)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(shape, lw, lengths, pre, xb, n_steps, workload):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    ql = O.quantize_layer(lw)
+    times = []
+    for _ in range(n_steps):
+        cache = O.build_cache(shape, lengths, pre)
+        t = time.time()
+        O.decode_block(shape, ql, cache, xb, lengths)
+        times.append(time.time() - t)
+    us = float(np.median(times)) * 1e6
+    return {"value": round(us, 1), "unit": "us/step", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n_steps} block steps of {workload} (median; fp64 numpy, weights dequantized "
+                      f"each step)"}
+
+
+if __name__ == "__main__":
+    main()

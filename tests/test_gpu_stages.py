@@ -201,14 +201,21 @@ def test_projection_stages(gpu, layers, name, M):
 # whole block, small shapes
 # ---------------------------------------------------------------------------
 
-def run_block(gpu, shape, seed, lengths, num_splits=0, dense_cache=None, lw=None):
+def run_block(gpu, shape, seed, lengths, num_splits=0, dense_cache=None, lw=None, memo=None):
+    """One decode step on the GPU and in the oracle.  ``memo`` (a dict) keeps
+    the packed device layer and the oracle's encoded layer between calls that
+    share the weights."""
     torch, B, D = gpu
     lengths = np.asarray(lengths, np.int32)
     M = len(lengths)
     lw = lw or synth.make_layer(shape, seed)
+    memo = {} if memo is None else memo
     pre = synth.make_cache_prefill(shape, lengths, seed)
     xb = synth.make_x(shape, M, seed)
-    layer = D.DeviceLayer(shape, lw)
+    if "layer" not in memo:
+        memo["layer"] = D.DeviceLayer(shape, lw)
+        memo["ql"] = O.quantize_layer(lw)
+    layer = memo["layer"]
     cache = D.DeviceCache(shape, lengths)
     cache.prefill(pre)
     maxL = int(lengths.max())
@@ -222,7 +229,7 @@ def run_block(gpu, shape, seed, lengths, num_splits=0, dense_cache=None, lw=None
                             ws.nbytes, attn)
     torch.cuda.synchronize()
     ocache = O.build_cache(shape, lengths, pre)
-    ref = O.decode_block(shape, O.quantize_layer(lw), ocache, xb, lengths, dense_cache)
+    ref = O.decode_block(shape, memo["ql"], ocache, xb, lengths, dense_cache)
     res = dict(out=D.bf16_tensor_to_f32(x_out), attn=attn.cpu().numpy(), ref=ref, cache=cache,
                layer=layer, x_in=x_in, x_out=x_out, ws=ws, ctx=ctx, lengths=lengths)
     return res
