@@ -111,11 +111,14 @@ i4d_status do_qkv(const i4d_layer* L, const uint16_t* x, const int32_t* ctx_len,
 
 i4d_status do_attention(const i4d_kv_cache* c, const i4d_layer_shape& s, const float* q,
                         const int32_t* ctx_len, int M, int max_ctx_len, int num_splits, void* ws,
-                        float* attn_f32, uint16_t* attn_bf16, hipStream_t st) {
+                        float* attn_f32, uint16_t* attn_bf16, const uint16_t* k_new,
+                        const uint16_t* v_new, hipStream_t st) {
   AttnArgs a;
   a.kv = kv_args(c);
   a.q = q;
   a.ctx_len = ctx_len;
+  a.k_new = k_new;
+  a.v_new = v_new;
   a.M = M;
   a.n_q = s.n_q_heads;
   a.G = s.n_q_heads / s.n_kv_heads;
@@ -213,7 +216,7 @@ i4d_status i4d_attention(const i4d_kv_cache* cache, const i4d_layer_shape* shape
   if (workspace_bytes < need_ws)
     return fail(I4D_ERR_WORKSPACE, "attention workspace %zu < %zu bytes", workspace_bytes, need_ws);
   return do_attention(cache, *shape, q, ctx_len, M, max_ctx_len, num_splits, workspace, attn_f32,
-                      attn_bf16, (hipStream_t)stream);
+                      attn_bf16, nullptr, nullptr, (hipStream_t)stream);
 }
 
 i4d_status i4d_attn_out_proj(const i4d_layer* layer, const uint16_t* attn_bf16, const uint16_t* x,
@@ -277,18 +280,10 @@ i4d_status i4d_decode_block_step(const i4d_layer* layer, const i4d_kv_cache* cac
   const i4d_layer_shape& s = layer->shape;
 
   I4D_TRY(do_qkv(layer, x_in, ctx_len, M, q, k, v, st));
-  // the new token of row m goes to position ctx_len[m] - 1 of cache row m
-  AppendArgs ap;
-  ap.kv = kv_args(cache);
-  ap.k = k;
-  ap.v = v;
-  ap.row_idx = nullptr;
-  ap.pos = nullptr;
-  ap.len = nullptr;
-  ap.T = M;
-  I4D_TRY(launch_kv_append_at_len(ap, ctx_len, st));
+  // the attention launch first appends the new token of row m at position
+  // ctx_len[m] - 1 of cache row m (inside the workgroup that owns that block)
   I4D_TRY(do_attention(cache, s, q, ctx_len, M, max_ctx_len, num_splits, ws + wl.attn_ws, attn_f32,
-                       attn, st));
+                       attn, k, v, st));
   I4D_TRY(do_o(layer, attn, x_in, M, h, hb, st));
   I4D_TRY(do_gu(layer, hb, M, act, st));
   I4D_TRY(do_down(layer, act, h, M, x_out, st));

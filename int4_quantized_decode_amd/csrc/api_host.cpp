@@ -53,14 +53,18 @@ i4d_status check_shape(const i4d_layer_shape* s) {
 }
 
 int choose_splits(const i4d_layer_shape* s, int M, int max_ctx_len, int num_splits) {
-  int nblk = (max_ctx_len + kVBlock - 1) / kVBlock;
   if (num_splits > 0) return std::min(num_splits, I4D_MAX_SPLITS);
-  // aim for about two 32-token blocks per wave and at most ~4096 waves
-  long units = (long)M * s->n_kv_heads;
-  long waves_wanted = std::min<long>(4096, std::max<long>(1, units * nblk / 2));
-  long S = (waves_wanted + units * kAttnWaves - 1) / (units * kAttnWaves);
-  S = std::max<long>(1, std::min<long>(S, std::min(nblk, I4D_MAX_SPLITS)));
-  return (int)S;
+  // One workgroup of NWA waves per (row, kv head, split).  Split only as far
+  // as needed: at most 16 blocks of 32 tokens per wave, and enough waves
+  // (about 2048) to cover the chip when few rows and heads are active.
+  const long nblk = (max_ctx_len + kVBlock - 1) / kVBlock;
+  const long nwa = attn_waves(s->n_q_heads / s->n_kv_heads);
+  const long units = (long)M * s->n_kv_heads;
+  const long s_len = (nblk + nwa * 16 - 1) / (nwa * 16);
+  const long s_par = (2048 + units * nwa - 1) / (units * nwa);
+  const long s_max = std::max<long>(1, (nblk + nwa - 1) / nwa);  // at least one block per wave
+  long S = std::max(s_len, std::min(s_par, s_max));
+  return (int)std::max<long>(1, std::min<long>(S, I4D_MAX_SPLITS));
 }
 
 AttnWs attn_ws_layout(const i4d_layer_shape* s, int M, int S) {

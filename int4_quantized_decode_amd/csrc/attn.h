@@ -31,6 +31,8 @@ struct AttnArgs {
   KvArgs kv;
   const float* q;          // fp32 [M][n_q][hd], not rotated
   const int32_t* ctx_len;  // [M]
+  const uint16_t* k_new;   // optional bf16 [M][n_kv][hd]: appended at ctx_len-1 first
+  const uint16_t* v_new;
   int M, n_q, G, S;
   float score_scale;       // log2(e) / (hd * sqrt(hd))
   float* part_ml;          // [M][n_q][S][2]
@@ -40,8 +42,7 @@ struct AttnArgs {
 };
 
 i4d_status launch_kv_append(const AppendArgs& a, hipStream_t st);
-// decode step: token t of row t goes to position ctx_len[t] - 1
-i4d_status launch_kv_append_at_len(AppendArgs a, const int32_t* ctx_len, hipStream_t st);
 i4d_status launch_attention(const AttnArgs& a, hipStream_t st);
+int attn_waves_per_group(int G);
 
 }  // namespace i4d

@@ -1,27 +1,30 @@
-// attn.hip - INT4 KV cache append and GQA split-KV flash-decode (gfx950).
+// attn.hip - INT4 KV cache append and GQA decode attention (gfx950).
 //
-// kv_append: one wave per (token, kv head, K|V).  The head_dim values are
-//   spread over the 64 lanes, rotated by the unnormalised fast Walsh-Hadamard
-//   transform in fp32 (stage order h = 1, 2, 4, ...; cross-lane stages use
-//   lane shuffles, the add DAG is the same as the plain transform so the
-//   result is bit-identical), reduced to the absmax, quantized with
-//   scale = fp16(absmax / 7) (correctly rounded fp32 division) and written in
-//   the MFMA operand layout of the cache ("how it differs": rotation before
-//   cache quantization; "how it works": direct placement at
+// Append: one wave rotates one key or value vector with the unnormalised fast
+//   Walsh-Hadamard transform in fp32 (stage order h = 1, 2, 4, ...; the
+//   cross-lane stages use lane shuffles with the same add DAG as the plain
+//   transform, so the result is bit-identical), takes the absmax, quantizes
+//   with scale = fp16(absmax / 7) (correctly rounded fp32 division) and writes
+//   the codes in the MFMA operand layout of the cache ("how it differs":
+//   rotation before cache quantization; "how it works": direct placement at
 //   offset(request, head, position, channel)).
 //
-// attention: one workgroup per (row, kv head, split); its waves take
-//   interleaved 32-token blocks.  Per block:
-//     S[token][col]  = K_codes(16 tokens x hd, fp16) . [q~_hi | q~_lo]  (MFMA)
-//     online softmax in fp32 (log2 domain), p' = p * v_scale
-//     O[ch][col]    += V_codes^T(16 ch x 32 tokens, fp16) . [p'_hi | p'_lo]
-//   The G query heads of the kv head share every K/V load ("premises and
-//   limits": the 8-head cache is read without expanding it).  Columns 0..G-1
-//   carry the high fp16 part of q~ / p', columns G..2G-1 the low part, so
-//   scores and outputs keep ~fp32 precision on fp16 MFMA.  The waves merge in
-//   LDS and write one (max, sum, output) partial per split; the combine
-//   kernel merges the splits and applies the inverse rotation H o~ / hd
+// Attention: one workgroup per (row, kv head, split) with 8 or 16 waves that
+//   take interleaved 32-token blocks.  Per block and wave:
+//     S[token][col] = K_codes(16 tokens x hd, fp16) . [q~_hi ; q~_lo]  (MFMA,
+//                     the hi/lo halves of the rotated query along k)
+//     online softmax in fp32 (log2 domain), p' = p * v_scale (fp16)
+//     O[ch][col]   += V_codes^T(16 channels x 32 tokens, fp16) . p'      (MFMA)
+//   Column c of both products is query head c of the kv head, so the G heads
+//   share every K/V load ("premises and limits": the 8-head cache is read
+//   without expanding it).  The next block's codes and scales are loaded
+//   while the current one is computed.  The waves merge in LDS; with one split
+//   the workgroup normalises and undoes the rotation (o = H o~ / hd) itself,
+//   otherwise it writes (max, sum, output) partials for the combine kernel
 //   ("how it differs": split-KV reduction, same rotation on the output).
+//   In a decode step the workgroup whose split holds position L-1 first
+//   appends the step's new key and value, so no separate append launch sits
+//   on the critical path.
 #include <math.h>
 
 #include "attn.h"
@@ -43,32 +46,13 @@ __device__ __forceinline__ uint16_t f32_to_f16_sat(float f) {
 }
 
 // ---------------------------------------------------------------------------
-// append
+// append of one vector by one wave
 // ---------------------------------------------------------------------------
 
+// region = first slot of (row, head); pos < capacity; kind 0 = key, 1 = value
 template <int HD>
-__global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int idx = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const KvArgs& kv = a.kv;
-  if (idx >= a.T * kv.n_kv * 2) return;
-  const int kind = idx & 1;
-  const int rest = idx >> 1;
-  const int head = rest % kv.n_kv;
-  const int t = rest / kv.n_kv;
-  const int row = a.row_idx ? a.row_idx[t] : t;
-  const int pos = a.len ? a.len[t] - 1 : a.pos[t];
-  if (row < 0 || row >= kv.n_rows) {
-    if (lane == 0 && kv.err_word) atomicOr(kv.err_word, I4D_DEVERR_APPEND_POS);
-    return;
-  }
-  const int64_t base = kv.row_base[row];
-  const int64_t cap = kv.row_base[row + 1] - base;
-  if (pos < 0 || pos >= cap) {
-    if (lane == 0 && kv.err_word) atomicOr(kv.err_word, I4D_DEVERR_APPEND_POS);
-    return;
-  }
-  const uint16_t* src = (kind ? a.v : a.k) + ((size_t)t * kv.n_kv + head) * HD;
+__device__ void append_vector(const KvArgs& kv, const uint16_t* src, int64_t region, int pos,
+                              int kind, int lane) {
   float x0 = bf16_to_f32(src[lane]);
   float x1 = (HD == 128) ? bf16_to_f32(src[lane + 64]) : 0.f;
   // FWHT, stages h = 1 .. 32 across lanes, then h = 64 inside the lane
@@ -94,7 +78,6 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
     u0 = (int)fminf(7.f, fmaxf(-8.f, rintf(__fdiv_rn(x0, sf)))) + 8;
     u1 = (int)fminf(7.f, fmaxf(-8.f, rintf(__fdiv_rn(x1, sf)))) + 8;
   }
-  const int64_t region = base * kv.n_kv + (int64_t)head * cap;  // first slot of (row, head)
   const int64_t slot = region + pos;
   if (kind == 0) {
     // key slot: dword d = jj*(HD/32) + kb holds channels 32kb + 8jj + e
@@ -104,53 +87,149 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int c = 32 * kb + 8 * jj + e;
-      const int src_lane = c & 63;
-      const int v0 = __shfl(u0, src_lane, 64);
-      const int v1 = __shfl(u1, src_lane, 64);
-      const int u = (c < 64) ? v0 : v1;
-      word |= (uint32_t)u << (4 * nibble_slot(e));
+      const int v0 = __shfl(u0, c & 63, 64);
+      const int v1 = __shfl(u1, c & 63, 64);
+      word |= (uint32_t)((c < 64) ? v0 : v1) << (4 * nibble_slot(e));
     }
-    if (d < HD / 8) {
-      uint32_t* dst = reinterpret_cast<uint32_t*>(kv.k_codes + (size_t)slot * (HD / 2));
-      dst[d] = word;
-    }
+    if (d < HD / 8) reinterpret_cast<uint32_t*>(kv.k_codes + (size_t)slot * (HD / 2))[d] = word;
     if (lane == 0) kv.k_scales[slot] = s16;
   } else {
+    // value block: token w of the block sits in slot group jj, slot e
     const int w = pos % kVBlock;
-    int jj, e;
-    if (w < 16) {
-      jj = w / 4;
-      e = w % 4;
-    } else {
-      jj = (w - 16) / 4;
-      e = 4 + (w - 16) % 4;
-    }
+    const int jj = (w % 16) / 4;
+    const int e = (w % 4) + (w >= 16 ? 4 : 0);
     const int sh = 4 * nibble_slot(e);
     uint32_t* blk = kv.v_codes + (size_t)(region / kVBlock + pos / kVBlock) * 4 * HD;
 #pragma unroll
     for (int q = 0; q < HD / 64; ++q) {
       const int c = lane + 64 * q;
-      const int u = q ? u1 : u0;
       uint32_t* dw = blk + jj * HD + (c % 16) * (HD / 16) + c / 16;
       atomicAnd(dw, ~(0xFu << sh));
-      atomicOr(dw, (uint32_t)u << sh);
+      atomicOr(dw, (uint32_t)(q ? u1 : u0) << sh);
     }
     if (lane == 0) kv.v_scales[slot] = s16;
   }
 }
 
+template <int HD>
+__global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int idx = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const KvArgs& kv = a.kv;
+  if (idx >= a.T * kv.n_kv * 2) return;
+  const int kind = idx & 1;
+  const int rest = idx >> 1;
+  const int head = rest % kv.n_kv;
+  const int t = rest / kv.n_kv;
+  const int row = a.row_idx ? a.row_idx[t] : t;
+  const int pos = a.len ? a.len[t] - 1 : a.pos[t];
+  if (row < 0 || row >= kv.n_rows) {
+    if (lane == 0 && kv.err_word) atomicOr(kv.err_word, I4D_DEVERR_APPEND_POS);
+    return;
+  }
+  const int64_t base = kv.row_base[row];
+  const int64_t cap = kv.row_base[row + 1] - base;
+  if (pos < 0 || pos >= cap) {
+    if (lane == 0 && kv.err_word) atomicOr(kv.err_word, I4D_DEVERR_APPEND_POS);
+    return;
+  }
+  const uint16_t* src = (kind ? a.v : a.k) + ((size_t)t * kv.n_kv + head) * HD;
+  append_vector<HD>(kv, src, base * kv.n_kv + (int64_t)head * cap, pos, kind, lane);
+}
+
 // ---------------------------------------------------------------------------
-// split flash-decode
+// attention
 // ---------------------------------------------------------------------------
 
 template <int HD>
-__global__ __launch_bounds__(kAttnWaves * 64) void attn_split_kernel(AttnArgs a) {
-  constexpr int NWA = kAttnWaves;
+struct BlockRegs {
+  uint32_t kw[2][HD / 32];  // key codes, 2 tiles of 16 tokens
+  uint32_t vw[HD / 16];     // value codes, one dword per 16-channel block
+  u32x2_t ks[2], vs[2];     // 4 fp16 scales per tile
+};
+
+template <int HD>
+__device__ __forceinline__ void load_block(BlockRegs<HD>& b, const uint8_t* kbase, const uint32_t* vbase,
+                                           const uint16_t* ksc, const uint16_t* vsc, int blk, int c,
+                                           int jj) {
+  constexpr int KB = HD / 32, CB = HD / 16;
+  const int t0 = blk * kVBlock;
+#pragma unroll
+  for (int tile = 0; tile < 2; ++tile) {
+    const uint8_t* kp = kbase + (size_t)(t0 + 16 * tile + c) * (HD / 2) + jj * (HD / 8);
+    if (HD == 128) {
+      const u32x4_t v = load16(kp);
+      b.kw[tile][0] = v.x;
+      b.kw[tile][1] = v.y;
+      b.kw[tile][2] = v.z;
+      b.kw[tile][3] = v.w;
+    } else {
+      const u32x2_t v = *reinterpret_cast<const u32x2_t*>(kp);
+      b.kw[tile][0] = v.x;
+      b.kw[tile][1] = v.y;
+    }
+    b.ks[tile] = *reinterpret_cast<const u32x2_t*>(ksc + t0 + 16 * tile + 4 * jj);
+    b.vs[tile] = *reinterpret_cast<const u32x2_t*>(vsc + t0 + 16 * tile + 4 * jj);
+  }
+  const uint32_t* vp = vbase + (size_t)blk * 4 * HD + jj * HD + c * CB;
+#pragma unroll
+  for (int q = 0; q < CB / 4; ++q) {
+    const u32x4_t v = load16(vp + 4 * q);
+    b.vw[4 * q + 0] = v.x;
+    b.vw[4 * q + 1] = v.y;
+    b.vw[4 * q + 2] = v.z;
+    b.vw[4 * q + 3] = v.w;
+  }
+  (void)KB;
+}
+
+__device__ __forceinline__ float f16_half(const u32x2_t& w, int i) {
+  const uint32_t word = w[i >> 1];
+  return f16_bits_to_f32((uint16_t)((i & 1) ? (word >> 16) : (word & 0xffffu)));
+}
+
+// inverse rotation of one head held by a wave (channels lane, lane + 64), / HD
+template <int HD>
+__device__ __forceinline__ void inverse_rotate(float& o0, float& o1, int lane) {
+#pragma unroll
+  for (int h = 1; h < 64 && h < HD; h <<= 1) {
+    const float p0 = shfl_xor(o0, h);
+    o0 = (lane & h) ? (p0 - o0) : (o0 + p0);
+    if (HD == 128) {
+      const float p1 = shfl_xor(o1, h);
+      o1 = (lane & h) ? (p1 - o1) : (o1 + p1);
+    }
+  }
+  if (HD == 128) {
+    const float s0 = o0 + o1, s1 = o0 - o1;
+    o0 = s0;
+    o1 = s1;
+  }
+  const float scale = 1.0f / (float)HD;
+  o0 *= scale;
+  o1 *= scale;
+}
+
+template <int HD>
+__device__ __forceinline__ void write_output(const AttnArgs& a, size_t head_row, float o0, float o1,
+                                             int lane) {
+  const size_t base = head_row * HD;
+  if (a.attn_f32) {
+    a.attn_f32[base + lane] = o0;
+    if (HD == 128) a.attn_f32[base + lane + 64] = o1;
+  }
+  a.attn_bf16[base + lane] = f32_to_bf16(o0);
+  if (HD == 128) a.attn_bf16[base + lane + 64] = f32_to_bf16(o1);
+}
+
+template <int HD, int NWA>
+__global__ __launch_bounds__(NWA * 64) void attn_kernel(AttnArgs a) {
   constexpr int KB = HD / 32;  // 32-channel MFMA steps for q.k
   constexpr int CB = HD / 16;  // 16-channel output blocks
-  __shared__ float wm[NWA][8];
-  __shared__ float wl[NWA][8];
-  __shared__ float wo[NWA][8][HD];
+  constexpr int GMAX = (NWA == 16) ? 4 : 8;
+  __shared__ float wm[NWA][GMAX];
+  __shared__ float wl[NWA][GMAX];
+  __shared__ float wo[NWA][GMAX][HD];
 
   const KvArgs& kv = a.kv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -164,7 +243,8 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_split_kernel(AttnArgs a)
   const int64_t base = kv.row_base[m];
   const int64_t cap = kv.row_base[m + 1] - base;
   int L = a.ctx_len[m];
-  if (L < 1 || L > cap) {
+  const bool len_ok = L >= 1 && L <= cap;
+  if (!len_ok) {
     if (tid == 0 && kv.err_word) atomicOr(kv.err_word, I4D_DEVERR_CTX_LEN);
     L = (int)max((int64_t)0, min((int64_t)max(L, 1), cap));
   }
@@ -174,13 +254,24 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_split_kernel(AttnArgs a)
   const int b1 = min(nblk, b0 + bps);
   const int64_t region = base * kv.n_kv + (int64_t)j * cap;
 
-  // --- rotated query, fp16 hi/lo B operands: column c -> head c % G (c < 2G)
+  // decode step: the split holding position L-1 appends the new key/value
+  if (a.k_new && len_ok) {
+    const int last_blk = (L - 1) / kVBlock;
+    if (last_blk >= b0 && last_blk < b1) {
+      if (wave < 2) {
+        const uint16_t* src = (wave ? a.v_new : a.k_new) + ((size_t)m * kv.n_kv + j) * HD;
+        append_vector<HD>(kv, src, region, L - 1, wave, lane);
+      }
+      __syncthreads();
+    }
+  }
+
+  // rotated query as fp16 hi/lo B operands; column c < G is query head c
   f16x8_t qhi[KB], qlo[KB];
   {
     float qv[KB][8];
-    const bool active = c < 2 * G;
-    const int g = c % G;
-    const float* qsrc = a.q + ((size_t)m * a.n_q + (size_t)j * G + g) * HD + 8 * jj;
+    const bool active = c < G;
+    const float* qsrc = a.q + ((size_t)m * a.n_q + (size_t)j * G + (active ? c : 0)) * HD + 8 * jj;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       if (active) {
@@ -196,8 +287,8 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_split_kernel(AttnArgs a)
         for (int e = 0; e < 8; ++e) qv[kb][e] = 0.f;
       }
     }
-    // channel = 32*kb + 8*jj + e: bits 0-2 in-lane (e), 3-4 across lanes
-    // (jj: lane ^ 16, lane ^ 32), 5-6 in-lane (kb)
+    // channel = 32*kb + 8*jj + e: bits 0-2 in-lane (e), bits 3-4 across lanes
+    // (jj: lane ^ 16, lane ^ 32), bits 5-6 in-lane (kb)
 #pragma unroll
     for (int h = 1; h < 8; h <<= 1)
 #pragma unroll
@@ -252,46 +343,15 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_split_kernel(AttnArgs a)
   const uint32_t* vbase = kv.v_codes + (size_t)(region / kVBlock) * 4 * HD;
   const float sscale = a.score_scale;
 
-  for (int blk = b0 + wave; blk < b1; blk += NWA) {
+  int blk = b0 + wave;
+  BlockRegs<HD> cur;
+  if (blk < b1) load_block<HD>(cur, kbase, vbase, ksc, vsc, blk, c, jj);
+  for (; blk < b1; blk += NWA) {
+    BlockRegs<HD> nxt;
+    const bool more = blk + NWA < b1;
+    if (more) load_block<HD>(nxt, kbase, vbase, ksc, vsc, blk + NWA, c, jj);
     const int t0 = blk * kVBlock;
-    // loads: keys for 2 tiles of 16 tokens (lane row = token c), values,
-    // scales for the tokens whose scores this lane holds (t0 + 16 tile + 4 jj + i)
-    uint32_t kw[2][KB];
-#pragma unroll
-    for (int tile = 0; tile < 2; ++tile) {
-      const uint8_t* kp = kbase + (size_t)(t0 + 16 * tile + c) * (HD / 2) + jj * (HD / 8);
-      if (HD == 128) {
-        const u32x4_t v = load16(kp);
-        kw[tile][0] = v.x;
-        kw[tile][1] = v.y;
-        kw[tile][2] = v.z;
-        kw[tile][3] = v.w;
-      } else {
-        const u32x2_t v = *reinterpret_cast<const u32x2_t*>(kp);
-        kw[tile][0] = v.x;
-        kw[tile][1] = v.y;
-      }
-    }
-    uint32_t vw[CB];
-    {
-      const uint32_t* vp = vbase + (size_t)blk * 4 * HD + jj * HD + c * CB;
-#pragma unroll
-      for (int q = 0; q < CB / 4; ++q) {
-        const u32x4_t v = load16(vp + 4 * q);
-        vw[4 * q + 0] = v.x;
-        vw[4 * q + 1] = v.y;
-        vw[4 * q + 2] = v.z;
-        vw[4 * q + 3] = v.w;
-      }
-    }
-    u32x2_t ks2[2], vs2[2];
-#pragma unroll
-    for (int tile = 0; tile < 2; ++tile) {
-      ks2[tile] = *reinterpret_cast<const u32x2_t*>(ksc + t0 + 16 * tile + 4 * jj);
-      vs2[tile] = *reinterpret_cast<const u32x2_t*>(vsc + t0 + 16 * tile + 4 * jj);
-    }
 
-    // scores
     float sc[8];
     float mx = -INFINITY;
 #pragma unroll
@@ -299,16 +359,14 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_split_kernel(AttnArgs a)
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        const f16x8_t kf = dword_to_f16x8_signed(kw[tile][kb]);
+        const f16x8_t kf = dword_to_f16x8_signed_fast(cur.kw[tile][kb]);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qhi[kb], acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qlo[kb], acc, 0, 0, 0);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int tok = t0 + 16 * tile + 4 * jj + i;
-        const uint32_t word = ks2[tile][i >> 1];
-        const float ks = f16_bits_to_f32((uint16_t)((i & 1) ? (word >> 16) : (word & 0xffffu)));
-        const float v = (tok < L) ? acc[i] * ks * sscale : -INFINITY;
+        const float v = (tok < L) ? acc[i] * f16_half(cur.ks[tile], i) * sscale : -INFINITY;
         sc[tile * 4 + i] = v;
         mx = fmaxf(mx, v);
       }
@@ -316,39 +374,32 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_split_kernel(AttnArgs a)
     mx = fmaxf(mx, shfl_xor(mx, 16));
     mx = fmaxf(mx, shfl_xor(mx, 32));
     const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2f(m_run - m_new);
-    l_run *= alpha;
+    if (__any(m_new > m_run)) {
+      const float alpha = exp2f(m_run - m_new);
+      l_run *= alpha;
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) o[cb] *= alpha;
-
+      for (int cb = 0; cb < CB; ++cb) o[cb] *= alpha;
+    }
     f16x8_t pb;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const int tile = q >> 2, i = q & 3;
       const int tok = t0 + 16 * tile + 4 * jj + i;
-      const uint32_t word = vs2[tile][i >> 1];
-      const float vs = f16_bits_to_f32((uint16_t)((i & 1) ? (word >> 16) : (word & 0xffffu)));
       const float p = (tok < L) ? exp2f(sc[q] - m_new) : 0.f;
       l_run += p;
-      const float pv = (tok < L) ? p * vs : 0.f;
-      const _Float16 hi = (_Float16)pv;
-      const _Float16 lo = (_Float16)(pv - (float)hi);
-      pb[q] = (c < G) ? hi : ((c < 2 * G) ? lo : (_Float16)0.0f);
+      const float pv = (tok < L && c < G) ? p * f16_half(cur.vs[tile], i) : 0.f;
+      pb[q] = (_Float16)pv;
     }
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
-      o[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dword_to_f16x8_signed(vw[cb]), pb, o[cb], 0, 0, 0);
+      o[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dword_to_f16x8_signed_fast(cur.vw[cb]), pb, o[cb],
+                                                     0, 0, 0);
     m_run = m_new;
+    if (more) cur = nxt;
   }
 
-  // merge the four lane rows (jj) of l, and the hi/lo columns of o
   l_run += shfl_xor(l_run, 16);
   l_run += shfl_xor(l_run, 32);
-#pragma unroll
-  for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) o[cb][i] += __shfl_xor(o[cb][i], G, 64);
-
   if (c < G) {
     if (jj == 0) {
       wm[wave][c] = m_run;
@@ -361,30 +412,41 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_split_kernel(AttnArgs a)
   }
   __syncthreads();
 
-  // merge the waves and write this split's partial for the G heads
-  for (int idx = tid; idx < G * HD; idx += NWA * 64) {
-    const int g = idx / HD, ch = idx % HD;
+  // wave g merges head g over the waves
+  if (wave < G) {
+    const int g = wave;
     float M_ = -INFINITY;
     for (int w = 0; w < NWA; ++w)
       if (wl[w][g] > 0.f) M_ = fmaxf(M_, wm[w][g]);
-    float lsum = 0.f, osum = 0.f;
+    float lsum = 0.f, o0 = 0.f, o1 = 0.f;
     for (int w = 0; w < NWA; ++w) {
       if (wl[w][g] > 0.f) {
         const float f = exp2f(wm[w][g] - M_);
         lsum += f * wl[w][g];
-        osum += f * wo[w][g][ch];
+        o0 += f * wo[w][g][lane];
+        if (HD == 128) o1 += f * wo[w][g][lane + 64];
       }
     }
-    const size_t ph = ((size_t)m * a.n_q + (size_t)j * G + g) * S + s;
-    a.part_o[ph * HD + ch] = osum;
-    if (ch == 0) {
-      a.part_ml[ph * 2] = M_;
-      a.part_ml[ph * 2 + 1] = lsum;
+    const size_t head_row = (size_t)m * a.n_q + (size_t)j * G + g;
+    if (S == 1) {
+      const float inv = 1.0f / lsum;
+      o0 *= inv;
+      o1 *= inv;
+      inverse_rotate<HD>(o0, o1, lane);
+      write_output<HD>(a, head_row, o0, o1, lane);
+    } else {
+      const size_t ph = head_row * S + s;
+      a.part_o[ph * HD + lane] = o0;
+      if (HD == 128) a.part_o[ph * HD + lane + 64] = o1;
+      if (lane == 0) {
+        a.part_ml[ph * 2] = M_;
+        a.part_ml[ph * 2 + 1] = lsum;
+      }
     }
   }
 }
 
-// combine the splits of one (row, q head) and undo the rotation: o = H o~ / hd
+// merge the splits of one (row, q head) and undo the rotation: o = H o~ / hd
 template <int HD>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   const int lane = threadIdx.x & 63;
@@ -409,30 +471,8 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   const float inv = 1.0f / lsum;
   o0 *= inv;
   o1 *= inv;
-#pragma unroll
-  for (int h = 1; h < 64 && h < HD; h <<= 1) {
-    const float p0 = shfl_xor(o0, h);
-    o0 = (lane & h) ? (p0 - o0) : (o0 + p0);
-    if (HD == 128) {
-      const float p1 = shfl_xor(o1, h);
-      o1 = (lane & h) ? (p1 - o1) : (o1 + p1);
-    }
-  }
-  if (HD == 128) {
-    const float s0 = o0 + o1, s1 = o0 - o1;
-    o0 = s0;
-    o1 = s1;
-  }
-  const float scale = 1.0f / (float)HD;
-  o0 *= scale;
-  o1 *= scale;
-  const size_t base = (size_t)idx * HD;
-  if (a.attn_f32) {
-    a.attn_f32[base + lane] = o0;
-    if (HD == 128) a.attn_f32[base + lane + 64] = o1;
-  }
-  a.attn_bf16[base + lane] = f32_to_bf16(o0);
-  if (HD == 128) a.attn_bf16[base + lane + 64] = f32_to_bf16(o1);
+  inverse_rotate<HD>(o0, o1, lane);
+  write_output<HD>(a, (size_t)idx, o0, o1, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -450,26 +490,27 @@ i4d_status launch_kv_append(const AppendArgs& a, hipStream_t st) {
   return ok();
 }
 
-i4d_status launch_kv_append_at_len(AppendArgs a, const int32_t* ctx_len, hipStream_t st) {
-  a.len = ctx_len;
-  a.pos = nullptr;
-  a.row_idx = nullptr;
-  return launch_kv_append(a, st);
+template <int HD>
+static void launch_attn_hd(const AttnArgs& a, hipStream_t st) {
+  const int grid = a.M * a.kv.n_kv * a.S;
+  if (a.G <= 4)
+    hipLaunchKernelGGL((attn_kernel<HD, 16>), dim3(grid), dim3(16 * 64), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_kernel<HD, 8>), dim3(grid), dim3(8 * 64), 0, st, a);
+  if (a.S > 1)
+    hipLaunchKernelGGL(attn_combine_kernel<HD>, dim3((a.M * a.n_q + 3) / 4), dim3(256), 0, st, a);
 }
 
 i4d_status launch_attention(const AttnArgs& a, hipStream_t st) {
-  const int grid = a.M * a.kv.n_kv * a.S;
-  const int cgrid = (a.M * a.n_q + 3) / 4;
-  if (a.kv.hd == 128) {
-    hipLaunchKernelGGL(attn_split_kernel<128>, dim3(grid), dim3(kAttnWaves * 64), 0, st, a);
-    hipLaunchKernelGGL(attn_combine_kernel<128>, dim3(cgrid), dim3(256), 0, st, a);
-  } else {
-    hipLaunchKernelGGL(attn_split_kernel<64>, dim3(grid), dim3(kAttnWaves * 64), 0, st, a);
-    hipLaunchKernelGGL(attn_combine_kernel<64>, dim3(cgrid), dim3(256), 0, st, a);
-  }
+  if (a.kv.hd == 128)
+    launch_attn_hd<128>(a, st);
+  else
+    launch_attn_hd<64>(a, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(I4D_ERR_HIP, "attention launch: %s", hipGetErrorString(e));
   return ok();
 }
+
+int attn_waves_per_group(int G) { return G <= 4 ? 16 : 8; }
 
 }  // namespace i4d

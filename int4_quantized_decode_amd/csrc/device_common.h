@@ -50,6 +50,27 @@ __device__ __forceinline__ f16x8_t dword_to_f16x8_signed(uint32_t w) {
   return bitcast<f16x8_t>(v);
 }
 
+// Same result with fewer instructions: the fp16 mantissa holds a nibble at
+// bits 0-3 (value 1024 + u) or at bits 4-7 (value 1024 + 16u), so one shift
+// and four v_and_or give all eight codes; (1024 + 16u)/16 - 72 = u - 8 is
+// exact in one packed FMA.
+__device__ __forceinline__ f16x8_t dword_to_f16x8_signed_fast(uint32_t w) {
+  const f16x2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
+  const f16x2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const f16x2_t off72 = {(_Float16)72.0f, (_Float16)72.0f};
+  const uint32_t t = w >> 8;
+  f16x2_t p0 = bitcast<f16x2_t>((w & 0x000F000Fu) | 0x64006400u) - off;
+  f16x2_t p1 = bitcast<f16x2_t>((w & 0x00F000F0u) | 0x64006400u) * sixteenth - off72;
+  f16x2_t p2 = bitcast<f16x2_t>((t & 0x000F000Fu) | 0x64006400u) - off;
+  f16x2_t p3 = bitcast<f16x2_t>((t & 0x00F000F0u) | 0x64006400u) * sixteenth - off72;
+  u32x4_t v;
+  v.x = bitcast<uint32_t>(p0);
+  v.y = bitcast<uint32_t>(p1);
+  v.z = bitcast<uint32_t>(p2);
+  v.w = bitcast<uint32_t>(p3);
+  return bitcast<f16x8_t>(v);
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }

@@ -63,12 +63,16 @@ __device__ void run_epilogue(const ProjArgs& a, int strip0, const float* ot, con
         const int head = t / per_head, sp = t % per_head;
         const int c0 = 8 * sp + i, c1 = c0 + a.hd / 2;
         if (head < a.n_q + a.n_kv) {
-          // RoPE, rotate-half pair (c0, c0 + hd/2) at position ctx_len - 1
+          // RoPE, rotate-half pair (c0, c0 + hd/2) at position ctx_len - 1:
+          // angle pos * theta^(-2 c0 / hd) in fp64, reduced to [-pi, pi],
+          // then fp32 sin/cos
           const double pos = (double)(a.ctx_len[m] - 1);
-          const double ang = pos * pow((double)a.theta, -2.0 * (double)c0 / (double)a.hd);
-          double sn, cs;
-          sincos(ang, &sn, &cs);
-          const float c = (float)cs, sn_f = (float)sn;
+          const double ang = pos * exp2(-(2.0 * (double)c0 / (double)a.hd) * log2((double)a.theta));
+          const double k2pi = rint(ang * 0.15915494309189535);
+          double red = fma(-k2pi, 6.283185307179586, ang);
+          red = fma(-k2pi, 2.4492935982947064e-16, red);
+          float sn_f, c;
+          sincosf((float)red, &sn_f, &c);
           const float r0 = y0 * c - y1 * sn_f;
           const float r1 = y1 * c + y0 * sn_f;
           y0 = r0;
@@ -111,7 +115,25 @@ __device__ void run_epilogue(const ProjArgs& a, int strip0, const float* ot, con
 // M = 1: VALU GEMV
 // ---------------------------------------------------------------------------
 
-template <int EPI, int S, int NW>
+template <int U, int S, bool NT>
+__device__ __forceinline__ void gemv_issue(u32x4_t (&w)[U][S], const uint8_t* codes, int strip0,
+                                           int nstrips, int G, int g0, int NW) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int g = g0 + u * NW;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const int t = strip0 + s;
+      if (g < G && t < nstrips)
+        w[u][s] = NT ? load16_stream(codes + ((size_t)t * G + g) * kAtomBytes)
+                     : load16(codes + ((size_t)t * G + g) * kAtomBytes);
+      else
+        w[u][s] = u32x4_t{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
+    }
+  }
+}
+
+template <int EPI, int S, int NW, int U, bool NT>
 __global__ __launch_bounds__(NW * 64) void proj_gemv_kernel(ProjArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int K = a.K, G = a.G;
@@ -125,6 +147,12 @@ __global__ __launch_bounds__(NW * 64) void proj_gemv_kernel(ProjArgs a) {
   const int r = lane & 15, j = lane >> 4;
   const int strip0 = blockIdx.x * S;
   const int nstrips = a.Np / kStrip;
+  const uint8_t* codes = a.codes + (size_t)lane * 16;
+
+  // the weight stream does not depend on x: start it before staging x
+  // (U groups per batch and wave, two batches in flight)
+  u32x4_t wa[U][S], wb[U][S];
+  gemv_issue<U, S, NT>(wa, codes, strip0, nstrips, G, wave, NW);
 
   // stage x (bf16) in LDS and accumulate its sum of squares
   float sq = 0.f;
@@ -152,14 +180,14 @@ __global__ __launch_bounds__(NW * 64) void proj_gemv_kernel(ProjArgs a) {
   for (int idx = tid; idx < G * 4; idx += NW * 64) {
     const int g = idx >> 2, jj = idx & 3;
     const u32x4_t* xl = reinterpret_cast<const u32x4_t*>(xs);
-    float s = 0.f;
+    float sm = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const u32x4_t v = xl[(128 * g + 32 * kb + 8 * jj) / 8];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) s += bf16_lo(v[q]) + bf16_hi(v[q]);
+      for (int q = 0; q < 4; ++q) sm += bf16_lo(v[q]) + bf16_hi(v[q]);
     }
-    Xs[idx] = s;
+    Xs[idx] = sm;
   }
   if (needs_rho<EPI>() && tid == 0) {
     float t = 0.f;
@@ -172,27 +200,12 @@ __global__ __launch_bounds__(NW * 64) void proj_gemv_kernel(ProjArgs a) {
 #pragma unroll
   for (int s = 0; s < S; ++s) part[s] = 0.f;
 
-  const uint8_t* codes = a.codes + (size_t)lane * 16;
-  constexpr int U = 4;  // groups in flight per wave
-  for (int g0 = wave; g0 < G; g0 += NW * U) {
-    u32x4_t w[U][S];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int g = g0 + u * NW;
-#pragma unroll
-      for (int s = 0; s < S; ++s) {
-        const int t = strip0 + s;
-        if (g < G && t < nstrips)
-          w[u][s] = load16_stream(codes + ((size_t)t * G + g) * kAtomBytes);
-        else
-          w[u][s] = u32x4_t{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
-      }
-    }
+  const u32x4_t* xl = reinterpret_cast<const u32x4_t*>(xs);
+  auto consume = [&](u32x4_t (&w)[U][S], int g0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int g = g0 + u * NW;
       if (g >= G) break;
-      const u32x4_t* xl = reinterpret_cast<const u32x4_t*>(xs);
       u32x4_t xv[4];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) xv[kb] = xl[(128 * g + 32 * kb + 8 * j) / 8];
@@ -209,11 +222,21 @@ __global__ __launch_bounds__(NW * 64) void proj_gemv_kernel(ProjArgs a) {
                                                   bitcast<bf16x2_t>(xv[kb][i]), acc, false);
         }
         const int t = min(strip0 + s, nstrips - 1);
-        const float sc = f16_bits_to_f32(
-            a.scales[(((size_t)t * a.G8 + g / 8) * 16 + r) * 8 + (g % 8)]);
+        const float sc = f16_bits_to_f32(a.scales[(((size_t)t * a.G8 + g / 8) * 16 + r) * 8 + (g % 8)]);
         part[s] = fmaf(sc, acc - corr, part[s]);
       }
     }
+  };
+  // double-buffered batches of U groups: issue batch b+1, then consume batch b
+  for (int g0 = wave;; g0 += 2 * NW * U) {
+    const int g1 = g0 + NW * U;
+    if (g1 < G) gemv_issue<U, S, NT>(wb, codes, strip0, nstrips, G, g1, NW);
+    consume(wa, g0);
+    if (g1 >= G) break;
+    const int g2 = g1 + NW * U;
+    if (g2 < G) gemv_issue<U, S, NT>(wa, codes, strip0, nstrips, G, g2, NW);
+    consume(wb, g1);
+    if (g2 >= G) break;
   }
 #pragma unroll
   for (int s = 0; s < S; ++s) {
@@ -349,21 +372,35 @@ __global__ __launch_bounds__(NW * 64) void proj_mfma_kernel(ProjArgs a) {
 // launcher
 // ---------------------------------------------------------------------------
 
+// waves per workgroup of the M = 1 kernel: enough waves in flight (>= 2048)
+// and at most 8 groups per wave when the shape allows
+static int gemv_waves(int nstrips, int G) {
+  int nw = 4;
+  while (nw < 16 && ((long)nstrips * nw < 2048 || (G + nw - 1) / nw > 8)) nw *= 2;
+  while (nw > 4 && nw > G) nw /= 2;
+  return nw;
+}
+
 template <int EPI>
 static hipError_t launch_epi(const ProjArgs& a, hipStream_t st) {
   const int nstrips = a.Np / kStrip;
-  constexpr int NW = 4;
   if (a.M == 1) {
     constexpr int S = 1;
-    const size_t lds = gemv_lds_bytes(a.K, S, NW);
+    const int nw = gemv_waves(nstrips, a.G);
+    const size_t lds = gemv_lds_bytes(a.K, S, nw);
     const int grid = (nstrips + S - 1) / S;
-    hipLaunchKernelGGL((proj_gemv_kernel<EPI, S, NW>), dim3(grid), dim3(NW * 64), lds, st, a);
+    if (nw == 4)
+      hipLaunchKernelGGL((proj_gemv_kernel<EPI, S, 4, 8, true>), dim3(grid), dim3(4 * 64), lds, st, a);
+    else if (nw == 8)
+      hipLaunchKernelGGL((proj_gemv_kernel<EPI, S, 8, 8, true>), dim3(grid), dim3(8 * 64), lds, st, a);
+    else
+      hipLaunchKernelGGL((proj_gemv_kernel<EPI, S, 16, 8, true>), dim3(grid), dim3(16 * 64), lds, st, a);
   } else if (a.M <= 16) {
-    constexpr int S = 2;
+    constexpr int S = 2, NW = 4;
     const int grid = (nstrips + S - 1) / S;
     hipLaunchKernelGGL((proj_mfma_kernel<EPI, S, NW, 1>), dim3(grid), dim3(NW * 64), 0, st, a);
   } else {
-    constexpr int S = 2;
+    constexpr int S = 2, NW = 4;
     const int grid = (nstrips + S - 1) / S;
     hipLaunchKernelGGL((proj_mfma_kernel<EPI, S, NW, 2>), dim3(grid), dim3(NW * 64), 0, st, a);
   }
@@ -372,7 +409,7 @@ static hipError_t launch_epi(const ProjArgs& a, hipStream_t st) {
 
 i4d_status launch_projection(int epi, const ProjArgs& a, hipStream_t st) {
   if (a.M == 1) {
-    const size_t lds = gemv_lds_bytes(a.K, 1, 4);
+    const size_t lds = gemv_lds_bytes(a.K, 1, 16);
     if (lds > (size_t)kMaxLdsBytes)
       return fail(I4D_ERR_UNSUPPORTED, "K=%d too large for the M=1 kernel (LDS %zu bytes)", a.K, lds);
   }
