@@ -112,7 +112,8 @@ i4d_status do_qkv(const i4d_layer* L, const uint16_t* x, const int32_t* ctx_len,
 i4d_status do_attention(const i4d_kv_cache* c, const i4d_layer_shape& s, const float* q,
                         const int32_t* ctx_len, int M, int max_ctx_len, int num_splits, void* ws,
                         float* attn_f32, uint16_t* attn_bf16, const uint16_t* k_new,
-                        const uint16_t* v_new, hipStream_t st) {
+                        const uint16_t* v_new, bool combine, hipStream_t st) {
+  const AttnPlan plan = attn_plan(&s, M, max_ctx_len, num_splits);
   AttnArgs a;
   a.kv = kv_args(c);
   a.q = q;
@@ -122,14 +123,14 @@ i4d_status do_attention(const i4d_kv_cache* c, const i4d_layer_shape& s, const f
   a.M = M;
   a.n_q = s.n_q_heads;
   a.G = s.n_q_heads / s.n_kv_heads;
-  a.S = choose_splits(&s, M, max_ctx_len, num_splits);
+  a.S = plan.S;
   a.score_scale = (float)(1.4426950408889634 / ((double)s.head_dim * sqrt((double)s.head_dim)));
   AttnWs w = attn_ws_layout(&s, M, a.S);
   a.part_ml = (float*)((char*)ws + w.ml);
   a.part_o = (float*)((char*)ws + w.o);
   a.attn_f32 = attn_f32;
   a.attn_bf16 = attn_bf16;
-  return launch_attention(a, st);
+  return launch_attention(a, plan.nwa, combine, st);
 }
 
 i4d_status do_o(const i4d_layer* L, const uint16_t* attn, const uint16_t* x, int M, float* h,
@@ -216,7 +217,7 @@ i4d_status i4d_attention(const i4d_kv_cache* cache, const i4d_layer_shape* shape
   if (workspace_bytes < need_ws)
     return fail(I4D_ERR_WORKSPACE, "attention workspace %zu < %zu bytes", workspace_bytes, need_ws);
   return do_attention(cache, *shape, q, ctx_len, M, max_ctx_len, num_splits, workspace, attn_f32,
-                      attn_bf16, nullptr, nullptr, (hipStream_t)stream);
+                      attn_bf16, nullptr, nullptr, true, (hipStream_t)stream);
 }
 
 i4d_status i4d_attn_out_proj(const i4d_layer* layer, const uint16_t* attn_bf16, const uint16_t* x,
@@ -283,7 +284,7 @@ i4d_status i4d_decode_block_step(const i4d_layer* layer, const i4d_kv_cache* cac
   // the attention launch first appends the new token of row m at position
   // ctx_len[m] - 1 of cache row m (inside the workgroup that owns that block)
   I4D_TRY(do_attention(cache, s, q, ctx_len, M, max_ctx_len, num_splits, ws + wl.attn_ws, attn_f32,
-                       attn, k, v, st));
+                       attn, k, v, true, st));
   I4D_TRY(do_o(layer, attn, x_in, M, h, hb, st));
   I4D_TRY(do_gu(layer, hb, M, act, st));
   I4D_TRY(do_down(layer, act, h, M, x_out, st));

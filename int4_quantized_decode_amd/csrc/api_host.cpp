@@ -52,19 +52,29 @@ i4d_status check_shape(const i4d_layer_shape* s) {
   return ok();
 }
 
-int choose_splits(const i4d_layer_shape* s, int M, int max_ctx_len, int num_splits) {
-  if (num_splits > 0) return std::min(num_splits, I4D_MAX_SPLITS);
-  // One workgroup of NWA waves per (row, kv head, split).  Split only as far
-  // as needed: at most 16 blocks of 32 tokens per wave, and enough waves
-  // (about 2048) to cover the chip when few rows and heads are active.
+AttnPlan attn_plan(const i4d_layer_shape* s, int M, int max_ctx_len, int num_splits) {
+  // One workgroup per (row, kv head, split).  Automatic split count: about
+  // 64 workgroups when few (row, kv head) pairs are active, no split once
+  // there are 64 pairs or more, at least 4 blocks of 32 tokens per split.
+  // Then as many waves per workgroup (4, 8, 16) as keep every wave at one
+  // block or more while the launch has fewer than 4096 waves.
   const long nblk = (max_ctx_len + kVBlock - 1) / kVBlock;
-  const long nwa = attn_waves(s->n_q_heads / s->n_kv_heads);
   const long units = (long)M * s->n_kv_heads;
-  const long s_len = (nblk + nwa * 16 - 1) / (nwa * 16);
-  const long s_par = (2048 + units * nwa - 1) / (units * nwa);
-  const long s_max = std::max<long>(1, (nblk + nwa - 1) / nwa);  // at least one block per wave
-  long S = std::max(s_len, std::min(s_par, s_max));
-  return (int)std::max<long>(1, std::min<long>(S, I4D_MAX_SPLITS));
+  long S;
+  if (num_splits > 0) {
+    S = std::min(num_splits, I4D_MAX_SPLITS);
+  } else {
+    S = (64 + units - 1) / units;
+    S = std::min<long>(S, std::max<long>(1, nblk / 4));
+    S = std::max<long>(S, 1);
+  }
+  const long bps = (nblk + S - 1) / S;
+  int nwa = 4;
+  while (nwa < 16 && units * S * nwa < 4096 && bps >= 2L * nwa) nwa *= 2;
+  AttnPlan p;
+  p.S = (int)S;
+  p.nwa = nwa;
+  return p;
 }
 
 AttnWs attn_ws_layout(const i4d_layer_shape* s, int M, int S) {
@@ -345,7 +355,7 @@ i4d_status i4d_attention_workspace_bytes(const i4d_layer_shape* shape, int M, in
   if (max_ctx_len < 1) return fail(I4D_ERR_RANGE, "max_ctx_len must be >= 1");
   if (num_splits < 0 || num_splits > I4D_MAX_SPLITS)
     return fail(I4D_ERR_RANGE, "num_splits %d outside [0, %d]", num_splits, I4D_MAX_SPLITS);
-  int S = choose_splits(shape, M, max_ctx_len, num_splits);
+  const int S = attn_plan(shape, M, max_ctx_len, num_splits).S;
   *bytes = attn_ws_layout(shape, M, S).total;
   return ok();
 }

@@ -42,7 +42,9 @@ struct AttnArgs {
 };
 
 i4d_status launch_kv_append(const AppendArgs& a, hipStream_t st);
-i4d_status launch_attention(const AttnArgs& a, hipStream_t st);
-int attn_waves_per_group(int G);
+// nwa = waves per workgroup (4, 8 or 16).  With S > 1 the launch writes
+// per-split partials; combine = true adds the kernel that merges them into
+// attn_bf16 / attn_f32 (otherwise the consumer merges them itself).
+i4d_status launch_attention(const AttnArgs& a, int nwa, bool combine, hipStream_t st);
 
 }  // namespace i4d

@@ -141,6 +141,29 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
 // attention
 // ---------------------------------------------------------------------------
 
+// Codes of one dword as an exact f16 MFMA operand with no bias: the nibble
+// is the mantissa of an f16 subnormal, so e in {0, 1, 4, 5} -> u * 2^-24 and
+// e in {2, 3, 6, 7} -> 16 u * 2^-24 (nibble at mantissa bits 4-7).  The
+// partner operand carries a factor 1/16 at e in {2, 3, 6, 7}, so every
+// product is 2^-24 * (partner value) * u; the code offset 8 is removed after
+// the MFMA as 8 * (sum of the partner values).
+__device__ __forceinline__ f16x8_t dword_to_f16x8_sub(uint32_t w) {
+  const uint32_t t = w >> 8;
+  u32x4_t v;
+  v.x = w & 0x000F000Fu;
+  v.y = w & 0x00F000F0u;
+  v.z = t & 0x000F000Fu;
+  v.w = t & 0x00F000F0u;
+  return bitcast<f16x8_t>(v);
+}
+constexpr float kTwo24 = 16777216.0f;
+__device__ __forceinline__ bool slot16(int e) { return (e & 2) != 0; }
+
+// value of lane (l & ~15) | ((l + 8) & 15): the other half of a 16-lane row
+__device__ __forceinline__ float dpp_row_ror8(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, false));
+}
+
 template <int HD>
 struct BlockRegs {
   uint32_t kw[2][HD / 32];  // key codes, 2 tiles of 16 tokens
@@ -149,10 +172,8 @@ struct BlockRegs {
 };
 
 template <int HD>
-__device__ __forceinline__ void load_block(BlockRegs<HD>& b, const uint8_t* kbase, const uint32_t* vbase,
-                                           const uint16_t* ksc, const uint16_t* vsc, int blk, int c,
-                                           int jj) {
-  constexpr int KB = HD / 32, CB = HD / 16;
+__device__ __forceinline__ void load_keys(BlockRegs<HD>& b, const uint8_t* kbase, const uint16_t* ksc,
+                                          int blk, int c, int jj) {
   const int t0 = blk * kVBlock;
 #pragma unroll
   for (int tile = 0; tile < 2; ++tile) {
@@ -169,8 +190,17 @@ __device__ __forceinline__ void load_block(BlockRegs<HD>& b, const uint8_t* kbas
       b.kw[tile][1] = v.y;
     }
     b.ks[tile] = *reinterpret_cast<const u32x2_t*>(ksc + t0 + 16 * tile + 4 * jj);
-    b.vs[tile] = *reinterpret_cast<const u32x2_t*>(vsc + t0 + 16 * tile + 4 * jj);
   }
+}
+
+template <int HD>
+__device__ __forceinline__ void load_values(BlockRegs<HD>& b, const uint32_t* vbase, const uint16_t* vsc,
+                                            int blk, int c, int jj) {
+  constexpr int CB = HD / 16;
+  const int t0 = blk * kVBlock;
+#pragma unroll
+  for (int tile = 0; tile < 2; ++tile)
+    b.vs[tile] = *reinterpret_cast<const u32x2_t*>(vsc + t0 + 16 * tile + 4 * jj);
   const uint32_t* vp = vbase + (size_t)blk * 4 * HD + jj * HD + c * CB;
 #pragma unroll
   for (int q = 0; q < CB / 4; ++q) {
@@ -180,7 +210,14 @@ __device__ __forceinline__ void load_block(BlockRegs<HD>& b, const uint8_t* kbas
     b.vw[4 * q + 2] = v.z;
     b.vw[4 * q + 3] = v.w;
   }
-  (void)KB;
+}
+
+template <int HD>
+__device__ __forceinline__ void load_block(BlockRegs<HD>& b, const uint8_t* kbase, const uint32_t* vbase,
+                                           const uint16_t* ksc, const uint16_t* vsc, int blk, int c,
+                                           int jj) {
+  load_keys<HD>(b, kbase, ksc, blk, c, jj);
+  load_values<HD>(b, vbase, vsc, blk, c, jj);
 }
 
 __device__ __forceinline__ float f16_half(const u32x2_t& w, int i) {
@@ -210,9 +247,14 @@ __device__ __forceinline__ void inverse_rotate(float& o0, float& o1, int lane) {
   o1 *= scale;
 }
 
+// normalise, undo the rotation and store one head (one wave)
 template <int HD>
-__device__ __forceinline__ void write_output(const AttnArgs& a, size_t head_row, float o0, float o1,
-                                             int lane) {
+__device__ __forceinline__ void finish_head(const AttnArgs& a, size_t head_row, float lsum, float o0,
+                                            float o1, int lane) {
+  const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+  o0 *= inv;
+  o1 *= inv;
+  inverse_rotate<HD>(o0, o1, lane);
   const size_t base = head_row * HD;
   if (a.attn_f32) {
     a.attn_f32[base + lane] = o0;
@@ -222,14 +264,37 @@ __device__ __forceinline__ void write_output(const AttnArgs& a, size_t head_row,
   if (HD == 128) a.attn_bf16[base + lane + 64] = f32_to_bf16(o1);
 }
 
+// FWHT of one head (fp32, unnormalised) by one wave: channels lane and
+// lane + 64 in registers, stages h = 1 .. 32 across lanes, h = 64 in-lane.
+template <int HD>
+__device__ __forceinline__ void fwht_wave(float& x0, float& x1, int lane) {
+#pragma unroll
+  for (int h = 1; h < 64 && h < HD; h <<= 1) {
+    const float p0 = shfl_xor(x0, h);
+    x0 = (lane & h) ? (p0 - x0) : (x0 + p0);
+    if (HD == 128) {
+      const float p1 = shfl_xor(x1, h);
+      x1 = (lane & h) ? (p1 - x1) : (x1 + p1);
+    }
+  }
+  if (HD == 128) {
+    const float s0 = x0 + x1, s1 = x0 - x1;
+    x0 = s0;
+    x1 = s1;
+  }
+}
+
+// One workgroup per (row m, kv head j, split s); its NWA waves take
+// interleaved 32-token blocks of the split.
 template <int HD, int NWA>
 __global__ __launch_bounds__(NWA * 64) void attn_kernel(AttnArgs a) {
   constexpr int KB = HD / 32;  // 32-channel MFMA steps for q.k
   constexpr int CB = HD / 16;  // 16-channel output blocks
-  constexpr int GMAX = (NWA == 16) ? 4 : 8;
+  constexpr int GMAX = 8;
   __shared__ float wm[NWA][GMAX];
   __shared__ float wl[NWA][GMAX];
   __shared__ float wo[NWA][GMAX][HD];
+  float (*qrot)[HD] = wo[0];  // rotated queries [GMAX][HD], before the merge
 
   const KvArgs& kv = a.kv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -253,153 +318,150 @@ __global__ __launch_bounds__(NWA * 64) void attn_kernel(AttnArgs a) {
   const int b0 = s * bps;
   const int b1 = min(nblk, b0 + bps);
   const int64_t region = base * kv.n_kv + (int64_t)j * cap;
-
-  // decode step: the split holding position L-1 appends the new key/value
-  if (a.k_new && len_ok) {
-    const int last_blk = (L - 1) / kVBlock;
-    if (last_blk >= b0 && last_blk < b1) {
-      if (wave < 2) {
-        const uint16_t* src = (wave ? a.v_new : a.k_new) + ((size_t)m * kv.n_kv + j) * HD;
-        append_vector<HD>(kv, src, region, L - 1, wave, lane);
-      }
-      __syncthreads();
-    }
-  }
-
-  // rotated query as fp16 hi/lo B operands; column c < G is query head c
-  f16x8_t qhi[KB], qlo[KB];
-  {
-    float qv[KB][8];
-    const bool active = c < G;
-    const float* qsrc = a.q + ((size_t)m * a.n_q + (size_t)j * G + (active ? c : 0)) * HD + 8 * jj;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      if (active) {
-        const u32x4_t v0 = load16(qsrc + 32 * kb);
-        const u32x4_t v1 = load16(qsrc + 32 * kb + 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          qv[kb][e] = __uint_as_float(v0[e]);
-          qv[kb][4 + e] = __uint_as_float(v1[e]);
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qv[kb][e] = 0.f;
-      }
-    }
-    // channel = 32*kb + 8*jj + e: bits 0-2 in-lane (e), bits 3-4 across lanes
-    // (jj: lane ^ 16, lane ^ 32), bits 5-6 in-lane (kb)
-#pragma unroll
-    for (int h = 1; h < 8; h <<= 1)
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (!(e & h)) {
-            const float x = qv[kb][e], y = qv[kb][e + h];
-            qv[kb][e] = x + y;
-            qv[kb][e + h] = x - y;
-          }
-#pragma unroll
-    for (int hl = 16; hl <= 32; hl <<= 1) {
-      const bool upper = (lane & hl) != 0;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = shfl_xor(qv[kb][e], hl);
-          qv[kb][e] = upper ? (p - qv[kb][e]) : (qv[kb][e] + p);
-        }
-    }
-#pragma unroll
-    for (int h = 1; h < KB; h <<= 1)
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-        if (!(kb & h))
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float x = qv[kb][e], y = qv[kb + h][e];
-            qv[kb][e] = x + y;
-            qv[kb + h][e] = x - y;
-          }
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const _Float16 hi = (_Float16)qv[kb][e];
-        qhi[kb][e] = hi;
-        qlo[kb][e] = (_Float16)(qv[kb][e] - (float)hi);
-      }
-  }
-
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x4_t o[CB];
-#pragma unroll
-  for (int cb = 0; cb < CB; ++cb) o[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
   const uint8_t* kbase = kv.k_codes + (size_t)region * (HD / 2);
   const uint16_t* ksc = kv.k_scales + region;
   const uint16_t* vsc = kv.v_scales + region;
   const uint32_t* vbase = kv.v_codes + (size_t)(region / kVBlock) * 4 * HD;
+  // every load of the kernel is issued unconditionally (a wave without work
+  // reads a valid block it then ignores), so the compiler can wait on exact
+  // load counts instead of draining all loads at control-flow joins
+  const int last_valid = max(b1, 1) - 1;  // block 0 exists: capacity >= 32
+
+  // In a decode step the split holding position L-1 first appends the new
+  // key/value there.  Cache reads do not depend on the query, so every wave
+  // starts loading its first block now, except a load of the block being
+  // appended to, which waits for the append.
+  const int last_blk = (L - 1) / kVBlock;
+  const bool appending = a.k_new && len_ok && last_blk >= b0 && last_blk < b1;
+  int blk = b0 + wave;
+  const bool defer = appending && blk == last_blk;
+  BlockRegs<HD> cur;
+  if (!defer) load_block<HD>(cur, kbase, vbase, ksc, vsc, min(blk, last_valid), c, jj);
+
+  // rotate the G query heads of this kv head (one wave per head) into LDS
+  for (int g = wave; g < G; g += NWA) {
+    const float* src = a.q + ((size_t)m * a.n_q + (size_t)j * G + g) * HD;
+    float x0 = src[lane];
+    float x1 = (HD == 128) ? src[lane + 64] : 0.f;
+    fwht_wave<HD>(x0, x1, lane);
+    qrot[g][lane] = x0;
+    if (HD == 128) qrot[g][lane + 64] = x1;
+  }
+  if (appending && wave < 2) {
+    const uint16_t* src = (wave ? a.v_new : a.k_new) + ((size_t)m * kv.n_kv + j) * HD;
+    append_vector<HD>(kv, src, region, L - 1, wave, lane);
+  }
+  __syncthreads();
+
+  // Rotated query as the partner operand of q.k: columns c < 8 hold the
+  // high fp16 part of query head j*G + c (c < G), columns 8 + c the low part
+  // (the residual), with the factor 1/16 at e in {2,3,6,7}.  Each lane also
+  // keeps cq = 8 * sum of the query values its operand represents.
+  f16x8_t qop[KB];
+  float cq = 0.f;
+  {
+    const int head = c & 7;
+    const bool active = head < G;
+    const bool lo_part = c >= 8;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      float qv[8];
+      const float4* src = reinterpret_cast<const float4*>(&qrot[head][32 * kb + 8 * jj]);
+      const float4 v0 = src[0], v1 = src[1];
+      qv[0] = v0.x; qv[1] = v0.y; qv[2] = v0.z; qv[3] = v0.w;
+      qv[4] = v1.x; qv[5] = v1.y; qv[6] = v1.z; qv[7] = v1.w;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float w = active ? (slot16(e) ? qv[e] * 0.0625f : qv[e]) : 0.f;
+        const _Float16 hi = (_Float16)w;
+        const _Float16 op = lo_part ? (_Float16)(w - (float)hi) : hi;
+        qop[kb][e] = op;
+        cq = fmaf((float)op, slot16(e) ? 128.f : 8.f, cq);
+      }
+    }
+    cq += shfl_xor(cq, 16);
+    cq += shfl_xor(cq, 32);
+  }
+  if (defer) {
+    // the CU's L1 may hold lines of this block from before the append
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    load_block<HD>(cur, kbase, vbase, ksc, vsc, blk, c, jj);
+  }
+  __syncthreads();  // qrot shares LDS with the merge buffers
+
+  float m_run = -INFINITY, l_run = 0.f, psum = 0.f;
+  f32x4_t o[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) o[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const float sscale = a.score_scale;
 
-  int blk = b0 + wave;
-  BlockRegs<HD> cur;
-  if (blk < b1) load_block<HD>(cur, kbase, vbase, ksc, vsc, blk, c, jj);
-  for (; blk < b1; blk += NWA) {
-    BlockRegs<HD> nxt;
-    const bool more = blk + NWA < b1;
-    if (more) load_block<HD>(nxt, kbase, vbase, ksc, vsc, blk + NWA, c, jj);
+  // One block in registers; the next block's keys are requested once the
+  // current keys are consumed, its values once the current values are.  The
+  // last block of the wave runs the same body without those requests.
+  auto body = [&](const int nb, const bool prefetch) {
     const int t0 = blk * kVBlock;
-
     float sc[8];
     float mx = -INFINITY;
 #pragma unroll
     for (int tile = 0; tile < 2; ++tile) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const f16x8_t kf = dword_to_f16x8_signed_fast(cur.kw[tile][kb]);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qhi[kb], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qlo[kb], acc, 0, 0, 0);
-      }
+      for (int kb = 0; kb < KB; ++kb)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(dword_to_f16x8_sub(cur.kw[tile][kb]), qop[kb], acc,
+                                                     0, 0, 0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
+        // high part (column c) + low part (column c + 8, rotated in by DPP)
+        const float part = fmaf(acc[i], kTwo24, -cq);
+        const float full = part + dpp_row_ror8(part);
         const int tok = t0 + 16 * tile + 4 * jj + i;
-        const float v = (tok < L) ? acc[i] * f16_half(cur.ks[tile], i) * sscale : -INFINITY;
-        sc[tile * 4 + i] = v;
-        mx = fmaxf(mx, v);
+        const float v = full * f16_half(cur.ks[tile], i) * sscale;
+        sc[tile * 4 + i] = (tok < L) ? v : -INFINITY;
+        mx = fmaxf(mx, sc[tile * 4 + i]);
       }
     }
+    if (prefetch) load_keys<HD>(cur, kbase, ksc, nb, c, jj);
     mx = fmaxf(mx, shfl_xor(mx, 16));
     mx = fmaxf(mx, shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    if (__any(m_new > m_run)) {
-      const float alpha = exp2f(m_run - m_new);
-      l_run *= alpha;
+    const float m_new = fmaxf(m_run, mx);  // finite: the block holds a valid token
+    const float alpha = exp2f(m_run - m_new);
+    l_run *= alpha;
+    psum *= alpha;
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) o[cb] *= alpha;
-    }
+    for (int cb = 0; cb < CB; ++cb) o[cb] *= alpha;
+    // P operand: element e is token 4jj+e (e < 4) or 16+4jj+e-4 (e >= 4),
+    // i.e. score register e; value scale folded in, 1/16 at e in {2,3,6,7}
     f16x8_t pb;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int tile = q >> 2, i = q & 3;
-      const int tok = t0 + 16 * tile + 4 * jj + i;
-      const float p = (tok < L) ? exp2f(sc[q] - m_new) : 0.f;
+    for (int e = 0; e < 8; ++e) {
+      const int tile = e >> 2, i = e & 3;
+      const float p = exp2f(sc[e] - m_new);  // 0 for masked tokens
       l_run += p;
-      const float pv = (tok < L && c < G) ? p * f16_half(cur.vs[tile], i) : 0.f;
-      pb[q] = (_Float16)pv;
+      float pv = p * f16_half(cur.vs[tile], i);
+      pv = (c < G && p > 0.f) ? pv : 0.f;
+      if (slot16(e)) pv *= 0.0625f;
+      const _Float16 ph = (_Float16)pv;
+      pb[e] = ph;
+      psum = fmaf((float)ph, slot16(e) ? 16.f : 1.f, psum);
     }
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
-      o[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dword_to_f16x8_signed_fast(cur.vw[cb]), pb, o[cb],
-                                                     0, 0, 0);
+      o[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dword_to_f16x8_sub(cur.vw[cb]), pb, o[cb], 0, 0, 0);
+    if (prefetch) load_values<HD>(cur, vbase, vsc, nb, c, jj);
     m_run = m_new;
-    if (more) cur = nxt;
+  };
+  if (blk < b1) {
+    for (; blk + NWA < b1; blk += NWA) body(blk + NWA, true);
+    body(blk, false);
   }
 
+  // per-column totals over the 4 lane quarters; undo the 2^-24 operand
+  // scale and remove the code offset: o = 2^24 acc - 8 * sum p'
   l_run += shfl_xor(l_run, 16);
   l_run += shfl_xor(l_run, 32);
+  psum += shfl_xor(psum, 16);
+  psum += shfl_xor(psum, 32);
+  const float vbias = 8.f * psum;
   if (c < G) {
     if (jj == 0) {
       wm[wave][c] = m_run;
@@ -408,13 +470,12 @@ __global__ __launch_bounds__(NWA * 64) void attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) wo[wave][c][16 * cb + 4 * jj + i] = o[cb][i];
+      for (int i = 0; i < 4; ++i) wo[wave][c][16 * cb + 4 * jj + i] = fmaf(o[cb][i], kTwo24, -vbias);
   }
   __syncthreads();
 
-  // wave g merges head g over the waves
-  if (wave < G) {
-    const int g = wave;
+  // wave w merges heads w, w + NWA, ... over the waves
+  for (int g = wave; g < G; g += NWA) {
     float M_ = -INFINITY;
     for (int w = 0; w < NWA; ++w)
       if (wl[w][g] > 0.f) M_ = fmaxf(M_, wm[w][g]);
@@ -429,11 +490,7 @@ __global__ __launch_bounds__(NWA * 64) void attn_kernel(AttnArgs a) {
     }
     const size_t head_row = (size_t)m * a.n_q + (size_t)j * G + g;
     if (S == 1) {
-      const float inv = 1.0f / lsum;
-      o0 *= inv;
-      o1 *= inv;
-      inverse_rotate<HD>(o0, o1, lane);
-      write_output<HD>(a, head_row, o0, o1, lane);
+      finish_head<HD>(a, head_row, lsum, o0, o1, lane);
     } else {
       const size_t ph = head_row * S + s;
       a.part_o[ph * HD + lane] = o0;
@@ -446,33 +503,71 @@ __global__ __launch_bounds__(NWA * 64) void attn_kernel(AttnArgs a) {
   }
 }
 
-// merge the splits of one (row, q head) and undo the rotation: o = H o~ / hd
+// Merge the splits of one (row, q head) and undo the rotation:
+// o = H o~ / hd with o~ = sum_s e^(m_s - m) o~_s / sum_s e^(m_s - m) l_s.
+// One wave per (row, head); lane t holds split t (t + 64, ...) for the
+// weights, the partial outputs are read with independent loads.
+template <int HD>
+__device__ __forceinline__ void combine_head(const AttnArgs& a, size_t head_row, int lane, float& lsum_out,
+                                             float& o0_out, float& o1_out) {
+  const int S = a.S;
+  const float* ml = a.part_ml + head_row * S * 2;
+  const float* po = a.part_o + head_row * S * HD;
+  float M_ = -INFINITY;
+  for (int t = lane; t < S; t += 64)
+    if (ml[2 * t + 1] > 0.f) M_ = fmaxf(M_, ml[2 * t]);
+  M_ = wave_max(M_);
+  float lsum = 0.f, o0 = 0.f, o1 = 0.f;
+  for (int t0 = 0; t0 < S; t0 += 64) {
+    const int t = t0 + lane;
+    float f = 0.f;
+    if (t < S) {
+      const float l = ml[2 * t + 1];
+      if (l > 0.f) {
+        f = exp2f(ml[2 * t] - M_);
+        lsum = fmaf(f, l, lsum);
+      }
+    }
+    const int n = min(64, S - t0);
+    int u = 0;
+    for (; u + 4 <= n; u += 4) {
+      float fu[4], x0[4], x1[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        fu[q] = __shfl(f, u + q, 64);
+        x0[q] = po[(size_t)(t0 + u + q) * HD + lane];
+        x1[q] = (HD == 128) ? po[(size_t)(t0 + u + q) * HD + lane + 64] : 0.f;
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (fu[q] > 0.f) {
+          o0 = fmaf(fu[q], x0[q], o0);
+          o1 = fmaf(fu[q], x1[q], o1);
+        }
+    }
+    for (; u < n; ++u) {
+      const float fu = __shfl(f, u, 64);
+      if (fu > 0.f) {
+        o0 = fmaf(fu, po[(size_t)(t0 + u) * HD + lane], o0);
+        if (HD == 128) o1 = fmaf(fu, po[(size_t)(t0 + u) * HD + lane + 64], o1);
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) lsum += shfl_xor(lsum, off);
+  lsum_out = lsum;
+  o0_out = o0;
+  o1_out = o1;
+}
+
 template <int HD>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   const int lane = threadIdx.x & 63;
   const int idx = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (idx >= a.M * a.n_q) return;
-  const int S = a.S;
-  const float* ml = a.part_ml + (size_t)idx * S * 2;
-  const float* po = a.part_o + (size_t)idx * S * HD;
-  float M_ = -INFINITY;
-  for (int s = 0; s < S; ++s)
-    if (ml[2 * s + 1] > 0.f) M_ = fmaxf(M_, ml[2 * s]);
-  float lsum = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int s = 0; s < S; ++s) {
-    const float l = ml[2 * s + 1];
-    if (l > 0.f) {
-      const float f = exp2f(ml[2 * s] - M_);
-      lsum += f * l;
-      o0 += f * po[(size_t)s * HD + lane];
-      if (HD == 128) o1 += f * po[(size_t)s * HD + lane + 64];
-    }
-  }
-  const float inv = 1.0f / lsum;
-  o0 *= inv;
-  o1 *= inv;
-  inverse_rotate<HD>(o0, o1, lane);
-  write_output<HD>(a, (size_t)idx, o0, o1, lane);
+  float lsum, o0, o1;
+  combine_head<HD>(a, (size_t)idx, lane, lsum, o0, o1);
+  finish_head<HD>(a, (size_t)idx, lsum, o0, o1, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -491,26 +586,33 @@ i4d_status launch_kv_append(const AppendArgs& a, hipStream_t st) {
 }
 
 template <int HD>
-static void launch_attn_hd(const AttnArgs& a, hipStream_t st) {
+static void launch_attn_hd(const AttnArgs& a, int nwa, hipStream_t st) {
   const int grid = a.M * a.kv.n_kv * a.S;
-  if (a.G <= 4)
-    hipLaunchKernelGGL((attn_kernel<HD, 16>), dim3(grid), dim3(16 * 64), 0, st, a);
-  else
+  if (nwa == 4)
+    hipLaunchKernelGGL((attn_kernel<HD, 4>), dim3(grid), dim3(4 * 64), 0, st, a);
+  else if (nwa == 8)
     hipLaunchKernelGGL((attn_kernel<HD, 8>), dim3(grid), dim3(8 * 64), 0, st, a);
-  if (a.S > 1)
-    hipLaunchKernelGGL(attn_combine_kernel<HD>, dim3((a.M * a.n_q + 3) / 4), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_kernel<HD, 16>), dim3(grid), dim3(16 * 64), 0, st, a);
 }
 
-i4d_status launch_attention(const AttnArgs& a, hipStream_t st) {
+i4d_status launch_attention(const AttnArgs& a, int nwa, bool combine, hipStream_t st) {
+  if (nwa != 4 && nwa != 8 && nwa != 16) return fail(I4D_ERR_RANGE, "attention waves %d", nwa);
+  if (a.G < 1 || a.G > 8) return fail(I4D_ERR_UNSUPPORTED, "GQA group %d > 8", a.G);
   if (a.kv.hd == 128)
-    launch_attn_hd<128>(a, st);
+    launch_attn_hd<128>(a, nwa, st);
   else
-    launch_attn_hd<64>(a, st);
+    launch_attn_hd<64>(a, nwa, st);
+  if (combine && a.S > 1) {
+    const dim3 grid((a.M * a.n_q + 3) / 4);
+    if (a.kv.hd == 128)
+      hipLaunchKernelGGL(attn_combine_kernel<128>, grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL(attn_combine_kernel<64>, grid, dim3(256), 0, st, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(I4D_ERR_HIP, "attention launch: %s", hipGetErrorString(e));
   return ok();
 }
-
-int attn_waves_per_group(int G) { return G <= 4 ? 16 : 8; }
 
 }  // namespace i4d

@@ -18,11 +18,13 @@ bool aligned16(const void* p);
 // validates a layer shape (returns I4D_OK or the error, message set)
 i4d_status check_shape(const i4d_layer_shape* s);
 
-// number of KV splits used for the attention launch
-int choose_splits(const i4d_layer_shape* s, int M, int max_ctx_len, int num_splits);
-
-// waves per attention workgroup (16 when G <= 4, 8 when G = 8)
-inline int attn_waves(int G) { return G <= 4 ? 16 : 8; }
+// launch plan of the attention kernel: KV splits per (row, kv head) and
+// waves per workgroup
+struct AttnPlan {
+  int S;
+  int nwa;
+};
+AttnPlan attn_plan(const i4d_layer_shape* s, int M, int max_ctx_len, int num_splits);
 
 struct AttnWs {
   size_t ml;      // fp32 [M][n_q][S][2]   (running max in log2 units, sum)

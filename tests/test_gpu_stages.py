@@ -97,6 +97,9 @@ ATTN_CASES = [
     (64, 8, 2, [300, 45], 16),
     (128, 8, 2, [70, 45], 64),              # more splits than blocks: empty splits
     (128, 32, 8, [2048], 0),                # 8B head layout
+    (128, 4, 4, [200, 1000], 0),            # G = 1
+    (128, 16, 2, [4096, 3000], 2),          # G = 8, 16 waves per workgroup
+    (64, 8, 2, [4096, 17], 2),              # hd 64, 16 waves per workgroup, one short row
 ]
 
 
@@ -130,6 +133,37 @@ def test_attention_parity(gpu, hd, n_q, n_kv, lengths, S):
     assert err <= ATT_TOL
     # the bf16 copy is the rounded fp32 output
     np.testing.assert_array_equal(D.to_host_u16(out16), synth.f32_to_bf16_bits(got))
+
+
+def test_attention_workspace_reuse(gpu):
+    """Two calls on one workspace that starts out dirty give identical
+    outputs (nothing in the workspace is read before it is written)."""
+    torch, B, D = gpu
+    hd, n_q, n_kv, lengths = 128, 8, 2, [900, 1500]
+    shape = synth.LayerShape(n_q * hd, n_q, n_kv, hd, 512)
+    rng = np.random.default_rng(5)
+    M = len(lengths)
+    k_rows = [random_bf16(rng, (L, n_kv, hd), 1.0, hd // 16) for L in lengths]
+    v_rows = [random_bf16(rng, (L, n_kv, hd), 1.0, hd // 16) for L in lengths]
+    q = torch.from_numpy((rng.standard_normal((M, n_q, hd)) * 1.3).astype(np.float32)).cuda()
+    cache = D.DeviceCache(shape, lengths)
+    cache.prefill(synth.CachePrefill(k_rows, v_rows))
+    cshape = B.make_shape(shape)
+    nbytes = B.i4d_attention_workspace_bytes(cshape, M, max(lengths), 8)
+    ws = torch.full((nbytes,), 0x7f, dtype=torch.uint8, device="cuda")
+    ctx = torch.tensor(lengths, dtype=torch.int32, device="cuda")
+    outs = []
+    say("attention workspace reuse, 8 splits")
+    for _ in range(2):
+        o32 = torch.empty((M, n_q * hd), dtype=torch.float32, device="cuda")
+        o16 = torch.empty((M, n_q * hd), dtype=torch.int16, device="cuda")
+        B.i4d_attention(cache.struct, cshape, q, ctx, M, max(lengths), 8, ws, nbytes, o32, o16)
+        torch.cuda.synchronize()
+        outs.append(o32.cpu().numpy())
+    np.testing.assert_array_equal(outs[0], outs[1])
+    ref = O.attention_stage(shape, oracle_cache_from_tokens(shape, k_rows, v_rows),
+                            q.cpu().numpy().astype(np.float64), lengths)
+    assert norm_maxabs(outs[0], ref) <= ATT_TOL
 
 
 # ---------------------------------------------------------------------------
@@ -258,6 +292,34 @@ def check_block(res, label=""):
 ])
 def test_block_small(gpu, shape, lengths):
     check_block(run_block(gpu, shape, 11, lengths))
+
+
+def test_block_dirty_workspace_forced_splits(gpu):
+    """A workspace holding garbage and a forced split count: nothing in the
+    workspace is read before the step writes it."""
+    torch, B, D = gpu
+    shape, seed, lengths = synth.SHAPE_SMALL128, 13, np.array([700, 1200, 45], np.int32)
+    M, maxL = len(lengths), int(lengths.max())
+    lw = synth.make_layer(shape, seed)
+    pre = synth.make_cache_prefill(shape, lengths, seed)
+    xb = synth.make_x(shape, M, seed)
+    layer = D.DeviceLayer(shape, lw)
+    cache = D.DeviceCache(shape, lengths)
+    cache.prefill(pre)
+    ws = D.Workspace(shape, M, maxL, 6)
+    ws.buf.fill_(0xA5)
+    x_in = D.to_device_u16(xb)
+    x_out = torch.empty_like(x_in)
+    ctx = torch.from_numpy(lengths).cuda()
+    attn = torch.empty((M, shape.n_q_heads * shape.head_dim), dtype=torch.float32, device="cuda")
+    say("block with a dirty workspace, 6 splits")
+    B.i4d_decode_block_step(layer.struct, cache.struct, x_in, x_out, ctx, M, maxL, 6, ws.buf, ws.nbytes,
+                            attn)
+    torch.cuda.synchronize()
+    ref = O.decode_block(shape, O.quantize_layer(lw), O.build_cache(shape, lengths, pre), xb, lengths)
+    assert cache.errors() == 0
+    assert rel_rms(D.bf16_tensor_to_f32(x_out), ref.out) <= REL_TOL
+    assert norm_maxabs(attn.cpu().numpy(), ref.attn) <= ATT_TOL
 
 
 def test_block_deterministic(gpu):
