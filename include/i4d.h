@@ -62,6 +62,7 @@ typedef enum {
  * clamped to the row's capacity (attention), so no access leaves the cache. */
 #define I4D_DEVERR_APPEND_POS 1 /* kv_append: pos outside [0, capacity) */
 #define I4D_DEVERR_CTX_LEN 2    /* attention: ctx_len outside [1, capacity] */
+#define I4D_DEVERR_SYNC 4       /* one-launch decode step: a stage wait timed out (results invalid) */
 
 const char* i4d_last_error(void);
 
@@ -265,9 +266,15 @@ i4d_status i4d_ffn_gate_up(const i4d_layer* layer, const uint16_t* h_bf16, int M
 i4d_status i4d_ffn_down(const i4d_layer* layer, const uint16_t* a, const float* h, int M,
                         uint16_t* x_out, void* stream);
 
-/* Workspace of i4d_decode_block_step. */
+/* Workspace of i4d_decode_block_step.  The workspace must be zero-filled
+ * (or passed to i4d_workspace_init) once before its first use; every step
+ * leaves its counters at zero again, so later steps need nothing. */
 i4d_status i4d_workspace_bytes(const i4d_layer_shape* shape, int M, int max_ctx_len,
                                int num_splits, size_t* bytes);
+
+/* Zero-fill a decode-step workspace (device, `bytes` long, 16-byte aligned)
+ * on `stream`. */
+i4d_status i4d_workspace_init(void* workspace, size_t bytes, void* stream);
 
 /* Byte offsets of the intermediates inside the decode-step workspace (for
  * inspection by tests; all 256-byte aligned). */
@@ -280,6 +287,7 @@ typedef struct {
   size_t h_bf16; /* bf16 [M][d] */
   size_t a;     /* bf16 [M][d_ffn] */
   size_t attn_ws; /* start of the attention workspace */
+  size_t sync;    /* counters of the one-launch step (must be zero before first use) */
   size_t total;
 } i4d_workspace_layout;
 i4d_status i4d_workspace_layout_of(const i4d_layer_shape* shape, int M, int max_ctx_len,
@@ -290,6 +298,12 @@ i4d_status i4d_workspace_layout_of(const i4d_layer_shape* shape, int M, int max_
  * (position ctx_len[m]-1) is appended by this call.  Runs stages 1-7:
  * QKV (+rho1, RoPE) -> kv_append of bf16 k, v at ctx_len-1 -> attention ->
  * O + residual -> gate/up + SwiGLU (+rho2) -> down + residual.
+ * For M = 1 the stages run in one persistent launch with one 16-wave
+ * workgroup per CU (each stage's weight loads start before the previous
+ * stage completes); it needs the GPU to itself for the duration of the
+ * call (its workgroups wait on each other; a wait that times out sets
+ * I4D_DEVERR_SYNC in the cache's err_word).  Other M, and shapes the
+ * one-launch kernel does not cover, run one launch per stage.
  * x_in, x_out: bf16 device [M][d] (may not alias).  ctx_len: device int32
  * [M].  attn_f32: optional device fp32 [M][n_q*hd] copy of the attention
  * output.  Re-running the step with the same inputs rewrites the same cache

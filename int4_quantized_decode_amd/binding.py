@@ -23,6 +23,7 @@ I4D_MAX_ROWS = 32
 I4D_MAX_SPLITS = 256
 I4D_DEVERR_APPEND_POS = 1
 I4D_DEVERR_CTX_LEN = 2
+I4D_DEVERR_SYNC = 4
 
 STATUS_NAMES = {0: "I4D_OK", -1: "I4D_ERR_NULL", -2: "I4D_ERR_SHAPE", -3: "I4D_ERR_UNSUPPORTED",
                 -4: "I4D_ERR_ALIGN", -5: "I4D_ERR_WORKSPACE", -6: "I4D_ERR_RANGE", -7: "I4D_ERR_HIP"}
@@ -58,7 +59,8 @@ class i4d_layer(ctypes.Structure):
 
 
 class i4d_workspace_layout(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_size_t) for n in ("q", "k", "v", "attn", "h", "h_bf16", "a", "attn_ws", "total")]
+    _fields_ = [(n, ctypes.c_size_t) for n in ("q", "k", "v", "attn", "h", "h_bf16", "a", "attn_ws", "sync",
+                                               "total")]
 
 
 _VP = ctypes.c_void_p
@@ -83,6 +85,7 @@ _SIGS = {
     "i4d_workspace_bytes": (_I, [ctypes.POINTER(i4d_layer_shape), _I, _I, _I, c_size_p]),
     "i4d_workspace_layout_of": (_I, [ctypes.POINTER(i4d_layer_shape), _I, _I, _I,
                                      ctypes.POINTER(i4d_workspace_layout)]),
+    "i4d_workspace_init": (_I, [_VP, ctypes.c_size_t, _VP]),
     "i4d_decode_block_step": (_I, [ctypes.POINTER(i4d_layer), ctypes.POINTER(i4d_kv_cache), _VP, _VP, _VP,
                                    _I, _I, _I, _VP, ctypes.c_size_t, _VP, _VP]),
     "i4d_lm_head_workspace_bytes": (_I, [_I, _I, c_size_p]),
@@ -233,6 +236,10 @@ def i4d_workspace_layout_of(shape: i4d_layer_shape, M: int, max_ctx_len: int, nu
     out = i4d_workspace_layout()
     _check(lib().i4d_workspace_layout_of(ctypes.byref(shape), M, max_ctx_len, num_splits, ctypes.byref(out)))
     return out
+
+
+def i4d_workspace_init(workspace, nbytes: int, stream=None):
+    _check(lib().i4d_workspace_init(ptr(workspace), nbytes, stream_handle(stream)))
 
 
 def i4d_lm_head_workspace_bytes(V: int, M: int):

@@ -4,9 +4,11 @@
 #include <math.h>
 
 #include "attn.h"
+#include "device_common.h"
 #include "i4d_internal.h"
 #include "lmhead.h"
 #include "proj.h"
+#include "step.h"
 
 using namespace i4d;
 
@@ -93,8 +95,8 @@ ProjArgs proj_args(const void* codes, const uint16_t* scales, const uint16_t* x,
   return a;
 }
 
-i4d_status do_qkv(const i4d_layer* L, const uint16_t* x, const int32_t* ctx_len, int M, float* q,
-                  uint16_t* k, uint16_t* v, hipStream_t st) {
+ProjArgs qkv_args(const i4d_layer* L, const uint16_t* x, const int32_t* ctx_len, int M, float* q,
+                  uint16_t* k, uint16_t* v) {
   const i4d_layer_shape& s = L->shape;
   ProjArgs a = proj_args(L->qkv_codes, L->qkv_scales, x,
                          (s.n_q_heads + 2 * s.n_kv_heads) * s.head_dim, s.d_model, M, s.rms_eps);
@@ -106,14 +108,18 @@ i4d_status do_qkv(const i4d_layer* L, const uint16_t* x, const int32_t* ctx_len,
   a.n_kv = s.n_kv_heads;
   a.hd = s.head_dim;
   a.theta = s.rope_theta;
-  return launch_projection(EPI_QKV, a, st);
+  a.rope_ratio = pow((double)s.rope_theta, -2.0 / (double)s.head_dim);
+  return a;
 }
 
-i4d_status do_attention(const i4d_kv_cache* c, const i4d_layer_shape& s, const float* q,
-                        const int32_t* ctx_len, int M, int max_ctx_len, int num_splits, void* ws,
-                        float* attn_f32, uint16_t* attn_bf16, const uint16_t* k_new,
-                        const uint16_t* v_new, bool combine, hipStream_t st) {
-  const AttnPlan plan = attn_plan(&s, M, max_ctx_len, num_splits);
+i4d_status do_qkv(const i4d_layer* L, const uint16_t* x, const int32_t* ctx_len, int M, float* q,
+                  uint16_t* k, uint16_t* v, hipStream_t st) {
+  return launch_projection(EPI_QKV, qkv_args(L, x, ctx_len, M, q, k, v), st);
+}
+
+AttnArgs attention_args(const i4d_kv_cache* c, const i4d_layer_shape& s, const float* q,
+                        const int32_t* ctx_len, int M, int S, void* ws, float* attn_f32,
+                        uint16_t* attn_bf16, const uint16_t* k_new, const uint16_t* v_new) {
   AttnArgs a;
   a.kv = kv_args(c);
   a.q = q;
@@ -123,41 +129,68 @@ i4d_status do_attention(const i4d_kv_cache* c, const i4d_layer_shape& s, const f
   a.M = M;
   a.n_q = s.n_q_heads;
   a.G = s.n_q_heads / s.n_kv_heads;
-  a.S = plan.S;
+  a.S = S;
   a.score_scale = (float)(1.4426950408889634 / ((double)s.head_dim * sqrt((double)s.head_dim)));
   AttnWs w = attn_ws_layout(&s, M, a.S);
   a.part_ml = (float*)((char*)ws + w.ml);
   a.part_o = (float*)((char*)ws + w.o);
   a.attn_f32 = attn_f32;
   a.attn_bf16 = attn_bf16;
+  return a;
+}
+
+i4d_status do_attention(const i4d_kv_cache* c, const i4d_layer_shape& s, const float* q,
+                        const int32_t* ctx_len, int M, int max_ctx_len, int num_splits, void* ws,
+                        float* attn_f32, uint16_t* attn_bf16, const uint16_t* k_new,
+                        const uint16_t* v_new, bool combine, hipStream_t st) {
+  const AttnPlan plan = attn_plan(&s, M, max_ctx_len, num_splits);
+  const AttnArgs a = attention_args(c, s, q, ctx_len, M, plan.S, ws, attn_f32, attn_bf16, k_new, v_new);
   return launch_attention(a, plan.nwa, combine, st);
 }
 
-i4d_status do_o(const i4d_layer* L, const uint16_t* attn, const uint16_t* x, int M, float* h,
-                uint16_t* hb, hipStream_t st) {
+ProjArgs o_args(const i4d_layer* L, const uint16_t* attn, const uint16_t* x, int M, float* h,
+                uint16_t* hb) {
   const i4d_layer_shape& s = L->shape;
   ProjArgs a = proj_args(L->o_codes, L->o_scales, attn, s.d_model, s.n_q_heads * s.head_dim, M,
                          s.rms_eps);
   a.resid_bf16 = x;
   a.h_f32 = h;
   a.h_bf16 = hb;
-  return launch_projection(EPI_O, a, st);
+  return a;
 }
 
-i4d_status do_gu(const i4d_layer* L, const uint16_t* hb, int M, uint16_t* out, hipStream_t st) {
+ProjArgs gu_args(const i4d_layer* L, const uint16_t* hb, int M, uint16_t* out) {
   const i4d_layer_shape& s = L->shape;
   ProjArgs a = proj_args(L->gu_codes, L->gu_scales, hb, 2 * s.d_ffn, s.d_model, M, s.rms_eps);
   a.a_out = out;
-  return launch_projection(EPI_GU, a, st);
+  return a;
 }
 
-i4d_status do_down(const i4d_layer* L, const uint16_t* act, const float* h, int M, uint16_t* out,
-                   hipStream_t st) {
+ProjArgs down_args(const i4d_layer* L, const uint16_t* act, const float* h, int M, uint16_t* out) {
   const i4d_layer_shape& s = L->shape;
   ProjArgs a = proj_args(L->down_codes, L->down_scales, act, s.d_model, s.d_ffn, M, s.rms_eps);
   a.resid_f32 = h;
   a.out_bf16 = out;
-  return launch_projection(EPI_DOWN, a, st);
+  return a;
+}
+
+i4d_status do_o(const i4d_layer* L, const uint16_t* attn, const uint16_t* x, int M, float* h,
+                uint16_t* hb, hipStream_t st) {
+  return launch_projection(EPI_O, o_args(L, attn, x, M, h, hb), st);
+}
+
+i4d_status do_gu(const i4d_layer* L, const uint16_t* hb, int M, uint16_t* out, hipStream_t st) {
+  return launch_projection(EPI_GU, gu_args(L, hb, M, out), st);
+}
+
+i4d_status do_down(const i4d_layer* L, const uint16_t* act, const float* h, int M, uint16_t* out,
+                   hipStream_t st) {
+  return launch_projection(EPI_DOWN, down_args(L, act, h, M, out), st);
+}
+
+__global__ void zero_fill_kernel(u32x4_t* p, size_t n16) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = u32x4_t{0u, 0u, 0u, 0u};
 }
 
 }  // namespace
@@ -280,6 +313,18 @@ i4d_status i4d_decode_block_step(const i4d_layer* layer, const i4d_kv_cache* cac
   uint16_t* act = (uint16_t*)(ws + wl.a);
   const i4d_layer_shape& s = layer->shape;
 
+  if (M == 1 && step_m1_supported(&s)) {
+    StepInputs in;
+    in.layer = layer;
+    in.qkv = qkv_args(layer, x_in, ctx_len, 1, q, k, v);
+    in.o = o_args(layer, attn, x_in, 1, h, hb);
+    in.gu = gu_args(layer, hb, 1, act);
+    in.down = down_args(layer, act, h, 1, x_out);
+    in.attn = attention_args(cache, s, q, ctx_len, 1, step_m1_splits(&s, max_ctx_len, num_splits),
+                             ws + wl.attn_ws, attn_f32, attn, k, v);
+    in.sync = (unsigned*)(ws + wl.sync);
+    return launch_step_m1(in, st);
+  }
   I4D_TRY(do_qkv(layer, x_in, ctx_len, M, q, k, v, st));
   // the attention launch first appends the new token of row m at position
   // ctx_len[m] - 1 of cache row m (inside the workgroup that owns that block)
@@ -288,6 +333,18 @@ i4d_status i4d_decode_block_step(const i4d_layer* layer, const i4d_kv_cache* cac
   I4D_TRY(do_o(layer, attn, x_in, M, h, hb, st));
   I4D_TRY(do_gu(layer, hb, M, act, st));
   I4D_TRY(do_down(layer, act, h, M, x_out, st));
+  return ok();
+}
+
+i4d_status i4d_workspace_init(void* workspace, size_t bytes, void* stream) {
+  I4D_TRY(need(workspace, "workspace"));
+  if (bytes % 16) return fail(I4D_ERR_RANGE, "workspace bytes %zu not a multiple of 16", bytes);
+  if (bytes == 0) return ok();
+  const size_t n16 = bytes / 16;
+  const unsigned grid = (unsigned)std::min<size_t>(1024, (n16 + 255) / 256);
+  hipLaunchKernelGGL(zero_fill_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, (u32x4_t*)workspace, n16);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(I4D_ERR_HIP, "workspace init: %s", hipGetErrorString(e));
   return ok();
 }
 

@@ -77,6 +77,12 @@ AttnPlan attn_plan(const i4d_layer_shape* s, int M, int max_ctx_len, int num_spl
   return p;
 }
 
+int step_m1_splits(const i4d_layer_shape* s, int max_ctx_len, int num_splits) {
+  if (num_splits > 0) return std::min(num_splits, I4D_MAX_SPLITS);
+  const int nblk = (max_ctx_len + kVBlock - 1) / kVBlock;
+  return std::max(1, std::min(256 / s->n_kv_heads, nblk));
+}
+
 AttnWs attn_ws_layout(const i4d_layer_shape* s, int M, int S) {
   AttnWs w;
   size_t n = (size_t)M * s->n_q_heads * S;
@@ -366,6 +372,8 @@ i4d_status i4d_workspace_layout_of(const i4d_layer_shape* s, int M, int max_ctx_
   size_t attn_bytes;
   i4d_status st = i4d_attention_workspace_bytes(s, M, max_ctx_len, num_splits, &attn_bytes);
   if (st) return st;
+  if (M == 1)  // the one-launch step may use another split count
+    attn_bytes = std::max(attn_bytes, attn_ws_layout(s, 1, step_m1_splits(s, max_ctx_len, num_splits)).total);
   size_t nq = (size_t)M * s->n_q_heads * s->head_dim;
   size_t nk = (size_t)M * s->n_kv_heads * s->head_dim;
   size_t off = 0;
@@ -377,6 +385,7 @@ i4d_status i4d_workspace_layout_of(const i4d_layer_shape* s, int M, int max_ctx_
   out->h_bf16 = off;  off += align256((size_t)M * s->d_model * 2);
   out->a = off;       off += align256((size_t)M * s->d_ffn * 2);
   out->attn_ws = off; off += align256(attn_bytes);
+  out->sync = off;    off += align256(kStepSyncBytes);
   out->total = off;
   return ok();
 }

@@ -1,0 +1,551 @@
+// attn_core.h - INT4 KV append and GQA decode attention as device functions,
+// shared by the stand-alone kernels and the one-launch decode step.
+//
+// Append: one wave rotates one key or value vector with the unnormalised fast
+//   Walsh-Hadamard transform in fp32 (stage order h = 1, 2, 4, ...; the
+//   cross-lane stages use lane shuffles with the same add DAG as the plain
+//   transform, so the result is bit-identical), takes the absmax, quantizes
+//   with scale = fp16(absmax / 7) (correctly rounded fp32 division) and writes
+//   the codes in the MFMA operand layout of the cache ("how it differs":
+//   rotation before cache quantization; "how it works": direct placement at
+//   offset(request, head, position, channel)).
+//
+// Attention: one workgroup per (row, kv head, split) with 4, 8 or 16 waves
+//   that take interleaved 32-token blocks.  Per block and wave:
+//     S[token][col] = K_codes(16 tokens x hd) . q~  (MFMA, fp16; the rotated
+//                     query's high part in columns c < 8, its residual in
+//                     columns 8 + c, recombined by a DPP row rotation)
+//     online softmax in fp32 (log2 domain), p' = p * v_scale (fp16)
+//     O[ch][col]   += V_codes^T(16 channels x 32 tokens, fp16) . p'  (MFMA)
+//   Column c of both products is query head c of the kv head, so the G heads
+//   share every K/V load ("premises and limits": the 8-head cache is read
+//   without expanding it).  The waves merge in LDS; with one split the
+//   workgroup normalises and undoes the rotation (o = H o~ / hd) itself,
+//   otherwise it writes (max, sum, output) partials that a combine step
+//   merges ("how it differs": split-KV reduction, same rotation on the
+//   output).  In a decode step the workgroup whose split holds position L-1
+//   first appends the step's new key and value.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "attn.h"
+#include "coherent.h"
+#include "device_common.h"
+
+namespace i4d {
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ uint16_t f32_to_f16_sat(float f) {
+  _Float16 h = (_Float16)f;  // round to nearest even
+  uint16_t b = bitcast<uint16_t>(h);
+  if ((b & 0x7fffu) == 0x7c00u && isfinite(f)) b = (uint16_t)((b & 0x8000u) | 0x7bffu);
+  return b;
+}
+
+// ---------------------------------------------------------------------------
+// append of one vector by one wave
+// ---------------------------------------------------------------------------
+
+// region = first slot of (row, head); pos < capacity; kind 0 = key, 1 = value
+template <int HD, bool COH = false>
+__device__ void append_vector(const KvArgs& kv, const uint16_t* src, int64_t region, int pos,
+                              int kind, int lane) {
+  float x0 = bf16_to_f32(COH ? ld_coh(&src[lane]) : src[lane]);
+  float x1 = (HD == 128) ? bf16_to_f32(COH ? ld_coh(&src[lane + 64]) : src[lane + 64]) : 0.f;
+  // FWHT, stages h = 1 .. 32 across lanes, then h = 64 inside the lane
+#pragma unroll
+  for (int h = 1; h < 64 && h < HD; h <<= 1) {
+    const float p0 = shfl_xor(x0, h);
+    x0 = (lane & h) ? (p0 - x0) : (x0 + p0);
+    if (HD == 128) {
+      const float p1 = shfl_xor(x1, h);
+      x1 = (lane & h) ? (p1 - x1) : (x1 + p1);
+    }
+  }
+  if (HD == 128) {
+    const float s0 = x0 + x1, s1 = x0 - x1;
+    x0 = s0;
+    x1 = s1;
+  }
+  const float amax = wave_max(fmaxf(fabsf(x0), (HD == 128) ? fabsf(x1) : 0.f));
+  const uint16_t s16 = f32_to_f16_sat(__fdiv_rn(amax, 7.0f));
+  const float sf = f16_bits_to_f32(s16);
+  int u0 = 8, u1 = 8;
+  if (sf != 0.f) {
+    u0 = (int)fminf(7.f, fmaxf(-8.f, rintf(__fdiv_rn(x0, sf)))) + 8;
+    u1 = (int)fminf(7.f, fmaxf(-8.f, rintf(__fdiv_rn(x1, sf)))) + 8;
+  }
+  const int64_t slot = region + pos;
+  if (kind == 0) {
+    // key slot: dword d = jj*(HD/32) + kb holds channels 32kb + 8jj + e
+    uint32_t word = 0;
+    const int d = lane;
+    const int jj = d / (HD / 32), kb = d % (HD / 32);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int c = 32 * kb + 8 * jj + e;
+      const int v0 = __shfl(u0, c & 63, 64);
+      const int v1 = __shfl(u1, c & 63, 64);
+      word |= (uint32_t)((c < 64) ? v0 : v1) << (4 * nibble_slot(e));
+    }
+    if (d < HD / 8) reinterpret_cast<uint32_t*>(kv.k_codes + (size_t)slot * (HD / 2))[d] = word;
+    if (lane == 0) kv.k_scales[slot] = s16;
+  } else {
+    // value block: token w of the block sits in slot group jj, slot e
+    const int w = pos % kVBlock;
+    const int jj = (w % 16) / 4;
+    const int e = (w % 4) + (w >= 16 ? 4 : 0);
+    const int sh = 4 * nibble_slot(e);
+    uint32_t* blk = kv.v_codes + (size_t)(region / kVBlock + pos / kVBlock) * 4 * HD;
+#pragma unroll
+    for (int q = 0; q < HD / 64; ++q) {
+      const int c = lane + 64 * q;
+      uint32_t* dw = blk + jj * HD + (c % 16) * (HD / 16) + c / 16;
+      atomicAnd(dw, ~(0xFu << sh));
+      atomicOr(dw, (uint32_t)(q ? u1 : u0) << sh);
+    }
+    if (lane == 0) kv.v_scales[slot] = s16;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// attention
+// ---------------------------------------------------------------------------
+
+// Codes of one dword as an exact f16 MFMA operand with no bias: the nibble
+// is the mantissa of an f16 subnormal, so e in {0, 1, 4, 5} -> u * 2^-24 and
+// e in {2, 3, 6, 7} -> 16 u * 2^-24 (nibble at mantissa bits 4-7).  The
+// partner operand carries a factor 1/16 at e in {2, 3, 6, 7}, so every
+// product is 2^-24 * (partner value) * u; the code offset 8 is removed after
+// the MFMA as 8 * (sum of the partner values).
+__device__ __forceinline__ f16x8_t dword_to_f16x8_sub(uint32_t w) {
+  const uint32_t t = w >> 8;
+  u32x4_t v;
+  v.x = w & 0x000F000Fu;
+  v.y = w & 0x00F000F0u;
+  v.z = t & 0x000F000Fu;
+  v.w = t & 0x00F000F0u;
+  return bitcast<f16x8_t>(v);
+}
+constexpr float kTwo24 = 16777216.0f;
+__device__ __forceinline__ bool slot16(int e) { return (e & 2) != 0; }
+
+// value of lane (l & ~15) | ((l + 8) & 15): the other half of a 16-lane row
+__device__ __forceinline__ float dpp_row_ror8(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, false));
+}
+
+template <int HD>
+struct BlockRegs {
+  uint32_t kw[2][HD / 32];  // key codes, 2 tiles of 16 tokens
+  uint32_t vw[HD / 16];     // value codes, one dword per 16-channel block
+  u32x2_t ks[2], vs[2];     // 4 fp16 scales per tile
+};
+
+template <int HD>
+__device__ __forceinline__ void load_keys(BlockRegs<HD>& b, const uint8_t* kbase, const uint16_t* ksc,
+                                          int blk, int c, int jj) {
+  const int t0 = blk * kVBlock;
+#pragma unroll
+  for (int tile = 0; tile < 2; ++tile) {
+    const uint8_t* kp = kbase + (size_t)(t0 + 16 * tile + c) * (HD / 2) + jj * (HD / 8);
+    if (HD == 128) {
+      const u32x4_t v = load16(kp);
+      b.kw[tile][0] = v.x;
+      b.kw[tile][1] = v.y;
+      b.kw[tile][2] = v.z;
+      b.kw[tile][3] = v.w;
+    } else {
+      const u32x2_t v = *reinterpret_cast<const u32x2_t*>(kp);
+      b.kw[tile][0] = v.x;
+      b.kw[tile][1] = v.y;
+    }
+    b.ks[tile] = *reinterpret_cast<const u32x2_t*>(ksc + t0 + 16 * tile + 4 * jj);
+  }
+}
+
+template <int HD>
+__device__ __forceinline__ void load_values(BlockRegs<HD>& b, const uint32_t* vbase, const uint16_t* vsc,
+                                            int blk, int c, int jj) {
+  constexpr int CB = HD / 16;
+  const int t0 = blk * kVBlock;
+#pragma unroll
+  for (int tile = 0; tile < 2; ++tile)
+    b.vs[tile] = *reinterpret_cast<const u32x2_t*>(vsc + t0 + 16 * tile + 4 * jj);
+  const uint32_t* vp = vbase + (size_t)blk * 4 * HD + jj * HD + c * CB;
+#pragma unroll
+  for (int q = 0; q < CB / 4; ++q) {
+    const u32x4_t v = load16(vp + 4 * q);
+    b.vw[4 * q + 0] = v.x;
+    b.vw[4 * q + 1] = v.y;
+    b.vw[4 * q + 2] = v.z;
+    b.vw[4 * q + 3] = v.w;
+  }
+}
+
+template <int HD>
+__device__ __forceinline__ void load_block(BlockRegs<HD>& b, const uint8_t* kbase, const uint32_t* vbase,
+                                           const uint16_t* ksc, const uint16_t* vsc, int blk, int c,
+                                           int jj) {
+  load_keys<HD>(b, kbase, ksc, blk, c, jj);
+  load_values<HD>(b, vbase, vsc, blk, c, jj);
+}
+
+__device__ __forceinline__ float f16_half(const u32x2_t& w, int i) {
+  const uint32_t word = w[i >> 1];
+  return f16_bits_to_f32((uint16_t)((i & 1) ? (word >> 16) : (word & 0xffffu)));
+}
+
+// inverse rotation of one head held by a wave (channels lane, lane + 64), / HD
+template <int HD>
+__device__ __forceinline__ void inverse_rotate(float& o0, float& o1, int lane) {
+#pragma unroll
+  for (int h = 1; h < 64 && h < HD; h <<= 1) {
+    const float p0 = shfl_xor(o0, h);
+    o0 = (lane & h) ? (p0 - o0) : (o0 + p0);
+    if (HD == 128) {
+      const float p1 = shfl_xor(o1, h);
+      o1 = (lane & h) ? (p1 - o1) : (o1 + p1);
+    }
+  }
+  if (HD == 128) {
+    const float s0 = o0 + o1, s1 = o0 - o1;
+    o0 = s0;
+    o1 = s1;
+  }
+  const float scale = 1.0f / (float)HD;
+  o0 *= scale;
+  o1 *= scale;
+}
+
+// normalise, undo the rotation and store one head (one wave)
+template <int HD, bool COH = false>
+__device__ __forceinline__ void finish_head(const AttnArgs& a, size_t head_row, float lsum, float o0,
+                                            float o1, int lane) {
+  const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+  o0 *= inv;
+  o1 *= inv;
+  inverse_rotate<HD>(o0, o1, lane);
+  const size_t base = head_row * HD;
+  if (a.attn_f32) {
+    a.attn_f32[base + lane] = o0;
+    if (HD == 128) a.attn_f32[base + lane + 64] = o1;
+  }
+  if (COH) {
+    st_coh(&a.attn_bf16[base + lane], f32_to_bf16(o0));
+    if (HD == 128) st_coh(&a.attn_bf16[base + lane + 64], f32_to_bf16(o1));
+  } else {
+    a.attn_bf16[base + lane] = f32_to_bf16(o0);
+    if (HD == 128) a.attn_bf16[base + lane + 64] = f32_to_bf16(o1);
+  }
+}
+
+// FWHT of one head (fp32, unnormalised) by one wave: channels lane and
+// lane + 64 in registers, stages h = 1 .. 32 across lanes, h = 64 in-lane.
+template <int HD>
+__device__ __forceinline__ void fwht_wave(float& x0, float& x1, int lane) {
+#pragma unroll
+  for (int h = 1; h < 64 && h < HD; h <<= 1) {
+    const float p0 = shfl_xor(x0, h);
+    x0 = (lane & h) ? (p0 - x0) : (x0 + p0);
+    if (HD == 128) {
+      const float p1 = shfl_xor(x1, h);
+      x1 = (lane & h) ? (p1 - x1) : (x1 + p1);
+    }
+  }
+  if (HD == 128) {
+    const float s0 = x0 + x1, s1 = x0 - x1;
+    x0 = s0;
+    x1 = s1;
+  }
+}
+
+// One (row m, kv head j, split s) unit by one workgroup of NWA waves taking
+// interleaved 32-token blocks of the split.  `wait_input` runs after the
+// first cache loads are issued and before the query is read.  LDS: wm, wl [NWA][8], wo
+// [NWA][8][HD] (the rotated queries [8][HD] alias wo before the merge).
+// COH: the query, the new key/value and the partials are exchanged with
+// other workgroups of the same launch (agent-coherent loads and stores).
+template <int HD, int NWA, bool COH, typename Wait>
+__device__ void attn_body(const AttnArgs& a, const int m, const int j, const int s, float* lds,
+                          Wait&& wait_input) {
+  constexpr int KB = HD / 32;  // 32-channel MFMA steps for q.k
+  constexpr int CB = HD / 16;  // 16-channel output blocks
+  constexpr int GMAX = 8;
+  float (*wm)[GMAX] = reinterpret_cast<float (*)[GMAX]>(lds);
+  float (*wl)[GMAX] = reinterpret_cast<float (*)[GMAX]>(lds + NWA * GMAX);
+  float (*wo)[GMAX][HD] = reinterpret_cast<float (*)[GMAX][HD]>(lds + 2 * NWA * GMAX);
+  float (*qrot)[HD] = wo[0];  // rotated queries [GMAX][HD], before the merge
+
+  const KvArgs& kv = a.kv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane & 15, jj = lane >> 4;
+  const int S = a.S, G = a.G;
+
+  const int64_t base = kv.row_base[m];
+  const int64_t cap = kv.row_base[m + 1] - base;
+  int L = a.ctx_len[m];
+  const bool len_ok = L >= 1 && L <= cap;
+  if (!len_ok) {
+    if (tid == 0 && kv.err_word) atomicOr(kv.err_word, I4D_DEVERR_CTX_LEN);
+    L = (int)max((int64_t)0, min((int64_t)max(L, 1), cap));
+  }
+  const int nblk = (L + kVBlock - 1) / kVBlock;
+  const int bps = (nblk + S - 1) / S;
+  const int b0 = s * bps;
+  const int b1 = min(nblk, b0 + bps);
+  const int64_t region = base * kv.n_kv + (int64_t)j * cap;
+  const uint8_t* kbase = kv.k_codes + (size_t)region * (HD / 2);
+  const uint16_t* ksc = kv.k_scales + region;
+  const uint16_t* vsc = kv.v_scales + region;
+  const uint32_t* vbase = kv.v_codes + (size_t)(region / kVBlock) * 4 * HD;
+  // every load of the kernel is issued unconditionally (a wave without work
+  // reads a valid block it then ignores), so the compiler can wait on exact
+  // load counts instead of draining all loads at control-flow joins
+  const int last_valid = max(b1, 1) - 1;  // block 0 exists: capacity >= 32
+
+  // In a decode step the split holding position L-1 first appends the new
+  // key/value there.  Cache reads do not depend on the query, so every wave
+  // starts loading its first block now, except a load of the block being
+  // appended to, which waits for the append.
+  const int last_blk = (L - 1) / kVBlock;
+  const bool appending = a.k_new && len_ok && last_blk >= b0 && last_blk < b1;
+  int blk = b0 + wave;
+  const bool defer = appending && blk == last_blk;
+  BlockRegs<HD> cur;
+  if (!defer) load_block<HD>(cur, kbase, vbase, ksc, vsc, min(blk, last_valid), c, jj);
+  // the query and the new key/value may come from other workgroups of the
+  // same launch: wait for them only now
+  wait_input();
+
+  // rotate the G query heads of this kv head (one wave per head) into LDS
+  for (int g = wave; g < G; g += NWA) {
+    const float* src = a.q + ((size_t)m * a.n_q + (size_t)j * G + g) * HD;
+    float x0 = COH ? ld_coh(&src[lane]) : src[lane];
+    float x1 = (HD == 128) ? (COH ? ld_coh(&src[lane + 64]) : src[lane + 64]) : 0.f;
+    fwht_wave<HD>(x0, x1, lane);
+    qrot[g][lane] = x0;
+    if (HD == 128) qrot[g][lane + 64] = x1;
+  }
+  if (appending && wave < 2) {
+    const uint16_t* src = (wave ? a.v_new : a.k_new) + ((size_t)m * kv.n_kv + j) * HD;
+    append_vector<HD, COH>(kv, src, region, L - 1, wave, lane);
+  }
+  __syncthreads();
+
+  // Rotated query as the partner operand of q.k: columns c < 8 hold the
+  // high fp16 part of query head j*G + c (c < G), columns 8 + c the low part
+  // (the residual), with the factor 1/16 at e in {2,3,6,7}.  Each lane also
+  // keeps cq = 8 * sum of the query values its operand represents.
+  f16x8_t qop[KB];
+  float cq = 0.f;
+  {
+    const int head = c & 7;
+    const bool active = head < G;
+    const bool lo_part = c >= 8;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      float qv[8];
+      const float4* src = reinterpret_cast<const float4*>(&qrot[head][32 * kb + 8 * jj]);
+      const float4 v0 = src[0], v1 = src[1];
+      qv[0] = v0.x; qv[1] = v0.y; qv[2] = v0.z; qv[3] = v0.w;
+      qv[4] = v1.x; qv[5] = v1.y; qv[6] = v1.z; qv[7] = v1.w;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float w = active ? (slot16(e) ? qv[e] * 0.0625f : qv[e]) : 0.f;
+        const _Float16 hi = (_Float16)w;
+        const _Float16 op = lo_part ? (_Float16)(w - (float)hi) : hi;
+        qop[kb][e] = op;
+        cq = fmaf((float)op, slot16(e) ? 128.f : 8.f, cq);
+      }
+    }
+    cq += shfl_xor(cq, 16);
+    cq += shfl_xor(cq, 32);
+  }
+  if (defer) {
+    // the CU's L1 may hold lines of this block from before the append
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    load_block<HD>(cur, kbase, vbase, ksc, vsc, blk, c, jj);
+  }
+  __syncthreads();  // qrot shares LDS with the merge buffers
+
+  float m_run = -INFINITY, l_run = 0.f, psum = 0.f;
+  f32x4_t o[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) o[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const float sscale = a.score_scale;
+
+  // One block in registers; the next block's keys are requested once the
+  // current keys are consumed, its values once the current values are.  The
+  // last block of the wave runs the same body without those requests.
+  auto body = [&](const int nb, const bool prefetch) {
+    const int t0 = blk * kVBlock;
+    float sc[8];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(dword_to_f16x8_sub(cur.kw[tile][kb]), qop[kb], acc,
+                                                     0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // high part (column c) + low part (column c + 8, rotated in by DPP)
+        const float part = fmaf(acc[i], kTwo24, -cq);
+        const float full = part + dpp_row_ror8(part);
+        const int tok = t0 + 16 * tile + 4 * jj + i;
+        const float v = full * f16_half(cur.ks[tile], i) * sscale;
+        sc[tile * 4 + i] = (tok < L) ? v : -INFINITY;
+        mx = fmaxf(mx, sc[tile * 4 + i]);
+      }
+    }
+    if (prefetch) load_keys<HD>(cur, kbase, ksc, nb, c, jj);
+    mx = fmaxf(mx, shfl_xor(mx, 16));
+    mx = fmaxf(mx, shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);  // finite: the block holds a valid token
+    const float alpha = exp2f(m_run - m_new);
+    l_run *= alpha;
+    psum *= alpha;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) o[cb] *= alpha;
+    // P operand: element e is token 4jj+e (e < 4) or 16+4jj+e-4 (e >= 4),
+    // i.e. score register e; value scale folded in, 1/16 at e in {2,3,6,7}
+    f16x8_t pb;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int tile = e >> 2, i = e & 3;
+      const float p = exp2f(sc[e] - m_new);  // 0 for masked tokens
+      l_run += p;
+      float pv = p * f16_half(cur.vs[tile], i);
+      pv = (c < G && p > 0.f) ? pv : 0.f;
+      if (slot16(e)) pv *= 0.0625f;
+      const _Float16 ph = (_Float16)pv;
+      pb[e] = ph;
+      psum = fmaf((float)ph, slot16(e) ? 16.f : 1.f, psum);
+    }
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+      o[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dword_to_f16x8_sub(cur.vw[cb]), pb, o[cb], 0, 0, 0);
+    if (prefetch) load_values<HD>(cur, vbase, vsc, nb, c, jj);
+    m_run = m_new;
+  };
+  if (blk < b1) {
+    for (; blk + NWA < b1; blk += NWA) body(blk + NWA, true);
+    body(blk, false);
+  }
+
+  // per-column totals over the 4 lane quarters; undo the 2^-24 operand
+  // scale and remove the code offset: o = 2^24 acc - 8 * sum p'
+  l_run += shfl_xor(l_run, 16);
+  l_run += shfl_xor(l_run, 32);
+  psum += shfl_xor(psum, 16);
+  psum += shfl_xor(psum, 32);
+  const float vbias = 8.f * psum;
+  if (c < G) {
+    if (jj == 0) {
+      wm[wave][c] = m_run;
+      wl[wave][c] = l_run;
+    }
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wo[wave][c][16 * cb + 4 * jj + i] = fmaf(o[cb][i], kTwo24, -vbias);
+  }
+  __syncthreads();
+
+  // wave w merges heads w, w + NWA, ... over the waves
+  for (int g = wave; g < G; g += NWA) {
+    float M_ = -INFINITY;
+    for (int w = 0; w < NWA; ++w)
+      if (wl[w][g] > 0.f) M_ = fmaxf(M_, wm[w][g]);
+    float lsum = 0.f, o0 = 0.f, o1 = 0.f;
+    for (int w = 0; w < NWA; ++w) {
+      if (wl[w][g] > 0.f) {
+        const float f = exp2f(wm[w][g] - M_);
+        lsum += f * wl[w][g];
+        o0 += f * wo[w][g][lane];
+        if (HD == 128) o1 += f * wo[w][g][lane + 64];
+      }
+    }
+    const size_t head_row = (size_t)m * a.n_q + (size_t)j * G + g;
+    if (S == 1) {
+      finish_head<HD, COH>(a, head_row, lsum, o0, o1, lane);
+    } else {
+      const size_t ph = head_row * S + s;
+      if (COH) {
+        st_coh(&a.part_o[ph * HD + lane], o0);
+        if (HD == 128) st_coh(&a.part_o[ph * HD + lane + 64], o1);
+        if (lane == 0) {
+          st_coh(&a.part_ml[ph * 2], M_);
+          st_coh(&a.part_ml[ph * 2 + 1], lsum);
+        }
+      } else {
+        a.part_o[ph * HD + lane] = o0;
+        if (HD == 128) a.part_o[ph * HD + lane + 64] = o1;
+        if (lane == 0) {
+          a.part_ml[ph * 2] = M_;
+          a.part_ml[ph * 2 + 1] = lsum;
+        }
+      }
+    }
+  }
+}
+
+// Merge the splits of one (row, q head) and undo the rotation:
+// o = H o~ / hd with o~ = sum_s e^(m_s - m) o~_s / sum_s e^(m_s - m) l_s.
+// One wave per (row, head); lane t holds split t (t + 64, ...) for the
+// weights, the partial outputs are read with independent loads.
+template <int HD, bool COH = false>
+__device__ __forceinline__ void combine_head(const AttnArgs& a, size_t head_row, int lane, float& lsum_out,
+                                             float& o0_out, float& o1_out) {
+  auto ld = [](const float* p) { return COH ? ld_coh(p) : *p; };
+  constexpr int CH = 32;  // splits whose partial outputs are in flight at once
+  const int S = a.S;
+  const float* ml = a.part_ml + head_row * S * 2;
+  const float* po = a.part_o + head_row * S * HD;
+  float M_ = -INFINITY;
+  for (int t = lane; t < S; t += 64)
+    if (ld(&ml[2 * t + 1]) > 0.f) M_ = fmaxf(M_, ld(&ml[2 * t]));
+  M_ = wave_max(M_);
+  float lsum = 0.f, o0 = 0.f, o1 = 0.f;
+  for (int t0 = 0; t0 < S; t0 += CH) {
+    // lane u < CH: weight of split t0 + u
+    float f = 0.f;
+    if (lane < CH && t0 + lane < S) {
+      const float l = ld(&ml[2 * (t0 + lane) + 1]);
+      if (l > 0.f) {
+        f = exp2f(ld(&ml[2 * (t0 + lane)]) - M_);
+        lsum = fmaf(f, l, lsum);
+      }
+    }
+    float x0[CH], x1[CH];
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      const int t = min(t0 + u, S - 1);
+      x0[u] = ld(&po[(size_t)t * HD + lane]);
+      x1[u] = (HD == 128) ? ld(&po[(size_t)t * HD + lane + 64]) : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      const float fu = __shfl(f, u, 64);
+      if (t0 + u < S && fu > 0.f) {
+        o0 = fmaf(fu, x0[u], o0);
+        o1 = fmaf(fu, x1[u], o1);
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) lsum += shfl_xor(lsum, off);
+  lsum_out = lsum;
+  o0_out = o0;
+  o1_out = o1;
+}
+
+}  // namespace i4d

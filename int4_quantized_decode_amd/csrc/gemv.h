@@ -1,0 +1,424 @@
+// gemv.h - M = 1 INT4 projection (VALU GEMV) as a device function, shared by
+// the stand-alone projection kernels and the one-launch decode step.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "coherent.h"
+#include "device_common.h"
+#include "i4d_internal.h"
+#include "proj.h"
+
+namespace i4d {
+
+template <int EPI>
+__device__ __forceinline__ bool needs_rho() {
+  return EPI == EPI_QKV || EPI == EPI_GU;
+}
+
+// the wait hook of a stage whose input is ready at entry
+struct NoWait {
+  __device__ void operator()() const {}
+};
+
+template <bool COH>
+__device__ __forceinline__ void st_out(float* p, float v) {
+  if (COH) st_coh(p, v); else *p = v;
+}
+template <bool COH>
+__device__ __forceinline__ void st_out(uint16_t* p, uint16_t v) {
+  if (COH) st_coh(p, v); else *p = v;
+}
+
+// Epilogue from the LDS tile ot[row][M] (rows of strips strip0 .. strip0+S-1).
+// COH: outputs consumed inside the same launch are stored agent-coherently
+// and the in-launch residual (h, down projection) is loaded the same way.
+template <int EPI, bool COH = false>
+__device__ void run_epilogue(const ProjArgs& a, int strip0, int S, const float* ot, const float* rho) {
+  const int M = a.M;
+  const int nthreads = blockDim.x;
+  if (EPI == EPI_QKV || EPI == EPI_GU) {
+    for (int idx = threadIdx.x; idx < S * 8 * M; idx += nthreads) {
+      const int m = idx % M, pi = idx / M, s = pi / 8, i = pi % 8;
+      const int t = strip0 + s;
+      if (t * kStrip >= a.Np) continue;
+      float y0 = ot[(s * 16 + i) * M + m] * rho[m];
+      float y1 = ot[(s * 16 + 8 + i) * M + m] * rho[m];
+      if (EPI == EPI_GU) {
+        const int f = 8 * t + i;
+        const float silu = y0 / (1.0f + expf(-y0));
+        st_out<COH>(&a.a_out[(size_t)m * (a.Np / 2) + f], f32_to_bf16(silu * y1));
+      } else {
+        const int per_head = a.hd / kStrip;
+        const int head = t / per_head, sp = t % per_head;
+        const int c0 = 8 * sp + i, c1 = c0 + a.hd / 2;
+        if (head < a.n_q + a.n_kv) {
+          // RoPE, rotate-half pair (c0, c0 + hd/2) at position ctx_len - 1:
+          // angle pos * theta^(-2 c0 / hd) in fp64 (the frequency as
+          // (theta^(-2/hd))^c0 by binary powering of the host's fp64 ratio),
+          // reduced to [-pi, pi], then fp32 sin/cos
+          const double pos = (double)(a.ctx_len[m] - 1);
+          double freq = 1.0, base = a.rope_ratio;
+          for (int e = c0; e; e >>= 1) {
+            if (e & 1) freq *= base;
+            base *= base;
+          }
+          const double ang = pos * freq;
+          const double k2pi = rint(ang * 0.15915494309189535);
+          double red = fma(-k2pi, 6.283185307179586, ang);
+          red = fma(-k2pi, 2.4492935982947064e-16, red);
+          float sn_f, c;
+          sincosf((float)red, &sn_f, &c);
+          const float r0 = y0 * c - y1 * sn_f;
+          const float r1 = y1 * c + y0 * sn_f;
+          y0 = r0;
+          y1 = r1;
+        }
+        if (head < a.n_q) {
+          float* q = a.q_out + ((size_t)m * a.n_q + head) * a.hd;
+          st_out<COH>(&q[c0], y0);
+          st_out<COH>(&q[c1], y1);
+        } else if (head < a.n_q + a.n_kv) {
+          uint16_t* k = a.k_out + ((size_t)m * a.n_kv + (head - a.n_q)) * a.hd;
+          st_out<COH>(&k[c0], f32_to_bf16(y0));
+          st_out<COH>(&k[c1], f32_to_bf16(y1));
+        } else {
+          uint16_t* v = a.v_out + ((size_t)m * a.n_kv + (head - a.n_q - a.n_kv)) * a.hd;
+          st_out<COH>(&v[c0], f32_to_bf16(y0));
+          st_out<COH>(&v[c1], f32_to_bf16(y1));
+        }
+      }
+    }
+  } else {
+    for (int idx = threadIdx.x; idx < S * 16 * M; idx += nthreads) {
+      const int m = idx % M, row = idx / M;
+      const int n = strip0 * kStrip + row;
+      if (n >= a.Np) continue;
+      const float y = ot[row * M + m];
+      const size_t o = (size_t)m * a.Np + n;
+      if (EPI == EPI_O) {
+        const float h = bf16_to_f32(a.resid_bf16[o]) + y;
+        st_out<COH>(&a.h_f32[o], h);
+        st_out<COH>(&a.h_bf16[o], f32_to_bf16(h));
+      } else {
+        const float res = COH ? ld_coh(&a.resid_f32[o]) : a.resid_f32[o];
+        a.out_bf16[o] = f32_to_bf16(res + y);
+      }
+    }
+  }
+}
+
+
+// Workgroup barrier that waits for LDS traffic only: weight loads stay in
+// flight across it (__syncthreads would also drain every outstanding global
+// load of the wave).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Launch shape of the M = 1 kernel: NW waves, SP strips per workgroup, GPW
+// = G / NW groups per wave (the K range is split across the waves).
+struct GemvPlan {
+  int NW, SP, GPW;
+};
+
+// LDS: x [K] fp16 | group sums [G][4] | partials [SP][NW][16] | tile [SP*16]
+// | per-wave sums of squares [NW] | per-wave max |x| [NW]
+inline size_t gemv_lds_bytes(int K, const GemvPlan& p) {
+  return (size_t)K * 2 + (size_t)(K / kGroup) * 16 + (size_t)p.SP * p.NW * 16 * 4 +
+         (size_t)p.SP * 16 * 4 + (size_t)p.NW * 8;
+}
+
+// Nibble pair q of a code dword as exact fp16 subnormals: q = 0 -> codes
+// e = 0, 1 as u * 2^-24; q = 1 -> e = 2, 3 as 16 u * 2^-24 (nibbles at
+// mantissa bits 4-7); q = 2, 3 likewise for e = 4..7 after a shift by 8.
+// The partner x carries the factor 1/16 at e in {2, 3, 6, 7}.
+__device__ __forceinline__ f16x2_t code_pair_sub(uint32_t w, uint32_t t, int q) {
+  const uint32_t v = (q == 0) ? (w & 0x000F000Fu) : (q == 1) ? (w & 0x00F000F0u)
+                   : (q == 2) ? (t & 0x000F000Fu) : (t & 0x00F000F0u);
+  return bitcast<f16x2_t>(v);
+}
+
+// dot of one atom row quarter (4 code dwords) with its 32 x values (fp16
+// pairs in k order), times 2^-24
+__device__ __forceinline__ float atom_dot(const u32x4_t w, const u32x4_t (&xk)[4]) {
+  float acc = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const uint32_t dw = w[kb], t = dw >> 8;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      acc = __builtin_amdgcn_fdot2(code_pair_sub(dw, t, q), bitcast<f16x2_t>(xk[kb][q]), acc, false);
+  }
+  return acc;
+}
+
+// sum of the x values that 16 fp16 words of one group quarter represent
+// (the factor 16 undoes the 1/16 at e in {2, 3, 6, 7})
+__device__ __forceinline__ float quarter_sum(const u32x4_t (&xk)[4]) {
+  const f16x2_t one = {(_Float16)1.0f, (_Float16)1.0f};
+  const f16x2_t sixteen = {(_Float16)16.0f, (_Float16)16.0f};
+  float s = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      s = __builtin_amdgcn_fdot2(bitcast<f16x2_t>(xk[kb][q]), (q & 1) ? sixteen : one, s, false);
+  return s;
+}
+
+// One wave streams its atoms (strip s of the workgroup, group g of its K
+// range) through a ring of U outstanding 16-byte loads per lane (plus the
+// 2-byte scale of each atom).  The atom sequence is padded to a multiple of
+// U with repeats of its last atom (L2 hits, no HBM traffic), so every round
+// issues exactly U loads and the compiler can wait on exact counts.
+//
+// x is staged once per workgroup as fp16 scaled by a power of two sigma
+// (max |x| sigma in [2^12, 2^13), so the conversion from bf16 is exact for
+// every value above 2^-23 of the row maximum) and by 1/16 at the positions
+// paired with the high nibble of a byte.  With GPW > 0 (compile time, a
+// divisor of U) each wave keeps its GPW groups of x in registers; GPW == 0
+// reads x from LDS for every atom.
+//
+// The body serves the stand-alone kernel and the one-launch decode step
+// (COH = true): there the weight ring is issued first, then `wait_input`
+// blocks until the producers of x are done, then x is read agent-coherently
+// and the outputs are stored the same way.  `strip0`, `ns`: the strips of
+// this workgroup (ns <= pl.SP).
+template <int EPI, int NW, int U, int GPW, bool COH, typename Wait>
+__device__ __forceinline__ void gemv_body(const ProjArgs& a, const GemvPlan& pl, const int strip0,
+                                          const int ns, unsigned char* smem, Wait&& wait_input) {
+  const int K = a.K, G = a.G;
+  const int SP = pl.SP;
+  const int GW = GPW > 0 ? GPW : pl.GPW;
+  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);                  // [K] fp16
+  float* Xs = reinterpret_cast<float*>(smem + (size_t)K * 2);        // [G][4]
+  float* red = Xs + (size_t)G * 4;                                   // [SP][NW][16]
+  float* ot = red + (size_t)SP * NW * 16;                            // [SP*16]
+  float* ssq = ot + SP * 16;                                         // [NW]
+  float* wmx = ssq + NW;                                             // [NW]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
+  const int r = lane & 15, j = lane >> 4;
+  const int nstrips = a.Np / kStrip;
+  const int g0 = wave * GW;                   // first group of this wave
+  const int gpw = max(0, min(GW, G - g0));    // groups of this wave
+  const int n = ns * gpw;                     // atoms of this wave
+  const int npad = ((max(n, 1) + U - 1) / U) * U;
+  constexpr int GR = GPW > 0 ? GPW : 1;
+  static_assert(U % GR == 0, "the ring must hold whole strips");
+
+  // 1. x: the loads of this thread's 16-byte chunks (clamped, so every
+  // thread issues the same number of loads).  Stand-alone: issued first, so
+  // that every wave's x enters the memory pipeline before any weight load
+  // (otherwise the x of the last waves queues behind the first waves'
+  // atoms).  One-launch step: issued after the producers are done.
+  constexpr int XMAX = 4;  // K <= XMAX * 8 * NW * 64 (host-checked)
+  const int xn = (K / 8 + NW * 64 - 1) / (NW * 64);  // chunks per thread (uniform)
+  u32x4_t xv[XMAX];
+  auto load_x = [&]() {
+#pragma unroll
+    for (int q = 0; q < XMAX; ++q) {
+      if (q < xn) {
+        const int cidx = min(tid + q * NW * 64, K / 8 - 1);
+        xv[q] = COH ? ld_coh16(a.x, (uint32_t)cidx * 16, (uint32_t)K * 2) : load16(a.x + (size_t)cidx * 8);
+      }
+    }
+  };
+  constexpr bool X_FIRST = !COH || std::is_same<std::decay_t<Wait>, NoWait>::value;
+  if (X_FIRST) {
+    load_x();
+    lds_barrier();
+  }
+
+  // 2. the first U atoms of the weight stream.  The refill cursor (rs, rg)
+  // walks strip by strip through the wave's groups and stops on the last
+  // atom, which pads the sequence.  With GPW > 0 the slot of a strip's
+  // first group also loads the strip's GPW scales (one load per strip: a
+  // row's 8 consecutive groups are contiguous); GPW == 0 loads each
+  // atom's scale.
+  int rs = 0, rg = 0;
+  auto next_atom = [&](const uint8_t*& cp, const uint16_t*& sp, const uint16_t*& sv) {
+    const int t = min(strip0 + rs, nstrips - 1);
+    const int g = min(g0 + rg, G - 1);
+    cp = a.codes + ((size_t)t * G + g) * kAtomBytes + (size_t)lane * 16;
+    sp = a.scales + (((size_t)t * a.G8 + g / 8) * 16 + r) * 8 + (g % 8);
+    const int gs = min(g0, G - 1);
+    sv = a.scales + (((size_t)t * a.G8 + gs / 8) * 16 + r) * 8 + (gs % 8);
+    if (rs < ns - 1 || rg < gpw - 1) {
+      if (++rg >= gpw) {
+        rg = 0;
+        ++rs;
+      }
+    }
+  };
+  u32x4_t ring[U];
+  uint16_t sring[U];
+  auto fill = [&](const int k) {
+    const uint8_t* cp;
+    const uint16_t* sp;
+    const uint16_t* sv;
+    next_atom(cp, sp, sv);
+    ring[k] = load16_stream(cp);
+    if (GPW == 0) {
+      sring[k] = *sp;
+    } else if (k % GR == 0) {
+      if (GR == 1) {
+        sring[k] = *sv;
+      } else if (GR == 2) {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(sv);
+        sring[k] = (uint16_t)w;
+        sring[k + 1] = (uint16_t)(w >> 16);
+      } else {
+        const u32x2_t w = *reinterpret_cast<const u32x2_t*>(sv);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sring[k + q] = (uint16_t)(w[q >> 1] >> (16 * (q & 1)));
+      }
+    }
+  };
+#pragma unroll
+  for (int k = 0; k < U; ++k) fill(k);
+  if (!X_FIRST) {
+    wait_input();
+    load_x();
+  }
+
+  // 3. row statistics: sum of squares (rho) and max |x| (the fp16 scale)
+  float sq = 0.f, mx = 0.f;
+#pragma unroll
+  for (int q = 0; q < XMAX; ++q) {
+    if (q < xn && tid + q * NW * 64 < K / 8) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float lo = bf16_lo(xv[q][e]), hi = bf16_hi(xv[q][e]);
+        sq = fmaf(lo, lo, sq);
+        sq = fmaf(hi, hi, sq);
+        mx = fmaxf(mx, fmaxf(fabsf(lo), fabsf(hi)));
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    sq += shfl_xor(sq, o);
+    mx = fmaxf(mx, shfl_xor(mx, o));
+  }
+  if (lane == 0) {
+    ssq[wave] = sq;
+    wmx[wave] = mx;
+  }
+  lds_barrier();
+  float xm = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) xm = fmaxf(xm, wmx[w]);
+  int ex = 0;
+  if (xm > 0.f) frexpf(xm, &ex);
+  const int sh = max(-100, min(100, 13 - ex));
+  const float sigma = ldexpf(1.0f, sh);
+
+  // 4. stage x as fp16 (x sigma, / 16 at e in {2,3,6,7})
+#pragma unroll
+  for (int q = 0; q < XMAX; ++q) {
+    const int cidx = tid + q * NW * 64;
+    if (q < xn && cidx < K / 8) {
+      u32x4_t o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float f = (e & 1) ? sigma * 0.0625f : sigma;
+        const f16x2_t h = {(_Float16)(bf16_lo(xv[q][e]) * f), (_Float16)(bf16_hi(xv[q][e]) * f)};
+        o[e] = bitcast<uint32_t>(h);
+      }
+      reinterpret_cast<u32x4_t*>(xs)[cidx] = o;
+    }
+  }
+  lds_barrier();
+
+  // 5. x of the wave's groups (registers) or group sums for every group (LDS)
+  const u32x4_t* xl = reinterpret_cast<const u32x4_t*>(xs);
+  u32x4_t xr[GR][4];
+  float xsum[GR];
+  if (GPW > 0) {
+#pragma unroll
+    for (int gi = 0; gi < GR; ++gi) {
+      const int g = min(g0 + gi, G - 1);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) xr[gi][kb] = xl[(128 * g + 32 * kb + 8 * j) / 8];
+      xsum[gi] = quarter_sum(xr[gi]);
+    }
+  } else {
+    for (int idx = tid; idx < G * 4; idx += NW * 64) {
+      const int g = idx >> 2, jj = idx & 3;
+      u32x4_t xk[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) xk[kb] = xl[(128 * g + 32 * kb + 8 * jj) / 8];
+      Xs[idx] = quarter_sum(xk);
+    }
+    lds_barrier();
+  }
+
+  // 6. stream: consume atom i from the ring, then refill its slot with atom
+  // i + U (the loaded registers stay in place across iterations)
+  float part = 0.f;
+  int sl = 0, gi_rt = 0;  // strip and group of the atom being consumed (GPW == 0)
+  auto consume = [&](const u32x4_t w, const uint16_t sbits, int i, int k) {
+    if (i < n) {
+      float y;
+      if (GPW > 0) {
+        const int gi = k % GR;
+        y = fmaf(atom_dot(w, xr[gi]), 16777216.0f, -8.0f * xsum[gi]);
+      } else {
+        const int g = g0 + gi_rt;
+        u32x4_t xk[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) xk[kb] = xl[(128 * g + 32 * kb + 8 * j) / 8];
+        y = fmaf(atom_dot(w, xk), 16777216.0f, -8.0f * Xs[g * 4 + j]);
+      }
+      part = fmaf(f16_bits_to_f32(sbits), y, part);
+      const bool last_of_strip = (GPW > 0) ? (k % GR == GR - 1) : (gi_rt == gpw - 1);
+      if (last_of_strip) {
+        part += shfl_xor(part, 16);
+        part += shfl_xor(part, 32);
+        if (j == 0) red[((size_t)sl * NW + wave) * 16 + r] = part;
+        part = 0.f;
+        ++sl;
+      }
+      if (GPW == 0) gi_rt = last_of_strip ? 0 : gi_rt + 1;
+    }
+  };
+  int i0 = 0;
+  for (; i0 + U < npad; i0 += U) {
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      consume(ring[k], sring[k], i0 + k, k);
+      fill(k);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < U; ++k) consume(ring[k], sring[k], i0 + k, k);
+  // waves without a group range leave zero partials
+  if (j == 0)
+    for (int s2 = sl; s2 < ns; ++s2) red[((size_t)s2 * NW + wave) * 16 + r] = 0.f;
+  lds_barrier();
+
+  // 7. reduce over the waves and the four lane quarters; undo sigma; epilogue
+  if (tid < ns * 16) {
+    const int s2 = tid >> 4, rr = tid & 15;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) v += red[((size_t)s2 * NW + w) * 16 + rr];
+    ot[tid] = v * ldexpf(1.0f, -sh);
+  }
+  if (needs_rho<EPI>() && tid == 0) {
+    float t = 0.f;
+    for (int w = 0; w < NW; ++w) t += ssq[w];
+    ssq[0] = 1.0f / sqrtf(t / (float)K + a.eps);
+  }
+  lds_barrier();
+  float one = 1.0f;
+  run_epilogue<EPI, COH>(a, strip0, ns, ot, needs_rho<EPI>() ? &ssq[0] : &one);
+}
+
+}  // namespace i4d

@@ -26,6 +26,13 @@ struct AttnPlan {
 };
 AttnPlan attn_plan(const i4d_layer_shape* s, int M, int max_ctx_len, int num_splits);
 
+// KV splits of the one-launch decode step (M = 1): one attention unit per
+// (kv head, split), about 256 units, at least one 32-token block each
+int step_m1_splits(const i4d_layer_shape* s, int max_ctx_len, int num_splits);
+
+// size of the sync region of the decode-step workspace (zero before first use)
+constexpr size_t kStepSyncBytes = 8192;
+
 struct AttnWs {
   size_t ml;      // fp32 [M][n_q][S][2]   (running max in log2 units, sum)
   size_t o;       // fp32 [M][n_q][S][hd]  unnormalised rotated output

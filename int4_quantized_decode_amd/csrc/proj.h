@@ -22,6 +22,7 @@ struct ProjArgs {
   const int32_t* ctx_len;
   int n_q, n_kv, hd;
   float theta;
+  double rope_ratio;  // theta^(-2/hd), fp64 (RoPE frequency of pair i = ratio^i)
   // O epilogue
   const uint16_t* resid_bf16;
   float* h_f32;

@@ -1,0 +1,343 @@
+// step.hip - the whole decode step of one layer for one row (M = 1) in one
+// persistent launch (gfx950).
+//
+// At M = 1 the step is a chain of five memory-bound stages (QKV, attention,
+// O, gate/up, down) whose data are small but whose every stage depends on
+// all of the previous one.  As separate kernels each boundary costs a
+// launch (about 1.8 us here), the drain of the previous stage and the first
+// load latency of the next.  Here one workgroup of 8 waves per CU runs all
+// stages; a stage's weight stream does not depend on the activations, so
+// each workgroup issues its first weight loads before it waits for the
+// previous stage, and HBM keeps streaming across the stage boundaries.
+//
+// Stages and hand-offs (counters in the zeroed sync region of the
+// workspace; data exchanged with agent-coherent stores and loads):
+//   1. QKV strips (+ rho1, RoPE): each finished strip counts for its kv head.
+//   2. Attention unit (kv head j, split s): waits for the strips of head j's
+//      query heads, key and value; appends the new key/value (the unit that
+//      owns position L-1); writes a partial; the last unit of kv head j
+//      merges the splits, undoes the rotation and counts head j done.
+//   3. O strips (+ residual): wait for all kv heads; then a grid barrier.
+//   4. gate/up strips (+ rho2, SwiGLU): after the barrier; barrier again.
+//   5. down strips (+ residual) -> x_out.
+// The last workgroup to finish clears the counters for the next launch.
+// Every wait is bounded: a timeout sets I4D_DEVERR_SYNC and the step runs
+// on (with wrong results) instead of hanging.
+#include <math.h>
+
+#include "attn.h"
+#include "attn_core.h"
+#include "coherent.h"
+#include "gemv.h"
+#include "i4d_internal.h"
+#include "proj.h"
+#include "step.h"
+
+namespace i4d {
+
+// word offsets in the sync region (one 128-byte line per counter)
+constexpr int kLine = 32;
+constexpr int kSyncQkv = 0;               // [n_kv] finished QKV strips per kv head
+constexpr int kSyncAttn = 16 * kLine;     // [n_kv] finished attention splits per kv head
+constexpr int kSyncAttnDone = 32 * kLine; // kv heads whose attention output is written
+constexpr int kSyncBar1 = 33 * kLine;     // 8 group counters + top (after O)
+constexpr int kSyncBar2 = 42 * kLine;     // 8 group counters + top (after gate/up)
+constexpr int kSyncExit = 51 * kLine;
+constexpr int kSyncWords = 52 * kLine;    // cleared at exit
+constexpr int kSyncErr = 52 * kLine;      // sticky timeout flag (not cleared)
+
+// waves per workgroup: 8 (one workgroup per CU, 256 registers per lane)
+constexpr int kStepWaves = 8;
+
+struct StepArgs {
+  ProjArgs qkv, o, gu, down;
+  GemvPlan pq, po, pg, pd;
+  AttnArgs at;
+  unsigned* sync;
+  int32_t* err_word;  // optional (the cache's)
+  int n_kv, G, hd, Sf;
+};
+
+__device__ __forceinline__ void strip_range(int N, int wg, int nwg, int& s0, int& ns) {
+  s0 = (int)((long)wg * N / nwg);
+  ns = (int)((long)(wg + 1) * N / nwg) - s0;
+}
+
+// QKV strip t -> kv head whose attention needs it
+__device__ __forceinline__ int strip_kv_head(int t, int hd, int n_q, int n_kv, int G) {
+  const int head = t / (hd / kStrip);
+  if (head < n_q) return head / G;
+  if (head < n_q + n_kv) return head - n_q;
+  return head - n_q - n_kv;
+}
+
+__device__ __forceinline__ void flag_error(unsigned* sync, int32_t* err_word) {
+  atomicOr(&sync[kSyncErr], 1u);
+  if (err_word) atomicOr(err_word, I4D_DEVERR_SYNC);
+}
+
+// all of this workgroup's stores are complete and visible device-wide
+__device__ __forceinline__ void stores_done() {
+  wait_vmem();
+  __builtin_amdgcn_s_barrier();
+}
+
+// two-level grid barrier (8 groups of workgroups, then a top counter)
+__device__ __forceinline__ void bar_arrive(unsigned* bar, int wg, int nwg) {
+  const int g = wg & 7;
+  const unsigned gs = (unsigned)((nwg - g + 7) / 8);
+  const unsigned old = atomic_add_agent(&bar[g * kLine], 1u);
+  if (old == gs - 1) atomic_add_agent(&bar[8 * kLine], 1u);
+}
+
+template <int HD, int GQ, int GD>
+__global__ __launch_bounds__(kStepWaves * 64) void step_m1_kernel(StepArgs sa) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int NW = kStepWaves;
+  constexpr int UQ = 16;  // gate/up: deep ring (the prefetch spans the barrier)
+  constexpr int UO = GQ == 0 ? 8 : (GQ > 4 ? GQ : 4);  // O: one strip per workgroup
+  constexpr int UD = 16;
+  const int tid = threadIdx.x;
+  const int wg = blockIdx.x, nwg = gridDim.x;
+  const int ngroups = nwg < 8 ? nwg : 8;
+
+  // ---- 1. QKV
+  {
+    const StepArgs* A = &sa;
+    const ProjArgs pa = A->qkv;
+    const GemvPlan pl = A->pq;
+    unsigned* sync = A->sync;
+    const int hd = A->hd, n_kv = A->n_kv, G = A->G;
+    int s0, ns;
+    strip_range(pa.Np / kStrip, wg, nwg, s0, ns);
+    if (ns > 0) {
+      gemv_body<EPI_QKV, NW, 8, GQ, true>(pa, pl, s0, ns, smem, NoWait());
+      stores_done();
+      if (tid == 0)
+        for (int t = s0; t < s0 + ns; ++t)
+          atomic_add_agent(&sync[kSyncQkv + kLine * strip_kv_head(t, hd, pa.n_q, n_kv, G)], 1u);
+    }
+  }
+
+  // ---- 2. attention units (kv head j, split s), head-interleaved
+  {
+    const StepArgs* A = &sa;
+    const AttnArgs at = A->at;
+    unsigned* sync = A->sync;
+    int32_t* err_word = A->err_word;
+    const int n_kv = A->n_kv, G = A->G, Sf = A->Sf;
+    const int units = n_kv * Sf;
+    const unsigned need = (unsigned)((G + 2) * (A->hd / kStrip));
+    for (int u = wg; u < units; u += nwg) {
+      const int j = u % n_kv, s = u / n_kv;
+      __syncthreads();  // LDS reuse
+      auto wait_qkv = [&] {
+        if (tid == 0 && !spin_geq(&sync[kSyncQkv + kLine * j], need, &sync[kSyncErr], 1u))
+          flag_error(sync, err_word);
+        lds_barrier();
+      };
+      attn_body<HD, NW, true>(at, 0, j, s, reinterpret_cast<float*>(smem), wait_qkv);
+      stores_done();
+      if (Sf > 1) {
+        __shared__ int last;
+        if (tid == 0) last = (atomic_add_agent(&sync[kSyncAttn + kLine * j], 1u) == (unsigned)(Sf - 1));
+        __syncthreads();
+        if (last) {
+          const int lane = tid & 63, wave = tid >> 6;
+          for (int g = wave; g < G; g += NW) {
+            float lsum, o0, o1;
+            const size_t head_row = (size_t)j * G + g;
+            combine_head<HD, true>(at, head_row, lane, lsum, o0, o1);
+            finish_head<HD, true>(at, head_row, lsum, o0, o1, lane);
+          }
+          stores_done();
+          if (tid == 0) atomic_add_agent(&sync[kSyncAttnDone], 1u);
+        }
+      } else if (tid == 0) {
+        atomic_add_agent(&sync[kSyncAttnDone], 1u);
+      }
+    }
+  }
+
+  // ---- 3. O + residual (waits for every kv head's attention output)
+  {
+    const StepArgs* A = &sa;
+    const ProjArgs pa = A->o;
+    const GemvPlan pl = A->po;
+    unsigned* sync = A->sync;
+    int32_t* err_word = A->err_word;
+    const int n_kv = A->n_kv;
+    int s0, ns;
+    strip_range(pa.Np / kStrip, wg, nwg, s0, ns);
+    auto wait_attn = [&] {
+      if (tid == 0 && !spin_geq(&sync[kSyncAttnDone], (unsigned)n_kv, &sync[kSyncErr], 1u)) flag_error(sync, err_word);
+      lds_barrier();
+    };
+    __syncthreads();
+    if (ns > 0) gemv_body<EPI_O, NW, UO, GQ, true>(pa, pl, s0, ns, smem, wait_attn);
+    stores_done();
+    if (tid == 0) bar_arrive(&sync[kSyncBar1], wg, nwg);
+  }
+
+  // ---- 4. gate/up + SwiGLU (after every O strip)
+  {
+    const StepArgs* A = &sa;
+    const ProjArgs pa = A->gu;
+    const GemvPlan pl = A->pg;
+    unsigned* sync = A->sync;
+    int32_t* err_word = A->err_word;
+    int s0, ns;
+    strip_range(pa.Np / kStrip, wg, nwg, s0, ns);
+    auto wait_o = [&] {
+      if (tid == 0 && !spin_geq(&sync[kSyncBar1 + 8 * kLine], (unsigned)ngroups, &sync[kSyncErr], 1u))
+        flag_error(sync, err_word);
+      lds_barrier();
+    };
+    __syncthreads();
+    if (ns > 0) gemv_body<EPI_GU, NW, UQ, GQ, true>(pa, pl, s0, ns, smem, wait_o);
+    stores_done();
+    if (tid == 0) bar_arrive(&sync[kSyncBar2], wg, nwg);
+  }
+
+  // ---- 5. down + residual (after every gate/up strip)
+  {
+    const StepArgs* A = &sa;
+    const ProjArgs pa = A->down;
+    const GemvPlan pl = A->pd;
+    unsigned* sync = A->sync;
+    int32_t* err_word = A->err_word;
+    int s0, ns;
+    strip_range(pa.Np / kStrip, wg, nwg, s0, ns);
+    auto wait_gu = [&] {
+      if (tid == 0 && !spin_geq(&sync[kSyncBar2 + 8 * kLine], (unsigned)ngroups, &sync[kSyncErr], 1u))
+        flag_error(sync, err_word);
+      lds_barrier();
+    };
+    __syncthreads();
+    if (ns > 0) gemv_body<EPI_DOWN, NW, UD, GD, true>(pa, pl, s0, ns, smem, wait_gu);
+  }
+
+  // ---- exit: the last workgroup clears the counters for the next launch
+  // (word 0 of every counter line; one line per thread)
+  {
+    __shared__ int last_out;
+    if (tid == 0) last_out = atomic_add_agent(&sa.sync[kSyncExit], 1u) == (unsigned)(nwg - 1);
+    __syncthreads();
+    if (last_out && tid < kSyncWords / kLine) st_coh(&sa.sync[tid * kLine], 0u);
+  }
+}
+
+// ---------------------------------------------------------------------------
+
+namespace {
+
+int gpw_template(int G) {
+  // groups per wave of the workgroup: 1, 2, 4 kept in registers, else 0
+  const int gpw = G / kStepWaves;
+  return (G % kStepWaves == 0 && (gpw == 1 || gpw == 2 || gpw == 4)) ? gpw : 0;
+}
+
+GemvPlan step_plan(int nstrips, int G, int nwg) {
+  GemvPlan p;
+  p.NW = kStepWaves;
+  p.GPW = (G + kStepWaves - 1) / kStepWaves;
+  p.SP = (nstrips + nwg - 1) / nwg;
+  return p;
+}
+
+template <int HD, int GQ, int GD>
+hipError_t launch_t(const StepArgs& sa, int nwg, size_t lds, hipStream_t st) {
+  hipLaunchKernelGGL((step_m1_kernel<HD, GQ, GD>), dim3(nwg), dim3(kStepWaves * 64), lds, st, sa);
+  return hipGetLastError();
+}
+
+template <int HD, int GQ, int GD>
+int occupancy_t(size_t lds) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, step_m1_kernel<HD, GQ, GD>, kStepWaves * 64, lds) !=
+      hipSuccess)
+    return 0;
+  return n;
+}
+
+template <int HD>
+int dispatch_occ(int gq, int gd, size_t lds) {
+#define I4D_OCC(Q, D) \
+  if (gq == Q && gd == D) return occupancy_t<HD, Q, D>(lds);
+  I4D_OCC(1, 4) I4D_OCC(1, 0) I4D_OCC(2, 0) I4D_OCC(2, 4) I4D_OCC(4, 0) I4D_OCC(4, 4) I4D_OCC(0, 0)
+  I4D_OCC(0, 4)
+#undef I4D_OCC
+  return 0;
+}
+
+template <int HD>
+hipError_t dispatch_launch(int gq, int gd, const StepArgs& sa, int nwg, size_t lds, hipStream_t st) {
+#define I4D_LAUNCH(Q, D) \
+  if (gq == Q && gd == D) return launch_t<HD, Q, D>(sa, nwg, lds, st);
+  I4D_LAUNCH(1, 4) I4D_LAUNCH(1, 0) I4D_LAUNCH(2, 0) I4D_LAUNCH(2, 4) I4D_LAUNCH(4, 0) I4D_LAUNCH(4, 4)
+  I4D_LAUNCH(0, 0) I4D_LAUNCH(0, 4)
+#undef I4D_LAUNCH
+  return hipErrorInvalidValue;
+}
+
+size_t attn_lds_bytes(int hd) { return (size_t)(2 * kStepWaves * 8 + kStepWaves * 8 * hd) * 4; }
+
+}  // namespace
+
+bool step_m1_supported(const i4d_layer_shape* s) {
+  const int gq = gpw_template(s->d_model / kGroup);
+  const int go = gpw_template(s->n_q_heads * s->head_dim / kGroup);
+  const int G = s->n_q_heads / s->n_kv_heads;
+  // one kernel variant for QKV, O and gate/up; every K within the x staging
+  // of one workgroup (4 chunks of 8 per thread); at most 16 kv heads
+  const int kmax = 4 * 8 * kStepWaves * 64;
+  return gq == go && G <= 8 && s->n_kv_heads <= 16 && s->d_model <= kmax &&
+         s->n_q_heads * s->head_dim <= kmax && s->d_ffn <= kmax;
+}
+
+i4d_status launch_step_m1(const StepInputs& in, hipStream_t st) {
+  const i4d_layer_shape& s = in.layer->shape;
+  const int gq = gpw_template(s.d_model / kGroup);
+  const int gd = gpw_template(s.d_ffn / kGroup) == 4 ? 4 : 0;
+
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return fail(I4D_ERR_HIP, "device query failed");
+
+  StepArgs sa = {};
+  sa.qkv = in.qkv;
+  sa.o = in.o;
+  sa.gu = in.gu;
+  sa.down = in.down;
+  sa.at = in.attn;
+  sa.sync = in.sync;
+  sa.err_word = in.attn.kv.err_word;
+  sa.n_kv = s.n_kv_heads;
+  sa.G = s.n_q_heads / s.n_kv_heads;
+  sa.hd = s.head_dim;
+  sa.Sf = in.attn.S;
+
+  // LDS: the largest stage (attention, or a projection)
+  const int nwg_guess = cus;
+  sa.pq = step_plan(sa.qkv.Np / kStrip, sa.qkv.G, nwg_guess);
+  sa.po = step_plan(sa.o.Np / kStrip, sa.o.G, nwg_guess);
+  sa.pg = step_plan(sa.gu.Np / kStrip, sa.gu.G, nwg_guess);
+  sa.pd = step_plan(sa.down.Np / kStrip, sa.down.G, nwg_guess);
+  size_t lds = attn_lds_bytes(s.head_dim);
+  lds = std::max(lds, gemv_lds_bytes(sa.qkv.K, sa.pq));
+  lds = std::max(lds, gemv_lds_bytes(sa.o.K, sa.po));
+  lds = std::max(lds, gemv_lds_bytes(sa.gu.K, sa.pg));
+  lds = std::max(lds, gemv_lds_bytes(sa.down.K, sa.pd));
+
+  // every workgroup must be resident at once (they wait on each other)
+  const int occ = s.head_dim == 128 ? dispatch_occ<128>(gq, gd, lds) : dispatch_occ<64>(gq, gd, lds);
+  if (occ < 1) return fail(I4D_ERR_UNSUPPORTED, "one-launch step does not fit a CU (LDS %zu)", lds);
+  const int nwg = cus;  // one workgroup per CU
+  hipError_t e = s.head_dim == 128 ? dispatch_launch<128>(gq, gd, sa, nwg, lds, st)
+                                   : dispatch_launch<64>(gq, gd, sa, nwg, lds, st);
+  if (e != hipSuccess) return fail(I4D_ERR_HIP, "one-launch step: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace i4d

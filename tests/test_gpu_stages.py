@@ -322,6 +322,27 @@ def test_block_dirty_workspace_forced_splits(gpu):
     assert norm_maxabs(attn.cpu().numpy(), ref.attn) <= ATT_TOL
 
 
+# shapes the one-launch M = 1 step covers (every K a multiple of 8 groups)
+ONE_LAUNCH_SHAPES = [synth.LayerShape(1024, 8, 2, 128, 2048), synth.LayerShape(1024, 16, 4, 64, 2048)]
+
+
+@pytest.mark.parametrize("shape", ONE_LAUNCH_SHAPES, ids=["hd128", "hd64"])
+@pytest.mark.parametrize("L", [1, 33, 700])
+def test_block_m1_one_launch(gpu, shape, L):
+    """M = 1 runs as one persistent launch; two steps in a row on one
+    workspace (the second relies on the counters the first left at zero)
+    give identical outputs."""
+    torch, B, D = gpu
+    res = run_block(gpu, shape, 21, [L])
+    check_block(res, f"one-launch hd={shape.head_dim} L={L}")
+    first = res["x_out"].clone()
+    B.i4d_decode_block_step(res["layer"].struct, res["cache"].struct, res["x_in"], res["x_out"], res["ctx"], 1,
+                            L, 0, res["ws"].buf, res["ws"].nbytes, None)
+    torch.cuda.synchronize()
+    assert res["cache"].errors() == 0
+    assert torch.equal(first, res["x_out"])
+
+
 def test_block_deterministic(gpu):
     torch, B, D = gpu
     res = run_block(gpu, synth.SHAPE_SMALL128, 12, [100, 700, 33])
