@@ -272,6 +272,10 @@ i4d_status i4d_ffn_down(const i4d_layer* layer, const uint16_t* a, const float* 
 i4d_status i4d_workspace_bytes(const i4d_layer_shape* shape, int M, int max_ctx_len,
                                int num_splits, size_t* bytes);
 
+/* *one_launch = 1 if i4d_decode_block_step runs as a single persistent
+ * launch for this shape and M on the current device, else 0. */
+i4d_status i4d_decode_step_is_one_launch(const i4d_layer_shape* shape, int M, int* one_launch);
+
 /* Zero-fill a decode-step workspace (device, `bytes` long, 16-byte aligned)
  * on `stream`. */
 i4d_status i4d_workspace_init(void* workspace, size_t bytes, void* stream);

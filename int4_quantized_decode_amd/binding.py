@@ -86,6 +86,7 @@ _SIGS = {
     "i4d_workspace_layout_of": (_I, [ctypes.POINTER(i4d_layer_shape), _I, _I, _I,
                                      ctypes.POINTER(i4d_workspace_layout)]),
     "i4d_workspace_init": (_I, [_VP, ctypes.c_size_t, _VP]),
+    "i4d_decode_step_is_one_launch": (_I, [ctypes.POINTER(i4d_layer_shape), _I, ctypes.POINTER(_I)]),
     "i4d_decode_block_step": (_I, [ctypes.POINTER(i4d_layer), ctypes.POINTER(i4d_kv_cache), _VP, _VP, _VP,
                                    _I, _I, _I, _VP, ctypes.c_size_t, _VP, _VP]),
     "i4d_lm_head_workspace_bytes": (_I, [_I, _I, c_size_p]),
@@ -236,6 +237,12 @@ def i4d_workspace_layout_of(shape: i4d_layer_shape, M: int, max_ctx_len: int, nu
     out = i4d_workspace_layout()
     _check(lib().i4d_workspace_layout_of(ctypes.byref(shape), M, max_ctx_len, num_splits, ctypes.byref(out)))
     return out
+
+
+def i4d_decode_step_is_one_launch(shape: i4d_layer_shape, M: int) -> bool:
+    out = _I()
+    _check(lib().i4d_decode_step_is_one_launch(ctypes.byref(shape), M, ctypes.byref(out)))
+    return bool(out.value)
 
 
 def i4d_workspace_init(workspace, nbytes: int, stream=None):

@@ -336,6 +336,13 @@ i4d_status i4d_decode_block_step(const i4d_layer* layer, const i4d_kv_cache* cac
   return ok();
 }
 
+i4d_status i4d_decode_step_is_one_launch(const i4d_layer_shape* shape, int M, int* one_launch) {
+  I4D_TRY(check_shape(shape));
+  if (!one_launch) return fail(I4D_ERR_NULL, "one_launch is NULL");
+  *one_launch = (M == 1 && step_m1_supported(shape)) ? 1 : 0;
+  return ok();
+}
+
 i4d_status i4d_workspace_init(void* workspace, size_t bytes, void* stream) {
   I4D_TRY(need(workspace, "workspace"));
   if (bytes % 16) return fail(I4D_ERR_RANGE, "workspace bytes %zu not a multiple of 16", bytes);

@@ -510,21 +510,22 @@ __device__ __forceinline__ void combine_head(const AttnArgs& a, size_t head_row,
   const int S = a.S;
   const float* ml = a.part_ml + head_row * S * 2;
   const float* po = a.part_o + head_row * S * HD;
+  // every load of a chunk is issued before any of them is used: one round
+  // trip per 32 splits (lane u < CH holds split t0 + u's max and sum)
+  float mt[(I4D_MAX_SPLITS + CH - 1) / CH], lt[(I4D_MAX_SPLITS + CH - 1) / CH];
   float M_ = -INFINITY;
-  for (int t = lane; t < S; t += 64)
-    if (ld(&ml[2 * t + 1]) > 0.f) M_ = fmaxf(M_, ld(&ml[2 * t]));
+  const int nch = (S + CH - 1) / CH;
+  for (int c = 0; c < nch; ++c) {
+    const int t = min(c * CH + (lane & (CH - 1)), S - 1);
+    mt[c] = ld(&ml[2 * t]);
+    lt[c] = ld(&ml[2 * t + 1]);
+    const bool valid = (lane < CH) && (c * CH + lane < S) && lt[c] > 0.f;
+    M_ = fmaxf(M_, valid ? mt[c] : -INFINITY);
+  }
   M_ = wave_max(M_);
   float lsum = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int t0 = 0; t0 < S; t0 += CH) {
-    // lane u < CH: weight of split t0 + u
-    float f = 0.f;
-    if (lane < CH && t0 + lane < S) {
-      const float l = ld(&ml[2 * (t0 + lane) + 1]);
-      if (l > 0.f) {
-        f = exp2f(ld(&ml[2 * (t0 + lane)]) - M_);
-        lsum = fmaf(f, l, lsum);
-      }
-    }
+  for (int c = 0; c < nch; ++c) {
+    const int t0 = c * CH;
     float x0[CH], x1[CH];
 #pragma unroll
     for (int u = 0; u < CH; ++u) {
@@ -532,13 +533,14 @@ __device__ __forceinline__ void combine_head(const AttnArgs& a, size_t head_row,
       x0[u] = ld(&po[(size_t)t * HD + lane]);
       x1[u] = (HD == 128) ? ld(&po[(size_t)t * HD + lane + 64]) : 0.f;
     }
+    const bool valid = (lane < CH) && (t0 + lane < S) && lt[c] > 0.f;
+    const float f = valid ? exp2f(mt[c] - M_) : 0.f;
+    lsum = fmaf(f, valid ? lt[c] : 0.f, lsum);
 #pragma unroll
     for (int u = 0; u < CH; ++u) {
       const float fu = __shfl(f, u, 64);
-      if (t0 + u < S && fu > 0.f) {
-        o0 = fmaf(fu, x0[u], o0);
-        o1 = fmaf(fu, x1[u], o1);
-      }
+      o0 = fmaf(fu, x0[u], o0);
+      o1 = fmaf(fu, x1[u], o1);
     }
   }
 #pragma unroll

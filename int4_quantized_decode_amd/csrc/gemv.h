@@ -238,7 +238,7 @@ __device__ __forceinline__ void gemv_body(const ProjArgs& a, const GemvPlan& pl,
   // 2. the first U atoms of the weight stream.  The refill cursor (rs, rg)
   // walks strip by strip through the wave's groups and stops on the last
   // atom, which pads the sequence.  With GPW > 0 the slot of a strip's
-  // first group also loads the strip's GPW scales (one load per strip: a
+  // last group also loads the strip's GPW scales (one load per strip: a
   // row's 8 consecutive groups are contiguous); GPW == 0 loads each
   // atom's scale.
   int rs = 0, rg = 0;
@@ -266,17 +266,20 @@ __device__ __forceinline__ void gemv_body(const ProjArgs& a, const GemvPlan& pl,
     ring[k] = load16_stream(cp);
     if (GPW == 0) {
       sring[k] = *sp;
-    } else if (k % GR == 0) {
+    } else if (k % GR == GR - 1) {
+      // the strip's last slot: every slot of the strip has been consumed
+      // and refilled with the next strip's atoms
+      const int k0 = k - (GR - 1);
       if (GR == 1) {
-        sring[k] = *sv;
+        sring[k0] = *sv;
       } else if (GR == 2) {
         const uint32_t w = *reinterpret_cast<const uint32_t*>(sv);
-        sring[k] = (uint16_t)w;
-        sring[k + 1] = (uint16_t)(w >> 16);
+        sring[k0] = (uint16_t)w;
+        sring[k0 + 1] = (uint16_t)(w >> 16);
       } else {
         const u32x2_t w = *reinterpret_cast<const u32x2_t*>(sv);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) sring[k + q] = (uint16_t)(w[q >> 1] >> (16 * (q & 1)));
+        for (int q = 0; q < 4; ++q) sring[k0 + q] = (uint16_t)(w[q >> 1] >> (16 * (q & 1)));
       }
     }
   };

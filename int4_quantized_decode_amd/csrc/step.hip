@@ -40,8 +40,8 @@ constexpr int kLine = 32;
 constexpr int kSyncQkv = 0;               // [n_kv] finished QKV strips per kv head
 constexpr int kSyncAttn = 16 * kLine;     // [n_kv] finished attention splits per kv head
 constexpr int kSyncAttnDone = 32 * kLine; // kv heads whose attention output is written
-constexpr int kSyncBar1 = 33 * kLine;     // 8 group counters + top (after O)
-constexpr int kSyncBar2 = 42 * kLine;     // 8 group counters + top (after gate/up)
+constexpr int kSyncBar1 = 33 * kLine;     // 8 group counters (after O)
+constexpr int kSyncBar2 = 42 * kLine;     // 8 group counters (after gate/up)
 constexpr int kSyncExit = 51 * kLine;
 constexpr int kSyncWords = 52 * kLine;    // cleared at exit
 constexpr int kSyncErr = 52 * kLine;      // sticky timeout flag (not cleared)
@@ -82,12 +82,24 @@ __device__ __forceinline__ void stores_done() {
   __builtin_amdgcn_s_barrier();
 }
 
-// two-level grid barrier (8 groups of workgroups, then a top counter)
-__device__ __forceinline__ void bar_arrive(unsigned* bar, int wg, int nwg) {
-  const int g = wg & 7;
-  const unsigned gs = (unsigned)((nwg - g + 7) / 8);
-  const unsigned old = atomic_add_agent(&bar[g * kLine], 1u);
-  if (old == gs - 1) atomic_add_agent(&bar[8 * kLine], 1u);
+// grid barrier on 8 group counters (workgroup w counts in group w % 8, so
+// arrivals spread over 8 addresses); the waiter polls the 8 counters at once
+__device__ __forceinline__ void bar_arrive(unsigned* bar, int wg) {
+  atomic_add_agent(&bar[(wg & 7) * kLine], 1u);
+}
+__device__ __forceinline__ bool bar_wait(unsigned* bar, int nwg, unsigned* err) {
+  for (int it = 0; it < (1 << 21); ++it) {
+    bool all = true;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      const unsigned gs = (unsigned)((nwg - g + 7) / 8);
+      all &= __hip_atomic_load(&bar[g * kLine], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= gs;
+    }
+    if (all) return true;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  atomicOr(err, 1u);
+  return false;
 }
 
 template <int HD, int GQ, int GD>
@@ -99,7 +111,6 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_m1_kernel(StepArgs sa) {
   constexpr int UD = 16;
   const int tid = threadIdx.x;
   const int wg = blockIdx.x, nwg = gridDim.x;
-  const int ngroups = nwg < 8 ? nwg : 8;
 
   // ---- 1. QKV
   {
@@ -176,7 +187,7 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_m1_kernel(StepArgs sa) {
     __syncthreads();
     if (ns > 0) gemv_body<EPI_O, NW, UO, GQ, true>(pa, pl, s0, ns, smem, wait_attn);
     stores_done();
-    if (tid == 0) bar_arrive(&sync[kSyncBar1], wg, nwg);
+    if (tid == 0) bar_arrive(&sync[kSyncBar1], wg);
   }
 
   // ---- 4. gate/up + SwiGLU (after every O strip)
@@ -189,14 +200,13 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_m1_kernel(StepArgs sa) {
     int s0, ns;
     strip_range(pa.Np / kStrip, wg, nwg, s0, ns);
     auto wait_o = [&] {
-      if (tid == 0 && !spin_geq(&sync[kSyncBar1 + 8 * kLine], (unsigned)ngroups, &sync[kSyncErr], 1u))
-        flag_error(sync, err_word);
+      if (tid == 0 && !bar_wait(&sync[kSyncBar1], nwg, &sync[kSyncErr])) flag_error(sync, err_word);
       lds_barrier();
     };
     __syncthreads();
     if (ns > 0) gemv_body<EPI_GU, NW, UQ, GQ, true>(pa, pl, s0, ns, smem, wait_o);
     stores_done();
-    if (tid == 0) bar_arrive(&sync[kSyncBar2], wg, nwg);
+    if (tid == 0) bar_arrive(&sync[kSyncBar2], wg);
   }
 
   // ---- 5. down + residual (after every gate/up strip)
@@ -209,8 +219,7 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_m1_kernel(StepArgs sa) {
     int s0, ns;
     strip_range(pa.Np / kStrip, wg, nwg, s0, ns);
     auto wait_gu = [&] {
-      if (tid == 0 && !spin_geq(&sync[kSyncBar2 + 8 * kLine], (unsigned)ngroups, &sync[kSyncErr], 1u))
-        flag_error(sync, err_word);
+      if (tid == 0 && !bar_wait(&sync[kSyncBar2], nwg, &sync[kSyncErr])) flag_error(sync, err_word);
       lds_barrier();
     };
     __syncthreads();

@@ -170,7 +170,9 @@ def test_attention_workspace_reuse(gpu):
 # projections
 # ---------------------------------------------------------------------------
 
-SHAPES = {"tiny": synth.SHAPE_TINY, "small128": synth.SHAPE_SMALL128}
+SHAPES = {"tiny": synth.SHAPE_TINY, "small128": synth.SHAPE_SMALL128,
+          # K = 4096 and 8192: two and four weight groups per wave in the M = 1 kernel
+          "k4096": synth.LayerShape(4096, 8, 2, 128, 8192)}
 
 
 @pytest.fixture(scope="module")
@@ -323,10 +325,11 @@ def test_block_dirty_workspace_forced_splits(gpu):
 
 
 # shapes the one-launch M = 1 step covers (every K a multiple of 8 groups)
-ONE_LAUNCH_SHAPES = [synth.LayerShape(1024, 8, 2, 128, 2048), synth.LayerShape(1024, 16, 4, 64, 2048)]
+ONE_LAUNCH_SHAPES = [synth.LayerShape(1024, 8, 2, 128, 2048), synth.LayerShape(1024, 16, 4, 64, 2048),
+                     synth.LayerShape(4096, 8, 2, 128, 2048)]
 
 
-@pytest.mark.parametrize("shape", ONE_LAUNCH_SHAPES, ids=["hd128", "hd64"])
+@pytest.mark.parametrize("shape", ONE_LAUNCH_SHAPES, ids=["hd128", "hd64", "k4096"])
 @pytest.mark.parametrize("L", [1, 33, 700])
 def test_block_m1_one_launch(gpu, shape, L):
     """M = 1 runs as one persistent launch; two steps in a row on one
