@@ -291,6 +291,8 @@ typedef struct {
   size_t h_bf16; /* bf16 [M][d] */
   size_t a;     /* bf16 [M][d_ffn] */
   size_t attn_ws; /* start of the attention workspace */
+  size_t split_cnt;  /* arrival counters of the projections' K split (zero before first use) */
+  size_t split_part; /* partial tiles of the projections' K split */
   size_t sync;    /* counters of the one-launch step (must be zero before first use) */
   size_t total;
 } i4d_workspace_layout;

@@ -59,7 +59,7 @@ class i4d_layer(ctypes.Structure):
 
 
 class i4d_workspace_layout(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_size_t) for n in ("q", "k", "v", "attn", "h", "h_bf16", "a", "attn_ws", "sync",
+    _fields_ = [(n, ctypes.c_size_t) for n in ("q", "k", "v", "attn", "h", "h_bf16", "a", "attn_ws", "split_cnt", "split_part", "sync",
                                                "total")]
 
 

@@ -325,14 +325,21 @@ i4d_status i4d_decode_block_step(const i4d_layer* layer, const i4d_kv_cache* cac
     in.sync = (unsigned*)(ws + wl.sync);
     return launch_step_m1(in, st);
   }
-  I4D_TRY(do_qkv(layer, x_in, ctx_len, M, q, k, v, st));
+  // the projections may split K across workgroups through the workspace
+  auto split = [&](ProjArgs a) {
+    a.split_cnt = (unsigned*)(ws + wl.split_cnt);
+    a.split_part = (float*)(ws + wl.split_part);
+    a.split_bytes = wl.sync - wl.split_part;
+    return a;
+  };
+  I4D_TRY(launch_projection(EPI_QKV, split(qkv_args(layer, x_in, ctx_len, M, q, k, v)), st));
   // the attention launch first appends the new token of row m at position
   // ctx_len[m] - 1 of cache row m (inside the workgroup that owns that block)
   I4D_TRY(do_attention(cache, s, q, ctx_len, M, max_ctx_len, num_splits, ws + wl.attn_ws, attn_f32,
                        attn, k, v, true, st));
-  I4D_TRY(do_o(layer, attn, x_in, M, h, hb, st));
-  I4D_TRY(do_gu(layer, hb, M, act, st));
-  I4D_TRY(do_down(layer, act, h, M, x_out, st));
+  I4D_TRY(launch_projection(EPI_O, split(o_args(layer, attn, x_in, M, h, hb)), st));
+  I4D_TRY(launch_projection(EPI_GU, split(gu_args(layer, hb, M, act)), st));
+  I4D_TRY(launch_projection(EPI_DOWN, split(down_args(layer, act, h, M, x_out)), st));
   return ok();
 }
 

@@ -385,6 +385,20 @@ i4d_status i4d_workspace_layout_of(const i4d_layer_shape* s, int M, int max_ctx_
   out->h_bf16 = off;  off += align256((size_t)M * s->d_model * 2);
   out->a = off;       off += align256((size_t)M * s->d_ffn * 2);
   out->attn_ws = off; off += align256(attn_bytes);
+  // the four projections run one after another and leave their counters
+  // at zero, so they share one split buffer
+  const int nqkv = (s->n_q_heads + 2 * s->n_kv_heads) * s->head_dim;
+  const SplitNeed need[4] = {projection_split_need(nqkv, s->d_model, M),
+                             projection_split_need(s->d_model, s->n_q_heads * s->head_dim, M),
+                             projection_split_need(2 * s->d_ffn, s->d_model, M),
+                             projection_split_need(s->d_model, s->d_ffn, M)};
+  size_t cnt = 0, part = 0;
+  for (const SplitNeed& n : need) {
+    cnt = std::max(cnt, n.counters);
+    part = std::max(part, n.part_bytes);
+  }
+  out->split_cnt = off;  off += align256(cnt * sizeof(unsigned));
+  out->split_part = off; off += align256(part);
   out->sync = off;    off += align256(kStepSyncBytes);
   out->total = off;
   return ok();

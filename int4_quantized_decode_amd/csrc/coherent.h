@@ -45,6 +45,13 @@ __device__ __forceinline__ u32x4_t ld_coh16(const void* base, uint32_t off, uint
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 16 /* sc1 */);
 }
 
+// 16-byte agent-coherent store at byte offset `off` of a buffer of `bytes`
+// bytes (the sc1 policy of the relaxed agent-scope stores above)
+__device__ __forceinline__ void st_coh16(void* base, uint32_t off, uint32_t bytes, u32x4_t v) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, 0, bytes, 0x00020000);
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 16 /* sc1 */);
+}
+
 // wait until this wave's stores (and loads) have completed
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 

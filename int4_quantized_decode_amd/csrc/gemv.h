@@ -15,7 +15,7 @@
 namespace i4d {
 
 template <int EPI>
-__device__ __forceinline__ bool needs_rho() {
+__host__ __device__ __forceinline__ constexpr bool needs_rho() {
   return EPI == EPI_QKV || EPI == EPI_GU;
 }
 

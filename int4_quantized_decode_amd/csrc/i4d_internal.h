@@ -9,6 +9,15 @@
 
 namespace i4d {
 
+// split buffer a projection of Np x K at M rows uses when one is at hand
+// (0 bytes: it does not split K): partial tiles and strip-set counters
+struct SplitNeed {
+  size_t part_bytes;
+  size_t counters;
+};
+SplitNeed projection_split_need(int Np, int K, int M);
+
+
 // records the message for i4d_last_error() and returns `st`
 i4d_status fail(i4d_status st, const char* fmt, ...);
 i4d_status ok();

@@ -32,7 +32,13 @@ struct ProjArgs {
   // down epilogue
   const float* resid_f32;
   uint16_t* out_bf16;
+  // split of K across workgroups (M > 1; NULL: none): partial tiles and one
+  // arrival counter per strip set, zero between launches
+  float* split_part;
+  unsigned* split_cnt;
+  size_t split_bytes;
 };
+
 
 i4d_status launch_projection(int epi, const ProjArgs& a, hipStream_t st);
 

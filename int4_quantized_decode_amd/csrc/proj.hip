@@ -1,27 +1,29 @@
 // proj.hip - INT4 projection kernels (gfx950): QKV, O, gate/up, down.
 //
 // y[m][n] = sum_g s[n][g] * sum_{k in g} (u[n][k] - 8) * x[m][k]
-// ("how it differs": group scales applied after accumulation), computed as
-// sum_g s[n][g] * (A[n][g] - 136 * X[m][g]) where A accumulates
-// (128 + u) * x from the bf16 magic-exponent decode of each nibble and X is
-// the group sum of x; the per-group scale and the 136 correction are applied
-// once per group after the 128-wide accumulation.
+// ("how it differs": group scales applied after accumulation).
 //
-// M = 1: register-streaming VALU GEMV.  Each 64-lane wave streams 1 KiB
-//   atoms (16 rows x 128 k, one 16-byte load per lane) and accumulates with
-//   v_dot2_f32_bf16 against x staged in LDS.
-// M = 2..32: skinny GEMM on bf16 MFMA 16x16x32.  The atom lane layout is the
-//   A operand; x[m] rows are the B operand read straight from global memory;
-//   group sums of x and the RMSNorm sum of squares come from two extra MFMAs
-//   (ones . x and x . x^T diagonal) so no VALU work is spent on them.
+// M = 1: register-streaming VALU GEMV (gemv.h).  Each 64-lane wave streams
+//   1 KiB atoms (16 rows x 128 k, one 16-byte load per lane), decodes the
+//   nibbles as exact fp16 subnormals and accumulates with v_dot2_f32_f16
+//   against range-scaled fp16 x staged in LDS.
+// M = 2..32: skinny GEMM on bf16 MFMA 16x16x32, computed as
+//   sum_g s[n][g] * (A[n][g] - 136 * X[m][g]) where A accumulates
+//   (128 + u) * x from the bf16 magic-exponent decode of each nibble and X
+//   is the group sum of x (one more MFMA against ones); the scale and the
+//   136 correction are applied once per group after the 128-wide
+//   accumulation.  Large-K projections may split K across workgroups
+//   through the step workspace (the last slice to arrive reduces).
 //
-// Both kernels split K across the waves of a workgroup (interleaved groups),
-// reduce in LDS and run the epilogue once per output from an LDS tile:
+// Both split K across the waves of a workgroup, reduce in LDS and run the
+// epilogue once per output from an LDS tile:
 //   QKV : rho1 (from the staged input), RoPE on q/k pairs, q fp32, k/v bf16
 //   O   : h = x + y (fp32 and bf16 copies)
 //   GU  : rho2, a = silu(gate) * up (bf16)
 //   DOWN: out = h + y (bf16)
 #include <math.h>
+
+#include <type_traits>
 
 #include "device_common.h"
 #include "gemv.h"
@@ -47,116 +49,390 @@ __global__ __launch_bounds__(NW * 64) void proj_gemv_kernel(ProjArgs a, GemvPlan
 // ---------------------------------------------------------------------------
 // M = 2..32: bf16 MFMA skinny GEMM
 // ---------------------------------------------------------------------------
+//
+// A workgroup of 8 waves owns SP strips (16 output rows each) and one of
+// KS slices of K; the waves split the slice (wave w takes every 8th group
+// from w).  For each of its groups a wave loads the x rows of the group
+// (T tiles of 16 rows, one group ahead, row-contiguous), turns them into
+// B operands of the MFMA through its own LDS rows, and reuses them for the
+// SP atoms of the group, which stream through a ring of D groups of
+// outstanding 16-byte loads.  The atom lane layout is the A operand.
+// Scales are staged in LDS per workgroup, transposed so a lane reads its 4
+// rows of a group at once; the waves' partial tiles are summed in LDS in a
+// fixed order.
 
-template <int EPI, int S, int NW, int T>
-__global__ __launch_bounds__(NW * 64) void proj_mfma_kernel(ProjArgs a) {
-  __shared__ float red[NW][S * 16][T * 16];
-  __shared__ float sqred[NW][T * 16];
-  __shared__ float rho_s[T * 16];
-  __shared__ float ot[S * 16 * T * 16];
+constexpr int kSkinnyWaves = 8;
+constexpr int kScaleLoads = 4;  // scale loads per thread: SP * ceil(G/8) <= 128
 
+struct SkinnyPlan {
+  int SP;   // strips per workgroup
+  int KS;   // K slices (workgroups per strip set; > 1 needs the split buffers)
+  int GPW;  // groups per wave in the longest slice
+  int D;    // groups of atoms in flight per wave
+  int NB8;  // 8-group scale blocks a slice touches, at most
+};
+
+// floats per (strip set, slice) in the split buffer: the partial tile
+// [SP*16][32] and the slice's sums of squares [32]
+__host__ __device__ inline size_t split_block_floats(int SP) { return (size_t)SP * 16 * 32 + 32; }
+
+// x rows staged per wave: 256 bytes of a group plus 16 bytes of padding, so
+// that operand reads (16 rows at a 272-byte stride) hit distinct banks
+constexpr int kXRow = 272;
+
+// LDS: sums of squares [NW][T*16] f32 | rho [T*16] | tile [SP*16][T*16] |
+// then either scales [SP][8*NB8][16] fp16 + x staging [NW][16T][kXRow
+// bytes] (main loop) or partial tiles [4][SP*16][T*16+4] f32 (reduction)
+inline size_t skinny_lds_bytes(int NB8, int SP, int T) {
+  const size_t loop = (size_t)SP * NB8 * 8 * 16 * 2 + (size_t)kSkinnyWaves * 16 * T * kXRow;
+  const size_t reduce = (size_t)4 * SP * 16 * (T * 16 + 4) * 4;
+  return (size_t)kSkinnyWaves * T * 16 * 4 + (size_t)T * 16 * 4 + (size_t)SP * 16 * T * 16 * 4 +
+         std::max(loop, reduce);
+}
+
+template <int EPI, int SP, int T, int D>
+__global__ __launch_bounds__(kSkinnyWaves * 64) void proj_skinny_kernel(ProjArgs a, SkinnyPlan pl) {
+  constexpr int NW = kSkinnyWaves;
+  constexpr int U = D * SP;  // D groups of atoms in flight
+  extern __shared__ __align__(16) unsigned char smem[];
   const int K = a.K, G = a.G, M = a.M;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float* sqw = reinterpret_cast<float*>(smem);                                   // [NW][T*16]
+  float* rho_s = sqw + NW * T * 16;                                              // [T*16]
+  float* ot = rho_s + T * 16;                                                    // [SP*16][M]
+  uint16_t* sc = reinterpret_cast<uint16_t*>(ot + SP * 16 * T * 16);             // [SP][8*NB8][16]
+  unsigned char* xst = reinterpret_cast<unsigned char*>(sc + (size_t)SP * pl.NB8 * 8 * 16);  // [NW][16T][kXRow]
+  float* red = reinterpret_cast<float*>(sc);  // [4][SP*16][T*16+4], over sc and xst once the waves are done
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, j = lane >> 4;
-  const int strip0 = blockIdx.x * S;
   const int nstrips = a.Np / kStrip;
+  // workgroup = (strip set, K slice); the slice is groups [gs0, gs1)
+  const int KS = pl.KS;
+  const int set = blockIdx.x / KS, ks = blockIdx.x - set * KS;
+  const int strip0 = set * SP;
+  const int ns = min(SP, nstrips - strip0);
+  const int gs0 = ks * G / KS, Gs = (ks + 1) * G / KS - gs0;
+  // wave w takes groups w, w + NW, w + 2 NW, ... of the slice (the waves
+  // of a workgroup read neighbouring atoms of a strip at the same time);
+  // groups past the wave's share (padding to a multiple of D) re-read its
+  // last group and are weighted by zero
+  const int gpw = max(0, (Gs - wave + NW - 1) / NW);
+  auto group_of = [&](int gi) { return gs0 + min(wave + NW * min(gi, max(gpw - 1, 0)), Gs - 1); };
+
+  // ring of atoms: slot d * SP + s holds strip s of a group gi with
+  // gi % D == d
+  auto atom_ptr = [&](int gi, int s) -> const uint8_t* {
+    const int t = min(strip0 + min(s, ns - 1), nstrips - 1);
+    return a.codes + ((size_t)t * G + group_of(gi)) * kAtomBytes + (size_t)lane * 16;
+  };
+  // scales of the workgroup's strips and slice (8-group blocks b0 ..
+  // b0 + nb8 - 1), requested first (they are needed first); at most
+  // kScaleLoads 16-byte loads per thread
+  const int b0 = gs0 / 8, nb8 = (gs0 + Gs + 7) / 8 - b0;
+  const int nsc = ns * nb8 * 16;
+  u32x4_t scv[kScaleLoads];
+#pragma unroll
+  for (int q = 0; q < kScaleLoads; ++q) {
+    const int idx = min(tid + q * NW * 64, nsc - 1);
+    const int s = idx / (nb8 * 16), rest = idx % (nb8 * 16);
+    scv[q] = load16(a.scales + (((size_t)(strip0 + s) * a.G8 + b0 + rest / 16) * 16 + rest % 16) * 8);
+  }
+
+  u32x4_t ring[U];
+#pragma unroll
+  for (int k = 0; k < U; ++k) ring[k] = load16_stream(atom_ptr(k / SP, k % SP));
+
+  // x rows of one group as B operands: lane (col r, quarter j) holds row
+  // 16 t + r, k = 128 g + 32 kb + 8 j .. +7.  Columns past M re-read row
+  // M - 1 (unconditional loads keep the wait counts exact); their outputs
+  // are never stored.
+  // Global reads of x are row-contiguous (load q of a wave covers rows
+  // 4q .. 4q+3, 256 bytes each: whole cache lines); the wave transposes
+  // them through its own LDS rows into the operand layout.
+  auto load_xs = [&](u32x4_t (&xs)[4 * T], int gi) {
+    const int g = group_of(gi);
+#pragma unroll
+    for (int q = 0; q < 4 * T; ++q) {
+      const int m = min(4 * q + j, M - 1);
+      xs[q] = load16(a.x + (size_t)m * K + 128 * g + 8 * r);
+    }
+  };
+  unsigned char* xw = xst + (size_t)wave * (16 * T) * kXRow;
+  auto stage_bx = [&](const u32x4_t (&xs)[4 * T], u32x4_t (&bx)[T][4]) {
+#pragma unroll
+    for (int q = 0; q < 4 * T; ++q) *reinterpret_cast<u32x4_t*>(xw + (4 * q + j) * kXRow + 16 * r) = xs[q];
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        bx[t][kb] = *reinterpret_cast<const u32x4_t*>(xw + (16 * t + r) * kXRow + 64 * kb + 16 * j);
+  };
+  u32x4_t xs[4 * T];
+  load_xs(xs, 0);
+
+  // scales to LDS, transposed to [s][g][row] (threads past the end repeat
+  // the last item's identical writes); the barrier does not wait for the
+  // atoms and x still in flight
+  const int GP = pl.NB8 * 8;
+#pragma unroll
+  for (int q = 0; q < kScaleLoads; ++q) {
+    const int idx = min(tid + q * NW * 64, nsc - 1);
+    const int s = idx / (nb8 * 16), rest = idx % (nb8 * 16), g8 = rest / 16, row = rest % 16;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sc[((size_t)s * GP + 8 * g8 + e) * 16 + row] = (uint16_t)(scv[q][e >> 1] >> (16 * (e & 1)));
+  }
+  lds_barrier();
 
   const u32x4_t ones_u = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
   const bf16x8_t ones = bitcast<bf16x8_t>(ones_u);
-
-  f32x4_t acc[S][T];
-  f32x4_t gram[T];
+  f32x4_t acc[SP][T];
 #pragma unroll
-  for (int s = 0; s < S; ++s)
+  for (int s = 0; s < SP; ++s)
 #pragma unroll
     for (int t = 0; t < T; ++t) acc[s][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float sq[T];
 #pragma unroll
-  for (int t = 0; t < T; ++t) gram[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < T; ++t) sq[t] = 0.f;
 
-  const uint8_t* codes = a.codes + (size_t)lane * 16;
-  for (int g = wave; g < G; g += NW) {
-    u32x4_t w[S];
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-      const int t = strip0 + s;
-      w[s] = (t < nstrips) ? load16_stream(codes + ((size_t)t * G + g) * kAtomBytes)
-                           : u32x4_t{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
-    }
-    u32x4_t bx[T][4];
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-      const int m = 16 * t + r;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-        bx[t][kb] = (m < M) ? load16(a.x + (size_t)m * K + 128 * g + 32 * kb + 8 * j)
-                            : u32x4_t{0u, 0u, 0u, 0u};
-    }
+  // one group: column sums and sums of squares of x, then its SP atoms;
+  // each consumed slot is refilled with the same strip D groups ahead
+  auto do_group = [&](auto refill, const u32x4_t (&bxg)[T][4], const int gi, const int d) {
+    const bool valid = gi < gpw;
+    const int g = group_of(gi);
     f32x4_t X[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       X[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      float q = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        const bf16x8_t b = bitcast<bf16x8_t>(bx[t][kb]);
-        X[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, b, X[t], 0, 0, 0);
-        if (needs_rho<EPI>()) gram[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, b, gram[t], 0, 0, 0);
+        X[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, bitcast<bf16x8_t>(bxg[t][kb]), X[t], 0, 0, 0);
+        if (needs_rho<EPI>())
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            q = __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf16x2_t>(bxg[t][kb][e]), bitcast<bf16x2_t>(bxg[t][kb][e]), q,
+                                                false);
       }
+      if (needs_rho<EPI>()) sq[t] += valid ? q : 0.f;
     }
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
-      const int ts = min(strip0 + s, nstrips - 1);
-      float sc[4];
+    for (int s = 0; s < SP; ++s) {
+      const int k = d * SP + s;
+      bf16x8_t A[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) A[kb] = dword_to_bf16x8_biased(ring[k][kb]);
+      // refill only after the decode has read the slot, so that the new
+      // atom lands in the same registers (no copies or waits on the loop's
+      // back edge): the empty asm orders the decode before the load
+      asm volatile("" : "+v"(A[0]), "+v"(A[1]), "+v"(A[2]), "+v"(A[3])::"memory");
+      if constexpr (decltype(refill)::value) ring[k] = load16_stream(atom_ptr(gi + D, s));
+      const u32x2_t sv = *reinterpret_cast<const u32x2_t*>(&sc[((size_t)s * GP + g - 8 * b0) * 16 + 4 * j]);
+      float scl[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        sc[i] = f16_bits_to_f32(a.scales[(((size_t)ts * a.G8 + g / 8) * 16 + 4 * j + i) * 8 + (g % 8)]);
+        scl[i] = valid ? f16_bits_to_f32((uint16_t)(sv[i >> 1] >> (16 * (i & 1)))) : 0.f;
 #pragma unroll
       for (int t = 0; t < T; ++t) {
         f32x4_t ag = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
-          ag = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dword_to_bf16x8_biased(w[s][kb]),
-                                                        bitcast<bf16x8_t>(bx[t][kb]), ag, 0, 0, 0);
+          ag = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[kb], bitcast<bf16x8_t>(bxg[t][kb]), ag, 0, 0, 0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[s][t][i] = fmaf(sc[i], ag[i] - 136.0f * X[t][i], acc[s][t][i]);
+        for (int i = 0; i < 4; ++i) acc[s][t][i] = fmaf(scl[i], ag[i] - 136.0f * X[t][i], acc[s][t][i]);
       }
+      // one atom's decoded operands live at a time
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // every read of this group's x is done before the next group's x loads
+    // (into the same registers) are issued
+#pragma unroll
+    for (int s = 0; s < SP; ++s)
+#pragma unroll
+      for (int t = 0; t < T; ++t) asm volatile("" : "+v"(acc[s][t]));
+#pragma unroll
+    for (int t = 0; t < T; ++t) asm volatile("" : "+v"(sq[t])::"memory");
+  };
+  // all but the last D groups refill the ring; the last D consume what is
+  // in flight, so no load is still outstanding when the waves meet
+  const int ngr = (gpw + D - 1) / D * D;
+  int gb = 0;
+  u32x4_t bx[T][4];
+  for (; gb < ngr - D; gb += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      // the next group's x before this group's refills: the wait for x
+      // then leaves the refills (D groups ahead) in flight
+      stage_bx(xs, bx);
+      __builtin_amdgcn_sched_barrier(0);
+      load_xs(xs, gb + d + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      do_group(std::true_type(), bx, gb + d, d);
+      // keep the scheduler from hoisting later groups' loads (register
+      // pressure) across the group boundary
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  if (ngr > 0) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      stage_bx(xs, bx);
+      __builtin_amdgcn_sched_barrier(0);
+      if (d + 1 < D) load_xs(xs, gb + d + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      do_group(std::false_type(), bx, gb + d, d);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
-  // per-wave partials to LDS: lane holds rows 4j+i, column r of each tile
+  // partial tiles: lane holds rows 4j+i of column r of each tile.  Waves
+  // 0-3 store theirs, then waves 4-7 add theirs to the same slots (plain
+  // LDS reads and writes: LDS float atomics are slow); the row stride RS
+  // puts the four row quarters of a store on distinct banks.
+  constexpr int RS = T * 16 + 4;
+  auto slot = [&](int s, int t, int i) { return (((wave & 3) * SP + s) * 16 + 4 * j + i) * RS + t * 16 + r; };
+  lds_barrier();  // every wave is past its last read of sc and xst
+  if (wave < 4) {
 #pragma unroll
-  for (int s = 0; s < S; ++s)
+    for (int s = 0; s < SP; ++s)
 #pragma unroll
-    for (int t = 0; t < T; ++t)
+      for (int t = 0; t < T; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) red[wave][s * 16 + 4 * j + i][t * 16 + r] = acc[s][t][i];
+        for (int i = 0; i < 4; ++i) red[slot(s, t, i)] = acc[s][t][i];
+  }
+  lds_barrier();
+  if (wave >= 4) {
+#pragma unroll
+    for (int s = 0; s < SP; ++s)
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[slot(s, t, i)] += acc[s][t][i];
+  }
   if (needs_rho<EPI>()) {
-    // diagonal of x.x^T: element (r, r) sits in lane j = r/4, register r%4
 #pragma unroll
-    for (int t = 0; t < T; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (4 * j + i == r) sqred[wave][t * 16 + r] = gram[t][i];
+    for (int t = 0; t < T; ++t) {
+      float v = sq[t];
+      v += shfl_xor(v, 16);
+      v += shfl_xor(v, 32);
+      if (j == 0) sqw[wave * T * 16 + t * 16 + r] = v;
+    }
   }
   __syncthreads();
-  for (int idx = tid; idx < S * 16 * M; idx += NW * 64) {
-    const int row = idx / M, m = idx % M;
+  auto red_sum = [&](int row, int m) {
     float v = 0.f;
-    for (int w = 0; w < NW; ++w) v += red[w][row][m];
-    ot[row * M + m] = v;
-  }
-  if (tid < M) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v += red[((q * SP) * 16 + row) * RS + m];
+    return v;
+  };
+  auto sq_sum = [&](int m) {
     float v = 0.f;
-    if (needs_rho<EPI>())
-      for (int w = 0; w < NW; ++w) v += sqred[w][tid];
-    rho_s[tid] = needs_rho<EPI>() ? 1.0f / sqrtf(v / (float)K + a.eps) : 1.0f;
+    for (int w = 0; w < NW; ++w) v += sqw[w * T * 16 + m];
+    return v;
+  };
+  if (KS == 1) {
+    for (int idx = tid; idx < ns * 16 * M; idx += NW * 64) ot[idx] = red_sum(idx / M, idx % M);
+    if (tid < M) rho_s[tid] = needs_rho<EPI>() ? 1.0f / sqrtf(sq_sum(tid) / (float)K + a.eps) : 1.0f;
+  } else {
+    // split K: publish this slice's tile and sums of squares (coherent
+    // stores), count the slice in; the last slice of the set to arrive sums
+    // all KS of them in slice order and runs the epilogue
+    const size_t blk = split_block_floats(SP);
+    float* part = a.split_part + (size_t)blockIdx.x * blk;
+    const int n4 = ns * 16 * M / 4;  // the tile as 16-byte pieces
+    for (int i4 = tid; i4 < n4; i4 += NW * 64) {
+      u32x4_t v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = __float_as_uint(red_sum((4 * i4 + e) / M, (4 * i4 + e) % M));
+      st_coh16(part, (uint32_t)i4 * 16, (uint32_t)blk * 4, v);
+    }
+    if (needs_rho<EPI>() && tid < M) st_coh(&part[SP * 16 * 32 + tid], sq_sum(tid));
+    wait_vmem();
+    __syncthreads();
+    int* flag = reinterpret_cast<int*>(rho_s);
+    if (tid == 0) {
+      const unsigned prev = atomic_add_agent(&a.split_cnt[set], 1u);
+      const bool last = prev == (unsigned)(KS - 1);
+      if (last) __hip_atomic_store(&a.split_cnt[set], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      *flag = last ? 1 : 0;
+    }
+    __syncthreads();
+    if (*flag == 0) return;
+    __syncthreads();  // every thread has read the flag before rho_s is reused
+    // slices summed in order 0 .. KS-1, four loads in flight at a time
+    // (slices past KS read slice KS-1 and add zero)
+    const float* part0 = a.split_part + (size_t)set * KS * blk;
+    const uint32_t set_bytes = (uint32_t)(KS * blk * 4);
+    for (int i4 = tid; i4 < n4; i4 += NW * 64) {
+      f32x4_t v = {0.f, 0.f, 0.f, 0.f};
+      for (int k0 = 0; k0 < KS; k0 += 4) {
+        u32x4_t p[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          p[q] = ld_coh16(part0, (uint32_t)((min(k0 + q, KS - 1) * blk + 4 * i4) * 4), set_bytes);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4_t pv = bitcast<f32x4_t>(p[q]);
+          if (k0 + q < KS) v += pv;
+        }
+      }
+      *reinterpret_cast<f32x4_t*>(&ot[4 * i4]) = v;
+    }
+    if (tid < M) {
+      float v = 0.f;
+      if (needs_rho<EPI>())
+        for (int k = 0; k < KS; ++k) v += ld_coh(&part0[(size_t)k * blk + SP * 16 * 32 + tid]);
+      rho_s[tid] = needs_rho<EPI>() ? 1.0f / sqrtf(v / (float)K + a.eps) : 1.0f;
+    }
   }
   __syncthreads();
-  run_epilogue<EPI>(a, strip0, S, ot, rho_s);
+  run_epilogue<EPI>(a, strip0, ns, ot, rho_s);
 }
 
 // ---------------------------------------------------------------------------
 // launcher
 // ---------------------------------------------------------------------------
+
+// M = 2..32 launch shape.  Each workgroup (8 waves) takes SP strips and
+// one of KS slices of K.  More strips per workgroup means fewer re-reads of
+// x; more slices means more workgroups (and partial tiles to reduce).  The
+// plan takes the (SP, KS) that keeps the most CUs busy over the rounds of
+// workgroups (ties to more strips), with KS > 1 only when `split_bytes` of
+// split buffer are at hand and each wave gets at least one group.  D groups
+// of atoms are in flight per wave (about 8 atoms; `deep` allows D = 8 at
+// one strip, for the epilogues without RMSNorm).
+static SkinnyPlan skinny_plan(int nstrips, int G, int T, bool deep, size_t split_bytes) {
+  SkinnyPlan best{};
+  double best_score = -1.0;
+  for (int SP : {7, 5, 4, 3, 2, 1}) {
+    const int nsets = (nstrips + SP - 1) / SP;
+    int KS = 1;
+    if (split_bytes) {
+      KS = std::max(1, std::min(256 / nsets, G / kSkinnyWaves));
+      while (KS > 1 && (size_t)nsets * KS * split_block_floats(SP) * sizeof(float) > split_bytes) --KS;
+    }
+    const int gs_max = (G + KS - 1) / KS;
+    const int nb8 = std::min((G + 7) / 8, (gs_max + 7) / 8 + 1);
+    if (SP * nb8 * 16 > kScaleLoads * kSkinnyWaves * 64 || skinny_lds_bytes(nb8, SP, T) > (size_t)kMaxLdsBytes)
+      continue;
+    const int W = nsets * KS, rounds = (W + 255) / 256;
+    const double score = (double)W / (256.0 * rounds);
+    if (score > best_score + 1e-9) {
+      best_score = score;
+      best.SP = SP;
+      best.KS = KS;
+      best.NB8 = nb8;
+      best.GPW = (gs_max + kSkinnyWaves - 1) / kSkinnyWaves;
+    }
+  }
+  if (best.SP >= 4)
+    best.D = 2;
+  else if (best.SP >= 2)
+    best.D = T == 1 ? 4 : 2;
+  else
+    best.D = (deep && best.GPW > 4) ? 8 : 4;
+  return best;
+}
 
 // M = 1 launch shape.  16 waves per workgroup when that leaves at most 4
 // groups per wave (x kept in registers), else as few groups per wave as
@@ -184,6 +460,17 @@ static void launch_gemv(const ProjArgs& a, const GemvPlan& p, size_t lds, int gr
     hipLaunchKernelGGL((proj_gemv_kernel<EPI, NW, 8, 0>), dim3(grid), dim3(NW * 64), lds, st, a, p);
 }
 
+// split buffer bytes usable by a projection (0: no split of K)
+// Splitting K trades x re-reads for a reduction tail (publish, count,
+// sum, then the epilogue) of several microseconds; it pays only when each
+// unsplit workgroup would read more than kSplitMinXBytes of x.
+constexpr size_t kSplitMinXBytes = 512 * 1024;
+
+static size_t split_bytes_of(const ProjArgs& a) {
+  if (!a.split_part || !a.split_cnt || (size_t)a.M * a.K * 2 <= kSplitMinXBytes) return 0;
+  return a.split_bytes;
+}
+
 template <int EPI>
 static hipError_t launch_epi(const ProjArgs& a, hipStream_t st) {
   const int nstrips = a.Np / kStrip;
@@ -197,14 +484,22 @@ static hipError_t launch_epi(const ProjArgs& a, hipStream_t st) {
       launch_gemv<EPI, 8>(a, p, lds, grid, st);
     else
       launch_gemv<EPI, 4>(a, p, lds, grid, st);
-  } else if (a.M <= 16) {
-    constexpr int S = 2, NW = 4;
-    const int grid = (nstrips + S - 1) / S;
-    hipLaunchKernelGGL((proj_mfma_kernel<EPI, S, NW, 1>), dim3(grid), dim3(NW * 64), 0, st, a);
   } else {
-    constexpr int S = 2, NW = 4;
-    const int grid = (nstrips + S - 1) / S;
-    hipLaunchKernelGGL((proj_mfma_kernel<EPI, S, NW, 2>), dim3(grid), dim3(NW * 64), 0, st, a);
+    const int T = a.M <= 16 ? 1 : 2;
+    const SkinnyPlan p = skinny_plan(nstrips, a.G, T, !needs_rho<EPI>(), split_bytes_of(a));
+    const size_t lds = skinny_lds_bytes(p.NB8, p.SP, T);
+    const int grid = (nstrips + p.SP - 1) / p.SP * p.KS;
+#define I4D_SKINNY(SPV, TV, DV)                   \
+  if (p.SP == SPV && T == TV && p.D == DV)       \
+    hipLaunchKernelGGL((proj_skinny_kernel<EPI, SPV, TV, DV>), dim3(grid), dim3(kSkinnyWaves * 64), lds, st, a, p);
+    I4D_SKINNY(1, 1, 4) I4D_SKINNY(2, 1, 4) I4D_SKINNY(3, 1, 4) I4D_SKINNY(4, 1, 2) I4D_SKINNY(5, 1, 2)
+    I4D_SKINNY(7, 1, 2)
+    I4D_SKINNY(1, 2, 4) I4D_SKINNY(2, 2, 2) I4D_SKINNY(3, 2, 2) I4D_SKINNY(4, 2, 2) I4D_SKINNY(5, 2, 2)
+    I4D_SKINNY(7, 2, 2)
+    if constexpr (!needs_rho<EPI>()) {
+      I4D_SKINNY(1, 1, 8) I4D_SKINNY(1, 2, 8)
+    }
+#undef I4D_SKINNY
   }
   return hipGetLastError();
 }
@@ -215,6 +510,9 @@ i4d_status launch_projection(int epi, const ProjArgs& a, hipStream_t st) {
     const size_t lds = gemv_lds_bytes(a.K, p);
     if (lds > (size_t)kMaxLdsBytes || a.K > 4 * 8 * p.NW * 64)
       return fail(I4D_ERR_UNSUPPORTED, "K=%d too large for the M=1 kernel (LDS %zu bytes)", a.K, lds);
+  } else {
+    const SkinnyPlan p = skinny_plan(a.Np / kStrip, a.G, a.M <= 16 ? 1 : 2, true, split_bytes_of(a));
+    if (p.SP == 0) return fail(I4D_ERR_UNSUPPORTED, "K=%d too large for the M>1 kernel", a.K);
   }
   hipError_t e;
   switch (epi) {
@@ -226,6 +524,20 @@ i4d_status launch_projection(int epi, const ProjArgs& a, hipStream_t st) {
   }
   if (e != hipSuccess) return fail(I4D_ERR_HIP, "projection launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+SplitNeed projection_split_need(int Np, int K, int M) {
+  SplitNeed n{0, 0};
+  if (M <= 1) return n;
+  const int nstrips = Np / kStrip, G = K / kGroup;
+  if ((size_t)M * K * 2 <= kSplitMinXBytes) return n;
+  const SkinnyPlan p = skinny_plan(nstrips, G, M <= 16 ? 1 : 2, true, (size_t)-1);
+  if (p.KS > 1) {
+    const size_t nsets = (size_t)(nstrips + p.SP - 1) / p.SP;
+    n.part_bytes = nsets * p.KS * split_block_floats(p.SP) * sizeof(float);
+    n.counters = nsets;
+  }
+  return n;
 }
 
 }  // namespace i4d

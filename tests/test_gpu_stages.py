@@ -297,8 +297,9 @@ def test_block_small(gpu, shape, lengths):
 
 
 def test_block_dirty_workspace_forced_splits(gpu):
-    """A workspace holding garbage and a forced split count: nothing in the
-    workspace is read before the step writes it."""
+    """A workspace holding garbage (except its arrival counters) and a
+    forced split count: nothing in the workspace is read before the step
+    writes it."""
     torch, B, D = gpu
     shape, seed, lengths = synth.SHAPE_SMALL128, 13, np.array([700, 1200, 45], np.int32)
     M, maxL = len(lengths), int(lengths.max())
@@ -310,6 +311,11 @@ def test_block_dirty_workspace_forced_splits(gpu):
     cache.prefill(pre)
     ws = D.Workspace(shape, M, maxL, 6)
     ws.buf.fill_(0xA5)
+    # the arrival counters must be zero before first use (the library
+    # leaves them at zero); everything else may hold garbage
+    lay = ws.layout
+    ws.buf[lay.split_cnt:lay.split_part].zero_()
+    ws.buf[lay.sync:lay.total].zero_()
     x_in = D.to_device_u16(xb)
     x_out = torch.empty_like(x_in)
     ctx = torch.from_numpy(lengths).cuda()
@@ -344,6 +350,31 @@ def test_block_m1_one_launch(gpu, shape, L):
     torch.cuda.synchronize()
     assert res["cache"].errors() == 0
     assert torch.equal(first, res["x_out"])
+
+
+# d_ffn 16384: at M >= 17 each unsplit down workgroup would read more than
+# 512 KiB of the activation, so the down projection splits K across
+# workgroups through the workspace (partial tiles + arrival counters)
+SPLIT_SHAPE = synth.LayerShape(1024, 8, 2, 128, 16384)
+
+
+@pytest.mark.parametrize("M", [17, 32])
+def test_block_split_k(gpu, M):
+    """Split-K projections inside the block step match the oracle, and a
+    second step on the same workspace (counters left at zero by the first)
+    gives identical outputs."""
+    torch, B, D = gpu
+    lengths = list(np.random.default_rng(M).integers(1, 600, M))
+    res = run_block(gpu, SPLIT_SHAPE, 31 + M, lengths)
+    check_block(res, f"split-K M={M}")
+    first = res["x_out"].clone()
+    B.i4d_decode_block_step(res["layer"].struct, res["cache"].struct, res["x_in"], res["x_out"], res["ctx"], M,
+                            int(res["lengths"].max()), 0, res["ws"].buf, res["ws"].nbytes, None)
+    torch.cuda.synchronize()
+    assert res["cache"].errors() == 0
+    assert torch.equal(first, res["x_out"])
+    cnt = res["ws"].buf[res["ws"].layout.split_cnt:res["ws"].layout.split_part]
+    assert res["ws"].layout.split_part > res["ws"].layout.split_cnt and int(cnt.count_nonzero()) == 0
 
 
 def test_block_deterministic(gpu):
