@@ -30,6 +30,35 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 
+# HBM traffic of the dominant kernel per launch, from two rocprofv3 --pmc
+# runs (FETCH_SIZE, then WRITE_SIZE) scaled by the same counters on a plain
+# copy of known size; valid only for the kernel sources it was taken on
+# (sha256 over the csrc files), else the roofline entry reports null.
+TRAFFIC = {
+    "8b_m1_ctx4096": {"kernel": "step_m1_kernel (one-launch decode step)",
+                      "csrc_sha256": "d5f65a7cf173399ed813ea7de082291e00ecb8b41d8df04b8279741c1acdc004",
+                      "fetch_bytes": 119558349, "write_bytes": 751104},
+}
+
+
+def csrc_sha256():
+    import hashlib
+    d = os.path.join(ROOT, "int4_quantized_decode_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            h.update(name.encode())
+            with open(os.path.join(d, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_of(workload, kernel):
+    t = TRAFFIC.get(workload)
+    if not t or t["kernel"] != kernel or t["csrc_sha256"] != csrc_sha256():
+        return None
+    return t["fetch_bytes"] + t["write_bytes"]
+
 
 def algorithmic_bytes(shape, lengths):
     """INT4 codes (0.5 B/weight) + fp16 group scales + INT4 KV codes and
@@ -57,6 +86,9 @@ def main():
     ap.add_argument("--splits", type=int, default=-1)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-steps", type=int, default=3)
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB (the reference "
+                         "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -72,6 +104,15 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.copy_mib:
+        n = args.copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "launches": 3}), flush=True)
+        return
     B.lib()
     wl = synth.WORKLOADS[args.workload]
     shape = wl.shape
@@ -182,7 +223,8 @@ def main():
         "bytes_per_step": {"total": total_b, "weights": w_b, "kv": kv_b},
         "roofline": {"kernel": rf_kernel, "bound": "hbm",
                      "achieved": round(rf_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(rf_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(rf_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic_of(args.workload if not args.M else f"{args.workload}@M{M}", rf_kernel),
                      "avg_launch_us": round(rf_us, 3), "bytes_per_launch": rf_bytes},
         "setup_s": round(setup_s, 1),
     }

@@ -237,8 +237,10 @@ i4d_status i4d_attention_workspace_bytes(const i4d_layer_shape* shape, int M, in
  * ctx_len[m] cached tokens of kv head h / (n_q/n_kv) ("premises and
  * limits": the 8-head cache is read without expansion).  The query is
  * rotated (q~ = H q, fp32); scores s_t = scale_k[t] * (q~ . codes_k[t]) /
- * (head_dim * sqrt(head_dim)); softmax in fp32; each split of the token
- * range writes (max, sum, unnormalised output) and a combine step merges
+ * (head_dim * sqrt(head_dim)); softmax in fp32; the token range
+ * [0, max_ctx_len) is cut into num_splits equal spans of whole 32-token
+ * blocks, each split writes (max, sum, unnormalised output) of its part
+ * of [0, ctx_len[m]) (empty: max -inf, sum 0) and a combine step merges
  * the splits and applies the inverse rotation o = H o~ / head_dim
  * ("how it differs": split-KV reduction; same rotation on the attention
  * output).  max_ctx_len (host) bounds ctx_len and sizes the launch;
@@ -304,7 +306,7 @@ i4d_status i4d_workspace_layout_of(const i4d_layer_shape* shape, int M, int max_
  * (position ctx_len[m]-1) is appended by this call.  Runs stages 1-7:
  * QKV (+rho1, RoPE) -> kv_append of bf16 k, v at ctx_len-1 -> attention ->
  * O + residual -> gate/up + SwiGLU (+rho2) -> down + residual.
- * For M = 1 the stages run in one persistent launch with one 16-wave
+ * For M = 1 the stages run in one persistent launch with one 8-wave
  * workgroup per CU (each stage's weight loads start before the previous
  * stage completes); it needs the GPU to itself for the duration of the
  * call (its workgroups wait on each other; a wait that times out sets

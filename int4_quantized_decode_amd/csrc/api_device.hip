@@ -118,7 +118,7 @@ i4d_status do_qkv(const i4d_layer* L, const uint16_t* x, const int32_t* ctx_len,
 }
 
 AttnArgs attention_args(const i4d_kv_cache* c, const i4d_layer_shape& s, const float* q,
-                        const int32_t* ctx_len, int M, int S, void* ws, float* attn_f32,
+                        const int32_t* ctx_len, int M, int max_ctx_len, int S, void* ws, float* attn_f32,
                         uint16_t* attn_bf16, const uint16_t* k_new, const uint16_t* v_new) {
   AttnArgs a;
   a.kv = kv_args(c);
@@ -130,6 +130,7 @@ AttnArgs attention_args(const i4d_kv_cache* c, const i4d_layer_shape& s, const f
   a.n_q = s.n_q_heads;
   a.G = s.n_q_heads / s.n_kv_heads;
   a.S = S;
+  a.bps = std::max(1, ((max_ctx_len + kVBlock - 1) / kVBlock + S - 1) / S);
   a.score_scale = (float)(1.4426950408889634 / ((double)s.head_dim * sqrt((double)s.head_dim)));
   AttnWs w = attn_ws_layout(&s, M, a.S);
   a.part_ml = (float*)((char*)ws + w.ml);
@@ -144,7 +145,7 @@ i4d_status do_attention(const i4d_kv_cache* c, const i4d_layer_shape& s, const f
                         float* attn_f32, uint16_t* attn_bf16, const uint16_t* k_new,
                         const uint16_t* v_new, bool combine, hipStream_t st) {
   const AttnPlan plan = attn_plan(&s, M, max_ctx_len, num_splits);
-  const AttnArgs a = attention_args(c, s, q, ctx_len, M, plan.S, ws, attn_f32, attn_bf16, k_new, v_new);
+  const AttnArgs a = attention_args(c, s, q, ctx_len, M, max_ctx_len, plan.S, ws, attn_f32, attn_bf16, k_new, v_new);
   return launch_attention(a, plan.nwa, combine, st);
 }
 
@@ -320,7 +321,7 @@ i4d_status i4d_decode_block_step(const i4d_layer* layer, const i4d_kv_cache* cac
     in.o = o_args(layer, attn, x_in, 1, h, hb);
     in.gu = gu_args(layer, hb, 1, act);
     in.down = down_args(layer, act, h, 1, x_out);
-    in.attn = attention_args(cache, s, q, ctx_len, 1, step_m1_splits(&s, max_ctx_len, num_splits),
+    in.attn = attention_args(cache, s, q, ctx_len, 1, max_ctx_len, step_m1_splits(&s, max_ctx_len, num_splits),
                              ws + wl.attn_ws, attn_f32, attn, k, v);
     in.sync = (unsigned*)(ws + wl.sync);
     return launch_step_m1(in, st);

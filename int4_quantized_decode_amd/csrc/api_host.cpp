@@ -53,20 +53,23 @@ i4d_status check_shape(const i4d_layer_shape* s) {
 }
 
 AttnPlan attn_plan(const i4d_layer_shape* s, int M, int max_ctx_len, int num_splits) {
-  // One workgroup per (row, kv head, split).  Automatic split count: about
-  // 64 workgroups when few (row, kv head) pairs are active, no split once
-  // there are 64 pairs or more, at least 4 blocks of 32 tokens per split.
-  // Then as many waves per workgroup (4, 8, 16) as keep every wave at one
-  // block or more while the launch has fewer than 4096 waves.
+  // One workgroup per (row, kv head, split); every split spans the same
+  // number of blocks (sized by max_ctx_len), so a short row leaves splits
+  // empty.  Automatic split count: about one workgroup per CU (256) over
+  // all (row, kv head) pairs, at least 4 blocks of 32 tokens per split
+  // (more, shorter splits measured slower: per-split setup, the merge and
+  // the combine launch outweigh the better balance of ragged rows).  Then
+  // as many waves per workgroup (4, 8, 16) as keep every wave at one block
+  // or more while the launch has fewer than 4096 waves.
   const long nblk = (max_ctx_len + kVBlock - 1) / kVBlock;
   const long units = (long)M * s->n_kv_heads;
   long S;
   if (num_splits > 0) {
     S = std::min(num_splits, I4D_MAX_SPLITS);
   } else {
-    S = (64 + units - 1) / units;
+    S = (256 + units - 1) / units;
     S = std::min<long>(S, std::max<long>(1, nblk / 4));
-    S = std::max<long>(S, 1);
+    S = std::max<long>(std::min<long>(S, I4D_MAX_SPLITS), 1);
   }
   const long bps = (nblk + S - 1) / S;
   int nwa = 4;

@@ -34,6 +34,7 @@ struct AttnArgs {
   const uint16_t* k_new;   // optional bf16 [M][n_kv][hd]: appended at ctx_len-1 first
   const uint16_t* v_new;
   int M, n_q, G, S;
+  int bps;                 // 32-token blocks per split: split s = blocks [s bps, (s+1) bps)
   float score_scale;       // log2(e) / (hd * sqrt(hd))
   float* part_ml;          // [M][n_q][S][2]
   float* part_o;           // [M][n_q][S][hd]

@@ -29,6 +29,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <type_traits>
+
 #include "attn.h"
 #include "coherent.h"
 #include "device_common.h"
@@ -273,7 +275,7 @@ __device__ __forceinline__ void fwht_wave(float& x0, float& x1, int lane) {
 // COH: the query, the new key/value and the partials are exchanged with
 // other workgroups of the same launch (agent-coherent loads and stores).
 template <int HD, int NWA, bool COH, typename Wait>
-__device__ void attn_body(const AttnArgs& a, const int m, const int j, const int s, float* lds,
+__device__ __forceinline__ void attn_body(const AttnArgs& a, const int m, const int j, const int s, float* lds,
                           Wait&& wait_input) {
   constexpr int KB = HD / 32;  // 32-channel MFMA steps for q.k
   constexpr int CB = HD / 16;  // 16-channel output blocks
@@ -290,14 +292,16 @@ __device__ void attn_body(const AttnArgs& a, const int m, const int j, const int
 
   const int64_t base = kv.row_base[m];
   const int64_t cap = kv.row_base[m + 1] - base;
+  // the splits partition [0, S bps) blocks (sized for the longest row): a
+  // shorter row leaves its last splits empty
+  const int bps = a.bps;
   int L = a.ctx_len[m];
-  const bool len_ok = L >= 1 && L <= cap;
+  const bool len_ok = L >= 1 && L <= cap && L <= S * bps * kVBlock;
   if (!len_ok) {
     if (tid == 0 && kv.err_word) atomicOr(kv.err_word, I4D_DEVERR_CTX_LEN);
-    L = (int)max((int64_t)0, min((int64_t)max(L, 1), cap));
+    L = (int)max((int64_t)0, min((int64_t)max(L, 1), min(cap, (int64_t)S * bps * kVBlock)));
   }
   const int nblk = (L + kVBlock - 1) / kVBlock;
-  const int bps = (nblk + S - 1) / S;
   const int b0 = s * bps;
   const int b1 = min(nblk, b0 + bps);
   const int64_t region = base * kv.n_kv + (int64_t)j * cap;
@@ -383,8 +387,12 @@ __device__ void attn_body(const AttnArgs& a, const int m, const int j, const int
 
   // One block in registers; the next block's keys are requested once the
   // current keys are consumed, its values once the current values are.  The
-  // last block of the wave runs the same body without those requests.
-  auto body = [&](const int nb, const bool prefetch) {
+  // last block of the wave runs the same body without those requests and
+  // with the token mask (only the row's last block can be partial, and it
+  // is the last block of its wave; its slots past L may hold anything).
+  // Columns c >= G carry finite values that no output uses.
+  auto body = [&](const int nb, auto last_tag) {
+    constexpr bool LAST = decltype(last_tag)::value;
     const int t0 = blk * kVBlock;
     float sc[8];
     float mx = -INFINITY;
@@ -400,32 +408,35 @@ __device__ void attn_body(const AttnArgs& a, const int m, const int j, const int
         // high part (column c) + low part (column c + 8, rotated in by DPP)
         const float part = fmaf(acc[i], kTwo24, -cq);
         const float full = part + dpp_row_ror8(part);
-        const int tok = t0 + 16 * tile + 4 * jj + i;
-        const float v = full * f16_half(cur.ks[tile], i) * sscale;
-        sc[tile * 4 + i] = (tok < L) ? v : -INFINITY;
-        mx = fmaxf(mx, sc[tile * 4 + i]);
+        float v = full * (f16_half(cur.ks[tile], i) * sscale);
+        if (LAST) v = (t0 + 16 * tile + 4 * jj + i < L) ? v : -INFINITY;
+        sc[tile * 4 + i] = v;
       }
     }
-    if (prefetch) load_keys<HD>(cur, kbase, ksc, nb, c, jj);
+    if (!LAST) load_keys<HD>(cur, kbase, ksc, nb, c, jj);
+    mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
     mx = fmaxf(mx, shfl_xor(mx, 16));
     mx = fmaxf(mx, shfl_xor(mx, 32));
     const float m_new = fmaxf(m_run, mx);  // finite: the block holds a valid token
-    const float alpha = exp2f(m_run - m_new);
-    l_run *= alpha;
-    psum *= alpha;
+    // rescale only when some column's running maximum moved (alpha = 1
+    // exactly elsewhere)
+    if (__any(m_new > m_run)) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+      psum *= alpha;
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) o[cb] *= alpha;
+      for (int cb = 0; cb < CB; ++cb) o[cb] *= alpha;
+    }
     // P operand: element e is token 4jj+e (e < 4) or 16+4jj+e-4 (e >= 4),
     // i.e. score register e; value scale folded in, 1/16 at e in {2,3,6,7}
     f16x8_t pb;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int tile = e >> 2, i = e & 3;
-      const float p = exp2f(sc[e] - m_new);  // 0 for masked tokens
+      const float p = __builtin_amdgcn_exp2f(sc[e] - m_new);  // 0 for masked tokens
       l_run += p;
-      float pv = p * f16_half(cur.vs[tile], i);
-      pv = (c < G && p > 0.f) ? pv : 0.f;
-      if (slot16(e)) pv *= 0.0625f;
+      float pv = p * (f16_half(cur.vs[tile], i) * (slot16(e) ? 0.0625f : 1.0f));
+      if (LAST) pv = (p > 0.f) ? pv : 0.f;
       const _Float16 ph = (_Float16)pv;
       pb[e] = ph;
       psum = fmaf((float)ph, slot16(e) ? 16.f : 1.f, psum);
@@ -433,12 +444,12 @@ __device__ void attn_body(const AttnArgs& a, const int m, const int j, const int
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
       o[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dword_to_f16x8_sub(cur.vw[cb]), pb, o[cb], 0, 0, 0);
-    if (prefetch) load_values<HD>(cur, vbase, vsc, nb, c, jj);
+    if (!LAST) load_values<HD>(cur, vbase, vsc, nb, c, jj);
     m_run = m_new;
   };
   if (blk < b1) {
-    for (; blk + NWA < b1; blk += NWA) body(blk + NWA, true);
-    body(blk, false);
+    for (; blk + NWA < b1; blk += NWA) body(blk + NWA, std::false_type());
+    body(blk, std::true_type());
   }
 
   // per-column totals over the 4 lane quarters; undo the 2^-24 operand

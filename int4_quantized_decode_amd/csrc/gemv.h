@@ -145,15 +145,17 @@ __device__ __forceinline__ f16x2_t code_pair_sub(uint32_t w, uint32_t t, int q) 
 // dot of one atom row quarter (4 code dwords) with its 32 x values (fp16
 // pairs in k order), times 2^-24
 __device__ __forceinline__ float atom_dot(const u32x4_t w, const u32x4_t (&xk)[4]) {
-  float acc = 0.f;
+  // two accumulation chains (code dwords 0-1 and 2-3) halve the dependent
+  // chain of dot instructions
+  float acc[2] = {0.f, 0.f};
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
     const uint32_t dw = w[kb], t = dw >> 8;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      acc = __builtin_amdgcn_fdot2(code_pair_sub(dw, t, q), bitcast<f16x2_t>(xk[kb][q]), acc, false);
+      acc[kb >> 1] = __builtin_amdgcn_fdot2(code_pair_sub(dw, t, q), bitcast<f16x2_t>(xk[kb][q]), acc[kb >> 1], false);
   }
-  return acc;
+  return acc[0] + acc[1];
 }
 
 // sum of the x values that 16 fp16 words of one group quarter represent
@@ -185,8 +187,9 @@ __device__ __forceinline__ float quarter_sum(const u32x4_t (&xk)[4]) {
 //
 // The body serves the stand-alone kernel and the one-launch decode step
 // (COH = true): there the weight ring is issued first, then `wait_input`
-// blocks until the producers of x are done, then x is read agent-coherently
-// and the outputs are stored the same way.  `strip0`, `ns`: the strips of
+// blocks until the producers of x are done (the last wave polls, from lane
+// 0, and issues its own ring after the wait), then x is read
+// agent-coherently and the outputs are stored the same way.  `strip0`, `ns`: the strips of
 // this workgroup (ns <= pl.SP).
 template <int EPI, int NW, int U, int GPW, bool COH, typename Wait>
 __device__ __forceinline__ void gemv_body(const ProjArgs& a, const GemvPlan& pl, const int strip0,
@@ -283,10 +286,19 @@ __device__ __forceinline__ void gemv_body(const ProjArgs& a, const GemvPlan& pl,
       }
     }
   };
+  // In the one-launch step the last wave waits for the producers (its
+  // polls must not queue behind atom loads of its own: a wave's loads
+  // complete in order), so it issues its first atoms after the wait.
+  if (X_FIRST || wave != NW - 1) {
 #pragma unroll
-  for (int k = 0; k < U; ++k) fill(k);
+    for (int k = 0; k < U; ++k) fill(k);
+  }
   if (!X_FIRST) {
     wait_input();
+    if (wave == NW - 1) {
+#pragma unroll
+      for (int k = 0; k < U; ++k) fill(k);
+    }
     load_x();
   }
 

@@ -181,7 +181,8 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_m1_kernel(StepArgs sa) {
     int s0, ns;
     strip_range(pa.Np / kStrip, wg, nwg, s0, ns);
     auto wait_attn = [&] {
-      if (tid == 0 && !spin_geq(&sync[kSyncAttnDone], (unsigned)n_kv, &sync[kSyncErr], 1u)) flag_error(sync, err_word);
+      if (tid == (NW - 1) * 64 && !spin_geq(&sync[kSyncAttnDone], (unsigned)n_kv, &sync[kSyncErr], 1u))
+        flag_error(sync, err_word);
       lds_barrier();
     };
     __syncthreads();
@@ -200,7 +201,7 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_m1_kernel(StepArgs sa) {
     int s0, ns;
     strip_range(pa.Np / kStrip, wg, nwg, s0, ns);
     auto wait_o = [&] {
-      if (tid == 0 && !bar_wait(&sync[kSyncBar1], nwg, &sync[kSyncErr])) flag_error(sync, err_word);
+      if (tid == (NW - 1) * 64 && !bar_wait(&sync[kSyncBar1], nwg, &sync[kSyncErr])) flag_error(sync, err_word);
       lds_barrier();
     };
     __syncthreads();
@@ -219,7 +220,7 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_m1_kernel(StepArgs sa) {
     int s0, ns;
     strip_range(pa.Np / kStrip, wg, nwg, s0, ns);
     auto wait_gu = [&] {
-      if (tid == 0 && !bar_wait(&sync[kSyncBar2], nwg, &sync[kSyncErr])) flag_error(sync, err_word);
+      if (tid == (NW - 1) * 64 && !bar_wait(&sync[kSyncBar2], nwg, &sync[kSyncErr])) flag_error(sync, err_word);
       lds_barrier();
     };
     __syncthreads();
