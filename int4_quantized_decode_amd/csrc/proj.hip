@@ -62,6 +62,7 @@ __global__ __launch_bounds__(NW * 64) void proj_gemv_kernel(ProjArgs a, GemvPlan
 // fixed order.
 
 constexpr int kSkinnyWaves = 8;
+constexpr int kSkinnyMaxWorkgroups = 256;
 constexpr int kScaleLoads = 4;  // scale loads per thread: SP * ceil(G/8) <= 128
 
 struct SkinnyPlan {
@@ -90,7 +91,7 @@ inline size_t skinny_lds_bytes(int NB8, int SP, int T) {
          std::max(loop, reduce);
 }
 
-template <int EPI, int SP, int T, int D>
+template <int EPI, int SP, int T, int D, bool P>
 __global__ __launch_bounds__(kSkinnyWaves * 64) void proj_skinny_kernel(ProjArgs a, SkinnyPlan pl) {
   constexpr int NW = kSkinnyWaves;
   constexpr int U = D * SP;  // D groups of atoms in flight
@@ -107,37 +108,63 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void proj_skinny_kernel(ProjArgs
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, j = lane >> 4;
   const int nstrips = a.Np / kStrip;
-  // workgroup = (strip set, K slice); the slice is groups [gs0, gs1)
   const int KS = pl.KS;
-  const int set = blockIdx.x / KS, ks = blockIdx.x - set * KS;
-  const int strip0 = set * SP;
-  const int ns = min(SP, nstrips - strip0);
-  const int gs0 = ks * G / KS, Gs = (ks + 1) * G / KS - gs0;
-  // wave w takes groups w, w + NW, w + 2 NW, ... of the slice (the waves
+  const int ntiles = (nstrips + SP - 1) / SP * KS;
+  // A tile is (strip set, K slice); the slice is groups [gs0, gs0 + Gs).
+  // Wave w takes groups w, w + NW, w + 2 NW, ... of the slice (the waves
   // of a workgroup read neighbouring atoms of a strip at the same time);
   // groups past the wave's share (padding to a multiple of D) re-read its
-  // last group and are weighted by zero
-  const int gpw = max(0, (Gs - wave + NW - 1) / NW);
-  auto group_of = [&](int gi) { return gs0 + min(wave + NW * min(gi, max(gpw - 1, 0)), Gs - 1); };
+  // last group and are weighted by zero.  P: persistent workgroups take
+  // tiles blockIdx.x, + gridDim.x, ...; the last D groups of a tile refill
+  // the ring with the next tile's first atoms.
+  struct Tile {
+    int set, ks, strip0, ns, gs0, Gs, gpw, b0, nb8;
+  };
+  auto tile_of = [&](int t) {
+    Tile g;
+    g.set = t / KS;
+    g.ks = t - g.set * KS;
+    g.strip0 = g.set * SP;
+    g.ns = min(SP, nstrips - g.strip0);
+    g.gs0 = g.ks * G / KS;
+    g.Gs = (g.ks + 1) * G / KS - g.gs0;
+    g.gpw = max(0, (g.Gs - wave + NW - 1) / NW);
+    g.b0 = g.gs0 / 8;
+    g.nb8 = (g.gs0 + g.Gs + 7) / 8 - g.b0;
+    return g;
+  };
+  int tile = blockIdx.x;
+  Tile cur = tile_of(tile);
+  auto group_of_t = [&](const Tile& g, int gi) {
+    return g.gs0 + min(wave + NW * min(gi, max(g.gpw - 1, 0)), g.Gs - 1);
+  };
+  auto group_of = [&](int gi) { return group_of_t(cur, gi); };
 
   // ring of atoms: slot d * SP + s holds strip s of a group gi with
   // gi % D == d
-  auto atom_ptr = [&](int gi, int s) -> const uint8_t* {
-    const int t = min(strip0 + min(s, ns - 1), nstrips - 1);
-    return a.codes + ((size_t)t * G + group_of(gi)) * kAtomBytes + (size_t)lane * 16;
+  auto atom_ptr_t = [&](const Tile& g, int gi, int s) -> const uint8_t* {
+    const int t = min(g.strip0 + min(s, g.ns - 1), nstrips - 1);
+    return a.codes + ((size_t)t * G + group_of_t(g, gi)) * kAtomBytes + (size_t)lane * 16;
   };
-  // scales of the workgroup's strips and slice (8-group blocks b0 ..
-  // b0 + nb8 - 1), requested first (they are needed first); at most
-  // kScaleLoads 16-byte loads per thread
-  const int b0 = gs0 / 8, nb8 = (gs0 + Gs + 7) / 8 - b0;
-  const int nsc = ns * nb8 * 16;
+  auto atom_ptr = [&](int gi, int s) { return atom_ptr_t(cur, gi, s); };
+  // scales of the tile's strips and slice (8-group blocks b0 .. b0 + nb8 -
+  // 1), requested first (they are needed first); at most kScaleLoads
+  // 16-byte loads per thread
+  auto scale_item = [&](const Tile& g, int q, int& s, int& rest) {
+    const int idx = min(tid + q * NW * 64, g.ns * g.nb8 * 16 - 1);
+    s = idx / (g.nb8 * 16);
+    rest = idx % (g.nb8 * 16);
+  };
   u32x4_t scv[kScaleLoads];
+  auto load_scales = [&](const Tile& g) {
 #pragma unroll
-  for (int q = 0; q < kScaleLoads; ++q) {
-    const int idx = min(tid + q * NW * 64, nsc - 1);
-    const int s = idx / (nb8 * 16), rest = idx % (nb8 * 16);
-    scv[q] = load16(a.scales + (((size_t)(strip0 + s) * a.G8 + b0 + rest / 16) * 16 + rest % 16) * 8);
-  }
+    for (int q = 0; q < kScaleLoads; ++q) {
+      int s, rest;
+      scale_item(g, q, s, rest);
+      scv[q] = load16(a.scales + (((size_t)(g.strip0 + s) * a.G8 + g.b0 + rest / 16) * 16 + rest % 16) * 8);
+    }
+  };
+  load_scales(cur);
 
   u32x4_t ring[U];
 #pragma unroll
@@ -150,14 +177,15 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void proj_skinny_kernel(ProjArgs
   // Global reads of x are row-contiguous (load q of a wave covers rows
   // 4q .. 4q+3, 256 bytes each: whole cache lines); the wave transposes
   // them through its own LDS rows into the operand layout.
-  auto load_xs = [&](u32x4_t (&xs)[4 * T], int gi) {
-    const int g = group_of(gi);
+  auto load_xs_t = [&](const Tile& tg, u32x4_t (&xs)[4 * T], int gi) {
+    const int g = group_of_t(tg, gi);
 #pragma unroll
     for (int q = 0; q < 4 * T; ++q) {
       const int m = min(4 * q + j, M - 1);
       xs[q] = load16(a.x + (size_t)m * K + 128 * g + 8 * r);
     }
   };
+  auto load_xs = [&](u32x4_t (&xs)[4 * T], int gi) { load_xs_t(cur, xs, gi); };
   unsigned char* xw = xst + (size_t)wave * (16 * T) * kXRow;
   auto stage_bx = [&](const u32x4_t (&xs)[4 * T], u32x4_t (&bx)[T][4]) {
 #pragma unroll
@@ -171,14 +199,18 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void proj_skinny_kernel(ProjArgs
   u32x4_t xs[4 * T];
   load_xs(xs, 0);
 
+  const int GP = pl.NB8 * 8;
+  constexpr int RS = T * 16 + 4;
+  for (;;) {
+  const int set = cur.set, strip0 = cur.strip0, ns = cur.ns, gpw = cur.gpw, b0 = cur.b0;
   // scales to LDS, transposed to [s][g][row] (threads past the end repeat
   // the last item's identical writes); the barrier does not wait for the
   // atoms and x still in flight
-  const int GP = pl.NB8 * 8;
 #pragma unroll
   for (int q = 0; q < kScaleLoads; ++q) {
-    const int idx = min(tid + q * NW * 64, nsc - 1);
-    const int s = idx / (nb8 * 16), rest = idx % (nb8 * 16), g8 = rest / 16, row = rest % 16;
+    int s, rest;
+    scale_item(cur, q, s, rest);
+    const int g8 = rest / 16, row = rest % 16;
 #pragma unroll
     for (int e = 0; e < 8; ++e) sc[((size_t)s * GP + 8 * g8 + e) * 16 + row] = (uint16_t)(scv[q][e >> 1] >> (16 * (e & 1)));
   }
@@ -197,7 +229,9 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void proj_skinny_kernel(ProjArgs
 
   // one group: column sums and sums of squares of x, then its SP atoms;
   // each consumed slot is refilled with the same strip D groups ahead
-  auto do_group = [&](auto refill, const u32x4_t (&bxg)[T][4], const int gi, const int d) {
+  // refill mode: 0 none, 1 the same strip D groups ahead, 2 the next
+  // tile's atom of this slot
+  auto do_group = [&](auto refill, const u32x4_t (&bxg)[T][4], const int gi, const int d, const Tile& nx) {
     const bool valid = gi < gpw;
     const int g = group_of(gi);
     f32x4_t X[T];
@@ -226,7 +260,8 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void proj_skinny_kernel(ProjArgs
       // atom lands in the same registers (no copies or waits on the loop's
       // back edge): the empty asm orders the decode before the load
       asm volatile("" : "+v"(A[0]), "+v"(A[1]), "+v"(A[2]), "+v"(A[3])::"memory");
-      if constexpr (decltype(refill)::value) ring[k] = load16_stream(atom_ptr(gi + D, s));
+      if constexpr (decltype(refill)::value == 1) ring[k] = load16_stream(atom_ptr(gi + D, s));
+      if constexpr (decltype(refill)::value == 2) ring[k] = load16_stream(atom_ptr_t(nx, d, s));
       const u32x2_t sv = *reinterpret_cast<const u32x2_t*>(&sc[((size_t)s * GP + g - 8 * b0) * 16 + 4 * j]);
       float scl[4];
 #pragma unroll
@@ -267,29 +302,46 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void proj_skinny_kernel(ProjArgs
       __builtin_amdgcn_sched_barrier(0);
       load_xs(xs, gb + d + 1);
       __builtin_amdgcn_sched_barrier(0);
-      do_group(std::true_type(), bx, gb + d, d);
+      do_group(std::integral_constant<int, 1>(), bx, gb + d, d, cur);
       // keep the scheduler from hoisting later groups' loads (register
       // pressure) across the group boundary
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  if (ngr > 0) {
+  const int nxt_tile = tile + (int)gridDim.x;
+  const bool has_next = P && nxt_tile < ntiles;
+  const Tile nx = tile_of(has_next ? nxt_tile : tile);
+  auto tail = [&](auto mode) {
+    constexpr int MODE = decltype(mode)::value;
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       stage_bx(xs, bx);
       __builtin_amdgcn_sched_barrier(0);
       if (d + 1 < D) load_xs(xs, gb + d + 1);
+      else if (MODE == 2) load_xs_t(nx, xs, 0);
       __builtin_amdgcn_sched_barrier(0);
-      do_group(std::false_type(), bx, gb + d, d);
+      do_group(mode, bx, gb + d, d, nx);
       __builtin_amdgcn_sched_barrier(0);
     }
+  };
+  if (P && has_next) {
+    if (ngr > 0) {
+      tail(std::integral_constant<int, 2>());
+    } else {
+      // no groups in this tile for this wave: request the next tile directly
+#pragma unroll
+      for (int k = 0; k < U; ++k) ring[k] = load16_stream(atom_ptr_t(nx, k / SP, k % SP));
+      load_xs_t(nx, xs, 0);
+    }
+    load_scales(nx);
+  } else if (ngr > 0) {
+    tail(std::integral_constant<int, 0>());
   }
 
   // partial tiles: lane holds rows 4j+i of column r of each tile.  Waves
   // 0-3 store theirs, then waves 4-7 add theirs to the same slots (plain
   // LDS reads and writes: LDS float atomics are slow); the row stride RS
   // puts the four row quarters of a store on distinct banks.
-  constexpr int RS = T * 16 + 4;
   auto slot = [&](int s, int t, int i) { return (((wave & 3) * SP + s) * 16 + 4 * j + i) * RS + t * 16 + r; };
   lds_barrier();  // every wave is past its last read of sc and xst
   if (wave < 4) {
@@ -338,7 +390,7 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void proj_skinny_kernel(ProjArgs
     // stores), count the slice in; the last slice of the set to arrive sums
     // all KS of them in slice order and runs the epilogue
     const size_t blk = split_block_floats(SP);
-    float* part = a.split_part + (size_t)blockIdx.x * blk;
+    float* part = a.split_part + (size_t)tile * blk;
     const int n4 = ns * 16 * M / 4;  // the tile as 16-byte pieces
     for (int i4 = tid; i4 < n4; i4 += NW * 64) {
       u32x4_t v;
@@ -357,7 +409,14 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void proj_skinny_kernel(ProjArgs
       *flag = last ? 1 : 0;
     }
     __syncthreads();
-    if (*flag == 0) return;
+    if (*flag == 0) {
+      if (!has_next) return;
+      // the next tile's scale writes come after every wave read the flag
+      __syncthreads();
+      tile = nxt_tile;
+      cur = nx;
+      continue;
+    }
     __syncthreads();  // every thread has read the flag before rho_s is reused
     // slices summed in order 0 .. KS-1, four loads in flight at a time
     // (slices past KS read slice KS-1 and add zero)
@@ -387,6 +446,10 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void proj_skinny_kernel(ProjArgs
   }
   __syncthreads();
   run_epilogue<EPI>(a, strip0, ns, ot, rho_s);
+  if (!has_next) return;
+  tile = nxt_tile;
+  cur = nx;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -488,10 +551,18 @@ static hipError_t launch_epi(const ProjArgs& a, hipStream_t st) {
     const int T = a.M <= 16 ? 1 : 2;
     const SkinnyPlan p = skinny_plan(nstrips, a.G, T, !needs_rho<EPI>(), split_bytes_of(a));
     const size_t lds = skinny_lds_bytes(p.NB8, p.SP, T);
-    const int grid = (nstrips + p.SP - 1) / p.SP * p.KS;
-#define I4D_SKINNY(SPV, TV, DV)                   \
-  if (p.SP == SPV && T == TV && p.D == DV)       \
-    hipLaunchKernelGGL((proj_skinny_kernel<EPI, SPV, TV, DV>), dim3(grid), dim3(kSkinnyWaves * 64), lds, st, a, p);
+    const int ntiles = (nstrips + p.SP - 1) / p.SP * p.KS;
+    // more tiles than CUs at seven strips and one x tile: persistent
+    // workgroups, one per CU
+    const bool persist = ntiles > kSkinnyMaxWorkgroups && p.SP == 7 && T == 1;
+    const int grid = persist ? kSkinnyMaxWorkgroups : ntiles;
+#define I4D_SKINNY(SPV, TV, DV)                                                                                 \
+  if (p.SP == SPV && T == TV && p.D == DV && !persist)                                                          \
+    hipLaunchKernelGGL((proj_skinny_kernel<EPI, SPV, TV, DV, false>), dim3(grid), dim3(kSkinnyWaves * 64), lds, st, \
+                       a, p);
+    // (two x tiles with the persistent loop exceed the register file)
+    if (persist && p.D == 2)
+      hipLaunchKernelGGL((proj_skinny_kernel<EPI, 7, 1, 2, true>), dim3(grid), dim3(kSkinnyWaves * 64), lds, st, a, p);
     I4D_SKINNY(1, 1, 4) I4D_SKINNY(2, 1, 4) I4D_SKINNY(3, 1, 4) I4D_SKINNY(4, 1, 2) I4D_SKINNY(5, 1, 2)
     I4D_SKINNY(7, 1, 2)
     I4D_SKINNY(1, 2, 4) I4D_SKINNY(2, 2, 2) I4D_SKINNY(3, 2, 2) I4D_SKINNY(4, 2, 2) I4D_SKINNY(5, 2, 2)
