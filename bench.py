@@ -32,47 +32,34 @@ HBM_PEAK_GBPS = 8000.0
 
 # HBM traffic of the dominant kernel per launch, from two rocprofv3 --pmc
 # runs (FETCH_SIZE, then WRITE_SIZE) scaled by the same counters on a plain
-# copy of known size; valid only for the kernel sources it was taken on
-# (sha256 over the csrc files), else the roofline entry reports null.
+# copy of known size; valid only for the sources it was taken on (sha256
+# over the files that build and launch that kernel), else the roofline entry
+# reports null.
+STEP_M1_SOURCES = ("step.hip", "step.h", "gemv.h", "attn_core.h", "attn.h", "coherent.h", "device_common.h",
+                   "proj.h", "i4d_internal.h", "i4d_layout.h", "api_device.hip", "api_host.cpp")
 TRAFFIC = {
-    "8b_m1_ctx4096": {"kernel": "step_m1_kernel (one-launch decode step)",
-                      "csrc_sha256": "d5f65a7cf173399ed813ea7de082291e00ecb8b41d8df04b8279741c1acdc004",
+    "8b_m1_ctx4096": {"kernel": "step_m1_kernel (one-launch decode step)", "sources": STEP_M1_SOURCES,
+                      "sha256": "150b93f02866804e94724ceaf02ed1ca1da8b8b12f527f9d8484106b4483cf4c",
                       "fetch_bytes": 119558349, "write_bytes": 751104},
 }
 
 
-def csrc_sha256():
+def sources_sha256(names):
     import hashlib
     d = os.path.join(ROOT, "int4_quantized_decode_amd", "csrc")
     h = hashlib.sha256()
-    for name in sorted(os.listdir(d)):
-        if name.endswith((".hip", ".h", ".cpp")):
-            h.update(name.encode())
-            with open(os.path.join(d, name), "rb") as f:
-                h.update(f.read())
+    for name in names:
+        h.update(name.encode())
+        with open(os.path.join(d, name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()
 
 
 def traffic_of(workload, kernel):
     t = TRAFFIC.get(workload)
-    if not t or t["kernel"] != kernel or t["csrc_sha256"] != csrc_sha256():
+    if not t or t["kernel"] != kernel or t["sha256"] != sources_sha256(t["sources"]):
         return None
     return t["fetch_bytes"] + t["write_bytes"]
-
-
-def algorithmic_bytes(shape, lengths):
-    """INT4 codes (0.5 B/weight) + fp16 group scales + INT4 KV codes and
-    per-token-per-head fp16 scales read by one step."""
-    d, F, hd, nq, nkv = shape.d_model, shape.d_ffn, shape.head_dim, shape.n_q_heads, shape.n_kv_heads
-    weights = (shape.n_qkv * d + d * nq * hd + 2 * F * d + d * F)
-    w_bytes = weights // 2 + (weights // 128) * 2
-    kv_bytes = int(np.sum(lengths)) * nkv * 2 * (hd // 2 + 2)
-    return w_bytes + kv_bytes, w_bytes, kv_bytes
-
-
-def gate_up_bytes(shape):
-    n = 2 * shape.d_ffn * shape.d_model
-    return n // 2 + (n // 128) * 2
 
 
 def main():
