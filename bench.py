@@ -62,6 +62,21 @@ def traffic_of(workload, kernel):
     return t["fetch_bytes"] + t["write_bytes"]
 
 
+def algorithmic_bytes(shape, lengths):
+    """INT4 codes (0.5 B/weight) + fp16 group scales + INT4 KV codes and
+    per-token-per-head fp16 scales read by one step."""
+    d, F, hd, nq, nkv = shape.d_model, shape.d_ffn, shape.head_dim, shape.n_q_heads, shape.n_kv_heads
+    weights = (shape.n_qkv * d + d * nq * hd + 2 * F * d + d * F)
+    w_bytes = weights // 2 + (weights // 128) * 2
+    kv_bytes = int(np.sum(lengths)) * nkv * 2 * (hd // 2 + 2)
+    return w_bytes + kv_bytes, w_bytes, kv_bytes
+
+
+def gate_up_bytes(shape):
+    n = 2 * shape.d_ffn * shape.d_model
+    return n // 2 + (n // 128) * 2
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
