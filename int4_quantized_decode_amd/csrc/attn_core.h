@@ -521,22 +521,16 @@ __device__ __forceinline__ void combine_head(const AttnArgs& a, size_t head_row,
   const int S = a.S;
   const float* ml = a.part_ml + head_row * S * 2;
   const float* po = a.part_o + head_row * S * HD;
-  // every load of a chunk is issued before any of them is used: one round
-  // trip per 32 splits (lane u < CH holds split t0 + u's max and sum)
-  float mt[(I4D_MAX_SPLITS + CH - 1) / CH], lt[(I4D_MAX_SPLITS + CH - 1) / CH];
-  float M_ = -INFINITY;
+  // one round trip per 32 splits: the chunk's (max, sum) pairs (lane u < CH
+  // holds split t0 + u) and its partial outputs are requested together;
+  // the running maximum is rescaled per chunk
+  float M_ = -INFINITY, lsum = 0.f, o0 = 0.f, o1 = 0.f;
   const int nch = (S + CH - 1) / CH;
   for (int c = 0; c < nch; ++c) {
-    const int t = min(c * CH + (lane & (CH - 1)), S - 1);
-    mt[c] = ld(&ml[2 * t]);
-    lt[c] = ld(&ml[2 * t + 1]);
-    const bool valid = (lane < CH) && (c * CH + lane < S) && lt[c] > 0.f;
-    M_ = fmaxf(M_, valid ? mt[c] : -INFINITY);
-  }
-  M_ = wave_max(M_);
-  float lsum = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int c = 0; c < nch; ++c) {
     const int t0 = c * CH;
+    const int tl = min(t0 + (lane & (CH - 1)), S - 1);
+    const float mt = ld(&ml[2 * tl]);
+    const float lt = ld(&ml[2 * tl + 1]);
     float x0[CH], x1[CH];
 #pragma unroll
     for (int u = 0; u < CH; ++u) {
@@ -544,14 +538,24 @@ __device__ __forceinline__ void combine_head(const AttnArgs& a, size_t head_row,
       x0[u] = ld(&po[(size_t)t * HD + lane]);
       x1[u] = (HD == 128) ? ld(&po[(size_t)t * HD + lane + 64]) : 0.f;
     }
-    const bool valid = (lane < CH) && (t0 + lane < S) && lt[c] > 0.f;
-    const float f = valid ? exp2f(mt[c] - M_) : 0.f;
-    lsum = fmaf(f, valid ? lt[c] : 0.f, lsum);
+    // an empty split has sum 0 and contributes nothing
+    const bool valid = (lane < CH) && (t0 + lane < S) && lt > 0.f;
+    const float mc = wave_max(valid ? mt : -INFINITY);
+    const float M_new = fmaxf(M_, mc);
+    if (M_new > -INFINITY) {
+      const float alpha = exp2f(M_ - M_new);  // 0 while M_ is -inf
+      lsum *= alpha;
+      o0 *= alpha;
+      o1 *= alpha;
+      const float f = valid ? exp2f(mt - M_new) : 0.f;
+      lsum = fmaf(f, valid ? lt : 0.f, lsum);
 #pragma unroll
-    for (int u = 0; u < CH; ++u) {
-      const float fu = __shfl(f, u, 64);
-      o0 = fmaf(fu, x0[u], o0);
-      o1 = fmaf(fu, x1[u], o1);
+      for (int u = 0; u < CH; ++u) {
+        const float fu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), u));
+        o0 = fmaf(fu, x0[u], o0);
+        o1 = fmaf(fu, x1[u], o1);
+      }
+      M_ = M_new;
     }
   }
 #pragma unroll

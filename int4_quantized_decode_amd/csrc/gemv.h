@@ -261,11 +261,28 @@ __device__ __forceinline__ void gemv_body(const ProjArgs& a, const GemvPlan& pl,
   };
   u32x4_t ring[U];
   uint16_t sring[U];
+  // GPW > 0: every wave has GR groups of each strip (or none), so slot k
+  // always holds group k % GR of strip (round * U / GR + k / GR): one
+  // clamped strip index and one scalar base per strip and round (the lane
+  // offset is a fixed vector register), no cursor arithmetic per atom
+  int fill_round = 0;
+  const int last_strip = min(strip0 + max(ns, 1) - 1, nstrips - 1);
+  const uint32_t lane_off = (uint32_t)lane * 16;
   auto fill = [&](const int k) {
     const uint8_t* cp;
     const uint16_t* sp;
     const uint16_t* sv;
-    next_atom(cp, sp, sv);
+    if (GPW > 0) {
+      const int t = min(strip0 + fill_round * (U / GR) + k / GR, last_strip);
+      const uint8_t* base = a.codes + ((size_t)t * G + min(g0, G - 1) + (k % GR)) * kAtomBytes;
+      cp = base + lane_off;
+      sp = nullptr;
+      const int gs = min(g0, G - 1);
+      sv = a.scales + (((size_t)t * a.G8 + gs / 8) * 16 + r) * 8 + (gs % 8);
+      if (k == U - 1) ++fill_round;
+    } else {
+      next_atom(cp, sp, sv);
+    }
     ring[k] = load16_stream(cp);
     if (GPW == 0) {
       sring[k] = *sp;
