@@ -113,7 +113,8 @@ typedef struct {
  *              matching up rows (2N packed rows).
  * With a gain, the folded weight W' = fp32(gamma[k] * W[n][k]) is quantized
  * ("how it works": the gain is folded into the weights before
- * quantization). */
+ * quantization).  Device layout: codes in 1 KiB atoms (16 packed rows x
+ * 128 channels), [strip][group]; scales fp16 [strip][group][16 rows]. */
 typedef enum { I4D_PROJ_PLAIN = 0, I4D_PROJ_QKV = 1, I4D_PROJ_GATE_UP = 2 } i4d_proj_kind;
 
 /* Sizes of the packed buffers for a [N][K] projection (GATE_UP: two [N][K]).

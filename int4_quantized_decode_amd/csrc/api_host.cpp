@@ -233,7 +233,7 @@ i4d_status i4d_pack_weights(i4d_proj_kind kind, const float* W0, const float* W1
   if (kind == I4D_PROJ_PLAIN && gamma)
     return fail(I4D_ERR_RANGE, "PLAIN projections take no gain (gamma must be NULL)");
   const int Np = packed_rows(kind, N);
-  const int G = groups_of(K), G8 = g8_of(K);
+  const int G = groups_of(K);
   uint8_t* codes = (uint8_t*)codes_out;
   memset(scales_out, 0, packed_scale_elems(Np, K) * sizeof(uint16_t));
   parallel_for(Np / kStrip, threads, [&](long t0, long t1) {
@@ -252,7 +252,7 @@ i4d_status i4d_pack_weights(i4d_proj_kind kind, const float* W0, const float* W1
             w[k] = gamma ? gamma[g * kGroup + k] * v : v;  // one fp32 product
           }
           uint16_t s16 = quantize_group(w.data(), q);
-          scales_out[(((size_t)t * G8 + g / 8) * 16 + r) * 8 + (g % 8)] = s16;
+          scales_out[((size_t)t * G + g) * kStrip + r] = s16;
           uint8_t* atom = atom_base + (size_t)g * kAtomBytes;
           for (int kk = 0; kk < kGroup; ++kk) {
             int kb = kk / 32, j = (kk % 32) / 8, e = kk % 8;
@@ -265,7 +265,6 @@ i4d_status i4d_pack_weights(i4d_proj_kind kind, const float* W0, const float* W1
       }
     }
   });
-  (void)G8;
   return ok();
 }
 

@@ -238,20 +238,17 @@ __device__ __forceinline__ void gemv_body(const ProjArgs& a, const GemvPlan& pl,
     lds_barrier();
   }
 
-  // 2. the first U atoms of the weight stream.  The refill cursor (rs, rg)
-  // walks strip by strip through the wave's groups and stops on the last
-  // atom, which pads the sequence.  With GPW > 0 the slot of a strip's
-  // last group also loads the strip's GPW scales (one load per strip: a
-  // row's 8 consecutive groups are contiguous); GPW == 0 loads each
-  // atom's scale.
+  // 2. the first U atoms of the weight stream, each with its scale (lane r:
+  // row r of the atom's strip; scales are [strip][group][row], so a
+  // 2-byte load per atom).  The refill cursor (rs, rg) walks strip by strip
+  // through the wave's groups and stops on the last atom, which pads the
+  // sequence.
   int rs = 0, rg = 0;
-  auto next_atom = [&](const uint8_t*& cp, const uint16_t*& sp, const uint16_t*& sv) {
+  auto next_atom = [&](const uint8_t*& cp, const uint16_t*& sp) {
     const int t = min(strip0 + rs, nstrips - 1);
     const int g = min(g0 + rg, G - 1);
     cp = a.codes + ((size_t)t * G + g) * kAtomBytes + (size_t)lane * 16;
-    sp = a.scales + (((size_t)t * a.G8 + g / 8) * 16 + r) * 8 + (g % 8);
-    const int gs = min(g0, G - 1);
-    sv = a.scales + (((size_t)t * a.G8 + gs / 8) * 16 + r) * 8 + (gs % 8);
+    sp = a.scales + ((size_t)t * G + g) * kStrip + r;
     if (rs < ns - 1 || rg < gpw - 1) {
       if (++rg >= gpw) {
         rg = 0;
@@ -264,44 +261,24 @@ __device__ __forceinline__ void gemv_body(const ProjArgs& a, const GemvPlan& pl,
   // GPW > 0: every wave has GR groups of each strip (or none), so slot k
   // always holds group k % GR of strip (round * U / GR + k / GR): one
   // clamped strip index and one scalar base per strip and round (the lane
-  // offset is a fixed vector register), no cursor arithmetic per atom
+  // offsets are fixed vector registers), no cursor arithmetic per atom
   int fill_round = 0;
   const int last_strip = min(strip0 + max(ns, 1) - 1, nstrips - 1);
   const uint32_t lane_off = (uint32_t)lane * 16;
   auto fill = [&](const int k) {
     const uint8_t* cp;
     const uint16_t* sp;
-    const uint16_t* sv;
     if (GPW > 0) {
       const int t = min(strip0 + fill_round * (U / GR) + k / GR, last_strip);
-      const uint8_t* base = a.codes + ((size_t)t * G + min(g0, G - 1) + (k % GR)) * kAtomBytes;
-      cp = base + lane_off;
-      sp = nullptr;
-      const int gs = min(g0, G - 1);
-      sv = a.scales + (((size_t)t * a.G8 + gs / 8) * 16 + r) * 8 + (gs % 8);
+      const size_t atom = (size_t)t * G + min(g0 + (k % GR), G - 1);
+      cp = a.codes + atom * kAtomBytes + lane_off;
+      sp = a.scales + atom * kStrip + r;
       if (k == U - 1) ++fill_round;
     } else {
-      next_atom(cp, sp, sv);
+      next_atom(cp, sp);
     }
     ring[k] = load16_stream(cp);
-    if (GPW == 0) {
-      sring[k] = *sp;
-    } else if (k % GR == GR - 1) {
-      // the strip's last slot: every slot of the strip has been consumed
-      // and refilled with the next strip's atoms
-      const int k0 = k - (GR - 1);
-      if (GR == 1) {
-        sring[k0] = *sv;
-      } else if (GR == 2) {
-        const uint32_t w = *reinterpret_cast<const uint32_t*>(sv);
-        sring[k0] = (uint16_t)w;
-        sring[k0 + 1] = (uint16_t)(w >> 16);
-      } else {
-        const u32x2_t w = *reinterpret_cast<const u32x2_t*>(sv);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) sring[k0 + q] = (uint16_t)(w[q >> 1] >> (16 * (q & 1)));
-      }
-    }
+    sring[k] = *sp;
   };
   // In the one-launch step the last wave waits for the producers (its
   // polls must not queue behind atom loads of its own: a wave's loads

@@ -52,8 +52,9 @@ inline int groups_of(int K) { return K / kGroup; }
 inline int g8_of(int K) { return (K / kGroup + 7) / 8; }
 
 inline size_t packed_code_bytes(int Np, int K) { return (size_t)Np * (size_t)K / 2; }
+// scales: fp16 [strip][group][16 rows], 32 bytes per atom
 inline size_t packed_scale_elems(int Np, int K) {
-  return (size_t)(Np / kStrip) * (size_t)g8_of(K) * 128;
+  return (size_t)(Np / kStrip) * (size_t)groups_of(K) * kStrip;
 }
 
 // byte offset of code (packed row p, k) and the nibble slot inside it
@@ -68,7 +69,7 @@ inline size_t code_byte_offset(int p, int k, int K, int* nib_hi) {
 
 inline size_t scale_index(int p, int g, int K) {
   int t = p / kStrip, r = p % kStrip;
-  return (((size_t)t * g8_of(K) + g / 8) * 16 + r) * 8 + (g % 8);
+  return ((size_t)t * groups_of(K) + g) * kStrip + r;
 }
 
 // packed row -> logical row for each kind (QKV needs head_dim)

@@ -11,7 +11,7 @@ enum Epi { EPI_QKV = 0, EPI_O = 1, EPI_GU = 2, EPI_DOWN = 3 };
 
 struct ProjArgs {
   const uint8_t* codes;    // packed atoms [Np/16][K/128][64][16]
-  const uint16_t* scales;  // fp16 [Np/16][G8][16][8]
+  const uint16_t* scales;  // fp16 [Np/16][G][16]
   const uint16_t* x;       // bf16 input [M][K]
   int Np, K, G, G8, M;
   float eps;

@@ -63,14 +63,13 @@ __global__ __launch_bounds__(NW * 64) void proj_gemv_kernel(ProjArgs a, GemvPlan
 
 constexpr int kSkinnyWaves = 8;
 constexpr int kSkinnyMaxWorkgroups = 256;
-constexpr int kScaleLoads = 4;  // scale loads per thread: SP * ceil(G/8) <= 128
+constexpr int kScaleLoads = 4;  // 16-byte scale loads per lane: SP * GPW <= 128
 
 struct SkinnyPlan {
   int SP;   // strips per workgroup
   int KS;   // K slices (workgroups per strip set; > 1 needs the split buffers)
   int GPW;  // groups per wave in the longest slice
   int D;    // groups of atoms in flight per wave
-  int NB8;  // 8-group scale blocks a slice touches, at most
 };
 
 // floats per (strip set, slice) in the split buffer: the partial tile
@@ -82,10 +81,10 @@ __host__ __device__ inline size_t split_block_floats(int SP) { return (size_t)SP
 constexpr int kXRow = 272;
 
 // LDS: sums of squares [NW][T*16] f32 | rho [T*16] | tile [SP*16][T*16] |
-// then either scales [SP][8*NB8][16] fp16 + x staging [NW][16T][kXRow
+// then either the waves' scales [NW][SP][GPW][16] fp16 + x staging [NW][16T][kXRow
 // bytes] (main loop) or partial tiles [4][SP*16][T*16+4] f32 (reduction)
-inline size_t skinny_lds_bytes(int NB8, int SP, int T) {
-  const size_t loop = (size_t)SP * NB8 * 8 * 16 * 2 + (size_t)kSkinnyWaves * 16 * T * kXRow;
+inline size_t skinny_lds_bytes(int GW, int SP, int T) {
+  const size_t loop = (size_t)kSkinnyWaves * SP * GW * kStrip * 2 + (size_t)kSkinnyWaves * 16 * T * kXRow;
   const size_t reduce = (size_t)4 * SP * 16 * (T * 16 + 4) * 4;
   return (size_t)kSkinnyWaves * T * 16 * 4 + (size_t)T * 16 * 4 + (size_t)SP * 16 * T * 16 * 4 +
          std::max(loop, reduce);
@@ -100,8 +99,8 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void proj_skinny_kernel(ProjArgs
   float* sqw = reinterpret_cast<float*>(smem);                                   // [NW][T*16]
   float* rho_s = sqw + NW * T * 16;                                              // [T*16]
   float* ot = rho_s + T * 16;                                                    // [SP*16][M]
-  uint16_t* sc = reinterpret_cast<uint16_t*>(ot + SP * 16 * T * 16);             // [SP][8*NB8][16]
-  unsigned char* xst = reinterpret_cast<unsigned char*>(sc + (size_t)SP * pl.NB8 * 8 * 16);  // [NW][16T][kXRow]
+  uint16_t* sc = reinterpret_cast<uint16_t*>(ot + SP * 16 * T * 16);             // [NW][SP][GPW][16]
+  unsigned char* xst = reinterpret_cast<unsigned char*>(sc + (size_t)NW * SP * pl.GPW * kStrip);  // [NW][16T][kXRow]
   float* red = reinterpret_cast<float*>(sc);  // [4][SP*16][T*16+4], over sc and xst once the waves are done
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -118,7 +117,7 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void proj_skinny_kernel(ProjArgs
   // tiles blockIdx.x, + gridDim.x, ...; the last D groups of a tile refill
   // the ring with the next tile's first atoms.
   struct Tile {
-    int set, ks, strip0, ns, gs0, Gs, gpw, b0, nb8;
+    int set, ks, strip0, ns, gs0, Gs, gpw;
   };
   auto tile_of = [&](int t) {
     Tile g;
@@ -129,8 +128,6 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void proj_skinny_kernel(ProjArgs
     g.gs0 = g.ks * G / KS;
     g.Gs = (g.ks + 1) * G / KS - g.gs0;
     g.gpw = max(0, (g.Gs - wave + NW - 1) / NW);
-    g.b0 = g.gs0 / 8;
-    g.nb8 = (g.gs0 + g.Gs + 7) / 8 - g.b0;
     return g;
   };
   int tile = blockIdx.x;
@@ -147,21 +144,27 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void proj_skinny_kernel(ProjArgs
     return a.codes + ((size_t)t * G + group_of_t(g, gi)) * kAtomBytes + (size_t)lane * 16;
   };
   auto atom_ptr = [&](int gi, int s) { return atom_ptr_t(cur, gi, s); };
-  // scales of the tile's strips and slice (8-group blocks b0 .. b0 + nb8 -
-  // 1), requested first (they are needed first); at most kScaleLoads
-  // 16-byte loads per thread
-  auto scale_item = [&](const Tile& g, int q, int& s, int& rest) {
-    const int idx = min(tid + q * NW * 64, g.ns * g.nb8 * 16 - 1);
-    s = idx / (g.nb8 * 16);
-    rest = idx % (g.nb8 * 16);
+  // Each wave stages the scales of its own atoms (SP strips x GW groups,
+  // 32 bytes per atom in the [strip][group][row] layout) in its own LDS
+  // rows: requested first (they are needed first), no workgroup barrier.
+  // Item i of a wave is half i % 2 of atom i / 2; at most kScaleLoads
+  // 16-byte loads per lane (items past the wave's atoms re-read valid ones).
+  const int GW = pl.GPW;
+  auto scale_item = [&](int q, int& s, int& gi, int& half) {
+    const int idx = min(lane + q * 64, 2 * SP * GW - 1);
+    const int at = idx >> 1;
+    half = idx & 1;
+    s = at / GW;
+    gi = at % GW;
   };
   u32x4_t scv[kScaleLoads];
   auto load_scales = [&](const Tile& g) {
 #pragma unroll
     for (int q = 0; q < kScaleLoads; ++q) {
-      int s, rest;
-      scale_item(g, q, s, rest);
-      scv[q] = load16(a.scales + (((size_t)(g.strip0 + s) * a.G8 + g.b0 + rest / 16) * 16 + rest % 16) * 8);
+      int s, gi, half;
+      scale_item(q, s, gi, half);
+      const int t = min(g.strip0 + min(s, g.ns - 1), nstrips - 1);
+      scv[q] = load16(a.scales + ((size_t)t * G + group_of_t(g, gi)) * kStrip + 8 * half);
     }
   };
   load_scales(cur);
@@ -199,22 +202,16 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void proj_skinny_kernel(ProjArgs
   u32x4_t xs[4 * T];
   load_xs(xs, 0);
 
-  const int GP = pl.NB8 * 8;
   constexpr int RS = T * 16 + 4;
+  uint16_t* scw = sc + (size_t)wave * SP * GW * kStrip;  // this wave's [SP][GW][16]
   for (;;) {
-  const int set = cur.set, strip0 = cur.strip0, ns = cur.ns, gpw = cur.gpw, b0 = cur.b0;
-  // scales to LDS, transposed to [s][g][row] (threads past the end repeat
-  // the last item's identical writes); the barrier does not wait for the
-  // atoms and x still in flight
+  const int set = cur.set, strip0 = cur.strip0, ns = cur.ns, gpw = cur.gpw;
 #pragma unroll
   for (int q = 0; q < kScaleLoads; ++q) {
-    int s, rest;
-    scale_item(cur, q, s, rest);
-    const int g8 = rest / 16, row = rest % 16;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) sc[((size_t)s * GP + 8 * g8 + e) * 16 + row] = (uint16_t)(scv[q][e >> 1] >> (16 * (e & 1)));
+    int s, gi, half;
+    scale_item(q, s, gi, half);
+    *reinterpret_cast<u32x4_t*>(&scw[(s * GW + gi) * kStrip + 8 * half]) = scv[q];
   }
-  lds_barrier();
 
   const u32x4_t ones_u = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
   const bf16x8_t ones = bitcast<bf16x8_t>(ones_u);
@@ -262,7 +259,7 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void proj_skinny_kernel(ProjArgs
       asm volatile("" : "+v"(A[0]), "+v"(A[1]), "+v"(A[2]), "+v"(A[3])::"memory");
       if constexpr (decltype(refill)::value == 1) ring[k] = load16_stream(atom_ptr(gi + D, s));
       if constexpr (decltype(refill)::value == 2) ring[k] = load16_stream(atom_ptr_t(nx, d, s));
-      const u32x2_t sv = *reinterpret_cast<const u32x2_t*>(&sc[((size_t)s * GP + g - 8 * b0) * 16 + 4 * j]);
+      const u32x2_t sv = *reinterpret_cast<const u32x2_t*>(&scw[(s * GW + min(gi, GW - 1)) * kStrip + 4 * j]);
       float scl[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -475,17 +472,15 @@ static SkinnyPlan skinny_plan(int nstrips, int G, int T, bool deep, size_t split
       while (KS > 1 && (size_t)nsets * KS * split_block_floats(SP) * sizeof(float) > split_bytes) --KS;
     }
     const int gs_max = (G + KS - 1) / KS;
-    const int nb8 = std::min((G + 7) / 8, (gs_max + 7) / 8 + 1);
-    if (SP * nb8 * 16 > kScaleLoads * kSkinnyWaves * 64 || skinny_lds_bytes(nb8, SP, T) > (size_t)kMaxLdsBytes)
-      continue;
+    const int gw = (gs_max + kSkinnyWaves - 1) / kSkinnyWaves;
+    if (2 * SP * gw > kScaleLoads * 64 || skinny_lds_bytes(gw, SP, T) > (size_t)kMaxLdsBytes) continue;
     const int W = nsets * KS, rounds = (W + 255) / 256;
     const double score = (double)W / (256.0 * rounds);
     if (score > best_score + 1e-9) {
       best_score = score;
       best.SP = SP;
       best.KS = KS;
-      best.NB8 = nb8;
-      best.GPW = (gs_max + kSkinnyWaves - 1) / kSkinnyWaves;
+      best.GPW = gw;
     }
   }
   if (best.SP >= 4)
@@ -513,7 +508,10 @@ static GemvPlan gemv_plan(int nstrips, int G) {
 
 template <int EPI, int NW>
 static void launch_gemv(const ProjArgs& a, const GemvPlan& p, size_t lds, int grid, hipStream_t st) {
-  if (p.GPW == 1)
+  // x in registers (GPW > 0) needs every wave to own exactly GPW groups
+  if (a.G % NW != 0)
+    hipLaunchKernelGGL((proj_gemv_kernel<EPI, NW, 8, 0>), dim3(grid), dim3(NW * 64), lds, st, a, p);
+  else if (p.GPW == 1)
     hipLaunchKernelGGL((proj_gemv_kernel<EPI, NW, 8, 1>), dim3(grid), dim3(NW * 64), lds, st, a, p);
   else if (p.GPW == 2)
     hipLaunchKernelGGL((proj_gemv_kernel<EPI, NW, 8, 2>), dim3(grid), dim3(NW * 64), lds, st, a, p);
@@ -550,7 +548,7 @@ static hipError_t launch_epi(const ProjArgs& a, hipStream_t st) {
   } else {
     const int T = a.M <= 16 ? 1 : 2;
     const SkinnyPlan p = skinny_plan(nstrips, a.G, T, !needs_rho<EPI>(), split_bytes_of(a));
-    const size_t lds = skinny_lds_bytes(p.NB8, p.SP, T);
+    const size_t lds = skinny_lds_bytes(p.GPW, p.SP, T);
     const int ntiles = (nstrips + p.SP - 1) / p.SP * p.KS;
     // more tiles than CUs at seven strips and one x tile: persistent
     // workgroups, one per CU

@@ -206,9 +206,8 @@ def test_packed_bytes_follow_documented_layout():
         byte = ((t * G + g) * 64 + 16 * j + r) * 16 + kb * 4 + slot // 2
         nib = (codes[byte] >> 4) if slot & 1 else (codes[byte] & 15)
         assert nib == 15
-        # scale layout [strip][g/8][row][g%8]
-        g8 = (G + 7) // 8
-        assert scales[((t * g8 + g // 8) * 16 + r) * 8 + g % 8] == np.float16(n + 1).view(np.uint16)
+        # scale layout [strip][group][row]
+        assert scales[(t * G + g) * 16 + r] == np.float16(n + 1).view(np.uint16)
     # every other nibble encodes code 0
     assert np.count_nonzero(codes == 0x88) == codes.size - len(pos)
 
@@ -219,7 +218,7 @@ def test_qkv_and_gate_up_strip_interleave():
     for n in range(N):
         W[n, 0] = 7.0 * (n + 1)
     codes, scales = B.i4d_pack_weights(B.I4D_PROJ_QKV, W, None, None, hd)
-    sc = scales.view(np.float16).reshape(N // 16, 1, 16, 8)[:, 0, :, 0]
+    sc = scales.view(np.float16).reshape(N // 16, 1, 16)[:, 0, :]
     for t in range(N // 16):
         head, sp = t // (hd // 16), t % (hd // 16)
         want = [head * hd + 8 * sp + i for i in range(8)] + [head * hd + hd // 2 + 8 * sp + i for i in range(8)]
@@ -230,7 +229,7 @@ def test_qkv_and_gate_up_strip_interleave():
     Wg[:, 0] = 7.0 * (np.arange(F) + 1)
     Wu[:, 0] = -7.0 * (np.arange(F) + 101)
     codes, scales = B.i4d_pack_weights(B.I4D_PROJ_GATE_UP, Wg, Wu)
-    sc = scales.view(np.float16).reshape(2 * F // 16, 1, 16, 8)[:, 0, :, 0]
+    sc = scales.view(np.float16).reshape(2 * F // 16, 1, 16)[:, 0, :]
     for t in range(2 * F // 16):
         np.testing.assert_array_equal(sc[t, :8], np.arange(8 * t, 8 * t + 8) + 1)
         np.testing.assert_array_equal(sc[t, 8:], np.arange(8 * t, 8 * t + 8) + 101)

@@ -170,9 +170,13 @@ def test_attention_workspace_reuse(gpu):
 # projections
 # ---------------------------------------------------------------------------
 
+# group counts that do not split evenly over the waves (5 and 9 groups of
+# 128 channels): the M = 1 kernel reads x from LDS for every atom
+SHAPE_ODD = synth.LayerShape(640, 5, 5, 128, 1152)
 SHAPES = {"tiny": synth.SHAPE_TINY, "small128": synth.SHAPE_SMALL128,
           # K = 4096 and 8192: two and four weight groups per wave in the M = 1 kernel
-          "k4096": synth.LayerShape(4096, 8, 2, 128, 8192)}
+          "k4096": synth.LayerShape(4096, 8, 2, 128, 8192),
+          "odd_groups": SHAPE_ODD}
 
 
 @pytest.fixture(scope="module")
@@ -291,6 +295,8 @@ def check_block(res, label=""):
     (synth.SHAPE_TINY, [1, 2, 5, 67]),
     (synth.SHAPE_SMALL128, [1, 33, 300]),
     (synth.SHAPE_SMALL128, [4096] * 2 + [1000] * 15),   # M = 17: second MFMA tile
+    (SHAPE_ODD, [300]),                                   # one launch, uneven groups per wave
+    (SHAPE_ODD, [70, 300, 1]),
 ])
 def test_block_small(gpu, shape, lengths):
     check_block(run_block(gpu, shape, 11, lengths))
