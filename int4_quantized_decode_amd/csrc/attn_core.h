@@ -120,21 +120,6 @@ __device__ void append_vector(const KvArgs& kv, const uint16_t* src, int64_t reg
 // attention
 // ---------------------------------------------------------------------------
 
-// Codes of one dword as an exact f16 MFMA operand with no bias: the nibble
-// is the mantissa of an f16 subnormal, so e in {0, 1, 4, 5} -> u * 2^-24 and
-// e in {2, 3, 6, 7} -> 16 u * 2^-24 (nibble at mantissa bits 4-7).  The
-// partner operand carries a factor 1/16 at e in {2, 3, 6, 7}, so every
-// product is 2^-24 * (partner value) * u; the code offset 8 is removed after
-// the MFMA as 8 * (sum of the partner values).
-__device__ __forceinline__ f16x8_t dword_to_f16x8_sub(uint32_t w) {
-  const uint32_t t = w >> 8;
-  u32x4_t v;
-  v.x = w & 0x000F000Fu;
-  v.y = w & 0x00F000F0u;
-  v.z = t & 0x000F000Fu;
-  v.w = t & 0x00F000F0u;
-  return bitcast<f16x8_t>(v);
-}
 constexpr float kTwo24 = 16777216.0f;
 __device__ __forceinline__ bool slot16(int e) { return (e & 2) != 0; }
 

@@ -19,56 +19,41 @@ __device__ __forceinline__ To bitcast(const From& f) {
   return __builtin_bit_cast(To, f);
 }
 
-// nibble pairs (slot i, slot i+4) of a packed dword as bf16 (128 + u): the
-// magic-exponent decode; value - 136 is the signed code.
-__device__ __forceinline__ uint32_t nib_pair_bf16(uint32_t w, int i) {
-  return ((w >> (4 * i)) & 0x000F000Fu) | 0x43004300u;
+// (a & m) | c in one instruction (the compiler splits it into two when both
+// constants need the one constant-bus read a VOP3 instruction has here)
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
+  uint32_t d;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "s"(m), "v"(c));
+  return d;
 }
 
-// 8 codes of a dword as the bf16x8 MFMA operand (128 + u), k order e = 0..7
-__device__ __forceinline__ bf16x8_t dword_to_bf16x8_biased(uint32_t w) {
-  u32x4_t v;
-  v.x = nib_pair_bf16(w, 0);
-  v.y = nib_pair_bf16(w, 1);
-  v.z = nib_pair_bf16(w, 2);
-  v.w = nib_pair_bf16(w, 3);
-  return bitcast<bf16x8_t>(v);
-}
-
-// 8 codes of a dword as exact signed fp16 (u - 8): (1024 + u) - 1032
-__device__ __forceinline__ f16x8_t dword_to_f16x8_signed(uint32_t w) {
-  const f16x2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
-  f16x2_t p0 = bitcast<f16x2_t>(((w >> 0) & 0x000F000Fu) | 0x64006400u) - off;
-  f16x2_t p1 = bitcast<f16x2_t>(((w >> 4) & 0x000F000Fu) | 0x64006400u) - off;
-  f16x2_t p2 = bitcast<f16x2_t>(((w >> 8) & 0x000F000Fu) | 0x64006400u) - off;
-  f16x2_t p3 = bitcast<f16x2_t>(((w >> 12) & 0x000F000Fu) | 0x64006400u) - off;
-  u32x4_t v;
-  v.x = bitcast<uint32_t>(p0);
-  v.y = bitcast<uint32_t>(p1);
-  v.z = bitcast<uint32_t>(p2);
-  v.w = bitcast<uint32_t>(p3);
-  return bitcast<f16x8_t>(v);
-}
-
-// Same result with fewer instructions: the fp16 mantissa holds a nibble at
-// bits 0-3 (value 1024 + u) or at bits 4-7 (value 1024 + 16u), so one shift
-// and four v_and_or give all eight codes; (1024 + 16u)/16 - 72 = u - 8 is
-// exact in one packed FMA.
-__device__ __forceinline__ f16x8_t dword_to_f16x8_signed_fast(uint32_t w) {
-  const f16x2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
-  const f16x2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
-  const f16x2_t off72 = {(_Float16)72.0f, (_Float16)72.0f};
+// Codes of one dword as an exact f16 MFMA operand with no bias: the nibble
+// is the mantissa of an f16 subnormal, so e in {0, 1, 4, 5} -> u * 2^-24 and
+// e in {2, 3, 6, 7} -> 16 u * 2^-24 (nibble at mantissa bits 4-7).  The
+// partner operand carries a factor 1/16 at e in {2, 3, 6, 7}, so every
+// product is 2^-24 * (partner value) * u; the code offset 8 is removed after
+// the MFMA as 8 * (sum of the partner values).
+__device__ __forceinline__ f16x8_t dword_to_f16x8_sub(uint32_t w) {
   const uint32_t t = w >> 8;
-  f16x2_t p0 = bitcast<f16x2_t>((w & 0x000F000Fu) | 0x64006400u) - off;
-  f16x2_t p1 = bitcast<f16x2_t>((w & 0x00F000F0u) | 0x64006400u) * sixteenth - off72;
-  f16x2_t p2 = bitcast<f16x2_t>((t & 0x000F000Fu) | 0x64006400u) - off;
-  f16x2_t p3 = bitcast<f16x2_t>((t & 0x00F000F0u) | 0x64006400u) * sixteenth - off72;
   u32x4_t v;
-  v.x = bitcast<uint32_t>(p0);
-  v.y = bitcast<uint32_t>(p1);
-  v.z = bitcast<uint32_t>(p2);
-  v.w = bitcast<uint32_t>(p3);
+  v.x = w & 0x000F000Fu;
+  v.y = w & 0x00F000F0u;
+  v.z = t & 0x000F000Fu;
+  v.w = t & 0x00F000F0u;
   return bitcast<f16x8_t>(v);
+}
+
+// 8 codes of a dword as the bf16x8 MFMA operand (128 + u), k order e = 0..7:
+// nibble pair (slot i, slot i + 4) under the magic exponent 0x4300 (128.0);
+// value - 136 is the signed code
+__device__ __forceinline__ bf16x8_t dword_to_bf16x8_biased(uint32_t w) {
+  const uint32_t magic = 0x43004300u;
+  u32x4_t v;
+  v.x = and_or(w, 0x000F000Fu, magic);
+  v.y = and_or(w >> 4, 0x000F000Fu, magic);
+  v.z = and_or(w >> 8, 0x000F000Fu, magic);
+  v.w = and_or(w >> 12, 0x000F000Fu, magic);
+  return bitcast<bf16x8_t>(v);
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

@@ -1,5 +1,6 @@
-// gemv.h - M = 1 INT4 projection (VALU GEMV) as a device function, shared by
-// the stand-alone projection kernels and the one-launch decode step.
+// gemv.h - M = 1 INT4 projection (one row of x, MFMA dot products) as a
+// device function, shared by the stand-alone projection kernels and the
+// one-launch decode step.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -125,37 +126,11 @@ struct GemvPlan {
   int NW, SP, GPW;
 };
 
-// LDS: x [K] fp16 | group sums [G][4] | partials [SP][NW][16] | tile [SP*16]
+// LDS: x [K] fp16 | group offset terms [G] | partials [SP][NW][16] | tile [SP*16]
 // | per-wave sums of squares [NW] | per-wave max |x| [NW]
 inline size_t gemv_lds_bytes(int K, const GemvPlan& p) {
-  return (size_t)K * 2 + (size_t)(K / kGroup) * 16 + (size_t)p.SP * p.NW * 16 * 4 +
+  return (size_t)K * 2 + (size_t)(K / kGroup) * 4 + (size_t)p.SP * p.NW * 16 * 4 +
          (size_t)p.SP * 16 * 4 + (size_t)p.NW * 8;
-}
-
-// Nibble pair q of a code dword as exact fp16 subnormals: q = 0 -> codes
-// e = 0, 1 as u * 2^-24; q = 1 -> e = 2, 3 as 16 u * 2^-24 (nibbles at
-// mantissa bits 4-7); q = 2, 3 likewise for e = 4..7 after a shift by 8.
-// The partner x carries the factor 1/16 at e in {2, 3, 6, 7}.
-__device__ __forceinline__ f16x2_t code_pair_sub(uint32_t w, uint32_t t, int q) {
-  const uint32_t v = (q == 0) ? (w & 0x000F000Fu) : (q == 1) ? (w & 0x00F000F0u)
-                   : (q == 2) ? (t & 0x000F000Fu) : (t & 0x00F000F0u);
-  return bitcast<f16x2_t>(v);
-}
-
-// dot of one atom row quarter (4 code dwords) with its 32 x values (fp16
-// pairs in k order), times 2^-24
-__device__ __forceinline__ float atom_dot(const u32x4_t w, const u32x4_t (&xk)[4]) {
-  // two accumulation chains (code dwords 0-1 and 2-3) halve the dependent
-  // chain of dot instructions
-  float acc[2] = {0.f, 0.f};
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    const uint32_t dw = w[kb], t = dw >> 8;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      acc[kb >> 1] = __builtin_amdgcn_fdot2(code_pair_sub(dw, t, q), bitcast<f16x2_t>(xk[kb][q]), acc[kb >> 1], false);
-  }
-  return acc[0] + acc[1];
 }
 
 // sum of the x values that 16 fp16 words of one group quarter represent
@@ -198,8 +173,8 @@ __device__ __forceinline__ void gemv_body(const ProjArgs& a, const GemvPlan& pl,
   const int SP = pl.SP;
   const int GW = GPW > 0 ? GPW : pl.GPW;
   uint16_t* xs = reinterpret_cast<uint16_t*>(smem);                  // [K] fp16
-  float* Xs = reinterpret_cast<float*>(smem + (size_t)K * 2);        // [G][4]
-  float* red = Xs + (size_t)G * 4;                                   // [SP][NW][16]
+  float* Xs = reinterpret_cast<float*>(smem + (size_t)K * 2);        // [G]
+  float* red = Xs + G;                                               // [SP][NW][16]
   float* ot = red + (size_t)SP * NW * 16;                            // [SP*16]
   float* ssq = ot + SP * 16;                                         // [NW]
   float* wmx = ssq + NW;                                             // [NW]
@@ -345,51 +320,68 @@ __device__ __forceinline__ void gemv_body(const ProjArgs& a, const GemvPlan& pl,
   }
   lds_barrier();
 
-  // 5. x of the wave's groups (registers) or group sums for every group (LDS)
+  // 5. x of the wave's groups (registers) or for every group (LDS), and
+  // the code offset term -8 * 2^-24 * (sum of the group's x)
   const u32x4_t* xl = reinterpret_cast<const u32x4_t*>(xs);
   u32x4_t xr[GR][4];
-  float xsum[GR];
+  float xc[GR];
+  constexpr float kOffset = -8.0f / 16777216.0f;
   if (GPW > 0) {
 #pragma unroll
     for (int gi = 0; gi < GR; ++gi) {
       const int g = min(g0 + gi, G - 1);
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) xr[gi][kb] = xl[(128 * g + 32 * kb + 8 * j) / 8];
-      xsum[gi] = quarter_sum(xr[gi]);
+      float q = quarter_sum(xr[gi]);
+      q += shfl_xor(q, 16);
+      q += shfl_xor(q, 32);
+      xc[gi] = q * kOffset;
     }
   } else {
-    for (int idx = tid; idx < G * 4; idx += NW * 64) {
-      const int g = idx >> 2, jj = idx & 3;
-      u32x4_t xk[4];
+    for (int g = tid; g < G; g += NW * 64) {
+      float q = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) xk[kb] = xl[(128 * g + 32 * kb + 8 * jj) / 8];
-      Xs[idx] = quarter_sum(xk);
+      for (int jj = 0; jj < 4; ++jj) {
+        u32x4_t xk[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) xk[kb] = xl[(128 * g + 32 * kb + 8 * jj) / 8];
+        q += quarter_sum(xk);
+      }
+      Xs[g] = q * kOffset;
     }
     lds_barrier();
   }
 
   // 6. stream: consume atom i from the ring, then refill its slot with atom
-  // i + U (the loaded registers stay in place across iterations)
+  // i + U (the loaded registers stay in place across iterations).  Per
+  // atom, four MFMAs 16x16x32 with x in every row of A (lane (r, j) holds
+  // the same x quarter j for any r) and the decoded codes as B (column r =
+  // atom row r): every lane gets the whole 128-term dot of its row r,
+  // scaled by 2^-24; the code offset enters as the group constant xc.
   float part = 0.f;
   int sl = 0, gi_rt = 0;  // strip and group of the atom being consumed (GPW == 0)
   auto consume = [&](const u32x4_t w, const uint16_t sbits, int i, int k) {
     if (i < n) {
-      float y;
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      float c;
       if (GPW > 0) {
         const int gi = k % GR;
-        y = fmaf(atom_dot(w, xr[gi]), 16777216.0f, -8.0f * xsum[gi]);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(bitcast<f16x8_t>(xr[gi][kb]), dword_to_f16x8_sub(w[kb]),
+                                                       acc, 0, 0, 0);
+        c = xc[gi];
       } else {
         const int g = g0 + gi_rt;
-        u32x4_t xk[4];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) xk[kb] = xl[(128 * g + 32 * kb + 8 * j) / 8];
-        y = fmaf(atom_dot(w, xk), 16777216.0f, -8.0f * Xs[g * 4 + j]);
+        for (int kb = 0; kb < 4; ++kb)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(bitcast<f16x8_t>(xl[(128 * g + 32 * kb + 8 * j) / 8]),
+                                                       dword_to_f16x8_sub(w[kb]), acc, 0, 0, 0);
+        c = Xs[g];
       }
-      part = fmaf(f16_bits_to_f32(sbits), y, part);
+      part = fmaf(f16_bits_to_f32(sbits), acc[0] + c, part);
       const bool last_of_strip = (GPW > 0) ? (k % GR == GR - 1) : (gi_rt == gpw - 1);
       if (last_of_strip) {
-        part += shfl_xor(part, 16);
-        part += shfl_xor(part, 32);
         if (j == 0) red[((size_t)sl * NW + wave) * 16 + r] = part;
         part = 0.f;
         ++sl;
@@ -418,7 +410,7 @@ __device__ __forceinline__ void gemv_body(const ProjArgs& a, const GemvPlan& pl,
     float v = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) v += red[((size_t)s2 * NW + w) * 16 + rr];
-    ot[tid] = v * ldexpf(1.0f, -sh);
+    ot[tid] = v * ldexpf(1.0f, 24 - sh);
   }
   if (needs_rho<EPI>() && tid == 0) {
     float t = 0.f;

@@ -3,10 +3,11 @@
 // y[m][n] = sum_g s[n][g] * sum_{k in g} (u[n][k] - 8) * x[m][k]
 // ("how it differs": group scales applied after accumulation).
 //
-// M = 1: register-streaming VALU GEMV (gemv.h).  Each 64-lane wave streams
-//   1 KiB atoms (16 rows x 128 k, one 16-byte load per lane), decodes the
-//   nibbles as exact fp16 subnormals and accumulates with v_dot2_f32_f16
-//   against range-scaled fp16 x staged in LDS.
+// M = 1: register-streaming GEMV (gemv.h).  Each 64-lane wave streams 1 KiB
+//   atoms (16 rows x 128 k, one 16-byte load per lane), decodes the nibbles
+//   as exact fp16 subnormals (the B operand of four f16 MFMA 16x16x32, one
+//   per 32 k) against range-scaled fp16 x, staged in LDS and broadcast to
+//   every row of the A operand, so each lane gets the dot of its atom row.
 // M = 2..32: skinny GEMM on bf16 MFMA 16x16x32, computed as
 //   sum_g s[n][g] * (A[n][g] - 136 * X[m][g]) where A accumulates
 //   (128 + u) * x from the bf16 magic-exponent decode of each nibble and X
@@ -35,7 +36,7 @@ namespace i4d {
 constexpr int kMaxLdsBytes = 160 * 1024;
 
 // ---------------------------------------------------------------------------
-// M = 1: stand-alone VALU GEMV kernel
+// M = 1: stand-alone GEMV kernel
 // ---------------------------------------------------------------------------
 
 template <int EPI, int NW, int U, int GPW>
@@ -81,10 +82,11 @@ __host__ __device__ inline size_t split_block_floats(int SP) { return (size_t)SP
 constexpr int kXRow = 272;
 
 // LDS: sums of squares [NW][T*16] f32 | rho [T*16] | tile [SP*16][T*16] |
-// then either the waves' scales [NW][SP][GPW][16] fp16 + x staging [NW][16T][kXRow
-// bytes] (main loop) or partial tiles [4][SP*16][T*16+4] f32 (reduction)
+// then either the waves' scales [NW][SP * GPW + 1][16] fp16 (the last row
+// zero) + x staging [NW][16T][kXRow bytes] (main loop) or partial tiles
+// [4][SP*16][T*16+4] f32 (reduction)
 inline size_t skinny_lds_bytes(int GW, int SP, int T) {
-  const size_t loop = (size_t)kSkinnyWaves * SP * GW * kStrip * 2 + (size_t)kSkinnyWaves * 16 * T * kXRow;
+  const size_t loop = (size_t)kSkinnyWaves * (SP * GW + 1) * kStrip * 2 + (size_t)kSkinnyWaves * 16 * T * kXRow;
   const size_t reduce = (size_t)4 * SP * 16 * (T * 16 + 4) * 4;
   return (size_t)kSkinnyWaves * T * 16 * 4 + (size_t)T * 16 * 4 + (size_t)SP * 16 * T * 16 * 4 +
          std::max(loop, reduce);
@@ -100,7 +102,7 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void proj_skinny_kernel(ProjArgs
   float* rho_s = sqw + NW * T * 16;                                              // [T*16]
   float* ot = rho_s + T * 16;                                                    // [SP*16][M]
   uint16_t* sc = reinterpret_cast<uint16_t*>(ot + SP * 16 * T * 16);             // [NW][SP][GPW][16]
-  unsigned char* xst = reinterpret_cast<unsigned char*>(sc + (size_t)NW * SP * pl.GPW * kStrip);  // [NW][16T][kXRow]
+  unsigned char* xst = reinterpret_cast<unsigned char*>(sc + (size_t)NW * (SP * pl.GPW + 1) * kStrip);  // [NW][16T][kXRow]
   float* red = reinterpret_cast<float*>(sc);  // [4][SP*16][T*16+4], over sc and xst once the waves are done
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -203,7 +205,7 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void proj_skinny_kernel(ProjArgs
   load_xs(xs, 0);
 
   constexpr int RS = T * 16 + 4;
-  uint16_t* scw = sc + (size_t)wave * SP * GW * kStrip;  // this wave's [SP][GW][16]
+  uint16_t* scw = sc + (size_t)wave * (SP * GW + 1) * kStrip;  // this wave's [SP][GW][16] + a zero row
   for (;;) {
   const int set = cur.set, strip0 = cur.strip0, ns = cur.ns, gpw = cur.gpw;
 #pragma unroll
@@ -212,6 +214,7 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void proj_skinny_kernel(ProjArgs
     scale_item(q, s, gi, half);
     *reinterpret_cast<u32x4_t*>(&scw[(s * GW + gi) * kStrip + 8 * half]) = scv[q];
   }
+  if (lane < 2) *reinterpret_cast<u32x4_t*>(&scw[SP * GW * kStrip + 8 * lane]) = u32x4_t{0u, 0u, 0u, 0u};
 
   const u32x4_t ones_u = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
   const bf16x8_t ones = bitcast<bf16x8_t>(ones_u);
@@ -231,6 +234,7 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void proj_skinny_kernel(ProjArgs
   auto do_group = [&](auto refill, const u32x4_t (&bxg)[T][4], const int gi, const int d, const Tile& nx) {
     const bool valid = gi < gpw;
     const int g = group_of(gi);
+    // X[t] = -136 * (column sums of x): the accumulator start of every atom
     f32x4_t X[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
@@ -246,6 +250,7 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void proj_skinny_kernel(ProjArgs
                                                 false);
       }
       if (needs_rho<EPI>()) sq[t] += valid ? q : 0.f;
+      X[t] *= -136.0f;
     }
 #pragma unroll
     for (int s = 0; s < SP; ++s) {
@@ -259,19 +264,20 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void proj_skinny_kernel(ProjArgs
       asm volatile("" : "+v"(A[0]), "+v"(A[1]), "+v"(A[2]), "+v"(A[3])::"memory");
       if constexpr (decltype(refill)::value == 1) ring[k] = load16_stream(atom_ptr(gi + D, s));
       if constexpr (decltype(refill)::value == 2) ring[k] = load16_stream(atom_ptr_t(nx, d, s));
-      const u32x2_t sv = *reinterpret_cast<const u32x2_t*>(&scw[(s * GW + min(gi, GW - 1)) * kStrip + 4 * j]);
+      // a padding group reads the zero row of scales
+      const u32x2_t sv = *reinterpret_cast<const u32x2_t*>(&scw[(valid ? s * GW + min(gi, GW - 1) : SP * GW) *
+                                                                    kStrip + 4 * j]);
       float scl[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        scl[i] = valid ? f16_bits_to_f32((uint16_t)(sv[i >> 1] >> (16 * (i & 1)))) : 0.f;
+      for (int i = 0; i < 4; ++i) scl[i] = f16_bits_to_f32((uint16_t)(sv[i >> 1] >> (16 * (i & 1))));
 #pragma unroll
       for (int t = 0; t < T; ++t) {
-        f32x4_t ag = {0.f, 0.f, 0.f, 0.f};
+        f32x4_t ag = X[t];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
           ag = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[kb], bitcast<bf16x8_t>(bxg[t][kb]), ag, 0, 0, 0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[s][t][i] = fmaf(scl[i], ag[i] - 136.0f * X[t][i], acc[s][t][i]);
+        for (int i = 0; i < 4; ++i) acc[s][t][i] = fmaf(scl[i], ag[i], acc[s][t][i]);
       }
       // one atom's decoded operands live at a time
       __builtin_amdgcn_sched_barrier(0);
