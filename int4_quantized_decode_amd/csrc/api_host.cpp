@@ -59,8 +59,9 @@ AttnPlan attn_plan(const i4d_layer_shape* s, int M, int max_ctx_len, int num_spl
   // all (row, kv head) pairs, at least 4 blocks of 32 tokens per split
   // (more, shorter splits measured slower: per-split setup, the merge and
   // the combine launch outweigh the better balance of ragged rows).  Then
-  // as many waves per workgroup (4, 8, 16) as keep every wave at one block
-  // or more while the launch has fewer than 4096 waves.
+  // 4 or 8 waves per workgroup (8 while every wave keeps two blocks or more
+  // and the launch has fewer than 4096 waves; each wave holds two blocks in
+  // registers, which 16 waves would not fit).
   const long nblk = (max_ctx_len + kVBlock - 1) / kVBlock;
   const long units = (long)M * s->n_kv_heads;
   long S;
@@ -73,7 +74,7 @@ AttnPlan attn_plan(const i4d_layer_shape* s, int M, int max_ctx_len, int num_spl
   }
   const long bps = (nblk + S - 1) / S;
   int nwa = 4;
-  while (nwa < 16 && units * S * nwa < 4096 && bps >= 2L * nwa) nwa *= 2;
+  if (units * S * 8 < 4096 && bps >= 16) nwa = 8;
   AttnPlan p;
   p.S = (int)S;
   p.nwa = nwa;

@@ -73,14 +73,12 @@ static void launch_attn_hd(const AttnArgs& a, int nwa, hipStream_t st) {
   const int grid = a.M * a.kv.n_kv * a.S;
   if (nwa == 4)
     hipLaunchKernelGGL((attn_kernel<HD, 4>), dim3(grid), dim3(4 * 64), 0, st, a);
-  else if (nwa == 8)
-    hipLaunchKernelGGL((attn_kernel<HD, 8>), dim3(grid), dim3(8 * 64), 0, st, a);
   else
-    hipLaunchKernelGGL((attn_kernel<HD, 16>), dim3(grid), dim3(16 * 64), 0, st, a);
+    hipLaunchKernelGGL((attn_kernel<HD, 8>), dim3(grid), dim3(8 * 64), 0, st, a);
 }
 
 i4d_status launch_attention(const AttnArgs& a, int nwa, bool combine, hipStream_t st) {
-  if (nwa != 4 && nwa != 8 && nwa != 16) return fail(I4D_ERR_RANGE, "attention waves %d", nwa);
+  if (nwa != 4 && nwa != 8) return fail(I4D_ERR_RANGE, "attention waves %d", nwa);
   if (a.G < 1 || a.G > 8) return fail(I4D_ERR_UNSUPPORTED, "GQA group %d > 8", a.G);
   if (a.kv.hd == 128)
     launch_attn_hd<128>(a, nwa, st);

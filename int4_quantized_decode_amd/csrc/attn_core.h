@@ -10,7 +10,7 @@
 //   rotation before cache quantization; "how it works": direct placement at
 //   offset(request, head, position, channel)).
 //
-// Attention: one workgroup per (row, kv head, split) with 4, 8 or 16 waves
+// Attention: one workgroup per (row, kv head, split) with 4 or 8 waves
 //   that take interleaved 32-token blocks.  Per block and wave:
 //     S[token][col] = K_codes(16 tokens x hd) . q~  (MFMA, fp16; the rotated
 //                     query's high part in columns c < 8, its residual in
@@ -305,10 +305,16 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int m, const 
   // appended to, which waits for the append.
   const int last_blk = (L - 1) / kVBlock;
   const bool appending = a.k_new && len_ok && last_blk >= b0 && last_blk < b1;
+  // Stand-alone: two blocks per wave in flight (its first two, then two
+  // ahead of the one being consumed).  In the one-launch step a split has
+  // about one block per wave: one in flight.
+  constexpr bool TWO = !COH;
   int blk = b0 + wave;
   const bool defer = appending && blk == last_blk;
-  BlockRegs<HD> cur;
+  const bool defer2 = TWO && appending && blk + NWA == last_blk;
+  BlockRegs<HD> cur, nxt;
   if (!defer) load_block<HD>(cur, kbase, vbase, ksc, vsc, min(blk, last_valid), c, jj);
+  if (TWO && !defer2) load_block<HD>(nxt, kbase, vbase, ksc, vsc, min(blk + NWA, last_valid), c, jj);
   // the query and the new key/value may come from other workgroups of the
   // same launch: wait for them only now
   wait_input();
@@ -357,10 +363,11 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int m, const 
     cq += shfl_xor(cq, 16);
     cq += shfl_xor(cq, 32);
   }
-  if (defer) {
+  if (defer || defer2) {
     // the CU's L1 may hold lines of this block from before the append
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    load_block<HD>(cur, kbase, vbase, ksc, vsc, blk, c, jj);
+    if (defer) load_block<HD>(cur, kbase, vbase, ksc, vsc, blk, c, jj);
+    if (defer2) load_block<HD>(nxt, kbase, vbase, ksc, vsc, blk + NWA, c, jj);
   }
   __syncthreads();  // qrot shares LDS with the merge buffers
 
@@ -370,15 +377,16 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int m, const 
   for (int cb = 0; cb < CB; ++cb) o[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const float sscale = a.score_scale;
 
-  // One block in registers; the next block's keys are requested once the
-  // current keys are consumed, its values once the current values are.  The
-  // last block of the wave runs the same body without those requests and
-  // with the token mask (only the row's last block can be partial, and it
-  // is the last block of its wave; its slots past L may hold anything).
+  // Blocks in registers (cur, and nxt when two are in flight): once a
+  // block's keys are consumed, the keys of the wave's block one (two) ahead
+  // are requested into them, its values likewise once the values are.  The
+  // wave's last block(s) run the same body without those requests and with
+  // the token mask (only the row's last block can be partial, and it is the
+  // last block of its wave; its slots past L may hold anything).
   // Columns c >= G carry finite values that no output uses.
-  auto body = [&](const int nb, auto last_tag) {
+  auto body = [&](BlockRegs<HD>& cur, const int bcur, const int nb, auto last_tag) {
     constexpr bool LAST = decltype(last_tag)::value;
-    const int t0 = blk * kVBlock;
+    const int t0 = bcur * kVBlock;
     float sc[8];
     float mx = -INFINITY;
 #pragma unroll
@@ -433,8 +441,20 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int m, const 
     m_run = m_new;
   };
   if (blk < b1) {
-    for (; blk + NWA < b1; blk += NWA) body(blk + NWA, std::false_type());
-    body(blk, std::true_type());
+    if constexpr (TWO) {
+      const int nbw = (b1 - 1 - blk) / NWA + 1;  // blocks of this wave
+      int i = 0;
+      for (; i + 2 < nbw; i += 2) {
+        body(cur, blk, min(blk + 2 * NWA, last_valid), std::false_type());
+        body(nxt, blk + NWA, min(blk + 3 * NWA, last_valid), std::false_type());
+        blk += 2 * NWA;
+      }
+      body(cur, blk, 0, std::true_type());
+      if (i + 2 == nbw) body(nxt, blk + NWA, 0, std::true_type());
+    } else {
+      for (; blk + NWA < b1; blk += NWA) body(cur, blk, blk + NWA, std::false_type());
+      body(cur, blk, 0, std::true_type());
+    }
   }
 
   // per-column totals over the 4 lane quarters; undo the 2^-24 operand

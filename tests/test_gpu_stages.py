@@ -98,8 +98,8 @@ ATTN_CASES = [
     (128, 8, 2, [70, 45], 64),              # more splits than blocks: empty splits
     (128, 32, 8, [2048], 0),                # 8B head layout
     (128, 4, 4, [200, 1000], 0),            # G = 1
-    (128, 16, 2, [4096, 3000], 2),          # G = 8, 16 waves per workgroup
-    (64, 8, 2, [4096, 17], 2),              # hd 64, 16 waves per workgroup, one short row
+    (128, 16, 2, [4096, 3000], 2),          # G = 8, 8 waves per workgroup
+    (64, 8, 2, [4096, 17], 2),              # hd 64, 8 waves per workgroup, one short row
 ]
 
 
@@ -300,6 +300,17 @@ def check_block(res, label=""):
 ])
 def test_block_small(gpu, shape, lengths):
     check_block(run_block(gpu, shape, 11, lengths))
+
+
+@pytest.mark.parametrize("lengths", [
+    [500, 300, 270, 200, 33],   # one split, 8 waves: new token in a wave's first or second block
+    [200, 150, 129],            # one split, 4 waves: the same with the second block
+])
+def test_block_append_in_prefetched_block(gpu, lengths):
+    """The attention kernel requests a wave's first two blocks before the
+    step's new key and value are appended; a block that will hold them is
+    requested only after the append."""
+    check_block(run_block(gpu, synth.SHAPE_SMALL128, 17, lengths, num_splits=1))
 
 
 def test_block_dirty_workspace_forced_splits(gpu):
