@@ -7,8 +7,8 @@
 // launch (about 1.8 us here), the drain of the previous stage and the first
 // load latency of the next.  Here one workgroup of 8 waves per CU runs all
 // stages; a stage's weight stream does not depend on the activations, so
-// each workgroup issues its first weight loads before it waits for the
-// previous stage, and HBM keeps streaming across the stage boundaries.
+// each workgroup requests the first atoms of a stage (a few per wave)
+// before it waits for the previous stage.
 //
 // Stages and hand-offs (counters in the zeroed sync region of the
 // workspace; data exchanged with agent-coherent stores and loads):
@@ -106,9 +106,12 @@ template <int HD, int GQ, int GD>
 __global__ __launch_bounds__(kStepWaves * 64) void step_m1_kernel(StepArgs sa) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int NW = kStepWaves;
-  constexpr int UQ = 16;  // gate/up: deep ring (the prefetch spans the barrier)
+  // Shallow rings (4 atoms per wave): a wave's loads complete in order, so
+  // every atom in flight when a stage waits for its producers delays that
+  // wave's x loads behind it; deeper rings measured slower at every stage.
+  constexpr int UQ = 4;                                  // gate/up
   constexpr int UO = GQ == 0 ? 8 : (GQ > 4 ? GQ : 4);  // O: one strip per workgroup
-  constexpr int UD = 16;
+  constexpr int UD = 4;
   const int tid = threadIdx.x;
   const int wg = blockIdx.x, nwg = gridDim.x;
 
@@ -122,7 +125,7 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_m1_kernel(StepArgs sa) {
     int s0, ns;
     strip_range(pa.Np / kStrip, wg, nwg, s0, ns);
     if (ns > 0) {
-      gemv_body<EPI_QKV, NW, 8, GQ, true>(pa, pl, s0, ns, smem, NoWait());
+      gemv_body<EPI_QKV, NW, 4, GQ, true>(pa, pl, s0, ns, smem, NoWait());
       stores_done();
       if (tid == 0)
         for (int t = s0; t < s0 + ns; ++t)
