@@ -38,8 +38,9 @@
 namespace i4d {
 
 __device__ __forceinline__ float wave_max(float v) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, shfl_xor(v, o));
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, lane_xor(v, o, lane));
   return v;
 }
 
@@ -63,10 +64,10 @@ __device__ void append_vector(const KvArgs& kv, const uint16_t* src, int64_t reg
   // FWHT, stages h = 1 .. 32 across lanes, then h = 64 inside the lane
 #pragma unroll
   for (int h = 1; h < 64 && h < HD; h <<= 1) {
-    const float p0 = shfl_xor(x0, h);
+    const float p0 = lane_xor(x0, h, lane);
     x0 = (lane & h) ? (p0 - x0) : (x0 + p0);
     if (HD == 128) {
-      const float p1 = shfl_xor(x1, h);
+      const float p1 = lane_xor(x1, h, lane);
       x1 = (lane & h) ? (p1 - x1) : (x1 + p1);
     }
   }
@@ -194,10 +195,10 @@ template <int HD>
 __device__ __forceinline__ void inverse_rotate(float& o0, float& o1, int lane) {
 #pragma unroll
   for (int h = 1; h < 64 && h < HD; h <<= 1) {
-    const float p0 = shfl_xor(o0, h);
+    const float p0 = lane_xor(o0, h, lane);
     o0 = (lane & h) ? (p0 - o0) : (o0 + p0);
     if (HD == 128) {
-      const float p1 = shfl_xor(o1, h);
+      const float p1 = lane_xor(o1, h, lane);
       o1 = (lane & h) ? (p1 - o1) : (o1 + p1);
     }
   }
@@ -239,10 +240,10 @@ template <int HD>
 __device__ __forceinline__ void fwht_wave(float& x0, float& x1, int lane) {
 #pragma unroll
   for (int h = 1; h < 64 && h < HD; h <<= 1) {
-    const float p0 = shfl_xor(x0, h);
+    const float p0 = lane_xor(x0, h, lane);
     x0 = (lane & h) ? (p0 - x0) : (x0 + p0);
     if (HD == 128) {
-      const float p1 = shfl_xor(x1, h);
+      const float p1 = lane_xor(x1, h, lane);
       x1 = (lane & h) ? (p1 - x1) : (x1 + p1);
     }
   }
@@ -259,9 +260,16 @@ __device__ __forceinline__ void fwht_wave(float& x0, float& x1, int lane) {
 // [NWA][8][HD] (the rotated queries [8][HD] alias wo before the merge).
 // COH: the query, the new key/value and the partials are exchanged with
 // other workgroups of the same launch (agent-coherent loads and stores).
+// Row metadata of a unit read ahead of time (the one-launch step reads it
+// at its start, so that the read is not on the attention critical path).
+struct RowMeta {
+  int64_t base, cap;
+  int L;
+};
+
 template <int HD, int NWA, bool COH, typename Wait>
 __device__ __forceinline__ void attn_body(const AttnArgs& a, const int m, const int j, const int s, float* lds,
-                          Wait&& wait_input) {
+                                          Wait&& wait_input, const RowMeta* meta = nullptr) {
   constexpr int KB = HD / 32;  // 32-channel MFMA steps for q.k
   constexpr int CB = HD / 16;  // 16-channel output blocks
   constexpr int GMAX = 8;
@@ -275,12 +283,12 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int m, const 
   const int c = lane & 15, jj = lane >> 4;
   const int S = a.S, G = a.G;
 
-  const int64_t base = kv.row_base[m];
-  const int64_t cap = kv.row_base[m + 1] - base;
+  const int64_t base = meta ? meta->base : kv.row_base[m];
+  const int64_t cap = meta ? meta->cap : kv.row_base[m + 1] - base;
   // the splits partition [0, S bps) blocks (sized for the longest row): a
   // shorter row leaves its last splits empty
   const int bps = a.bps;
-  int L = a.ctx_len[m];
+  int L = meta ? meta->L : a.ctx_len[m];
   const bool len_ok = L >= 1 && L <= cap && L <= S * bps * kVBlock;
   if (!len_ok) {
     if (tid == 0 && kv.err_word) atomicOr(kv.err_word, I4D_DEVERR_CTX_LEN);
@@ -360,8 +368,8 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int m, const 
         cq = fmaf((float)op, slot16(e) ? 128.f : 8.f, cq);
       }
     }
-    cq += shfl_xor(cq, 16);
-    cq += shfl_xor(cq, 32);
+    cq += lane_xor(cq, 16, lane);
+    cq += lane_xor(cq, 32, lane);
   }
   if (defer || defer2) {
     // the CU's L1 may hold lines of this block from before the append
@@ -408,8 +416,8 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int m, const 
     }
     if (!LAST) load_keys<HD>(cur, kbase, ksc, nb, c, jj);
     mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-    mx = fmaxf(mx, shfl_xor(mx, 16));
-    mx = fmaxf(mx, shfl_xor(mx, 32));
+    mx = fmaxf(mx, lane_xor(mx, 16, lane));
+    mx = fmaxf(mx, lane_xor(mx, 32, lane));
     const float m_new = fmaxf(m_run, mx);  // finite: the block holds a valid token
     // rescale only when some column's running maximum moved (alpha = 1
     // exactly elsewhere)
@@ -459,10 +467,10 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int m, const 
 
   // per-column totals over the 4 lane quarters; undo the 2^-24 operand
   // scale and remove the code offset: o = 2^24 acc - 8 * sum p'
-  l_run += shfl_xor(l_run, 16);
-  l_run += shfl_xor(l_run, 32);
-  psum += shfl_xor(psum, 16);
-  psum += shfl_xor(psum, 32);
+  l_run += lane_xor(l_run, 16, lane);
+  l_run += lane_xor(l_run, 32, lane);
+  psum += lane_xor(psum, 16, lane);
+  psum += lane_xor(psum, 32, lane);
   const float vbias = 8.f * psum;
   if (c < G) {
     if (jj == 0) {
@@ -564,7 +572,7 @@ __device__ __forceinline__ void combine_head(const AttnArgs& a, size_t head_row,
     }
   }
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) lsum += shfl_xor(lsum, off);
+  for (int off = 32; off >= 1; off >>= 1) lsum += lane_xor(lsum, off, lane);
   lsum_out = lsum;
   o0_out = o0;
   o1_out = o1;

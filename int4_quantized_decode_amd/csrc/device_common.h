@@ -77,6 +77,30 @@ __device__ __forceinline__ T shfl_xor(T v, int m) {
   return __shfl_xor(v, m, 64);
 }
 
+// v of lane (lane ^ m) for m = 1, 2, 4, 8, 16, 32 (a compile-time constant
+// after unrolling) without the LDS crossbar: DPP quad permutations for
+// 1 and 2, a half-row mirror then a quad reversal for 4 (7 ^ 3), a row
+// rotation by 8 for 8, and the gfx950 row-pair / half-wave swaps for 16
+// and 32.  Same values as shfl_xor, so a butterfly built on it adds in the
+// same order.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane_xor(float v, int m, int lane) {
+  if (m == 1) return dpp_f32<0xB1>(v);                  // quad_perm [1,0,3,2]
+  if (m == 2) return dpp_f32<0x4E>(v);                  // quad_perm [2,3,0,1]
+  if (m == 4) return dpp_f32<0x1B>(dpp_f32<0x141>(v));  // row_half_mirror, quad_perm [3,2,1,0]
+  if (m == 8) return dpp_f32<0x128>(v);                 // row_ror:8
+  const unsigned u = __float_as_uint(v);
+  if (m == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return __uint_as_float((lane & 16) ? r[0] : r[1]);
+  }
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float((lane & 32) ? r[0] : r[1]);
+}
+
 __device__ __forceinline__ u32x4_t load16(const void* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
 }

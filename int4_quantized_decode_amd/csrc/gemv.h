@@ -287,8 +287,8 @@ __device__ __forceinline__ void gemv_body(const ProjArgs& a, const GemvPlan& pl,
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
-    sq += shfl_xor(sq, o);
-    mx = fmaxf(mx, shfl_xor(mx, o));
+    sq += lane_xor(sq, o, lane);
+    mx = fmaxf(mx, lane_xor(mx, o, lane));
   }
   if (lane == 0) {
     ssq[wave] = sq;
@@ -333,8 +333,8 @@ __device__ __forceinline__ void gemv_body(const ProjArgs& a, const GemvPlan& pl,
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) xr[gi][kb] = xl[(128 * g + 32 * kb + 8 * j) / 8];
       float q = quarter_sum(xr[gi]);
-      q += shfl_xor(q, 16);
-      q += shfl_xor(q, 32);
+      q += lane_xor(q, 16, lane);
+      q += lane_xor(q, 32, lane);
       xc[gi] = q * kOffset;
     }
   } else {

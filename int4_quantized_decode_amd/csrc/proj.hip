@@ -368,8 +368,8 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void proj_skinny_kernel(ProjArgs
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       float v = sq[t];
-      v += shfl_xor(v, 16);
-      v += shfl_xor(v, 32);
+      v += lane_xor(v, 16, lane);
+      v += lane_xor(v, 32, lane);
       if (j == 0) sqw[wave * T * 16 + t * 16 + r] = v;
     }
   }

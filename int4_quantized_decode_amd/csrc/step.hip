@@ -114,6 +114,12 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_m1_kernel(StepArgs sa) {
   constexpr int UD = 4;
   const int tid = threadIdx.x;
   const int wg = blockIdx.x, nwg = gridDim.x;
+  // the attention units' row metadata (one row), read now so that its
+  // latency overlaps the QKV stage
+  RowMeta meta;
+  meta.base = sa.at.kv.row_base[0];
+  meta.cap = sa.at.kv.row_base[1] - meta.base;
+  meta.L = sa.at.ctx_len[0];
 
   // ---- 1. QKV
   {
@@ -150,7 +156,7 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_m1_kernel(StepArgs sa) {
           flag_error(sync, err_word);
         lds_barrier();
       };
-      attn_body<HD, NW, true>(at, 0, j, s, reinterpret_cast<float*>(smem), wait_qkv);
+      attn_body<HD, NW, true>(at, 0, j, s, reinterpret_cast<float*>(smem), wait_qkv, &meta);
       stores_done();
       if (Sf > 1) {
         __shared__ int last;
