@@ -161,10 +161,9 @@ __device__ __forceinline__ float quarter_sum(const u32x4_t (&xk)[4]) {
 // reads x from LDS for every atom.
 //
 // The body serves the stand-alone kernel and the one-launch decode step
-// (COH = true): there the weight ring is issued first, then `wait_input`
-// blocks until the producers of x are done (the last wave polls, from lane
-// 0, and issues its own ring after the wait), then x is read
-// agent-coherently and the outputs are stored the same way.  `strip0`, `ns`: the strips of
+// (COH = true): there `wait_input` blocks until the producers of x are done
+// (the last wave polls, from lane 0), then x is read agent-coherently, then
+// the ring is requested; the outputs are stored agent-coherently.  `strip0`, `ns`: the strips of
 // this workgroup (ns <= pl.SP).
 template <int EPI, int NW, int U, int GPW, bool COH, typename Wait>
 __device__ __forceinline__ void gemv_body(const ProjArgs& a, const GemvPlan& pl, const int strip0,
@@ -255,20 +254,18 @@ __device__ __forceinline__ void gemv_body(const ProjArgs& a, const GemvPlan& pl,
     ring[k] = load16_stream(cp);
     sring[k] = *sp;
   };
-  // In the one-launch step the last wave waits for the producers (its
-  // polls must not queue behind atom loads of its own: a wave's loads
-  // complete in order), so it issues its first atoms after the wait.
-  if (X_FIRST || wave != NW - 1) {
+  // In the one-launch step the atoms are requested only after the wait and
+  // the x loads: a wave's loads complete in order, so atoms requested
+  // before would delay the polls and x behind them (measured slower).
+  if (X_FIRST) {
 #pragma unroll
     for (int k = 0; k < U; ++k) fill(k);
   }
   if (!X_FIRST) {
     wait_input();
-    if (wave == NW - 1) {
-#pragma unroll
-      for (int k = 0; k < U; ++k) fill(k);
-    }
     load_x();
+#pragma unroll
+    for (int k = 0; k < U; ++k) fill(k);
   }
 
   // 3. row statistics: sum of squares (rho) and max |x| (the fp16 scale)

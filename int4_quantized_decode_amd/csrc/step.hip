@@ -6,9 +6,10 @@
 // all of the previous one.  As separate kernels each boundary costs a
 // launch (about 1.8 us here), the drain of the previous stage and the first
 // load latency of the next.  Here one workgroup of 8 waves per CU runs all
-// stages; a stage's weight stream does not depend on the activations, so
-// each workgroup requests the first atoms of a stage (a few per wave)
-// before it waits for the previous stage.
+// stages.  A stage's weights do not depend on the activations, yet they are
+// requested only after the wait for the previous stage and the x loads: a
+// wave's loads complete in order, and weight loads ahead of a poll or of x
+// measured slower than the latency they would hide.
 //
 // Stages and hand-offs (counters in the zeroed sync region of the
 // workspace; data exchanged with agent-coherent stores and loads):
