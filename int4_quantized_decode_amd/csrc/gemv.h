@@ -126,11 +126,11 @@ struct GemvPlan {
   int NW, SP, GPW;
 };
 
-// LDS: x [K] fp16 | group offset terms [G] | partials [SP][NW][16] | tile [SP*16]
-// | per-wave sums of squares [NW] | per-wave max |x| [NW]
+// LDS: x [K] fp16 (GPW == 0) | per group (offset term, 2^-shift) [G] |
+// partials [SP][NW][16] | tile [SP*16] | per-wave sums of squares [NW]
 inline size_t gemv_lds_bytes(int K, const GemvPlan& p) {
-  return (size_t)K * 2 + (size_t)(K / kGroup) * 4 + (size_t)p.SP * p.NW * 16 * 4 +
-         (size_t)p.SP * 16 * 4 + (size_t)p.NW * 8;
+  return (size_t)K * 2 + (size_t)(K / kGroup) * 8 + (size_t)p.SP * p.NW * 16 * 4 +
+         (size_t)p.SP * 16 * 4 + (size_t)p.NW * 4;
 }
 
 // sum of the x values that 16 fp16 words of one group quarter represent
@@ -153,12 +153,14 @@ __device__ __forceinline__ float quarter_sum(const u32x4_t (&xk)[4]) {
 // U with repeats of its last atom (L2 hits, no HBM traffic), so every round
 // issues exactly U loads and the compiler can wait on exact counts.
 //
-// x is staged once per workgroup as fp16 scaled by a power of two sigma
-// (max |x| sigma in [2^12, 2^13), so the conversion from bf16 is exact for
-// every value above 2^-23 of the row maximum) and by 1/16 at the positions
-// paired with the high nibble of a byte.  With GPW > 0 (compile time, a
-// divisor of U) each wave keeps its GPW groups of x in registers; GPW == 0
-// reads x from LDS for every atom.
+// x enters the MFMA as fp16, per 128-group g scaled by a power of two
+// (max |x_g| 2^sh_g in [2^12, 2^13), so the conversion from bf16 is exact
+// for every value above 2^-23 of the group maximum) and by 1/16 at the
+// positions paired with the high nibble of a byte; the group's scale comes
+// from a reduction over the 16 lanes that stage it, so one workgroup
+// barrier separates the x loads from the stream.  With GPW > 0 (compile
+// time, a divisor of U) each wave then keeps its GPW groups of x in
+// registers; GPW == 0 reads x from LDS for every atom.
 //
 // The body serves the stand-alone kernel and the one-launch decode step
 // (COH = true): there `wait_input` blocks until the producers of x are done
@@ -172,11 +174,10 @@ __device__ __forceinline__ void gemv_body(const ProjArgs& a, const GemvPlan& pl,
   const int SP = pl.SP;
   const int GW = GPW > 0 ? GPW : pl.GPW;
   uint16_t* xs = reinterpret_cast<uint16_t*>(smem);                  // [K] fp16
-  float* Xs = reinterpret_cast<float*>(smem + (size_t)K * 2);        // [G]
-  float* red = Xs + G;                                               // [SP][NW][16]
+  float2* Xs = reinterpret_cast<float2*>(smem + (size_t)K * 2);      // [G]
+  float* red = reinterpret_cast<float*>(Xs + G);                     // [SP][NW][16]
   float* ot = red + (size_t)SP * NW * 16;                            // [SP*16]
   float* ssq = ot + SP * 16;                                         // [NW]
-  float* wmx = ssq + NW;                                             // [NW]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
@@ -191,9 +192,8 @@ __device__ __forceinline__ void gemv_body(const ProjArgs& a, const GemvPlan& pl,
 
   // 1. x: the loads of this thread's 16-byte chunks (clamped, so every
   // thread issues the same number of loads).  Stand-alone: issued first, so
-  // that every wave's x enters the memory pipeline before any weight load
-  // (otherwise the x of the last waves queues behind the first waves'
-  // atoms).  One-launch step: issued after the producers are done.
+  // that every wave's x enters the memory pipeline before any weight load.
+  // One-launch step: issued after the producers are done.
   constexpr int XMAX = 4;  // K <= XMAX * 8 * NW * 64 (host-checked)
   const int xn = (K / 8 + NW * 64 - 1) / (NW * 64);  // chunks per thread (uniform)
   u32x4_t xv[XMAX];
@@ -268,85 +268,87 @@ __device__ __forceinline__ void gemv_body(const ProjArgs& a, const GemvPlan& pl,
     for (int k = 0; k < U; ++k) fill(k);
   }
 
-  // 3. row statistics: sum of squares (rho) and max |x| (the fp16 scale)
-  float sq = 0.f, mx = 0.f;
+  // 3. fp16 x per group g, scaled by a power of two 2^sh_g (max|x_g| 2^sh_g
+  // in [2^12, 2^13), so bf16 -> fp16 is exact for every value above 2^-23
+  // of the group maximum) and by 1/16 at e in {2,3,6,7}; the group result
+  // is scaled back by 2^-sh_g.  Per group: the code offset term
+  // -8 * 2^-24 * (sum of the group's x) * 2^-sh_g and 2^-sh_g.  Also the
+  // sum of squares of x (rho).
+  constexpr float kOffset = -8.0f / 16777216.0f;
+  auto group_scale = [](float mx, float& sigma, float& unscale) {
+    int ex = 0;
+    if (mx > 0.f) frexpf(mx, &ex);
+    const int sh = max(-100, min(100, 13 - ex));
+    sigma = ldexpf(1.0f, sh);
+    unscale = ldexpf(1.0f, -sh);
+  };
+  auto to_f16 = [](const u32x4_t v, float sigma) {
+    u32x4_t o;
 #pragma unroll
-  for (int q = 0; q < XMAX; ++q) {
-    if (q < xn && tid + q * NW * 64 < K / 8) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float lo = bf16_lo(xv[q][e]), hi = bf16_hi(xv[q][e]);
-        sq = fmaf(lo, lo, sq);
-        sq = fmaf(hi, hi, sq);
-        mx = fmaxf(mx, fmaxf(fabsf(lo), fabsf(hi)));
-      }
+    for (int e = 0; e < 4; ++e) {
+      const float f = (e & 1) ? sigma * 0.0625f : sigma;
+      const f16x2_t h = {(_Float16)(bf16_lo(v[e]) * f), (_Float16)(bf16_hi(v[e]) * f)};
+      o[e] = bitcast<uint32_t>(h);
     }
-  }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    sq += lane_xor(sq, o, lane);
-    mx = fmaxf(mx, lane_xor(mx, o, lane));
-  }
-  if (lane == 0) {
-    ssq[wave] = sq;
-    wmx[wave] = mx;
-  }
-  lds_barrier();
-  float xm = 0.f;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) xm = fmaxf(xm, wmx[w]);
-  int ex = 0;
-  if (xm > 0.f) frexpf(xm, &ex);
-  const int sh = max(-100, min(100, 13 - ex));
-  const float sigma = ldexpf(1.0f, sh);
-
-  // 4. stage x as fp16 (x sigma, / 16 at e in {2,3,6,7})
-#pragma unroll
-  for (int q = 0; q < XMAX; ++q) {
-    const int cidx = tid + q * NW * 64;
-    if (q < xn && cidx < K / 8) {
-      u32x4_t o;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float f = (e & 1) ? sigma * 0.0625f : sigma;
-        const f16x2_t h = {(_Float16)(bf16_lo(xv[q][e]) * f), (_Float16)(bf16_hi(xv[q][e]) * f)};
-        o[e] = bitcast<uint32_t>(h);
-      }
-      reinterpret_cast<u32x4_t*>(xs)[cidx] = o;
-    }
-  }
-  lds_barrier();
-
-  // 5. x of the wave's groups (registers) or for every group (LDS), and
-  // the code offset term -8 * 2^-24 * (sum of the group's x)
+    return o;
+  };
   const u32x4_t* xl = reinterpret_cast<const u32x4_t*>(xs);
   u32x4_t xr[GR][4];
-  float xc[GR];
-  constexpr float kOffset = -8.0f / 16777216.0f;
+  float xc[GR], xf[GR];
+  float sq = 0.f;
+  {
+    // chunk c (16 per group) sits in lane c % 16 of a 16-lane row, so the
+    // group's maximum and sum are row reductions
+#pragma unroll
+    for (int q = 0; q < XMAX; ++q) {
+      const int cidx = tid + q * NW * 64;
+      if (q < xn) {
+        const bool valid = cidx < K / 8;  // whole groups: K is a multiple of 128
+        float mx = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float lo = bf16_lo(xv[q][e]), hi = bf16_hi(xv[q][e]);
+          if (valid) {
+            sq = fmaf(lo, lo, sq);
+            sq = fmaf(hi, hi, sq);
+          }
+          mx = fmaxf(mx, fmaxf(fabsf(lo), fabsf(hi)));
+        }
+#pragma unroll
+        for (int o = 8; o >= 1; o >>= 1) mx = fmaxf(mx, lane_xor(mx, o, lane));
+        float sigma, unscale;
+        group_scale(mx, sigma, unscale);
+        const u32x4_t h = to_f16(xv[q], sigma);
+        const f16x2_t one = {(_Float16)1.0f, (_Float16)1.0f};
+        const f16x2_t sixteen = {(_Float16)16.0f, (_Float16)16.0f};
+        float cs = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          cs = __builtin_amdgcn_fdot2(bitcast<f16x2_t>(h[e]), (e & 1) ? sixteen : one, cs, false);
+#pragma unroll
+        for (int o = 8; o >= 1; o >>= 1) cs += lane_xor(cs, o, lane);
+        if (valid) {
+          reinterpret_cast<u32x4_t*>(xs)[cidx] = h;
+          if ((lane & 15) == 0) Xs[cidx >> 4] = make_float2(cs * kOffset * unscale, unscale);
+        }
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) sq += lane_xor(sq, o, lane);
+    if (lane == 0) ssq[wave] = sq;
+    lds_barrier();
+  }
+  // the wave's own groups of x in registers
   if (GPW > 0) {
 #pragma unroll
     for (int gi = 0; gi < GR; ++gi) {
       const int g = min(g0 + gi, G - 1);
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) xr[gi][kb] = xl[(128 * g + 32 * kb + 8 * j) / 8];
-      float q = quarter_sum(xr[gi]);
-      q += lane_xor(q, 16, lane);
-      q += lane_xor(q, 32, lane);
-      xc[gi] = q * kOffset;
+      const float2 t = Xs[g];
+      xc[gi] = t.x;
+      xf[gi] = t.y;
     }
-  } else {
-    for (int g = tid; g < G; g += NW * 64) {
-      float q = 0.f;
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        u32x4_t xk[4];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) xk[kb] = xl[(128 * g + 32 * kb + 8 * jj) / 8];
-        q += quarter_sum(xk);
-      }
-      Xs[g] = q * kOffset;
-    }
-    lds_barrier();
   }
 
   // 6. stream: consume atom i from the ring, then refill its slot with atom
@@ -354,29 +356,35 @@ __device__ __forceinline__ void gemv_body(const ProjArgs& a, const GemvPlan& pl,
   // atom, four MFMAs 16x16x32 with x in every row of A (lane (r, j) holds
   // the same x quarter j for any r) and the decoded codes as B (column r =
   // atom row r): every lane gets the whole 128-term dot of its row r,
-  // scaled by 2^-24; the code offset enters as the group constant xc.
+  // scaled by 2^-24 and by the group's 2^sh; the code offset and 2^-sh
+  // enter as one FMA per atom.
   float part = 0.f;
   int sl = 0, gi_rt = 0;  // strip and group of the atom being consumed (GPW == 0)
   auto consume = [&](const u32x4_t w, const uint16_t sbits, int i, int k) {
     if (i < n) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-      float c;
       if (GPW > 0) {
         const int gi = k % GR;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
           acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(bitcast<f16x8_t>(xr[gi][kb]), dword_to_f16x8_sub(w[kb]),
                                                        acc, 0, 0, 0);
-        c = xc[gi];
       } else {
         const int g = g0 + gi_rt;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
           acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(bitcast<f16x8_t>(xl[(128 * g + 32 * kb + 8 * j) / 8]),
                                                        dword_to_f16x8_sub(w[kb]), acc, 0, 0, 0);
-        c = Xs[g];
       }
-      part = fmaf(f16_bits_to_f32(sbits), acc[0] + c, part);
+      float y;
+      if (GPW > 0) {
+        const int gi = k % GR;
+        y = fmaf(acc[0], xf[gi], xc[gi]);
+      } else {
+        const float2 t = Xs[g0 + gi_rt];
+        y = fmaf(acc[0], t.y, t.x);
+      }
+      part = fmaf(f16_bits_to_f32(sbits), y, part);
       const bool last_of_strip = (GPW > 0) ? (k % GR == GR - 1) : (gi_rt == gpw - 1);
       if (last_of_strip) {
         if (j == 0) red[((size_t)sl * NW + wave) * 16 + r] = part;
@@ -401,13 +409,13 @@ __device__ __forceinline__ void gemv_body(const ProjArgs& a, const GemvPlan& pl,
     for (int s2 = sl; s2 < ns; ++s2) red[((size_t)s2 * NW + wave) * 16 + r] = 0.f;
   lds_barrier();
 
-  // 7. reduce over the waves and the four lane quarters; undo sigma; epilogue
+  // 7. reduce over the waves; undo the 2^-24 of the code operand; epilogue
   if (tid < ns * 16) {
     const int s2 = tid >> 4, rr = tid & 15;
     float v = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) v += red[((size_t)s2 * NW + w) * 16 + rr];
-    ot[tid] = v * ldexpf(1.0f, 24 - sh);
+    ot[tid] = v * 16777216.0f;
   }
   if (needs_rho<EPI>() && tid == 0) {
     float t = 0.f;
