@@ -39,8 +39,8 @@ STEP_M1_SOURCES = ("step.hip", "step.h", "gemv.h", "attn_core.h", "attn.h", "coh
                    "proj.h", "i4d_internal.h", "i4d_layout.h", "api_device.hip", "api_host.cpp")
 TRAFFIC = {
     "8b_m1_ctx4096": {"kernel": "step_m1_kernel (one-launch decode step)", "sources": STEP_M1_SOURCES,
-                      "sha256": "99d3d9e4b4b7e20914ed7d08328fb800e5ca0baf535178d532a2aa02106923f2",
-                      "fetch_bytes": 118889472, "write_bytes": 751104},
+                      "sha256": "c3fe965a44a2d9c43205656e650d2d2a5249c8dfc31515c4a1f937130c513ff0",
+                      "fetch_bytes": 118785664, "write_bytes": 751104},
 }
 
 
