@@ -53,3 +53,13 @@ def test_70b_layer_ctx4096(gpu, layer70, M):
     lengths = synth.make_lengths(wl, M)
     check_block(run_block(gpu, wl.shape, wl.seed, lengths, dense_cache=dense, lw=lw, memo=memo),
                 f"{wl.name} M={M}")
+
+
+def test_8b_layer_m1_ctx32768_16_splits(gpu):
+    """One layer of the full-model workload (8B shape, context 32768, 16 KV
+    splits: the split count bench.py's full-model run passes), through the
+    one-launch step."""
+    wl = synth.WORKLOADS["8b_32layer_ctx32768"]
+    lengths = synth.make_lengths(wl)
+    assert int(lengths[0]) == 32768 and wl.num_splits == 16
+    check_block(run_block(gpu, wl.shape, wl.seed, lengths, num_splits=wl.num_splits), "8b_ctx32768 S=16")
