@@ -165,9 +165,10 @@ __device__ __forceinline__ float quarter_sum(const u32x4_t (&xk)[4]) {
 // The body serves the stand-alone kernel and the one-launch decode step
 // (COH = true): there `wait_input` blocks until the producers of x are done
 // (the last wave polls, from lane 0), then x is read agent-coherently, then
-// the ring is requested; the outputs are stored agent-coherently.  `strip0`, `ns`: the strips of
-// this workgroup (ns <= pl.SP).
-template <int EPI, int NW, int U, int GPW, bool COH, typename Wait>
+// the ring is requested (with PRE: before the wait, for a wait long enough
+// to cover the atoms' latency); the outputs are stored agent-coherently.
+// `strip0`, `ns`: the strips of this workgroup (ns <= pl.SP).
+template <int EPI, int NW, int U, int GPW, bool COH, bool PRE = false, typename Wait>
 __device__ __forceinline__ void gemv_body(const ProjArgs& a, const GemvPlan& pl, const int strip0,
                                           const int ns, unsigned char* smem, Wait&& wait_input) {
   const int K = a.K, G = a.G;
@@ -262,10 +263,16 @@ __device__ __forceinline__ void gemv_body(const ProjArgs& a, const GemvPlan& pl,
     for (int k = 0; k < U; ++k) fill(k);
   }
   if (!X_FIRST) {
+    if (PRE) {
+#pragma unroll
+      for (int k = 0; k < U; ++k) fill(k);
+    }
     wait_input();
     load_x();
+    if (!PRE) {
 #pragma unroll
-    for (int k = 0; k < U; ++k) fill(k);
+      for (int k = 0; k < U; ++k) fill(k);
+    }
   }
 
   // 3. fp16 x per group g, scaled by a power of two 2^sh_g (max|x_g| 2^sh_g

@@ -6,10 +6,12 @@
 // all of the previous one.  As separate kernels each boundary costs a
 // launch (about 1.8 us here), the drain of the previous stage and the first
 // load latency of the next.  Here one workgroup of 8 waves per CU runs all
-// stages.  A stage's weights do not depend on the activations, yet they are
-// requested only after the wait for the previous stage and the x loads: a
-// wave's loads complete in order, and weight loads ahead of a poll or of x
-// measured slower than the latency they would hide.
+// stages.  A stage's weights do not depend on the activations, yet QKV's
+// follow x and those of O and gate/up are requested only after the wait for
+// the previous stage and the x loads: a wave's loads complete in order, and
+// weight loads ahead of a short wait or of x measured slower than the
+// latency they would hide.  The down stage waits longest (a grid barrier
+// behind the gate/up stream) and requests its first atoms before it.
 //
 // Stages and hand-offs (counters in the zeroed sync region of the
 // workspace; data exchanged with agent-coherent stores and loads):
@@ -234,7 +236,12 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_m1_kernel(StepArgs sa) {
       lds_barrier();
     };
     __syncthreads();
-    if (ns > 0) gemv_body<EPI_DOWN, NW, UD, GD, true>(pa, pl, s0, ns, smem, wait_gu);
+    // the first ring of atoms is requested before the barrier: gate/up
+    // strips finish over about 2 us and every poll of the barrier is a
+    // round trip of about 1 us behind the gate/up stream, so the atoms have
+    // arrived when the wait ends (on the O and gate/up stages the same
+    // measured slower: their waits are short)
+    if (ns > 0) gemv_body<EPI_DOWN, NW, UD, GD, true, true>(pa, pl, s0, ns, smem, wait_gu);
   }
 
   // ---- exit: the last workgroup clears the counters for the next launch
