@@ -34,15 +34,42 @@ __device__ __forceinline__ void st_out(uint16_t* p, uint16_t v) {
   if (COH) st_coh(p, v); else *p = v;
 }
 
+// RoPE, rotate-half pair (c0, c0 + hd/2) at position pos: angle pos *
+// theta^(-2 c0 / hd) in fp64 (the frequency as (theta^(-2/hd))^c0 by binary
+// powering of the host's fp64 ratio), reduced to [-pi, pi], then fp32 sin/cos
+__device__ __forceinline__ void rope_angle(double ratio, int pos, int c0, float& cs, float& sn) {
+  double freq = 1.0, base = ratio;
+  for (int e = c0; e; e >>= 1) {
+    if (e & 1) freq *= base;
+    base *= base;
+  }
+  const double ang = (double)pos * freq;
+  const double k2pi = rint(ang * 0.15915494309189535);
+  double red = fma(-k2pi, 6.283185307179586, ang);
+  red = fma(-k2pi, 2.4492935982947064e-16, red);
+  sincosf((float)red, &sn, &cs);
+}
+
+// Inputs of the epilogue that do not depend on the weight stream, for the
+// thread's first output (idx = threadIdx.x): the residual of O and down, the
+// RoPE rotation of QKV.  The M = 1 kernel reads or computes them ahead of
+// the stream, so that their latency is not added after it.
+struct EpiPre {
+  float res, cs, sn;
+  bool valid;
+};
+
 // Epilogue from the LDS tile ot[row][M] (rows of strips strip0 .. strip0+S-1).
 // COH: outputs consumed inside the same launch are stored agent-coherently
 // and the in-launch residual (h, down projection) is loaded the same way.
 template <int EPI, bool COH = false>
-__device__ void run_epilogue(const ProjArgs& a, int strip0, int S, const float* ot, const float* rho) {
+__device__ void run_epilogue(const ProjArgs& a, int strip0, int S, const float* ot, const float* rho,
+                             const EpiPre* pre = nullptr) {
   const int M = a.M;
   const int nthreads = blockDim.x;
   if (EPI == EPI_QKV || EPI == EPI_GU) {
     for (int idx = threadIdx.x; idx < S * 8 * M; idx += nthreads) {
+      const bool use_pre = pre && pre->valid && idx == (int)threadIdx.x;
       const int m = idx % M, pi = idx / M, s = pi / 8, i = pi % 8;
       const int t = strip0 + s;
       if (t * kStrip >= a.Np) continue;
@@ -57,22 +84,13 @@ __device__ void run_epilogue(const ProjArgs& a, int strip0, int S, const float* 
         const int head = t / per_head, sp = t % per_head;
         const int c0 = 8 * sp + i, c1 = c0 + a.hd / 2;
         if (head < a.n_q + a.n_kv) {
-          // RoPE, rotate-half pair (c0, c0 + hd/2) at position ctx_len - 1:
-          // angle pos * theta^(-2 c0 / hd) in fp64 (the frequency as
-          // (theta^(-2/hd))^c0 by binary powering of the host's fp64 ratio),
-          // reduced to [-pi, pi], then fp32 sin/cos
-          const double pos = (double)(a.ctx_len[m] - 1);
-          double freq = 1.0, base = a.rope_ratio;
-          for (int e = c0; e; e >>= 1) {
-            if (e & 1) freq *= base;
-            base *= base;
-          }
-          const double ang = pos * freq;
-          const double k2pi = rint(ang * 0.15915494309189535);
-          double red = fma(-k2pi, 6.283185307179586, ang);
-          red = fma(-k2pi, 2.4492935982947064e-16, red);
           float sn_f, c;
-          sincosf((float)red, &sn_f, &c);
+          if (use_pre) {
+            c = pre->cs;
+            sn_f = pre->sn;
+          } else {
+            rope_angle(a.rope_ratio, a.ctx_len[m] - 1, c0, c, sn_f);
+          }
           const float r0 = y0 * c - y1 * sn_f;
           const float r1 = y1 * c + y0 * sn_f;
           y0 = r0;
@@ -95,23 +113,23 @@ __device__ void run_epilogue(const ProjArgs& a, int strip0, int S, const float* 
     }
   } else {
     for (int idx = threadIdx.x; idx < S * 16 * M; idx += nthreads) {
+      const bool use_pre = pre && pre->valid && idx == (int)threadIdx.x;
       const int m = idx % M, row = idx / M;
       const int n = strip0 * kStrip + row;
       if (n >= a.Np) continue;
       const float y = ot[row * M + m];
       const size_t o = (size_t)m * a.Np + n;
       if (EPI == EPI_O) {
-        const float h = bf16_to_f32(a.resid_bf16[o]) + y;
+        const float h = (use_pre ? pre->res : bf16_to_f32(a.resid_bf16[o])) + y;
         st_out<COH>(&a.h_f32[o], h);
         st_out<COH>(&a.h_bf16[o], f32_to_bf16(h));
       } else {
-        const float res = COH ? ld_coh(&a.resid_f32[o]) : a.resid_f32[o];
+        const float res = use_pre ? pre->res : (COH ? ld_coh(&a.resid_f32[o]) : a.resid_f32[o]);
         a.out_bf16[o] = f32_to_bf16(res + y);
       }
     }
   }
 }
-
 
 // Workgroup barrier that waits for LDS traffic only: weight loads stay in
 // flight across it (__syncthreads would also drain every outstanding global
@@ -208,8 +226,27 @@ __device__ __forceinline__ void gemv_body(const ProjArgs& a, const GemvPlan& pl,
     }
   };
   constexpr bool X_FIRST = !COH || std::is_same<std::decay_t<Wait>, NoWait>::value;
+  // the epilogue's inputs of this thread's output (M = 1: output tid),
+  // requested behind x: the residual, or the position for RoPE
+  EpiPre pre = {0.f, 1.f, 0.f, false};
+  int rope_pos = 0;
+  auto load_pre = [&]() {
+    if (a.M != 1) return;
+    if (EPI == EPI_O || EPI == EPI_DOWN) {
+      const int n = strip0 * kStrip + tid;
+      if (tid < ns * kStrip && n < a.Np) {
+        if (EPI == EPI_O) pre.res = bf16_to_f32(a.resid_bf16[n]);
+        else pre.res = COH ? ld_coh(&a.resid_f32[n]) : a.resid_f32[n];
+        pre.valid = true;
+      }
+    } else if (EPI == EPI_QKV && tid < ns * 8) {
+      rope_pos = a.ctx_len[0] - 1;
+      pre.valid = true;
+    }
+  };
   if (X_FIRST) {
     load_x();
+    load_pre();
     lds_barrier();
   }
 
@@ -269,6 +306,7 @@ __device__ __forceinline__ void gemv_body(const ProjArgs& a, const GemvPlan& pl,
     }
     wait_input();
     load_x();
+    load_pre();
     if (!PRE) {
 #pragma unroll
       for (int k = 0; k < U; ++k) fill(k);
@@ -357,6 +395,13 @@ __device__ __forceinline__ void gemv_body(const ProjArgs& a, const GemvPlan& pl,
       xf[gi] = t.y;
     }
   }
+  // RoPE rotation of this thread's output pair while the atoms are in flight
+  if (EPI == EPI_QKV && pre.valid) {
+    const int t = strip0 + tid / 8, i = tid % 8;
+    const int per_head = a.hd / kStrip;
+    const int head = t / per_head, sp = t % per_head;
+    if (t < nstrips && head < a.n_q + a.n_kv) rope_angle(a.rope_ratio, rope_pos, 8 * sp + i, pre.cs, pre.sn);
+  }
 
   // 6. stream: consume atom i from the ring, then refill its slot with atom
   // i + U (the loaded registers stay in place across iterations).  Per
@@ -431,7 +476,7 @@ __device__ __forceinline__ void gemv_body(const ProjArgs& a, const GemvPlan& pl,
   }
   lds_barrier();
   float one = 1.0f;
-  run_epilogue<EPI, COH>(a, strip0, ns, ot, needs_rho<EPI>() ? &ssq[0] : &one);
+  run_epilogue<EPI, COH>(a, strip0, ns, ot, needs_rho<EPI>() ? &ssq[0] : &one, &pre);
 }
 
 }  // namespace i4d

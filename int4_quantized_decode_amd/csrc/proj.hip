@@ -137,7 +137,6 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void proj_skinny_kernel(ProjArgs
   auto group_of_t = [&](const Tile& g, int gi) {
     return g.gs0 + min(wave + NW * min(gi, max(g.gpw - 1, 0)), g.Gs - 1);
   };
-  auto group_of = [&](int gi) { return group_of_t(cur, gi); };
 
   // ring of atoms: slot d * SP + s holds strip s of a group gi with
   // gi % D == d
@@ -233,7 +232,6 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void proj_skinny_kernel(ProjArgs
   // tile's atom of this slot
   auto do_group = [&](auto refill, const u32x4_t (&bxg)[T][4], const int gi, const int d, const Tile& nx) {
     const bool valid = gi < gpw;
-    const int g = group_of(gi);
     // X[t] = -136 * (column sums of x): the accumulator start of every atom
     f32x4_t X[T];
 #pragma unroll
