@@ -36,7 +36,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
 
 template <int HD, int NWA>
 __global__ __launch_bounds__(NWA * 64) void attn_kernel(AttnArgs a) {
-  __shared__ float lds[2 * NWA * 8 + NWA * 8 * HD];
+  __shared__ float lds[attn_lds_floats<HD, NWA>()];
   const int S = a.S;
   const int s = blockIdx.x % S;
   const int rest = blockIdx.x / S;

@@ -256,8 +256,8 @@ __device__ __forceinline__ void fwht_wave(float& x0, float& x1, int lane) {
 
 // One (row m, kv head j, split s) unit by one workgroup of NWA waves taking
 // interleaved 32-token blocks of the split.  `wait_input` runs after the
-// first cache loads are issued and before the query is read.  LDS: wm, wl [NWA][8], wo
-// [NWA][8][HD] (the rotated queries [8][HD] alias wo before the merge).
+// first cache loads are issued and before the query is read.  LDS: wm, wl
+// [NWA][8], wo [NWA][8][HD], then the query operand (attn_lds_floats).
 // COH: the query, the new key/value and the partials are exchanged with
 // other workgroups of the same launch (agent-coherent loads and stores).
 // Row metadata of a unit read ahead of time (the one-launch step reads it
@@ -266,6 +266,13 @@ struct RowMeta {
   int64_t base, cap;
   int L;
 };
+
+// LDS of attn_body in floats: wm, wl [NWA][8], wo [NWA][8][HD], the query
+// operand halves [2][8][HD] fp16 and their sums [8][2]
+template <int HD, int NWA>
+__host__ __device__ constexpr int attn_lds_floats() {
+  return 2 * NWA * 8 + NWA * 8 * HD + 8 * HD + 16;
+}
 
 template <int HD, int NWA, bool COH, typename Wait>
 __device__ __forceinline__ void attn_body(const AttnArgs& a, const int m, const int j, const int s, float* lds,
@@ -276,7 +283,12 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int m, const 
   float (*wm)[GMAX] = reinterpret_cast<float (*)[GMAX]>(lds);
   float (*wl)[GMAX] = reinterpret_cast<float (*)[GMAX]>(lds + NWA * GMAX);
   float (*wo)[GMAX][HD] = reinterpret_cast<float (*)[GMAX][HD]>(lds + 2 * NWA * GMAX);
-  float (*qrot)[HD] = wo[0];  // rotated queries [GMAX][HD], before the merge
+  // the rotated queries as the fp16 operand of q.k: high and low halves
+  // [GMAX][HD] each, and per (head, half) 8 * the sum of the values the
+  // half represents
+  uint16_t (*qh)[HD] = reinterpret_cast<uint16_t (*)[HD]>(lds + 2 * NWA * GMAX + NWA * GMAX * HD);
+  uint16_t (*ql)[HD] = qh + GMAX;
+  float (*cqs)[2] = reinterpret_cast<float (*)[2]>(ql + GMAX);
 
   const KvArgs& kv = a.kv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -327,14 +339,38 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int m, const 
   // same launch: wait for them only now
   wait_input();
 
-  // rotate the G query heads of this kv head (one wave per head) into LDS
+  // rotate the G query heads of this kv head (one wave per head) and store
+  // them as the partner operand of q.k: channel ch as w = q (1/16 at ch % 8
+  // in {2,3,6,7}, the slots paired with a high nibble) split into the fp16
+  // high part fp16(w) and the low part fp16(w - high); per half the sum of
+  // 8 (128 at the 1/16 slots) times its values (the code offset term)
   for (int g = wave; g < G; g += NWA) {
     const float* src = a.q + ((size_t)m * a.n_q + (size_t)j * G + g) * HD;
     float x0 = COH ? ld_coh(&src[lane]) : src[lane];
     float x1 = (HD == 128) ? (COH ? ld_coh(&src[lane + 64]) : src[lane + 64]) : 0.f;
     fwht_wave<HD>(x0, x1, lane);
-    qrot[g][lane] = x0;
-    if (HD == 128) qrot[g][lane + 64] = x1;
+    float sh = 0.f, sl = 0.f;
+    auto put = [&](const float x, const int ch) {
+      const bool s16 = slot16(ch & 7);
+      const float w = s16 ? x * 0.0625f : x;
+      const _Float16 hi = (_Float16)w;
+      const _Float16 lo = (_Float16)(w - (float)hi);
+      qh[g][ch] = bitcast<uint16_t>(hi);
+      ql[g][ch] = bitcast<uint16_t>(lo);
+      sh = fmaf((float)hi, s16 ? 128.f : 8.f, sh);
+      sl = fmaf((float)lo, s16 ? 128.f : 8.f, sl);
+    };
+    put(x0, lane);
+    if (HD == 128) put(x1, lane + 64);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      sh += lane_xor(sh, off, lane);
+      sl += lane_xor(sl, off, lane);
+    }
+    if (lane == 0) {
+      cqs[g][0] = sh;
+      cqs[g][1] = sl;
+    }
   }
   if (appending && wave < 2) {
     const uint16_t* src = (wave ? a.v_new : a.k_new) + ((size_t)m * kv.n_kv + j) * HD;
@@ -344,32 +380,21 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int m, const 
 
   // Rotated query as the partner operand of q.k: columns c < 8 hold the
   // high fp16 part of query head j*G + c (c < G), columns 8 + c the low part
-  // (the residual), with the factor 1/16 at e in {2,3,6,7}.  Each lane also
-  // keeps cq = 8 * sum of the query values its operand represents.
+  // (the residual).  cq: the code offset term of column c.
   f16x8_t qop[KB];
-  float cq = 0.f;
+  float cq;
   {
     const int head = c & 7;
     const bool active = head < G;
-    const bool lo_part = c >= 8;
+    const uint16_t* qsrc = (c >= 8 ? ql : qh)[head];
+    const f16x8_t zero = {};
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      float qv[8];
-      const float4* src = reinterpret_cast<const float4*>(&qrot[head][32 * kb + 8 * jj]);
-      const float4 v0 = src[0], v1 = src[1];
-      qv[0] = v0.x; qv[1] = v0.y; qv[2] = v0.z; qv[3] = v0.w;
-      qv[4] = v1.x; qv[5] = v1.y; qv[6] = v1.z; qv[7] = v1.w;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float w = active ? (slot16(e) ? qv[e] * 0.0625f : qv[e]) : 0.f;
-        const _Float16 hi = (_Float16)w;
-        const _Float16 op = lo_part ? (_Float16)(w - (float)hi) : hi;
-        qop[kb][e] = op;
-        cq = fmaf((float)op, slot16(e) ? 128.f : 8.f, cq);
-      }
+      const f16x8_t v = *reinterpret_cast<const f16x8_t*>(&qsrc[32 * kb + 8 * jj]);
+      qop[kb] = active ? v : zero;
     }
-    cq += lane_xor(cq, 16, lane);
-    cq += lane_xor(cq, 32, lane);
+    const float t = cqs[head][c >= 8 ? 1 : 0];
+    cq = active ? t : 0.f;
   }
   if (defer || defer2) {
     // the CU's L1 may hold lines of this block from before the append
@@ -377,7 +402,6 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int m, const 
     if (defer) load_block<HD>(cur, kbase, vbase, ksc, vsc, blk, c, jj);
     if (defer2) load_block<HD>(nxt, kbase, vbase, ksc, vsc, blk + NWA, c, jj);
   }
-  __syncthreads();  // qrot shares LDS with the merge buffers
 
   float m_run = -INFINITY, l_run = 0.f, psum = 0.f;
   f32x4_t o[CB];
@@ -484,18 +508,28 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int m, const 
   }
   __syncthreads();
 
-  // wave w merges heads w, w + NWA, ... over the waves
+  // wave w merges heads w, w + NWA, ... over the waves (every LDS read of
+  // the merge issued at once; a wave without tokens has sum 0)
   for (int g = wave; g < G; g += NWA) {
-    float M_ = -INFINITY;
-    for (int w = 0; w < NWA; ++w)
-      if (wl[w][g] > 0.f) M_ = fmaxf(M_, wm[w][g]);
-    float lsum = 0.f, o0 = 0.f, o1 = 0.f;
+    float mw[NWA], lw[NWA], p0[NWA], p1[NWA];
+#pragma unroll
     for (int w = 0; w < NWA; ++w) {
-      if (wl[w][g] > 0.f) {
-        const float f = exp2f(wm[w][g] - M_);
-        lsum += f * wl[w][g];
-        o0 += f * wo[w][g][lane];
-        if (HD == 128) o1 += f * wo[w][g][lane + 64];
+      mw[w] = wm[w][g];
+      lw[w] = wl[w][g];
+      p0[w] = wo[w][g][lane];
+      p1[w] = (HD == 128) ? wo[w][g][lane + 64] : 0.f;
+    }
+    float M_ = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NWA; ++w) M_ = lw[w] > 0.f ? fmaxf(M_, mw[w]) : M_;
+    float lsum = 0.f, o0 = 0.f, o1 = 0.f;
+#pragma unroll
+    for (int w = 0; w < NWA; ++w) {
+      if (lw[w] > 0.f) {
+        const float f = exp2f(mw[w] - M_);
+        lsum += f * lw[w];
+        o0 += f * p0[w];
+        o1 += f * p1[w];
       }
     }
     const size_t head_row = (size_t)m * a.n_q + (size_t)j * G + g;

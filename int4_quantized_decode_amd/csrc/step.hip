@@ -307,7 +307,9 @@ hipError_t dispatch_launch(int gq, int gd, const StepArgs& sa, int nwg, size_t l
   return hipErrorInvalidValue;
 }
 
-size_t attn_lds_bytes(int hd) { return (size_t)(2 * kStepWaves * 8 + kStepWaves * 8 * hd) * 4; }
+size_t attn_lds_bytes(int hd) {
+  return (size_t)(hd == 128 ? attn_lds_floats<128, kStepWaves>() : attn_lds_floats<64, kStepWaves>()) * 4;
+}
 
 }  // namespace
 
