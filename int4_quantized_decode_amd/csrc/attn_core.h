@@ -55,10 +55,17 @@ __device__ __forceinline__ uint16_t f32_to_f16_sat(float f) {
 // append of one vector by one wave
 // ---------------------------------------------------------------------------
 
-// region = first slot of (row, head); pos < capacity; kind 0 = key, 1 = value
+// region = first slot of (row, head); pos < capacity; kind 0 = key, 1 = value.
+// With `nt` the codes and the scale are also written to LDS (NewToken).
+struct NewToken {
+  uint32_t kw[32];  // the key's cache words (HD / 8 of them)
+  uint8_t v[128];   // the value's codes, one per channel
+  uint16_t ks, vs;  // fp16 scales
+};
+
 template <int HD, bool COH = false>
 __device__ void append_vector(const KvArgs& kv, const uint16_t* src, int64_t region, int pos,
-                              int kind, int lane) {
+                              int kind, int lane, NewToken* nt = nullptr) {
   float x0 = bf16_to_f32(COH ? ld_coh(&src[lane]) : src[lane]);
   float x1 = (HD == 128) ? bf16_to_f32(COH ? ld_coh(&src[lane + 64]) : src[lane + 64]) : 0.f;
   // FWHT, stages h = 1 .. 32 across lanes, then h = 64 inside the lane
@@ -99,6 +106,10 @@ __device__ void append_vector(const KvArgs& kv, const uint16_t* src, int64_t reg
     }
     if (d < HD / 8) reinterpret_cast<uint32_t*>(kv.k_codes + (size_t)slot * (HD / 2))[d] = word;
     if (lane == 0) kv.k_scales[slot] = s16;
+    if (nt) {
+      if (d < HD / 8) nt->kw[d] = word;
+      if (lane == 0) nt->ks = s16;
+    }
   } else {
     // value block: token w of the block sits in slot group jj, slot e
     const int w = pos % kVBlock;
@@ -112,8 +123,10 @@ __device__ void append_vector(const KvArgs& kv, const uint16_t* src, int64_t reg
       uint32_t* dw = blk + jj * HD + (c % 16) * (HD / 16) + c / 16;
       atomicAnd(dw, ~(0xFu << sh));
       atomicOr(dw, (uint32_t)(q ? u1 : u0) << sh);
+      if (nt) nt->v[c] = (uint8_t)(q ? u1 : u0);
     }
     if (lane == 0) kv.v_scales[slot] = s16;
+    if (nt && lane == 0) nt->vs = s16;
   }
 }
 
@@ -183,6 +196,42 @@ __device__ __forceinline__ void load_block(BlockRegs<HD>& b, const uint8_t* kbas
                                            int jj) {
   load_keys<HD>(b, kbase, ksc, blk, c, jj);
   load_values<HD>(b, vbase, vsc, blk, c, jj);
+}
+
+// Put token w (0..31) of a block, read before that token was appended, into
+// the block's registers from the append's LDS copy: the key words sit in
+// the 16-lane row c == w % 16 of tile w / 16; the value nibble and both
+// scales in the lanes of quarter jj == (w % 16) / 4.
+template <int HD>
+__device__ __forceinline__ void patch_new_token(BlockRegs<HD>& b, const NewToken& nt, int w, int c, int jj) {
+  constexpr int KB = HD / 32, CB = HD / 16;
+  const int tile = w / 16, tc = w % 16;
+  if (c == tc) {
+    uint32_t kw[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) kw[kb] = nt.kw[jj * KB + kb];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) b.kw[t][kb] = (t == tile) ? kw[kb] : b.kw[t][kb];
+  }
+  if (jj == tc / 4) {
+    const int i = tc % 4;
+    const int sh = 4 * nibble_slot(i + 4 * tile);
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+      b.vw[cb] = (b.vw[cb] & ~(0xFu << sh)) | ((uint32_t)nt.v[16 * cb + c] << sh);
+    const uint32_t hs = 16u * (i & 1);
+    const uint32_t keep = ~(0xFFFFu << hs);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        if (t == tile && q == (i >> 1)) {
+          b.ks[t][q] = (b.ks[t][q] & keep) | ((uint32_t)nt.ks << hs);
+          b.vs[t][q] = (b.vs[t][q] & keep) | ((uint32_t)nt.vs << hs);
+        }
+  }
 }
 
 __device__ __forceinline__ float f16_half(const u32x2_t& w, int i) {
@@ -268,10 +317,10 @@ struct RowMeta {
 };
 
 // LDS of attn_body in floats: wm, wl [NWA][8], wo [NWA][8][HD], the query
-// operand halves [2][8][HD] fp16 and their sums [8][2]
+// operand halves [2][8][HD] fp16 and their sums [8][2], the appended token
 template <int HD, int NWA>
 __host__ __device__ constexpr int attn_lds_floats() {
-  return 2 * NWA * 8 + NWA * 8 * HD + 8 * HD + 16;
+  return 2 * NWA * 8 + NWA * 8 * HD + 8 * HD + 16 + (int)(sizeof(NewToken) + 3) / 4;
 }
 
 template <int HD, int NWA, bool COH, typename Wait>
@@ -289,6 +338,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int m, const 
   uint16_t (*qh)[HD] = reinterpret_cast<uint16_t (*)[HD]>(lds + 2 * NWA * GMAX + NWA * GMAX * HD);
   uint16_t (*ql)[HD] = qh + GMAX;
   float (*cqs)[2] = reinterpret_cast<float (*)[2]>(ql + GMAX);
+  NewToken* nt = reinterpret_cast<NewToken*>(cqs + GMAX);
 
   const KvArgs& kv = a.kv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -321,8 +371,8 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int m, const 
 
   // In a decode step the split holding position L-1 first appends the new
   // key/value there.  Cache reads do not depend on the query, so every wave
-  // starts loading its first block now, except a load of the block being
-  // appended to, which waits for the append.
+  // starts loading its first block now; the block being appended to is
+  // read before the append and the new token put into its registers after.
   const int last_blk = (L - 1) / kVBlock;
   const bool appending = a.k_new && len_ok && last_blk >= b0 && last_blk < b1;
   // Stand-alone: two blocks per wave in flight (its first two, then two
@@ -330,11 +380,9 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int m, const 
   // about one block per wave: one in flight.
   constexpr bool TWO = !COH;
   int blk = b0 + wave;
-  const bool defer = appending && blk == last_blk;
-  const bool defer2 = TWO && appending && blk + NWA == last_blk;
   BlockRegs<HD> cur, nxt;
-  if (!defer) load_block<HD>(cur, kbase, vbase, ksc, vsc, min(blk, last_valid), c, jj);
-  if (TWO && !defer2) load_block<HD>(nxt, kbase, vbase, ksc, vsc, min(blk + NWA, last_valid), c, jj);
+  load_block<HD>(cur, kbase, vbase, ksc, vsc, min(blk, last_valid), c, jj);
+  if (TWO) load_block<HD>(nxt, kbase, vbase, ksc, vsc, min(blk + NWA, last_valid), c, jj);
   // the query and the new key/value may come from other workgroups of the
   // same launch: wait for them only now
   wait_input();
@@ -372,11 +420,16 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int m, const 
       cqs[g][1] = sl;
     }
   }
-  if (appending && wave < 2) {
-    const uint16_t* src = (wave ? a.v_new : a.k_new) + ((size_t)m * kv.n_kv + j) * HD;
-    append_vector<HD, COH>(kv, src, region, L - 1, wave, lane);
+  // the append by two waves that rotate no query head, where there are two
+  const int aw = (G + 2 <= NWA) ? G : 0;
+  if (appending && wave >= aw && wave < aw + 2) {
+    const uint16_t* src = (wave - aw ? a.v_new : a.k_new) + ((size_t)m * kv.n_kv + j) * HD;
+    append_vector<HD, COH>(kv, src, region, L - 1, wave - aw, lane, nt);
+    // the new codes are in memory before a later block read of this
+    // workgroup (stand-alone: a split with more blocks than waves)
+    wait_vmem();
   }
-  __syncthreads();
+  lds_barrier();
 
   // Rotated query as the partner operand of q.k: columns c < 8 hold the
   // high fp16 part of query head j*G + c (c < G), columns 8 + c the low part
@@ -396,11 +449,10 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int m, const 
     const float t = cqs[head][c >= 8 ? 1 : 0];
     cq = active ? t : 0.f;
   }
-  if (defer || defer2) {
-    // the CU's L1 may hold lines of this block from before the append
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    if (defer) load_block<HD>(cur, kbase, vbase, ksc, vsc, blk, c, jj);
-    if (defer2) load_block<HD>(nxt, kbase, vbase, ksc, vsc, blk + NWA, c, jj);
+  if (appending) {
+    const int w = (L - 1) % kVBlock;
+    if (blk == last_blk) patch_new_token<HD>(cur, *nt, w, c, jj);
+    if (TWO && blk + NWA == last_blk) patch_new_token<HD>(nxt, *nt, w, c, jj);
   }
 
   float m_run = -INFINITY, l_run = 0.f, psum = 0.f;

@@ -101,6 +101,13 @@ __device__ __forceinline__ float lane_xor(float v, int m, int lane) {
   return __uint_as_float((lane & 32) ? r[0] : r[1]);
 }
 
+// Workgroup barrier that waits for LDS traffic only: global loads stay in
+// flight across it (__syncthreads would also drain every outstanding global
+// load of the wave).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ u32x4_t load16(const void* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
 }

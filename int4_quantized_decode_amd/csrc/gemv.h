@@ -131,13 +131,6 @@ __device__ void run_epilogue(const ProjArgs& a, int strip0, int S, const float* 
   }
 }
 
-// Workgroup barrier that waits for LDS traffic only: weight loads stay in
-// flight across it (__syncthreads would also drain every outstanding global
-// load of the wave).
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
 // Launch shape of the M = 1 kernel: NW waves, SP strips per workgroup, GPW
 // = G / NW groups per wave (the K range is split across the waves).
 struct GemvPlan {
@@ -317,8 +310,8 @@ __device__ __forceinline__ void gemv_body(const ProjArgs& a, const GemvPlan& pl,
   // in [2^12, 2^13), so bf16 -> fp16 is exact for every value above 2^-23
   // of the group maximum) and by 1/16 at e in {2,3,6,7}; the group result
   // is scaled back by 2^-sh_g.  Per group: the code offset term
-  // -8 * 2^-24 * (sum of the group's x) * 2^-sh_g and 2^-sh_g.  Also the
-  // sum of squares of x (rho).
+  // -8 * 2^-24 * (sum of the group's x) * 2^-sh_g and 2^-sh_g.  For QKV and
+  // gate/up also the sum of squares of x (rho).
   constexpr float kOffset = -8.0f / 16777216.0f;
   auto group_scale = [](float mx, float& sigma, float& unscale) {
     int ex = 0;
@@ -353,7 +346,7 @@ __device__ __forceinline__ void gemv_body(const ProjArgs& a, const GemvPlan& pl,
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float lo = bf16_lo(xv[q][e]), hi = bf16_hi(xv[q][e]);
-          if (valid) {
+          if (needs_rho<EPI>() && valid) {
             sq = fmaf(lo, lo, sq);
             sq = fmaf(hi, hi, sq);
           }
@@ -378,9 +371,11 @@ __device__ __forceinline__ void gemv_body(const ProjArgs& a, const GemvPlan& pl,
         }
       }
     }
+    if (needs_rho<EPI>()) {
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) sq += lane_xor(sq, o, lane);
-    if (lane == 0) ssq[wave] = sq;
+      for (int o = 32; o >= 1; o >>= 1) sq += lane_xor(sq, o, lane);
+      if (lane == 0) ssq[wave] = sq;
+    }
     lds_barrier();
   }
   // the wave's own groups of x in registers
