@@ -387,9 +387,15 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int m, const 
   // same launch: wait for them only now
   wait_input();
 
+  // The score scale enters q.k in two parts: qs in [1, 2) with the query
+  // and the power of two unq = score_scale / qs after the product.
+  int sk = 0;
+  const float qs = 2.0f * frexpf(a.score_scale, &sk);
+  const float unq = ldexpf(1.0f, sk - 1);
   // rotate the G query heads of this kv head (one wave per head) and store
-  // them as the partner operand of q.k: channel ch as w = q (1/16 at ch % 8
-  // in {2,3,6,7}, the slots paired with a high nibble) split into the fp16
+  // them as the partner operand of q.k: channel ch as w = q * qs (and 1/16
+  // at ch % 8 in {2,3,6,7}, the slots paired with a high nibble) split into
+  // the fp16
   // high part fp16(w) and the low part fp16(w - high); per half the sum of
   // 8 (128 at the 1/16 slots) times its values (the code offset term)
   for (int g = wave; g < G; g += NWA) {
@@ -400,7 +406,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int m, const 
     float sh = 0.f, sl = 0.f;
     auto put = [&](const float x, const int ch) {
       const bool s16 = slot16(ch & 7);
-      const float w = s16 ? x * 0.0625f : x;
+      const float w = x * (s16 ? qs * 0.0625f : qs);
       const _Float16 hi = (_Float16)w;
       const _Float16 lo = (_Float16)(w - (float)hi);
       qh[g][ch] = bitcast<uint16_t>(hi);
@@ -433,7 +439,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int m, const 
 
   // Rotated query as the partner operand of q.k: columns c < 8 hold the
   // high fp16 part of query head j*G + c (c < G), columns 8 + c the low part
-  // (the residual).  cq: the code offset term of column c.
+  // (the residual).  cq: the code offset term of column c, times unq.
   f16x8_t qop[KB];
   float cq;
   {
@@ -447,7 +453,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int m, const 
       qop[kb] = active ? v : zero;
     }
     const float t = cqs[head][c >= 8 ? 1 : 0];
-    cq = active ? t : 0.f;
+    cq = active ? t * unq : 0.f;
   }
   if (appending) {
     const int w = (L - 1) % kVBlock;
@@ -455,11 +461,17 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int m, const 
     if (TWO && blk + NWA == last_blk) patch_new_token<HD>(nxt, *nt, w, c, jj);
   }
 
-  float m_run = -INFINITY, l_run = 0.f, psum = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  // per column c, the sum of the fp16 p' values (times 16 at the slots
+  // paired with a high nibble) over the tokens so far: one MFMA per block
+  // with a constant partner operand, so every row holds the column total
+  f32x4_t psv = {0.f, 0.f, 0.f, 0.f};
+  const float accf = kTwo24 * unq;  // undo the 2^-24 of the code operand and qs
+  const _Float16 h1 = (_Float16)1.0f, h16 = (_Float16)16.0f;
+  const f16x8_t pones = {h1, h1, h16, h16, h1, h1, h16, h16};
   f32x4_t o[CB];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) o[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const float sscale = a.score_scale;
 
   // Blocks in registers (cur, and nxt when two are in flight): once a
   // block's keys are consumed, the keys of the wave's block one (two) ahead
@@ -483,9 +495,9 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int m, const 
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         // high part (column c) + low part (column c + 8, rotated in by DPP)
-        const float part = fmaf(acc[i], kTwo24, -cq);
+        const float part = fmaf(acc[i], accf, -cq);
         const float full = part + dpp_row_ror8(part);
-        float v = full * (f16_half(cur.ks[tile], i) * sscale);
+        float v = full * f16_half(cur.ks[tile], i);
         if (LAST) v = (t0 + 16 * tile + 4 * jj + i < L) ? v : -INFINITY;
         sc[tile * 4 + i] = v;
       }
@@ -500,7 +512,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int m, const 
     if (__any(m_new > m_run)) {
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
-      psum *= alpha;
+      psv *= alpha;
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) o[cb] *= alpha;
     }
@@ -516,8 +528,8 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int m, const 
       if (LAST) pv = (p > 0.f) ? pv : 0.f;
       const _Float16 ph = (_Float16)pv;
       pb[e] = ph;
-      psum = fmaf((float)ph, slot16(e) ? 16.f : 1.f, psum);
     }
+    psv = __builtin_amdgcn_mfma_f32_16x16x32_f16(pones, pb, psv, 0, 0, 0);
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
       o[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dword_to_f16x8_sub(cur.vw[cb]), pb, o[cb], 0, 0, 0);
@@ -545,9 +557,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int m, const 
   // scale and remove the code offset: o = 2^24 acc - 8 * sum p'
   l_run += lane_xor(l_run, 16, lane);
   l_run += lane_xor(l_run, 32, lane);
-  psum += lane_xor(psum, 16, lane);
-  psum += lane_xor(psum, 32, lane);
-  const float vbias = 8.f * psum;
+  const float vbias = 8.f * psv[0];
   if (c < G) {
     if (jj == 0) {
       wm[wave][c] = m_run;
