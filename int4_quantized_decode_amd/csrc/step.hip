@@ -7,11 +7,12 @@
 // launch (about 1.8 us here), the drain of the previous stage and the first
 // load latency of the next.  Here one workgroup of 8 waves per CU runs all
 // stages.  A stage's weights do not depend on the activations, yet QKV's
-// follow x and those of O and gate/up are requested only after the wait for
-// the previous stage and the x loads: a wave's loads complete in order, and
+// follow x and those of gate/up are requested only after the wait for the
+// previous stage and the x loads: a wave's loads complete in order, and
 // weight loads ahead of a short wait or of x measured slower than the
-// latency they would hide.  The down stage waits longest (a grid barrier
-// behind the gate/up stream) and requests its first atoms before it.
+// latency they would hide.  O (behind the attention chain) and down (behind
+// a grid barrier after the gate/up stream) wait long enough: they request
+// their first atoms before the wait.
 //
 // Stages and hand-offs (counters in the zeroed sync region of the
 // workspace; data exchanged with agent-coherent stores and loads):
@@ -198,7 +199,9 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_m1_kernel(StepArgs sa) {
       lds_barrier();
     };
     __syncthreads();
-    if (ns > 0) gemv_body<EPI_O, NW, UO, GQ, true>(pa, pl, s0, ns, smem, wait_attn);
+    // the first ring of atoms (with one strip per workgroup, the whole O
+    // stream) is requested before the wait for the attention heads
+    if (ns > 0) gemv_body<EPI_O, NW, UO, GQ, true, true>(pa, pl, s0, ns, smem, wait_attn);
     stores_done();
     if (tid == 0) bar_arrive(&sync[kSyncBar1], wg);
   }
@@ -239,8 +242,8 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_m1_kernel(StepArgs sa) {
     // the first ring of atoms is requested before the barrier: gate/up
     // strips finish over about 2 us and every poll of the barrier is a
     // round trip of about 1 us behind the gate/up stream, so the atoms have
-    // arrived when the wait ends (on the O and gate/up stages the same
-    // measured slower: their waits are short)
+    // arrived when the wait ends (on the gate/up stage the same measured
+    // slower: its wait is short)
     if (ns > 0) gemv_body<EPI_DOWN, NW, UD, GD, true, true>(pa, pl, s0, ns, smem, wait_gu);
   }
 
