@@ -431,9 +431,9 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int m, const 
   if (appending && wave >= aw && wave < aw + 2) {
     const uint16_t* src = (wave - aw ? a.v_new : a.k_new) + ((size_t)m * kv.n_kv + j) * HD;
     append_vector<HD, COH>(kv, src, region, L - 1, wave - aw, lane, nt);
-    // the new codes are in memory before a later block read of this
-    // workgroup (stand-alone: a split with more blocks than waves)
-    wait_vmem();
+    // the new codes are in memory before a block read of this workgroup
+    // after the first (two) per wave, if one of those is the block appended to
+    if (last_blk >= b0 + (TWO ? 2 : 1) * NWA) wait_vmem();
   }
   lds_barrier();
 
