@@ -39,8 +39,8 @@ STEP_M1_SOURCES = ("step.hip", "step.h", "gemv.h", "attn_core.h", "attn.h", "coh
                    "proj.h", "i4d_internal.h", "i4d_layout.h", "api_device.hip", "api_host.cpp")
 TRAFFIC = {
     "8b_m1_ctx4096": {"kernel": "step_m1_kernel (one-launch decode step)", "sources": STEP_M1_SOURCES,
-                      "sha256": "c3fe965a44a2d9c43205656e650d2d2a5249c8dfc31515c4a1f937130c513ff0",
-                      "fetch_bytes": 118785664, "write_bytes": 751104},
+                      "sha256": "4687191358f8464c13f4ba0491241ae18ebd7b54043e7ad103f4e5eac814ae99",
+                      "fetch_bytes": 118782464, "write_bytes": 751104},
 }
 
 
