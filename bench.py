@@ -39,7 +39,7 @@ STEP_M1_SOURCES = ("step.hip", "step.h", "gemv.h", "attn_core.h", "attn.h", "coh
                    "proj.h", "i4d_internal.h", "i4d_layout.h", "api_device.hip", "api_host.cpp")
 TRAFFIC = {
     "8b_m1_ctx4096": {"kernel": "step_m1_kernel (one-launch decode step)", "sources": STEP_M1_SOURCES,
-                      "sha256": "4687191358f8464c13f4ba0491241ae18ebd7b54043e7ad103f4e5eac814ae99",
+                      "sha256": "9fe6b2d6a380d63dc30fae692c0bd1408e8129fcb103c2bc272f5cf2c2058978",
                       "fetch_bytes": 118782464, "write_bytes": 751104},
 }
 

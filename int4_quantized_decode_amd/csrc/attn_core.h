@@ -395,9 +395,9 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int m, const 
   // rotate the G query heads of this kv head (one wave per head) and store
   // them as the partner operand of q.k: channel ch as w = q * qs (and 1/16
   // at ch % 8 in {2,3,6,7}, the slots paired with a high nibble) split into
-  // the fp16
-  // high part fp16(w) and the low part fp16(w - high); per half the sum of
-  // 8 (128 at the 1/16 slots) times its values (the code offset term)
+  // the fp16 high part fp16(w) and the low part fp16(w - high); per half
+  // the sum of 8 (128 at the 1/16 slots) times its values (the code offset
+  // term)
   for (int g = wave; g < G; g += NWA) {
     const float* src = a.q + ((size_t)m * a.n_q + (size_t)j * G + g) * HD;
     float x0 = COH ? ld_coh(&src[lane]) : src[lane];
