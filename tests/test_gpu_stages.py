@@ -302,15 +302,19 @@ def test_block_small(gpu, shape, lengths):
     check_block(run_block(gpu, shape, 11, lengths))
 
 
+@pytest.mark.parametrize("shape", [synth.SHAPE_SMALL128, synth.SHAPE_TINY], ids=["hd128", "hd64"])
 @pytest.mark.parametrize("lengths", [
     [500, 300, 270, 200, 33],   # one split, 8 waves: new token in a wave's first or second block
     [200, 150, 129],            # one split, 4 waves: the same with the second block
+    [1100, 620, 47],            # one split: the block appended to is read later in the loop
 ])
-def test_block_append_in_prefetched_block(gpu, lengths):
-    """The attention kernel requests a wave's first two blocks before the
-    step's new key and value are appended; a block that will hold them is
-    requested only after the append."""
-    check_block(run_block(gpu, synth.SHAPE_SMALL128, 17, lengths, num_splits=1))
+def test_block_append_in_prefetched_block(gpu, shape, lengths):
+    """The attention kernel reads a wave's first two blocks before the
+    step's new key and value are appended; the new token's codes and scales
+    are then put into the registers of the block that holds them (key words
+    in tile 0 or 1, value nibble and both scales), or, for a block read
+    later, the append is complete before that read."""
+    check_block(run_block(gpu, shape, 17, lengths, num_splits=1))
 
 
 def test_block_dirty_workspace_forced_splits(gpu):
