@@ -129,6 +129,20 @@ i4d_status i4d_pack_weights(i4d_proj_kind kind, const float* W0, const float* W1
                             const float* gamma, int N, int K, int head_dim,
                             void* codes_out, uint16_t* scales_out, int threads);
 
+/* Pre-quantized import: the layout permutation alone, for codes and scales
+ * that another quantizer produced in the same INT4 format (the summary page
+ * [P1], "premises and limits", sets round-to-nearest codes beside GPTQ
+ * codes of one per-128-group fp16 scale format).  q [rows][K] int8 in
+ * [-8, 7] and s [rows][K/128] fp16 bits, rows as for i4d_unpack_weights
+ * (N, or 2N for GATE_UP: gate rows then up rows), go into the device layout
+ * exactly as i4d_pack_weights places its own codes, so
+ * i4d_pack_codes(i4d_unpack_weights(x)) == x.  Nothing is re-quantized: a
+ * norm gain must already be folded into the codes.  I4D_ERR_RANGE for a
+ * code outside [-8, 7] or a non-finite scale, checked before any output is
+ * written.  Host memory; up to `threads` CPU threads (0 = all). */
+i4d_status i4d_pack_codes(i4d_proj_kind kind, const int8_t* q, const uint16_t* s, int N, int K,
+                          int head_dim, void* codes_out, uint16_t* scales_out, int threads);
+
 /* Inverse of the layout permutation: logical codes q_out [rows][K] in
  * [-8, 7] and scales s_out [rows][K/128] (fp16 bits), with rows = N
  * (PLAIN, QKV, original row order) or 2N (GATE_UP: gate rows then up rows).

@@ -71,6 +71,7 @@ _SIGS = {
     "i4d_packed_sizes": (_I, [_I, _I, _I, _I, c_size_p, c_size_p]),
     "i4d_pack_weights": (_I, [_I, _VP, _VP, _VP, _I, _I, _I, _VP, _VP, _I]),
     "i4d_unpack_weights": (_I, [_I, _VP, _VP, _I, _I, _I, _VP, _VP]),
+    "i4d_pack_codes": (_I, [_I, _VP, _VP, _I, _I, _I, _VP, _VP, _I]),
     "i4d_pack_lm_head": (_I, [_VP, _VP, _I, _I, _VP, _I]),
     "i4d_kv_cache_bytes": (_I, [_I, _I, ctypes.c_int64, c_size_p, c_size_p, c_size_p, c_size_p]),
     "i4d_kv_append": (_I, [ctypes.POINTER(i4d_kv_cache), _VP, _VP, _VP, _VP, _I, _VP]),
@@ -179,6 +180,22 @@ def i4d_pack_weights(kind: int, W0, W1=None, gamma=None, head_dim: int = 0, thre
     scales = np.empty(sb // 2, np.uint16)
     _check(lib().i4d_pack_weights(kind, ptr(W0), ptr(W1), ptr(gamma), N, K, head_dim,
                                   ptr(codes), ptr(scales), threads))
+    return codes, scales
+
+
+def i4d_pack_codes(kind: int, q, s, N: int, K: int, head_dim: int = 0, threads: int = 0):
+    """Pre-quantized codes q [rows][K] int8 in [-8, 7] and fp16 scale bits
+    s [rows][K/128] (rows = N, or 2N for gate/up: gate rows then up rows)
+    -> (codes uint8, scales uint16) in the device layout."""
+    rows = 2 * N if kind == I4D_PROJ_GATE_UP else N
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    s = np.ascontiguousarray(s, dtype=np.uint16)
+    if q.shape != (rows, K) or s.shape != (rows, K // 128):
+        raise ValueError(f"q {q.shape} / s {s.shape}: expected ({rows}, {K}) / ({rows}, {K // 128})")
+    cb, sb = i4d_packed_sizes(kind, N, K, head_dim)
+    codes = np.empty(cb, np.uint8)
+    scales = np.empty(sb // 2, np.uint16)
+    _check(lib().i4d_pack_codes(kind, ptr(q), ptr(s), N, K, head_dim, ptr(codes), ptr(scales), threads))
     return codes, scales
 
 

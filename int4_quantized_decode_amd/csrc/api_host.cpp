@@ -224,6 +224,19 @@ i4d_status i4d_packed_sizes(i4d_proj_kind kind, int N, int K, int head_dim, size
   return ok();
 }
 
+// the 128 codes q (in [-8, 7]) of packed row r (0..15) into the group's
+// atom: nibble u = q + 8 of channel kk at lane (16 j + r), dword kb, slot
+// nibble_slot(e) for kk = 32 kb + 8 j + e
+static inline void place_group(uint8_t* atom, int r, const int8_t* q) {
+  for (int kk = 0; kk < kGroup; ++kk) {
+    const int kb = kk / 32, j = (kk % 32) / 8, e = kk % 8;
+    const int slot = nibble_slot(e);
+    const uint8_t u = (uint8_t)(q[kk] + 8);
+    uint8_t* byte = atom + (16 * j + r) * 16 + kb * 4 + slot / 2;
+    *byte |= (slot & 1) ? (uint8_t)(u << 4) : u;
+  }
+}
+
 i4d_status i4d_pack_weights(i4d_proj_kind kind, const float* W0, const float* W1,
                             const float* gamma, int N, int K, int head_dim, void* codes_out,
                             uint16_t* scales_out, int threads) {
@@ -254,14 +267,41 @@ i4d_status i4d_pack_weights(i4d_proj_kind kind, const float* W0, const float* W1
           }
           uint16_t s16 = quantize_group(w.data(), q);
           scales_out[((size_t)t * G + g) * kStrip + r] = s16;
-          uint8_t* atom = atom_base + (size_t)g * kAtomBytes;
-          for (int kk = 0; kk < kGroup; ++kk) {
-            int kb = kk / 32, j = (kk % 32) / 8, e = kk % 8;
-            int slot = nibble_slot(e);
-            uint8_t u = (uint8_t)(q[kk] + 8);
-            uint8_t* byte = atom + (16 * j + r) * 16 + kb * 4 + slot / 2;
-            *byte |= (slot & 1) ? (uint8_t)(u << 4) : u;
-          }
+          place_group(atom_base + (size_t)g * kAtomBytes, r, q);
+        }
+      }
+    }
+  });
+  return ok();
+}
+
+i4d_status i4d_pack_codes(i4d_proj_kind kind, const int8_t* q, const uint16_t* s, int N, int K,
+                          int head_dim, void* codes_out, uint16_t* scales_out, int threads) {
+  i4d_status st = check_pack_args(kind, N, K, head_dim);
+  if (st) return st;
+  if (!q || !s || !codes_out || !scales_out) return fail(I4D_ERR_NULL, "q/s/codes_out/scales_out NULL");
+  const int Np = packed_rows(kind, N);
+  const int G = groups_of(K);
+  const size_t rows = (size_t)Np;  // N, or 2N for gate/up
+  // everything is checked before anything is written
+  for (size_t i = 0; i < rows * (size_t)K; ++i)
+    if (q[i] < -8 || q[i] > 7)
+      return fail(I4D_ERR_RANGE, "code %d at row %zu, column %zu is outside [-8, 7]", (int)q[i], i / K, i % K);
+  for (size_t i = 0; i < rows * (size_t)G; ++i)
+    if ((s[i] & 0x7c00u) == 0x7c00u)
+      return fail(I4D_ERR_RANGE, "scale of row %zu, group %zu is not finite (0x%04x)", i / G, i % G, s[i]);
+  uint8_t* codes = (uint8_t*)codes_out;
+  parallel_for(Np / kStrip, threads, [&](long t0, long t1) {
+    for (long t = t0; t < t1; ++t) {
+      uint8_t* atom_base = codes + (size_t)t * G * kAtomBytes;
+      memset(atom_base, 0, (size_t)G * kAtomBytes);
+      for (int r = 0; r < kStrip; ++r) {
+        int p = (int)t * kStrip + r, mat, row;
+        source_row(kind, p, head_dim, &mat, &row);
+        const size_t in_row = (size_t)mat * N + row;
+        for (int g = 0; g < G; ++g) {
+          scales_out[((size_t)t * G + g) * kStrip + r] = s[in_row * G + g];
+          place_group(atom_base + (size_t)g * kAtomBytes, r, q + in_row * K + (size_t)g * kGroup);
         }
       }
     }

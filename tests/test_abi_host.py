@@ -235,6 +235,66 @@ def test_qkv_and_gate_up_strip_interleave():
         np.testing.assert_array_equal(sc[t, 8:], np.arange(8 * t, 8 * t + 8) + 101)
 
 
+# ---------------------------------------------------------------------------
+# pre-quantized import: the layout permutation alone
+# ---------------------------------------------------------------------------
+
+def _random_codes(rng, rows, K):
+    q = rng.integers(-8, 8, (rows, K)).astype(np.int8)
+    s = (rng.uniform(1e-4, 0.05, (rows, K // 128)) * rng.choice([1, -1], (rows, K // 128))).astype(np.float16)
+    return q, s.view(np.uint16)
+
+
+@pytest.mark.parametrize("kind,N,K,hd", [(0, 48, 384, 0), (1, 3 * 128, 256, 128), (1, 6 * 64, 128, 64),
+                                         (2, 32, 512, 0)], ids=["plain", "qkv128", "qkv64", "gate_up"])
+def test_pack_codes_round_trip(kind, N, K, hd):
+    """Arbitrary codes and scales (any sign, not from round-to-nearest) come
+    back unchanged through the device layout."""
+    rng = np.random.default_rng(8 + kind)
+    rows = 2 * N if kind == B.I4D_PROJ_GATE_UP else N
+    q, s = _random_codes(rng, rows, K)
+    codes, scales = B.i4d_pack_codes(kind, q, s, N, K, hd)
+    q2, s2 = B.i4d_unpack_weights(kind, codes, scales, N, K, hd)
+    np.testing.assert_array_equal(q2, q)
+    np.testing.assert_array_equal(s2, s)
+
+
+def test_pack_codes_places_bytes_as_the_quantizing_packer():
+    """Importing the codes and scales the quantizing packer produced gives
+    the same bytes (every projection kind of a layer)."""
+    shape = synth.SHAPE_TINY
+    lw = synth.make_layer(shape, 9)
+    hd = shape.head_dim
+    for kind, W0, W1, g in [(B.I4D_PROJ_QKV, lw.w_qkv, None, lw.gamma_attn), (B.I4D_PROJ_PLAIN, lw.w_o, None, None),
+                            (B.I4D_PROJ_GATE_UP, lw.w_gate, lw.w_up, lw.gamma_ffn),
+                            (B.I4D_PROJ_PLAIN, lw.w_down, None, None)]:
+        N, K = W0.shape
+        h = hd if kind == B.I4D_PROJ_QKV else 0
+        codes, scales = B.i4d_pack_weights(kind, W0, W1, g, h)
+        q, s = B.i4d_unpack_weights(kind, codes, scales, N, K, h)
+        c2, s2 = B.i4d_pack_codes(kind, q, s, N, K, h)
+        np.testing.assert_array_equal(c2, codes)
+        np.testing.assert_array_equal(s2, scales)
+
+
+def test_pack_codes_rejects_bad_input():
+    rng = np.random.default_rng(12)
+    q, s = _random_codes(rng, 32, 256)
+    for bad in (-9, 8):
+        qb = q.copy()
+        qb[17, 200] = bad
+        assert _status(lambda: B.i4d_pack_codes(B.I4D_PROJ_PLAIN, qb, s, 32, 256)) == -6
+        assert "outside [-8, 7]" in B.i4d_last_error()
+    for bits in (0x7c00, 0xfc00, 0x7e00):          # +inf, -inf, nan
+        sb = s.copy()
+        sb[5, 1] = bits
+        assert _status(lambda: B.i4d_pack_codes(B.I4D_PROJ_PLAIN, q, sb, 32, 256)) == -6
+        assert "not finite" in B.i4d_last_error()
+    assert _status(lambda: B.i4d_pack_codes(B.I4D_PROJ_PLAIN, q[:, :200], s[:, :1], 32, 200)) == -2
+    L = B.lib()
+    assert L.i4d_pack_codes(B.I4D_PROJ_PLAIN, None, None, 32, 256, 0, None, None, 0) == -1
+
+
 def test_lm_head_pack_matches_oracle_bf16():
     rng = np.random.default_rng(6)
     W = (rng.standard_normal((64, 256)) * 0.02).astype(np.float32)

@@ -438,3 +438,43 @@ def test_lm_head_parity(gpu, M):
             # only a near-tie may differ: the two logits agree within the logit error
             assert abs(rl[m, gt[m]] - rl[m, rt[m]]) <= 4 * np.abs(gl[m] - rl[m]).max()
         assert gt[m] == int(np.argmax(gl[m]))   # argmax of the GPU's own logits, lowest index on ties
+
+
+# ---------------------------------------------------------------------------
+# pre-quantized codes imported with i4d_pack_codes
+# ---------------------------------------------------------------------------
+
+def _other_quantizer(rng, W, gamma):
+    """Codes and scales that round-to-nearest of W would not give: the
+    oracle's encoding of a perturbed W with scales jittered by +-10 %."""
+    Wp = W + rng.standard_normal(W.shape).astype(np.float32) * np.float32(0.3 * np.abs(W).mean())
+    q, s = O.quantize_weight(Wp, gamma)
+    s = (s.astype(np.float32) * rng.uniform(0.9, 1.1, s.shape).astype(np.float32)).astype(np.float16)
+    return q, s
+
+
+@pytest.mark.parametrize("shape", [synth.SHAPE_SMALL128, ONE_LAUNCH_SHAPES[0]], ids=["small128", "one_launch"])
+@pytest.mark.parametrize("lengths", [[300], [300, 129, 40]], ids=["m1", "m3"])
+def test_block_with_imported_codes(gpu, shape, lengths):
+    """A layer whose codes and scales come from another quantizer, imported
+    with i4d_pack_codes (no re-quantization): the decode step matches the
+    oracle run on the same codes and scales."""
+    torch, B, D = gpu
+    rng = np.random.default_rng(21)
+    lw = synth.make_layer(shape, 21)
+    ql = O.QuantLayer(qkv=_other_quantizer(rng, lw.w_qkv, lw.gamma_attn), o=_other_quantizer(rng, lw.w_o, None),
+                      gate=_other_quantizer(rng, lw.w_gate, lw.gamma_ffn),
+                      up=_other_quantizer(rng, lw.w_up, lw.gamma_ffn), down=_other_quantizer(rng, lw.w_down, None))
+    d, F, hd = shape.d_model, shape.d_ffn, shape.head_dim
+    n_qkv = (shape.n_q_heads + 2 * shape.n_kv_heads) * hd
+    u16 = lambda s: s.view(np.uint16)
+    packed = {
+        "qkv": B.i4d_pack_codes(B.I4D_PROJ_QKV, ql.qkv[0], u16(ql.qkv[1]), n_qkv, d, hd),
+        "o": B.i4d_pack_codes(B.I4D_PROJ_PLAIN, ql.o[0], u16(ql.o[1]), d, shape.n_q_heads * hd),
+        "gu": B.i4d_pack_codes(B.I4D_PROJ_GATE_UP, np.concatenate([ql.gate[0], ql.up[0]]),
+                               u16(np.concatenate([ql.gate[1], ql.up[1]])), F, d),
+        "down": B.i4d_pack_codes(B.I4D_PROJ_PLAIN, ql.down[0], u16(ql.down[1]), d, F),
+    }
+    tensors = {k: (torch.from_numpy(c).cuda(), D.to_device_u16(s)) for k, (c, s) in packed.items()}
+    memo = {"layer": D.DeviceLayer.from_packed(shape, tensors), "ql": ql}
+    check_block(run_block(gpu, shape, 21, lengths, lw=lw, memo=memo))
