@@ -39,7 +39,7 @@ STEP_M1_SOURCES = ("step.hip", "step.h", "gemv.h", "attn_core.h", "attn.h", "coh
                    "proj.h", "i4d_internal.h", "i4d_layout.h", "api_device.hip", "api_host.cpp")
 TRAFFIC = {
     "8b_m1_ctx4096": {"kernel": "step_m1_kernel (one-launch decode step)", "sources": STEP_M1_SOURCES,
-                      "sha256": "6a0adf52430a232c064946924685db18c9982bddfe905f65d72ecca7870484c6",
+                      "sha256": "2c788a405efba1c9920cd4f92b7ebb040041773626a6aa1504c856102805acf8",
                       "fetch_bytes": 118782464, "write_bytes": 751104},
 }
 

@@ -151,7 +151,9 @@ i4d_status i4d_unpack_weights(i4d_proj_kind kind, const void* codes, const uint1
                               int N, int K, int head_dim, int8_t* q_out, uint16_t* s_out);
 
 /* LM head (full-model step only): bf16 weight = bf16(fp32(gamma_f[k] * W[v][k]))
- * in natural [V][d] row-major order (gamma_f may be NULL). Host memory. */
+ * (gamma_f may be NULL) in tiles of 16 rows x 32 channels: element (v, k)
+ * at ((v/16 * d/32 + k/32) * 16 + v%16) * 32 + k%32, so the kernel reads
+ * each tile as one contiguous KiB.  V % 16 == 0, d % 128 == 0.  Host memory. */
 i4d_status i4d_pack_lm_head(const float* W, const float* gamma, int V, int d,
                             uint16_t* out_bf16, int threads);
 
@@ -345,7 +347,8 @@ i4d_status i4d_lm_head_workspace_bytes(int V, int M, size_t* bytes);
 /* logits[m][v] = rho_f[m] * sum_k h[m][k] w[v][k], rho_f = 1/sqrt(mean h^2 +
  * eps), w = bf16 weight with the final-norm gain folded (i4d_pack_lm_head);
  * token_out[m] = argmax_v logits[m][v], lowest index on ties.
- * w_lm: device bf16 [V][d] (V % 16 == 0, d % 128 == 0); h: device bf16
+ * w_lm: device bf16 V x d in the tiled layout of i4d_pack_lm_head (V % 16
+ * == 0, d % 128 == 0); h: device bf16
  * [M][d]; logits_out: optional device fp32 [M][V]; token_out: device int32
  * [M]. */
 i4d_status i4d_lm_head_argmax(const uint16_t* w_lm, int V, int d, const uint16_t* h, int M,

@@ -210,10 +210,11 @@ def i4d_unpack_weights(kind: int, codes, scales, N: int, K: int, head_dim: int =
 
 
 def i4d_pack_lm_head(W, gamma=None, threads: int = 0):
+    """fp32 [V][d] -> bf16 bits in tiles [V/16][d/32][16][32]."""
     W = np.ascontiguousarray(W, dtype=np.float32)
     V, d = W.shape
     gamma = None if gamma is None else np.ascontiguousarray(gamma, dtype=np.float32)
-    out = np.empty((V, d), np.uint16)
+    out = np.empty((V // 16, d // 32, 16, 32) if V % 16 == 0 and d % 32 == 0 else (V, d), np.uint16)
     _check(lib().i4d_pack_lm_head(ptr(W), ptr(gamma), V, d, ptr(out), threads))
     return out
 

@@ -337,11 +337,15 @@ i4d_status i4d_pack_lm_head(const float* W, const float* gamma, int V, int d, ui
   if (!W || !out_bf16) return fail(I4D_ERR_NULL, "W/out NULL");
   if (V <= 0 || d <= 0 || V % kStrip || d % kGroup)
     return fail(I4D_ERR_SHAPE, "LM head V=%d must be a multiple of 16, d=%d of 128", V, d);
+  // tiles of 16 rows x 32 k ([V/16][d/32][16][32], 1 KiB each), so that
+  // one 16-byte load per lane of the kernel's MFMA operand reads one
+  // contiguous KiB
   parallel_for(V, threads, [&](long v0, long v1) {
     for (long v = v0; v < v1; ++v)
       for (int k = 0; k < d; ++k) {
         float w = W[(size_t)v * d + k];
-        out_bf16[(size_t)v * d + k] = f32_to_bf16_rne(gamma ? gamma[k] * w : w);
+        const size_t o = (((size_t)(v / kStrip) * (d / 32) + k / 32) * kStrip + v % kStrip) * 32 + k % 32;
+        out_bf16[o] = f32_to_bf16_rne(gamma ? gamma[k] * w : w);
       }
   });
   return ok();

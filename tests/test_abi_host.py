@@ -300,8 +300,16 @@ def test_lm_head_pack_matches_oracle_bf16():
     W = (rng.standard_normal((64, 256)) * 0.02).astype(np.float32)
     g = rng.uniform(0.5, 1.5, 256).astype(np.float32)
     out = B.i4d_pack_lm_head(W, g)
+    assert out.shape == (64 // 16, 256 // 32, 16, 32)
     ref = O.lm_head_weight_bf16(W, g)
-    np.testing.assert_array_equal(synth.bf16_bits_to_f32(out).astype(np.float64), ref)
+    # tiles [V/16][d/32][16 rows][32 channels] back to [V][d]
+    natural = out.transpose(0, 2, 1, 3).reshape(64, 256)
+    np.testing.assert_array_equal(synth.bf16_bits_to_f32(natural).astype(np.float64), ref)
+    # documented offset of element (v, k)
+    flat = out.reshape(-1)
+    for v, k in [(0, 0), (17, 33), (63, 255), (5, 130)]:
+        o = ((v // 16 * (256 // 32) + k // 32) * 16 + v % 16) * 32 + k % 32
+        assert synth.bf16_bits_to_f32(flat[o:o + 1])[0] == ref[v, k]
 
 
 # ---------------------------------------------------------------------------
