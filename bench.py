@@ -62,6 +62,25 @@ def traffic_of(workload, kernel):
     return t["fetch_bytes"] + t["write_bytes"]
 
 
+def device_errors(caches):
+    """OR of the caches' device error words (I4D_DEVERR_* bits: an invalid
+    length or position, or a wait of the one-launch step that timed out).
+    A timed region whose steps set any of them measured no valid step."""
+    e = 0
+    for c in caches:
+        e |= c.errors()
+    return e
+
+
+def require_clean(caches, what):
+    e = device_errors(caches)
+    if e:
+        print(f"bench.py: {what}: device error word 0x{e:x} is set (I4D_DEVERR_*); the timed steps are not "
+              f"valid and no result is printed", file=sys.stderr)
+        sys.exit(3)
+    return e
+
+
 def algorithmic_bytes(shape, lengths):
     """INT4 codes (0.5 B/weight) + fp16 group scales + INT4 KV codes and
     per-token-per-head fp16 scales read by one step."""
@@ -87,7 +106,7 @@ def main():
     ap.add_argument("--copies", type=int, default=8)
     ap.add_argument("--splits", type=int, default=-1)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-steps", type=int, default=3)
+    ap.add_argument("--cpu-steps", type=int, default=5)
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (the reference "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -174,6 +193,7 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     ms_total = e0.elapsed_time(e1)
+    require_clean(caches, "timed decode steps")
     ms_step = ms_total / args.steps
     us_step = ms_step * 1e3
     total_b, w_b, kv_b = algorithmic_bytes(shape, lengths)
@@ -230,6 +250,7 @@ def main():
                      "frac": round(rf_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": traffic_of(args.workload if not args.M else f"{args.workload}@M{M}", rf_kernel),
                      "avg_launch_us": round(rf_us, 3), "bytes_per_launch": rf_bytes},
+        "device_errors": device_errors(caches),
         "setup_s": round(setup_s, 1),
     }
 
@@ -241,29 +262,16 @@ def main():
 def full_model(args, wl, torch, B, D, synth):
     """n_layers stacked blocks (one row, the workload's context per layer and
     its split count) followed by the final RMSNorm, the bf16 LM head and the
-    argmax: one decode step of the whole model.  The layers share one seeded
-    weight set at distinct device addresses (same bytes per layer), each
-    with its own KV cache; one step reads every layer's weights and cache
-    once plus the LM head, so nothing stays in the 256 MB Infinity Cache
-    between steps."""
+    argmax: one decode step of the whole model.  Layer l has its own seed
+    (workload seed + l) for its weights and its cached tokens, and its own
+    KV cache; one step reads every layer's weights and cache once plus the
+    LM head, so nothing stays in the 256 MB Infinity Cache between steps."""
     shape, L, nl = wl.shape, wl.ctx, wl.n_layers
     lengths = np.array([L], np.int32)
     t0 = time.time()
-    lw = synth.make_layer(shape, wl.seed)
-    base = D.DeviceLayer(shape, lw)
-    layers = [base] + [base.clone() for _ in range(nl - 1)]
-    del lw
-    pre = synth.make_cache_prefill(shape, lengths, wl.seed)
-    c0 = D.DeviceCache(shape, lengths)
-    c0.prefill(pre)
-    caches = [c0]
-    for _ in range(nl - 1):
-        c = D.DeviceCache(shape, lengths)
-        for name in ("k_codes", "v_codes", "k_scales", "v_scales"):
-            getattr(c, name).copy_(getattr(c0, name))
-        caches.append(c)
+    layers, caches, _ = D.stacked_layers(shape, [wl.seed + l for l in range(nl)], lengths)
     V = synth.LM_VOCAB
-    w_lm, g_lm = synth.make_lm_head(shape.d_model, V, wl.seed + 999)
+    w_lm, g_lm = synth.make_lm_head(shape.d_model, V, synth.LM_HEAD_SEED)
     w16 = torch.from_numpy(B.i4d_pack_lm_head(w_lm, g_lm).view(np.int16)).cuda()
     del w_lm
     ws = D.Workspace(shape, 1, L, wl.num_splits)
@@ -287,6 +295,7 @@ def full_model(args, wl, torch, B, D, synth):
 
     step(0)
     torch.cuda.synchronize()
+    require_clean(caches, "eager full-model step")
     K = max(1, min(args.steps, 20))
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
@@ -300,6 +309,7 @@ def full_model(args, wl, torch, B, D, synth):
     g.replay()
     e1.record(stream)
     torch.cuda.synchronize()
+    require_clean(caches, "timed full-model steps")
     ms_step = e0.elapsed_time(e1) / K
     blk_b, w_b, kv_b = algorithmic_bytes(shape, lengths)
     lm_b = V * shape.d_model * 2
@@ -310,13 +320,15 @@ def full_model(args, wl, torch, B, D, synth):
         "value": round(ms_step, 4), "unit": "ms/step", "n_gpus": 1, "steps": K, "warmup": 1,
         "ms_per_step": round(ms_step, 4), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
         "dtype": "int4 x bf16/fp16 -> f32; bf16 LM head", "data": "synthetic",
-        "config": {"workload": wl.name, "n_layers": nl, "d_model": shape.d_model, "n_q_heads": shape.n_q_heads,
+        "config": {"workload": wl.name, "n_layers": nl, "layer_seeds": [wl.seed, wl.seed + nl - 1],
+                   "d_model": shape.d_model, "n_q_heads": shape.n_q_heads,
                    "n_kv_heads": shape.n_kv_heads, "head_dim": shape.head_dim, "d_ffn": shape.d_ffn, "M": 1,
                    "ctx_per_layer": L, "num_splits": wl.num_splits, "vocab": V,
                    "timing": "hip graph of K full steps, events on the launch stream"},
         "hbm_GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
         "bytes_per_step": {"total": total_b, "per_layer": blk_b, "lm_head": lm_b},
         "token": int(tok.item()),
+        "device_errors": device_errors(caches),
         "pages_context": "the pages report 2.8 ms per full Llama-3.1-8B decode step on one H100 "
                          "(context length not stated), so it is not the same workload",
         "setup_s": round(setup_s, 1),
@@ -324,25 +336,51 @@ def full_model(args, wl, torch, B, D, synth):
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(shape, lw, lengths, pre, xb, n_steps, workload):
-    """The CPU oracle, as it stands, on a bounded sample of the same workload."""
-    import oracle as O
+def host_cpu():
+    model = "unknown"
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count()
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        nproc = os.cpu_count()
+    return model, nproc
+
+
+def cpu_baseline(shape, lw, lengths, pre, xb, n_steps, workload):
+    """The CPU oracle, as it stands, on a bounded sample of the same
+    workload: the median of n_steps block steps with numpy's BLAS pool at
+    its default size (the threads it used are reported as `cores`), and of
+    two steps on one thread for the small single-row workloads."""
+    import oracle as O
+    from threadpoolctl import threadpool_info, threadpool_limits
+    blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    model, nproc = host_cpu()
     ql = O.quantize_layer(lw)
-    times = []
-    for _ in range(n_steps):
-        cache = O.build_cache(shape, lengths, pre)
-        t = time.time()
-        O.decode_block(shape, ql, cache, xb, lengths)
-        times.append(time.time() - t)
-    us = float(np.median(times)) * 1e6
-    return {"value": round(us, 1), "unit": "us/step", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n_steps} block steps of {workload} (median; fp64 numpy, weights dequantized "
-                      f"each step)"}
+
+    def timed(n):
+        times = []
+        for _ in range(n):
+            cache = O.build_cache(shape, lengths, pre)
+            t = time.time()
+            O.decode_block(shape, ql, cache, xb, lengths)
+            times.append(time.time() - t)
+        return float(np.median(times)) * 1e6
+
+    us = timed(n_steps)
+    out = {"value": round(us, 1), "unit": "us/step", "cores": int(blas_threads), "kind": "oracle",
+           "sample": f"{n_steps} block steps of {workload} (median; fp64 numpy, weights dequantized each step)",
+           "host_cpu": model, "nproc": int(nproc)}
+    if len(lengths) == 1 and shape.d_model <= 4096:
+        with threadpool_limits(limits=1):
+            out["value_1thread"] = round(timed(2), 1)
+    return out
 
 
 if __name__ == "__main__":

@@ -338,6 +338,26 @@ i4d_status i4d_decode_block_step(const i4d_layer* layer, const i4d_kv_cache* cac
                                  int M, int max_ctx_len, int num_splits, void* workspace,
                                  size_t workspace_bytes, float* attn_f32, void* stream);
 
+/* Launch plan of one projection stage as i4d_decode_block_step runs it at M
+ * rows (host only; diagnostics and tests).  stage: 0 QKV, 1 O, 2 gate/up,
+ * 3 down.  kernel 0 = the M = 1 GEMV, 1 = the skinny MFMA kernel;
+ * instantiated = 1 when the library holds a kernel for the plan (a step
+ * whose plan has none fails with I4D_ERR_UNSUPPORTED instead of launching
+ * nothing).  I4D_ERR_UNSUPPORTED when the shape exceeds the kernels' limits
+ * (the fields other than instantiated are still filled in). */
+typedef struct {
+  int kernel;
+  int waves;
+  int strips_per_workgroup;
+  int k_slices;
+  int depth;       /* groups of weight atoms in flight per wave (skinny) */
+  int persistent;  /* one persistent workgroup per CU (skinny) */
+  int grid;
+  size_t lds_bytes;
+  int instantiated;
+} i4d_projection_plan;
+i4d_status i4d_projection_plan_of(const i4d_layer_shape* shape, int stage, int M, i4d_projection_plan* out);
+
 /* ------------------------------------------------------------------------ */
 /* Final norm + LM head + greedy argmax (full-model step)                    */
 /* ------------------------------------------------------------------------ */

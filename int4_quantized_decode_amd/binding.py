@@ -58,6 +58,12 @@ class i4d_layer(ctypes.Structure):
                 ("down_codes", ctypes.c_void_p), ("down_scales", ctypes.c_void_p)]
 
 
+class i4d_projection_plan(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in ("kernel", "waves", "strips_per_workgroup", "k_slices", "depth",
+                                            "persistent", "grid")] + \
+               [("lds_bytes", ctypes.c_size_t), ("instantiated", ctypes.c_int)]
+
+
 class i4d_workspace_layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in ("q", "k", "v", "attn", "h", "h_bf16", "a", "attn_ws", "split_cnt", "split_part", "sync",
                                                "total")]
@@ -87,6 +93,7 @@ _SIGS = {
     "i4d_workspace_layout_of": (_I, [ctypes.POINTER(i4d_layer_shape), _I, _I, _I,
                                      ctypes.POINTER(i4d_workspace_layout)]),
     "i4d_workspace_init": (_I, [_VP, ctypes.c_size_t, _VP]),
+    "i4d_projection_plan_of": (_I, [ctypes.POINTER(i4d_layer_shape), _I, _I, ctypes.POINTER(i4d_projection_plan)]),
     "i4d_decode_step_is_one_launch": (_I, [ctypes.POINTER(i4d_layer_shape), _I, ctypes.POINTER(_I)]),
     "i4d_decode_block_step": (_I, [ctypes.POINTER(i4d_layer), ctypes.POINTER(i4d_kv_cache), _VP, _VP, _VP,
                                    _I, _I, _I, _VP, ctypes.c_size_t, _VP, _VP]),
@@ -261,6 +268,12 @@ def i4d_decode_step_is_one_launch(shape: i4d_layer_shape, M: int) -> bool:
     out = _I()
     _check(lib().i4d_decode_step_is_one_launch(ctypes.byref(shape), M, ctypes.byref(out)))
     return bool(out.value)
+
+
+def i4d_projection_plan_of(shape: i4d_layer_shape, stage: int, M: int) -> i4d_projection_plan:
+    out = i4d_projection_plan()
+    _check(lib().i4d_projection_plan_of(ctypes.byref(shape), stage, M, ctypes.byref(out)))
+    return out
 
 
 def i4d_workspace_init(workspace, nbytes: int, stream=None):

@@ -344,6 +344,35 @@ i4d_status i4d_decode_block_step(const i4d_layer* layer, const i4d_kv_cache* cac
   return ok();
 }
 
+i4d_status i4d_projection_plan_of(const i4d_layer_shape* shape, int stage, int M, i4d_projection_plan* out) {
+  I4D_TRY(check_shape(shape));
+  I4D_TRY(check_rows(M));
+  if (!out) return fail(I4D_ERR_NULL, "out is NULL");
+  if (stage < 0 || stage > 3) return fail(I4D_ERR_RANGE, "stage %d outside [0, 3]", stage);
+  i4d_workspace_layout wl;
+  I4D_TRY(i4d_workspace_layout_of(shape, M, 1, 0, &wl));
+  // the arguments as the block step builds them: null data pointers (only
+  // the plan is computed) and the workspace's split buffer, whose pointers
+  // only have to be non-null for the plan to consider a split of K
+  const i4d_layer_shape& s = *shape;
+  i4d_layer L = {};
+  L.shape = s;
+  ProjArgs a;
+  int epi = EPI_QKV;
+  switch (stage) {
+    case 0: a = qkv_args(&L, nullptr, nullptr, M, nullptr, nullptr, nullptr); epi = EPI_QKV; break;
+    case 1: a = o_args(&L, nullptr, nullptr, M, nullptr, nullptr); epi = EPI_O; break;
+    case 2: a = gu_args(&L, nullptr, M, nullptr); epi = EPI_GU; break;
+    default: a = down_args(&L, nullptr, nullptr, M, nullptr); epi = EPI_DOWN; break;
+  }
+  if (M > 1) {
+    a.split_cnt = reinterpret_cast<unsigned*>(wl.split_cnt + 256);
+    a.split_part = reinterpret_cast<float*>(wl.split_part + 256);
+    a.split_bytes = wl.sync - wl.split_part;
+  }
+  return projection_plan_of(epi, a, out);
+}
+
 i4d_status i4d_decode_step_is_one_launch(const i4d_layer_shape* shape, int M, int* one_launch) {
   I4D_TRY(check_shape(shape));
   if (!one_launch) return fail(I4D_ERR_NULL, "one_launch is NULL");

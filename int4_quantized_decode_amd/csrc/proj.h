@@ -41,5 +41,7 @@ struct ProjArgs {
 
 
 i4d_status launch_projection(int epi, const ProjArgs& a, hipStream_t st);
+// the launch plan of launch_projection for `a` (host only, nothing launched)
+i4d_status projection_plan_of(int epi, const ProjArgs& a, i4d_projection_plan* out);
 
 }  // namespace i4d

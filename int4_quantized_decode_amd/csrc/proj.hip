@@ -536,66 +536,131 @@ static size_t split_bytes_of(const ProjArgs& a) {
   return a.split_bytes;
 }
 
-template <int EPI>
-static hipError_t launch_epi(const ProjArgs& a, hipStream_t st) {
+// The launch shape of one projection: the M = 1 GEMV or the skinny MFMA
+// kernel, with its plan, LDS bytes and grid.
+struct ProjLaunch {
+  bool gemv;
+  GemvPlan g;
+  SkinnyPlan s;
+  int T;         // 16-row x tiles (skinny)
+  bool persist;  // persistent workgroups, one per CU (skinny)
+  size_t lds;
+  int grid;
+};
+
+static ProjLaunch plan_projection(const ProjArgs& a, bool rho) {
+  ProjLaunch l{};
   const int nstrips = a.Np / kStrip;
   if (a.M == 1) {
-    const GemvPlan p = gemv_plan(nstrips, a.G);
-    const size_t lds = gemv_lds_bytes(a.K, p);
-    const int grid = (nstrips + p.SP - 1) / p.SP;
-    if (p.NW == 16)
-      launch_gemv<EPI, 16>(a, p, lds, grid, st);
-    else if (p.NW == 8)
-      launch_gemv<EPI, 8>(a, p, lds, grid, st);
-    else
-      launch_gemv<EPI, 4>(a, p, lds, grid, st);
+    l.gemv = true;
+    l.g = gemv_plan(nstrips, a.G);
+    l.lds = gemv_lds_bytes(a.K, l.g);
+    l.grid = (nstrips + l.g.SP - 1) / l.g.SP;
   } else {
-    const int T = a.M <= 16 ? 1 : 2;
-    const SkinnyPlan p = skinny_plan(nstrips, a.G, T, !needs_rho<EPI>(), split_bytes_of(a));
-    const size_t lds = skinny_lds_bytes(p.GPW, p.SP, T);
-    const int ntiles = (nstrips + p.SP - 1) / p.SP * p.KS;
+    l.T = a.M <= 16 ? 1 : 2;
+    l.s = skinny_plan(nstrips, a.G, l.T, !rho, split_bytes_of(a));
+    l.lds = l.s.SP ? skinny_lds_bytes(l.s.GPW, l.s.SP, l.T) : 0;
+    const int ntiles = l.s.SP ? (nstrips + l.s.SP - 1) / l.s.SP * l.s.KS : 0;
     // more tiles than CUs at seven strips and one x tile: persistent
     // workgroups, one per CU
-    const bool persist = ntiles > kSkinnyMaxWorkgroups && p.SP == 7 && T == 1;
-    const int grid = persist ? kSkinnyMaxWorkgroups : ntiles;
-#define I4D_SKINNY(SPV, TV, DV)                                                                                 \
-  if (p.SP == SPV && T == TV && p.D == DV && !persist)                                                          \
-    hipLaunchKernelGGL((proj_skinny_kernel<EPI, SPV, TV, DV, false>), dim3(grid), dim3(kSkinnyWaves * 64), lds, st, \
-                       a, p);
-    // (two x tiles with the persistent loop exceed the register file)
-    if (persist && p.D == 2)
-      hipLaunchKernelGGL((proj_skinny_kernel<EPI, 7, 1, 2, true>), dim3(grid), dim3(kSkinnyWaves * 64), lds, st, a, p);
-    I4D_SKINNY(1, 1, 4) I4D_SKINNY(2, 1, 4) I4D_SKINNY(3, 1, 4) I4D_SKINNY(4, 1, 2) I4D_SKINNY(5, 1, 2)
-    I4D_SKINNY(7, 1, 2)
-    I4D_SKINNY(1, 2, 4) I4D_SKINNY(2, 2, 2) I4D_SKINNY(3, 2, 2) I4D_SKINNY(4, 2, 2) I4D_SKINNY(5, 2, 2)
-    I4D_SKINNY(7, 2, 2)
-    if constexpr (!needs_rho<EPI>()) {
-      I4D_SKINNY(1, 1, 8) I4D_SKINNY(1, 2, 8)
-    }
-#undef I4D_SKINNY
+    l.persist = ntiles > kSkinnyMaxWorkgroups && l.s.SP == 7 && l.T == 1;
+    l.grid = l.persist ? kSkinnyMaxWorkgroups : ntiles;
   }
-  return hipGetLastError();
+  return l;
+}
+
+// The skinny instantiation that matches a plan: launched (launch == true)
+// or only looked up.  Returns false when the library holds no kernel for
+// the plan, so a plan without one is an error instead of a silent no-op.
+// (Two x tiles with the persistent loop exceed the register file.)
+template <int EPI>
+static bool skinny_dispatch(const ProjArgs& a, const ProjLaunch& l, hipStream_t st, bool launch) {
+  const SkinnyPlan& p = l.s;
+#define I4D_SKINNY(SPV, TV, DV, PV)                                                                             \
+  if (p.SP == SPV && l.T == TV && p.D == DV && l.persist == PV) {                                               \
+    if (launch)                                                                                                 \
+      hipLaunchKernelGGL((proj_skinny_kernel<EPI, SPV, TV, DV, PV>), dim3(l.grid), dim3(kSkinnyWaves * 64), l.lds, \
+                         st, a, p);                                                                             \
+    return true;                                                                                                \
+  }
+  I4D_SKINNY(7, 1, 2, true)
+  I4D_SKINNY(1, 1, 4, false) I4D_SKINNY(2, 1, 4, false) I4D_SKINNY(3, 1, 4, false) I4D_SKINNY(4, 1, 2, false)
+  I4D_SKINNY(5, 1, 2, false) I4D_SKINNY(7, 1, 2, false)
+  I4D_SKINNY(1, 2, 4, false) I4D_SKINNY(2, 2, 2, false) I4D_SKINNY(3, 2, 2, false) I4D_SKINNY(4, 2, 2, false)
+  I4D_SKINNY(5, 2, 2, false) I4D_SKINNY(7, 2, 2, false)
+  if constexpr (!needs_rho<EPI>()) {
+    I4D_SKINNY(1, 1, 8, false) I4D_SKINNY(1, 2, 8, false)
+  }
+#undef I4D_SKINNY
+  return false;
+}
+
+template <int EPI>
+static bool launch_epi(const ProjArgs& a, hipStream_t st, bool launch) {
+  const ProjLaunch l = plan_projection(a, needs_rho<EPI>());
+  if (l.gemv) {
+    if (!launch) return true;  // launch_gemv has a kernel for every plan
+    if (l.g.NW == 16)
+      launch_gemv<EPI, 16>(a, l.g, l.lds, l.grid, st);
+    else if (l.g.NW == 8)
+      launch_gemv<EPI, 8>(a, l.g, l.lds, l.grid, st);
+    else
+      launch_gemv<EPI, 4>(a, l.g, l.lds, l.grid, st);
+    return true;
+  }
+  return skinny_dispatch<EPI>(a, l, st, launch);
+}
+
+static bool dispatch_epi(int epi, const ProjArgs& a, hipStream_t st, bool launch) {
+  switch (epi) {
+    case EPI_QKV: return launch_epi<EPI_QKV>(a, st, launch);
+    case EPI_O: return launch_epi<EPI_O>(a, st, launch);
+    case EPI_GU: return launch_epi<EPI_GU>(a, st, launch);
+    case EPI_DOWN: return launch_epi<EPI_DOWN>(a, st, launch);
+    default: return false;
+  }
+}
+
+// shape limits of the kernels (message set when unsupported)
+static i4d_status projection_fits(const ProjArgs& a, const ProjLaunch& l) {
+  if (l.gemv) {
+    if (l.lds > (size_t)kMaxLdsBytes || a.K > 4 * 8 * l.g.NW * 64)
+      return fail(I4D_ERR_UNSUPPORTED, "K=%d too large for the M=1 kernel (LDS %zu bytes)", a.K, l.lds);
+  } else if (l.s.SP == 0) {
+    return fail(I4D_ERR_UNSUPPORTED, "K=%d too large for the M>1 kernel", a.K);
+  }
+  return ok();
 }
 
 i4d_status launch_projection(int epi, const ProjArgs& a, hipStream_t st) {
-  if (a.M == 1) {
-    const GemvPlan p = gemv_plan(a.Np / kStrip, a.G);
-    const size_t lds = gemv_lds_bytes(a.K, p);
-    if (lds > (size_t)kMaxLdsBytes || a.K > 4 * 8 * p.NW * 64)
-      return fail(I4D_ERR_UNSUPPORTED, "K=%d too large for the M=1 kernel (LDS %zu bytes)", a.K, lds);
-  } else {
-    const SkinnyPlan p = skinny_plan(a.Np / kStrip, a.G, a.M <= 16 ? 1 : 2, true, split_bytes_of(a));
-    if (p.SP == 0) return fail(I4D_ERR_UNSUPPORTED, "K=%d too large for the M>1 kernel", a.K);
-  }
-  hipError_t e;
-  switch (epi) {
-    case EPI_QKV: e = launch_epi<EPI_QKV>(a, st); break;
-    case EPI_O: e = launch_epi<EPI_O>(a, st); break;
-    case EPI_GU: e = launch_epi<EPI_GU>(a, st); break;
-    case EPI_DOWN: e = launch_epi<EPI_DOWN>(a, st); break;
-    default: return fail(I4D_ERR_RANGE, "bad epilogue %d", epi);
-  }
+  if (epi < EPI_QKV || epi > EPI_DOWN) return fail(I4D_ERR_RANGE, "bad epilogue %d", epi);
+  const bool rho = epi == EPI_QKV || epi == EPI_GU;
+  const ProjLaunch l = plan_projection(a, rho);
+  const i4d_status fit = projection_fits(a, l);
+  if (fit != I4D_OK) return fit;
+  if (!dispatch_epi(epi, a, st, true))
+    return fail(I4D_ERR_UNSUPPORTED, "no projection kernel for the plan (SP %d, T %d, D %d, persistent %d)", l.s.SP,
+                l.T, l.s.D, (int)l.persist);
+  const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(I4D_ERR_HIP, "projection launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+i4d_status projection_plan_of(int epi, const ProjArgs& a, i4d_projection_plan* out) {
+  const bool rho = epi == EPI_QKV || epi == EPI_GU;
+  const ProjLaunch l = plan_projection(a, rho);
+  *out = i4d_projection_plan{};
+  out->kernel = l.gemv ? 0 : 1;
+  out->waves = l.gemv ? l.g.NW : kSkinnyWaves;
+  out->strips_per_workgroup = l.gemv ? l.g.SP : l.s.SP;
+  out->k_slices = l.gemv ? 1 : l.s.KS;
+  out->depth = l.gemv ? 0 : l.s.D;
+  out->persistent = l.persist ? 1 : 0;
+  out->grid = l.grid;
+  out->lds_bytes = l.lds;
+  const i4d_status fit = projection_fits(a, l);
+  if (fit != I4D_OK) return fit;
+  out->instantiated = dispatch_epi(epi, a, nullptr, false) ? 1 : 0;
   return ok();
 }
 

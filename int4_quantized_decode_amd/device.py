@@ -6,6 +6,8 @@ these classes only allocate tensors and fill the C structs with pointers.
 """
 from __future__ import annotations
 
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import torch
 
@@ -30,15 +32,30 @@ class DeviceLayer:
     """One layer's packed INT4 weights on the GPU and its i4d_layer struct."""
 
     def __init__(self, shape: synth.LayerShape, lw: synth.LayerWeights, device="cuda", threads: int = 0):
-        self.shape = shape
+        self._upload(shape, self.pack_host(shape, lw, threads), device)
+
+    @staticmethod
+    def pack_host(shape: synth.LayerShape, lw: synth.LayerWeights, threads: int = 0) -> dict:
+        """The library's host packer on the four projections of a layer:
+        {name: (codes uint8, scales uint16)} in the device layout."""
         hd = shape.head_dim
-        qkv = B.i4d_pack_weights(B.I4D_PROJ_QKV, lw.w_qkv, None, lw.gamma_attn, hd, threads)
-        o = B.i4d_pack_weights(B.I4D_PROJ_PLAIN, lw.w_o, None, None, 0, threads)
-        gu = B.i4d_pack_weights(B.I4D_PROJ_GATE_UP, lw.w_gate, lw.w_up, lw.gamma_ffn, 0, threads)
-        down = B.i4d_pack_weights(B.I4D_PROJ_PLAIN, lw.w_down, None, None, 0, threads)
-        self.host = dict(qkv=qkv, o=o, gu=gu, down=down)
+        return dict(
+            qkv=B.i4d_pack_weights(B.I4D_PROJ_QKV, lw.w_qkv, None, lw.gamma_attn, hd, threads),
+            o=B.i4d_pack_weights(B.I4D_PROJ_PLAIN, lw.w_o, None, None, 0, threads),
+            gu=B.i4d_pack_weights(B.I4D_PROJ_GATE_UP, lw.w_gate, lw.w_up, lw.gamma_ffn, 0, threads),
+            down=B.i4d_pack_weights(B.I4D_PROJ_PLAIN, lw.w_down, None, None, 0, threads))
+
+    @classmethod
+    def from_host(cls, shape: synth.LayerShape, host: dict, device="cuda") -> "DeviceLayer":
+        obj = cls.__new__(cls)
+        obj._upload(shape, host, device)
+        return obj
+
+    def _upload(self, shape, host, device):
+        self.shape = shape
+        self.host = host
         self.tensors = {}
-        for name, (codes, scales) in self.host.items():
+        for name, (codes, scales) in host.items():
             self.tensors[name] = (torch.from_numpy(codes).to(device), to_device_u16(scales, device))
         self.struct = self._make_struct()
 
@@ -149,3 +166,35 @@ class Workspace:
         off = getattr(self.layout, name)
         esize = torch.tensor([], dtype=dtype).element_size()
         return self.buf[off: off + count * esize].view(dtype)
+
+
+def stacked_layers(shape: synth.LayerShape, seeds, lengths, workers: int = 8, on_host=None):
+    """One independently seeded layer per seed, packed and uploaded, each
+    with its own KV cache prefilled with that seed's cached tokens (the
+    stack of a full-model step).  Weights and cache tokens are drawn and
+    packed in `workers` host threads; uploads and the prefill (kv_append)
+    run on the calling thread.  ``on_host(seed, lw, prefill)``, if given,
+    runs in the worker on the layer's host arrays before they are dropped;
+    its results are returned in seed order.  Returns (layers, caches,
+    results)."""
+    lengths = np.asarray(lengths, np.int32)
+
+    def host(seed):
+        lw = synth.make_layer(shape, seed)
+        packed = DeviceLayer.pack_host(shape, lw, threads=2)
+        pre = synth.make_cache_prefill(shape, lengths, seed)
+        extra = on_host(seed, lw, pre) if on_host else None
+        del lw
+        return packed, pre, extra
+
+    layers, caches, extras = [], [], []
+    with ThreadPoolExecutor(max(1, workers)) as ex:
+        for packed, pre, extra in ex.map(host, seeds):
+            layers.append(DeviceLayer.from_host(shape, packed))
+            c = DeviceCache(shape, lengths)
+            c.prefill(pre)
+            caches.append(c)
+            extras.append(extra)
+            for name in list(packed):  # the host copies are not needed once uploaded
+                packed[name] = None
+    return layers, caches, extras

@@ -65,6 +65,8 @@ SHAPE_TINY = LayerShape(256, 4, 2, 64, 512)
 SHAPE_SMALL128 = LayerShape(512, 8, 2, 128, 1024)
 
 LM_VOCAB = 128256
+# seed of the LM head of the 32-layer 8B-shape model (its layers take seeds 4000..4031)
+LM_HEAD_SEED = 4999
 
 
 @dataclasses.dataclass(frozen=True)

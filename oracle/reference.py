@@ -266,14 +266,15 @@ def attention_one_row(q_rot, k_codes, k_scales, v_codes, v_scales, L: int, b: in
     n_kv = k_codes.shape[1]
     G = n_q // n_kv
     out = np.empty((n_q, hd))
-    for h in range(n_q):
-        j = h // G
+    for j in range(n_kv):
+        # the G query heads of kv head j read the same dequantized entries
         k_hat = dequantize_kv(k_codes[:L, j, :], k_scales[:L, j])     # [L, hd]
         v_hat = dequantize_kv(v_codes[:L, j, :], v_scales[:L, j])
-        sc = (k_hat @ q_rot[h]) / (b * np.sqrt(hd))
-        p = np.exp(sc - sc.max())
-        p /= p.sum()
-        out[h] = fwht(p @ v_hat) / b
+        for h in range(j * G, (j + 1) * G):
+            sc = (k_hat @ q_rot[h]) / (b * np.sqrt(hd))
+            p = np.exp(sc - sc.max())
+            p /= p.sum()
+            out[h] = fwht(p @ v_hat) / b
     return out
 
 

@@ -47,3 +47,26 @@ def oracle_cache_from_tokens(shape, k_rows, v_rows):
         vq, vs = O.quantize_kv(synth.bf16_bits_to_f32(v))
         rows.append(O.RowCache(kq, ks, vq, vs))
     return rows
+
+
+def assert_appended_exact(cache, ws, shape, lengths):
+    """The codes and fp16 scales the decode step appended at position L-1
+    of every row equal the oracle's encoding (rotation, scale, rounding) of
+    the step's own bf16 key and value, read back from the workspace.  The
+    encoding is exact, so this is a bit-for-bit check of the in-step append
+    (the oracle's own fp64 projection may round a k or v differently to bf16;
+    that comparison is only reported)."""
+    import torch
+    from int4_quantized_decode_amd import device as D
+    M = len(lengths)
+    n = M * shape.n_kv_heads * shape.head_dim
+    kb = D.to_host_u16(ws.view("k", torch.int16, n)).reshape(M, shape.n_kv_heads, shape.head_dim)
+    vb = D.to_host_u16(ws.view("v", torch.int16, n)).reshape(M, shape.n_kv_heads, shape.head_dim)
+    rk, rks = O.quantize_kv(synth.bf16_bits_to_f32(kb))
+    rv, rvs = O.quantize_kv(synth.bf16_bits_to_f32(vb))
+    for r, L in enumerate(lengths):
+        k, v, ks, vs = cache.read_codes(r, int(L) - 1, int(L))
+        np.testing.assert_array_equal(k[0], rk[r], err_msg=f"key codes of row {r}")
+        np.testing.assert_array_equal(ks[0], rks[r].view(np.uint16), err_msg=f"key scales of row {r}")
+        np.testing.assert_array_equal(v[0], rv[r], err_msg=f"value codes of row {r}")
+        np.testing.assert_array_equal(vs[0], rvs[r].view(np.uint16), err_msg=f"value scales of row {r}")

@@ -350,3 +350,38 @@ def test_kv_unpack_reads_documented_layout():
             np.testing.assert_array_equal(v[:, j], codes_v[slots])
             np.testing.assert_array_equal(ks[:, j], sk[slots])
             np.testing.assert_array_equal(vs[:, j], sv[slots])
+
+
+# ---------------------------------------------------------------------------
+# projection launch plans
+# ---------------------------------------------------------------------------
+
+PLAN_SHAPES = [synth.SHAPE_1B, synth.SHAPE_8B, synth.SHAPE_70B, synth.SHAPE_TINY, synth.SHAPE_SMALL128,
+               synth.LayerShape(640, 5, 5, 128, 1152), synth.LayerShape(4096, 8, 2, 128, 8192),
+               synth.LayerShape(1024, 8, 2, 128, 16384), synth.LayerShape(1024, 16, 4, 64, 2048)]
+
+
+@pytest.mark.parametrize("shape", PLAN_SHAPES, ids=lambda s: f"d{s.d_model}_f{s.d_ffn}_hd{s.head_dim}")
+def test_every_projection_plan_has_a_kernel(shape):
+    """For every stage and every batch size the decode step takes, the plan
+    it would launch names a kernel the library holds (a plan without one
+    fails the call with I4D_ERR_UNSUPPORTED rather than launching nothing),
+    and it fits the 160 KiB of LDS of a CU."""
+    cs = B.make_shape(shape)
+    for M in range(1, B.I4D_MAX_ROWS + 1):
+        for stage in range(4):
+            p = B.i4d_projection_plan_of(cs, stage, M)
+            assert p.instantiated == 1, (M, stage, p.strips_per_workgroup, p.k_slices, p.depth, p.persistent)
+            assert p.kernel == (0 if M == 1 else 1)
+            assert 0 < p.lds_bytes <= 160 * 1024 and p.grid >= 1
+            if M > 1:
+                assert p.waves == 8 and p.strips_per_workgroup in (1, 2, 3, 4, 5, 7)
+
+
+def test_projection_plan_splits_large_k_only_with_many_rows():
+    cs = B.make_shape(synth.SHAPE_8B)
+    # down projection (K = 14336): unsplit at 16 rows, split at 32
+    assert B.i4d_projection_plan_of(cs, 3, 16).k_slices == 1
+    assert B.i4d_projection_plan_of(cs, 3, 32).k_slices > 1
+    with pytest.raises(B.I4DError):
+        B.i4d_projection_plan_of(cs, 4, 1)
