@@ -358,6 +358,28 @@ typedef struct {
 } i4d_projection_plan;
 i4d_status i4d_projection_plan_of(const i4d_layer_shape* shape, int stage, int M, i4d_projection_plan* out);
 
+/* Bytes of the library-owned scratch array of i4d_decode_block_step_noalloc
+ * (one per GPU, held until the process ends). */
+#define I4D_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * i4d_decode_block_step without a workspace argument.  The step's
+ * intermediates and counters live in a device array the library holds on
+ * each GPU (I4D_NOALLOC_SCRATCH_BYTES, enough for every shape here at the
+ * automatic split count; a step that needs more returns I4D_ERR_WORKSPACE
+ * before anything is enqueued).  Nothing is allocated: the first call on a
+ * device looks the array up (hipGetSymbolAddress) and clears its counters
+ * with a kernel on `stream`; every completed step leaves them at zero.
+ * The caller still owns every input and output.  All calls on one GPU share
+ * its array, so calls that overlap on one GPU (other streams, other
+ * threads) race and must be serialised by the caller.  Arguments, results
+ * and errors otherwise as for i4d_decode_block_step. */
+i4d_status i4d_decode_block_step_noalloc(const i4d_layer* layer, const i4d_kv_cache* cache,
+                                         const uint16_t* x_in, uint16_t* x_out, const int32_t* ctx_len,
+                                         int M, int max_ctx_len, int num_splits, float* attn_f32,
+                                         void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Final norm + LM head + greedy argmax (full-model step)                    */
 /* ------------------------------------------------------------------------ */

@@ -24,6 +24,7 @@ I4D_MAX_SPLITS = 256
 I4D_DEVERR_APPEND_POS = 1
 I4D_DEVERR_CTX_LEN = 2
 I4D_DEVERR_SYNC = 4
+I4D_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 STATUS_NAMES = {0: "I4D_OK", -1: "I4D_ERR_NULL", -2: "I4D_ERR_SHAPE", -3: "I4D_ERR_UNSUPPORTED",
                 -4: "I4D_ERR_ALIGN", -5: "I4D_ERR_WORKSPACE", -6: "I4D_ERR_RANGE", -7: "I4D_ERR_HIP"}
@@ -97,6 +98,8 @@ _SIGS = {
     "i4d_decode_step_is_one_launch": (_I, [ctypes.POINTER(i4d_layer_shape), _I, ctypes.POINTER(_I)]),
     "i4d_decode_block_step": (_I, [ctypes.POINTER(i4d_layer), ctypes.POINTER(i4d_kv_cache), _VP, _VP, _VP,
                                    _I, _I, _I, _VP, ctypes.c_size_t, _VP, _VP]),
+    "i4d_decode_block_step_noalloc": (_I, [ctypes.POINTER(i4d_layer), ctypes.POINTER(i4d_kv_cache), _VP, _VP,
+                                           _VP, _I, _I, _I, _VP, _VP]),
     "i4d_lm_head_workspace_bytes": (_I, [_I, _I, c_size_p]),
     "i4d_lm_head_argmax": (_I, [_VP, _I, _I, _VP, _I, ctypes.c_float, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
 }
@@ -326,6 +329,13 @@ def i4d_decode_block_step(layer: i4d_layer, cache: i4d_kv_cache, x_in, x_out, ct
     _check(lib().i4d_decode_block_step(ctypes.byref(layer), ctypes.byref(cache), ptr(x_in), ptr(x_out),
                                        ptr(ctx_len), M, max_ctx_len, num_splits, ptr(workspace),
                                        workspace_bytes, ptr(attn_f32), stream_handle(stream)))
+
+
+def i4d_decode_block_step_noalloc(layer: i4d_layer, cache: i4d_kv_cache, x_in, x_out, ctx_len, M: int,
+                                  max_ctx_len: int, num_splits: int, attn_f32=None, stream=None):
+    _check(lib().i4d_decode_block_step_noalloc(ctypes.byref(layer), ctypes.byref(cache), ptr(x_in), ptr(x_out),
+                                               ptr(ctx_len), M, max_ctx_len, num_splits, ptr(attn_f32),
+                                               stream_handle(stream)))
 
 
 def i4d_lm_head_argmax(w_lm, V: int, d: int, h, M: int, rms_eps: float, logits_out, token_out,

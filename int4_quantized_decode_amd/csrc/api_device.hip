@@ -196,6 +196,79 @@ __global__ void zero_fill_kernel(u32x4_t* p, size_t n16) {
 
 }  // namespace
 
+namespace i4d {
+
+i4d_status check_decode_step(const i4d_layer* layer, const i4d_kv_cache* cache, const uint16_t* x_in,
+                             const uint16_t* x_out, const int32_t* ctx_len, int M, int max_ctx_len,
+                             int num_splits, const float* attn_f32, i4d_workspace_layout* wl) {
+  I4D_TRY(check_layer(layer));
+  I4D_TRY(check_rows(M));
+  I4D_TRY(check_cache(cache, &layer->shape, M));
+  I4D_TRY(need(x_in, "x_in"));
+  I4D_TRY(need(x_out, "x_out"));
+  I4D_TRY(need(ctx_len, "ctx_len"));
+  if (attn_f32 && !aligned16(attn_f32)) return fail(I4D_ERR_ALIGN, "attn_f32 not 16-byte aligned");
+  if (x_in == x_out) return fail(I4D_ERR_RANGE, "x_in and x_out must not alias");
+  if (max_ctx_len < 1 || max_ctx_len > cache->total_capacity)
+    return fail(I4D_ERR_RANGE, "max_ctx_len %d outside [1, capacity]", max_ctx_len);
+  return i4d_workspace_layout_of(&layer->shape, M, max_ctx_len, num_splits, wl);
+}
+
+i4d_status run_decode_step(const i4d_layer* layer, const i4d_kv_cache* cache, const uint16_t* x_in,
+                           uint16_t* x_out, const int32_t* ctx_len, int M, int max_ctx_len, int num_splits,
+                           char* ws, const i4d_workspace_layout& wl, size_t split_part_bytes, float* attn_f32,
+                           hipStream_t st) {
+  float* q = (float*)(ws + wl.q);
+  uint16_t* k = (uint16_t*)(ws + wl.k);
+  uint16_t* v = (uint16_t*)(ws + wl.v);
+  uint16_t* attn = (uint16_t*)(ws + wl.attn);
+  float* h = (float*)(ws + wl.h);
+  uint16_t* hb = (uint16_t*)(ws + wl.h_bf16);
+  uint16_t* act = (uint16_t*)(ws + wl.a);
+  const i4d_layer_shape& s = layer->shape;
+
+  if (M == 1 && step_m1_supported(&s)) {
+    StepInputs in;
+    in.layer = layer;
+    in.qkv = qkv_args(layer, x_in, ctx_len, 1, q, k, v);
+    in.o = o_args(layer, attn, x_in, 1, h, hb);
+    in.gu = gu_args(layer, hb, 1, act);
+    in.down = down_args(layer, act, h, 1, x_out);
+    in.attn = attention_args(cache, s, q, ctx_len, 1, max_ctx_len, step_m1_splits(&s, max_ctx_len, num_splits),
+                             ws + wl.attn_ws, attn_f32, attn, k, v);
+    in.sync = (unsigned*)(ws + wl.sync);
+    return launch_step_m1(in, st);
+  }
+  // the projections may split K across workgroups through the workspace
+  auto split = [&](ProjArgs a) {
+    a.split_cnt = (unsigned*)(ws + wl.split_cnt);
+    a.split_part = (float*)(ws + wl.split_part);
+    a.split_bytes = split_part_bytes;
+    return a;
+  };
+  I4D_TRY(launch_projection(EPI_QKV, split(qkv_args(layer, x_in, ctx_len, M, q, k, v)), st));
+  // the attention launch first appends the new token of row m at position
+  // ctx_len[m] - 1 of cache row m (inside the workgroup that owns that block)
+  I4D_TRY(do_attention(cache, s, q, ctx_len, M, max_ctx_len, num_splits, ws + wl.attn_ws, attn_f32,
+                       attn, k, v, true, st));
+  I4D_TRY(launch_projection(EPI_O, split(o_args(layer, attn, x_in, M, h, hb)), st));
+  I4D_TRY(launch_projection(EPI_GU, split(gu_args(layer, hb, M, act)), st));
+  I4D_TRY(launch_projection(EPI_DOWN, split(down_args(layer, act, h, M, x_out)), st));
+  return ok();
+}
+
+i4d_status launch_zero_fill(void* p, size_t bytes, hipStream_t st) {
+  if (bytes == 0) return ok();
+  const size_t n16 = bytes / 16;
+  const unsigned grid = (unsigned)std::min<size_t>(1024, (n16 + 255) / 256);
+  hipLaunchKernelGGL(zero_fill_kernel, dim3(grid), dim3(256), 0, st, (u32x4_t*)p, n16);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(I4D_ERR_HIP, "zero fill: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace i4d
+
 extern "C" {
 
 i4d_status i4d_attn_qkv(const i4d_layer* layer, const uint16_t* x, const int32_t* ctx_len, int M,
@@ -288,60 +361,13 @@ i4d_status i4d_decode_block_step(const i4d_layer* layer, const i4d_kv_cache* cac
                                  const uint16_t* x_in, uint16_t* x_out, const int32_t* ctx_len,
                                  int M, int max_ctx_len, int num_splits, void* workspace,
                                  size_t workspace_bytes, float* attn_f32, void* stream) {
-  I4D_TRY(check_layer(layer));
-  I4D_TRY(check_rows(M));
-  I4D_TRY(check_cache(cache, &layer->shape, M));
-  I4D_TRY(need(x_in, "x_in"));
-  I4D_TRY(need(x_out, "x_out"));
-  I4D_TRY(need(ctx_len, "ctx_len"));
-  I4D_TRY(need(workspace, "workspace"));
-  if (attn_f32 && !aligned16(attn_f32)) return fail(I4D_ERR_ALIGN, "attn_f32 not 16-byte aligned");
-  if (x_in == x_out) return fail(I4D_ERR_RANGE, "x_in and x_out must not alias");
-  if (max_ctx_len < 1 || max_ctx_len > cache->total_capacity)
-    return fail(I4D_ERR_RANGE, "max_ctx_len %d outside [1, capacity]", max_ctx_len);
   i4d_workspace_layout wl;
-  I4D_TRY(i4d_workspace_layout_of(&layer->shape, M, max_ctx_len, num_splits, &wl));
+  I4D_TRY(check_decode_step(layer, cache, x_in, x_out, ctx_len, M, max_ctx_len, num_splits, attn_f32, &wl));
+  I4D_TRY(need(workspace, "workspace"));
   if (workspace_bytes < wl.total)
     return fail(I4D_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, wl.total);
-  hipStream_t st = (hipStream_t)stream;
-  char* ws = (char*)workspace;
-  float* q = (float*)(ws + wl.q);
-  uint16_t* k = (uint16_t*)(ws + wl.k);
-  uint16_t* v = (uint16_t*)(ws + wl.v);
-  uint16_t* attn = (uint16_t*)(ws + wl.attn);
-  float* h = (float*)(ws + wl.h);
-  uint16_t* hb = (uint16_t*)(ws + wl.h_bf16);
-  uint16_t* act = (uint16_t*)(ws + wl.a);
-  const i4d_layer_shape& s = layer->shape;
-
-  if (M == 1 && step_m1_supported(&s)) {
-    StepInputs in;
-    in.layer = layer;
-    in.qkv = qkv_args(layer, x_in, ctx_len, 1, q, k, v);
-    in.o = o_args(layer, attn, x_in, 1, h, hb);
-    in.gu = gu_args(layer, hb, 1, act);
-    in.down = down_args(layer, act, h, 1, x_out);
-    in.attn = attention_args(cache, s, q, ctx_len, 1, max_ctx_len, step_m1_splits(&s, max_ctx_len, num_splits),
-                             ws + wl.attn_ws, attn_f32, attn, k, v);
-    in.sync = (unsigned*)(ws + wl.sync);
-    return launch_step_m1(in, st);
-  }
-  // the projections may split K across workgroups through the workspace
-  auto split = [&](ProjArgs a) {
-    a.split_cnt = (unsigned*)(ws + wl.split_cnt);
-    a.split_part = (float*)(ws + wl.split_part);
-    a.split_bytes = wl.sync - wl.split_part;
-    return a;
-  };
-  I4D_TRY(launch_projection(EPI_QKV, split(qkv_args(layer, x_in, ctx_len, M, q, k, v)), st));
-  // the attention launch first appends the new token of row m at position
-  // ctx_len[m] - 1 of cache row m (inside the workgroup that owns that block)
-  I4D_TRY(do_attention(cache, s, q, ctx_len, M, max_ctx_len, num_splits, ws + wl.attn_ws, attn_f32,
-                       attn, k, v, true, st));
-  I4D_TRY(launch_projection(EPI_O, split(o_args(layer, attn, x_in, M, h, hb)), st));
-  I4D_TRY(launch_projection(EPI_GU, split(gu_args(layer, hb, M, act)), st));
-  I4D_TRY(launch_projection(EPI_DOWN, split(down_args(layer, act, h, M, x_out)), st));
-  return ok();
+  return run_decode_step(layer, cache, x_in, x_out, ctx_len, M, max_ctx_len, num_splits, (char*)workspace, wl,
+                         wl.sync - wl.split_part, attn_f32, (hipStream_t)stream);
 }
 
 i4d_status i4d_projection_plan_of(const i4d_layer_shape* shape, int stage, int M, i4d_projection_plan* out) {
@@ -383,13 +409,7 @@ i4d_status i4d_decode_step_is_one_launch(const i4d_layer_shape* shape, int M, in
 i4d_status i4d_workspace_init(void* workspace, size_t bytes, void* stream) {
   I4D_TRY(need(workspace, "workspace"));
   if (bytes % 16) return fail(I4D_ERR_RANGE, "workspace bytes %zu not a multiple of 16", bytes);
-  if (bytes == 0) return ok();
-  const size_t n16 = bytes / 16;
-  const unsigned grid = (unsigned)std::min<size_t>(1024, (n16 + 255) / 256);
-  hipLaunchKernelGGL(zero_fill_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, (u32x4_t*)workspace, n16);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(I4D_ERR_HIP, "workspace init: %s", hipGetErrorString(e));
-  return ok();
+  return launch_zero_fill(workspace, bytes, (hipStream_t)stream);
 }
 
 i4d_status i4d_lm_head_argmax(const uint16_t* w_lm, int V, int d, const uint16_t* h, int M,

@@ -385,3 +385,17 @@ def test_projection_plan_splits_large_k_only_with_many_rows():
     assert B.i4d_projection_plan_of(cs, 3, 32).k_slices > 1
     with pytest.raises(B.I4DError):
         B.i4d_projection_plan_of(cs, 4, 1)
+
+
+def test_noalloc_step_rejects_a_step_larger_than_its_scratch():
+    """A step whose intermediates exceed the library-owned scratch is
+    refused on the host, before any device call (70B shape, 32 rows, 256
+    forced KV splits: 272 MB of split partials)."""
+    shape = B.make_shape(synth.SHAPE_70B)
+    layer = _layer(shape)
+    cache = _cache(n_kv_heads=8, head_dim=128, total_capacity=32 * 4096, n_rows=32)
+    with pytest.raises(B.I4DError) as ei:
+        B.i4d_decode_block_step_noalloc(layer, cache, FAKE, FAKE + 4096, FAKE, 32, 4096, 256)
+    assert ei.value.status == -5 and "scratch" in str(ei.value)
+    # the same step fits a caller's workspace of the reported size
+    assert B.i4d_workspace_bytes(shape, 32, 4096, 256) > B.I4D_NOALLOC_SCRATCH_BYTES
