@@ -65,6 +65,18 @@ R10 the block's new k and v are rounded to bf16 before they are encoded
 R11 final norm and LM head: gamma_f folded into the bf16 LM head weight
     (fp32 product, then bf16 rounding), rho_f applied to the logits, argmax
     with ties to the lowest index.
+R12 E4M3 decode-weight variant: the pages report E4M3 decode weights beside
+    the INT4 ones [P1 premises-and-limits: +0.02 perplexity; the INT4 decode
+    path is 31-51% faster than the FP8 path; P3 abstract] and say nothing of
+    their scale.  Reading: only the weight format changes (the activations,
+    the gain fold, rho and the rotated INT4 KV cache stay as in the INT4
+    block); one fp16 scale per (output row, 128 consecutive input channels),
+    s = fp16(absmax / 448) with the R1 arithmetic, codes = E4M3 of
+    fp32(w / s) rounded to nearest, ties to even, saturating at +-448 (the
+    OCP FP8 E4M3 format: 1 sign, 4 exponent bits with bias 7, 3 mantissa
+    bits, subnormals m 2^-9, no infinities, largest finite 448); s == 0
+    gives zero codes.  The sign of a value that rounds to zero is kept
+    (code 0x80 for negative inputs).
 """
 from __future__ import annotations
 
@@ -165,6 +177,78 @@ def code_of_nibble_via_bf16_128(u) -> np.ndarray:
     u = np.asarray(u, dtype=np.uint32)
     bits = (np.uint32(0x4300) | u) << np.uint32(16)
     return bits.view(np.float32).astype(np.float64) - 136.0
+
+
+# ---------------------------------------------------------------------------
+# E4M3 weight encoding (R12)
+# ---------------------------------------------------------------------------
+
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Value of E4M3 codes (uint8) as fp64: (-1)^s 2^(e-7) (1 + m/8) for
+    exponent field e > 0, (-1)^s m 2^-9 for e == 0; the two NaN codes
+    (0x7F, 0xFF) decode to NaN.  [OCP FP8 E4M3]"""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    mag = np.where((c & 0x7F) == 0x7F, np.nan, mag)
+    return sign * mag
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """fp32 values -> E4M3 codes: nearest representable value, ties to the
+    even mantissa, magnitudes of 448 and above saturate to 448 (code 0x7E).
+    Below 2^-6 the spacing is 2^-9 (subnormals); in [2^E, 2^(E+1)) it is
+    2^(E-3).  The input sign is kept, also on zero.  [R12]"""
+    x = np.asarray(x, dtype=np.float32).astype(np.float64)
+    sign = np.where(np.signbit(x), 0x80, 0x00).astype(np.int64)
+    a = np.abs(x)
+    # the exponent E of a normal magnitude, and its spacing
+    E = np.floor(np.log2(np.where(a > 0, a, 1.0))).astype(np.int64)
+    E = np.clip(E, -6, 8)
+    step = np.exp2((E - 3).astype(np.float64))
+    q = np.rint(a / step)                                   # mantissa steps, ties to even
+    # rounding up to the next power of two moves to the next exponent
+    bump = q >= 16
+    E = np.where(bump, E + 1, E)
+    q = np.where(bump, 8.0, q)
+    normal = np.where(E + 7 > 15, 0x7E, ((E + 7) << 3) | (q.astype(np.int64) - 8))
+    # subnormal range: multiples of 2^-9 (rounding up to 2^-6 gives code 0x08)
+    sub = np.rint(np.minimum(a, 1.0) * 512.0).astype(np.int64)
+    mag = np.where(a < 2.0 ** -6, sub, normal)
+    mag = np.where(a >= E4M3_MAX, 0x7E, np.minimum(mag, 0x7E))
+    return (sign | mag).astype(np.uint8)
+
+
+def quantize_weight_e4m3(W, gamma=None) -> tuple[np.ndarray, np.ndarray, str]:
+    """Group-128 E4M3 codes of a [N, K] weight (gain folded first, R3):
+    per (row, group) s = fp16(absmax / 448) (fp32 division), codes =
+    E4M3(fp32(w / fp32(s))); s == 0 -> codes 0.  Returns (codes uint8
+    [N, K], scales fp16 [N, K/128], "e4m3").  [R12]"""
+    Wp = fold_gain(W, gamma)
+    N, K = Wp.shape
+    if K % GROUP:
+        raise ValueError("K must be a multiple of 128")
+    g = Wp.reshape(N, K // GROUP, GROUP)
+    a = np.max(np.abs(g), axis=-1)
+    s = fp16_round(a / np.float32(E4M3_MAX))
+    sf = s.astype(np.float32)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = g / sf
+    codes = e4m3_encode(np.where(sf == 0, np.float32(0.0), r))
+    return codes.reshape(N, K), s, "e4m3"
+
+
+def dequantize_weight_e4m3(codes, s) -> np.ndarray:
+    """W_hat[n, k] = fp64(s[n, k // 128]) * E4M3 value of code[n, k]."""
+    c = np.asarray(codes)
+    N, K = c.shape
+    sf = np.asarray(s, dtype=np.float16).astype(np.float64)
+    return (e4m3_decode(c).reshape(N, K // GROUP, GROUP) * sf[:, :, None]).reshape(N, K)
 
 
 # ---------------------------------------------------------------------------
@@ -305,6 +389,17 @@ def quantize_layer(lw) -> QuantLayer:
     )
 
 
+def quantize_layer_e4m3(lw) -> QuantLayer:
+    """The same layer with E4M3 decode weights (R12); gains fold as for INT4."""
+    return QuantLayer(
+        qkv=quantize_weight_e4m3(lw.w_qkv, lw.gamma_attn),
+        o=quantize_weight_e4m3(lw.w_o, None),
+        gate=quantize_weight_e4m3(lw.w_gate, lw.gamma_ffn),
+        up=quantize_weight_e4m3(lw.w_up, lw.gamma_ffn),
+        down=quantize_weight_e4m3(lw.w_down, None),
+    )
+
+
 @dataclasses.dataclass
 class RowCache:
     """Oracle-side INT4 cache of one row: logical codes per token."""
@@ -340,6 +435,10 @@ def _bf16_bits_to_values(bits) -> np.ndarray:
 
 
 def dense(ql_part) -> np.ndarray:
+    """fp64 weights of an encoded projection: INT4 (codes, scales) or E4M3
+    (codes, scales, "e4m3")."""
+    if len(ql_part) == 3 and ql_part[2] == "e4m3":
+        return dequantize_weight_e4m3(ql_part[0], ql_part[1])
     return dequantize_weight(*ql_part)
 
 
