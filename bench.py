@@ -81,12 +81,13 @@ def require_clean(caches, what):
     return e
 
 
-def algorithmic_bytes(shape, lengths):
-    """INT4 codes (0.5 B/weight) + fp16 group scales + INT4 KV codes and
-    per-token-per-head fp16 scales read by one step."""
+def algorithmic_bytes(shape, lengths, fmt="int4"):
+    """Weight codes (INT4: 0.5 B/weight, E4M3: 1 B/weight) + fp16 group
+    scales + INT4 KV codes and per-token-per-head fp16 scales read by one
+    step."""
     d, F, hd, nq, nkv = shape.d_model, shape.d_ffn, shape.head_dim, shape.n_q_heads, shape.n_kv_heads
     weights = (shape.n_qkv * d + d * nq * hd + 2 * F * d + d * F)
-    w_bytes = weights // 2 + (weights // 128) * 2
+    w_bytes = (weights if fmt == "e4m3" else weights // 2) + (weights // 128) * 2
     kv_bytes = int(np.sum(lengths)) * nkv * 2 * (hd // 2 + 2)
     return w_bytes + kv_bytes, w_bytes, kv_bytes
 
@@ -105,6 +106,8 @@ def main():
     ap.add_argument("--M", type=int, default=0, help="override the batch (70B shape sweep)")
     ap.add_argument("--copies", type=int, default=8)
     ap.add_argument("--splits", type=int, default=-1)
+    ap.add_argument("--weights", default="int4", choices=["int4", "e4m3"],
+                    help="decode-weight format (e4m3: the FP8 decode-weight variant)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-steps", type=int, default=5)
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -149,7 +152,7 @@ def main():
     lw = synth.make_layer(shape, wl.seed)
     pre = synth.make_cache_prefill(shape, lengths, wl.seed)
     xb = synth.make_x(shape, M, wl.seed)
-    base_layer = D.DeviceLayer(shape, lw)
+    base_layer = D.DeviceLayer(shape, lw, fmt=args.weights)
     base_cache = D.DeviceCache(shape, lengths)
     base_cache.prefill(pre)
     layers = [base_layer] + [base_layer.clone() for _ in range(C - 1)]
@@ -167,9 +170,11 @@ def main():
 
     stream = torch.cuda.current_stream()
 
+    step_fn = B.i4d_decode_block_step_e4m3 if args.weights == "e4m3" else B.i4d_decode_block_step
+
     def step(i):
-        B.i4d_decode_block_step(layers[i % C].struct, caches[i % C].struct, x_in, x_out, ctx, M, maxL,
-                                splits, ws.buf, ws.nbytes, None)
+        step_fn(layers[i % C].struct, caches[i % C].struct, x_in, x_out, ctx, M, maxL, splits, ws.buf, ws.nbytes,
+                None)
 
     # eager check that the step runs, then graphs
     step(0)
@@ -196,11 +201,15 @@ def main():
     require_clean(caches, "timed decode steps")
     ms_step = ms_total / args.steps
     us_step = ms_step * 1e3
-    total_b, w_b, kv_b = algorithmic_bytes(shape, lengths)
+    total_b, w_b, kv_b = algorithmic_bytes(shape, lengths, args.weights)
     gbps = total_b / (us_step * 1e-6) / 1e9
 
-    one_launch = B.i4d_decode_step_is_one_launch(B.make_shape(shape), M)
-    if one_launch:
+    one_launch = args.weights == "int4" and B.i4d_decode_step_is_one_launch(B.make_shape(shape), M)
+    if args.weights == "e4m3":
+        # the E4M3 variant's entry is the step as a whole (one launch per
+        # stage, no stage-level timing entry point for gate/up)
+        rf_kernel, rf_bytes, rf_us = "E4M3 decode step (all stage launches)", total_b, us_step
+    elif one_launch:
         # dominant kernel: the one-launch step itself (one kernel per step);
         # its average launch time is the step time measured above
         rf_kernel, rf_bytes, rf_us = "step_m1_kernel (one-launch decode step)", total_b, us_step
@@ -235,12 +244,12 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4 x bf16/fp16 -> f32",
+        "dtype": "e4m3 x bf16 -> f32" if args.weights == "e4m3" else "int4 x bf16/fp16 -> f32",
         "data": "synthetic",
         "config": {"workload": args.workload, "d_model": shape.d_model, "n_q_heads": shape.n_q_heads,
                    "n_kv_heads": shape.n_kv_heads, "head_dim": shape.head_dim, "d_ffn": shape.d_ffn,
                    "M": M, "ctx_total": int(lengths.sum()), "ctx_max": maxL, "num_splits": splits,
-                   "layer_copies": C, "one_launch_step": one_launch,
+                   "layer_copies": C, "one_launch_step": one_launch, "weights": args.weights,
                    "timing": "hip graph of K steps, events on the launch stream"},
         "hbm_GBps": round(gbps, 1),
         "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),

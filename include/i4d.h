@@ -150,6 +150,26 @@ i4d_status i4d_pack_codes(i4d_proj_kind kind, const int8_t* q, const uint16_t* s
 i4d_status i4d_unpack_weights(i4d_proj_kind kind, const void* codes, const uint16_t* scales,
                               int N, int K, int head_dim, int8_t* q_out, uint16_t* s_out);
 
+/* E4M3 decode weights (the FP8 decode-weight variant the summary page [P1]
+ * reports beside the INT4 one in "premises and limits"; its scale rule is
+ * not stated there and is read as the INT4 one with 448 in place of 7):
+ * per (row, 128-group) scale = fp16(absmax/448) (fp32 division, fp16
+ * round-to-nearest-even, saturating), codes = OCP FP8 E4M3 of
+ * fp32(w / scale) rounded to nearest with ties to even and saturating at
+ * +-448, the sign kept also on zero; a zero group stores scale 0 and code 0.
+ * Same kinds, gain fold and strip order as i4d_pack_weights; one byte per
+ * weight in 2 KiB atoms (16 packed rows x 128 channels, [strip][group]),
+ * scales as for INT4.  Host memory. */
+i4d_status i4d_packed_sizes_e4m3(i4d_proj_kind kind, int N, int K, int head_dim, size_t* code_bytes,
+                                 size_t* scale_bytes);
+i4d_status i4d_pack_weights_e4m3(i4d_proj_kind kind, const float* W0, const float* W1, const float* gamma,
+                                 int N, int K, int head_dim, void* codes_out, uint16_t* scales_out,
+                                 int threads);
+/* Inverse of the E4M3 layout permutation: codes q_out [rows][K] (uint8) and
+ * scales s_out [rows][K/128], rows as for i4d_unpack_weights.  Host. */
+i4d_status i4d_unpack_weights_e4m3(i4d_proj_kind kind, const void* codes, const uint16_t* scales, int N, int K,
+                                   int head_dim, uint8_t* q_out, uint16_t* s_out);
+
 /* LM head (full-model step only): bf16 weight = bf16(fp32(gamma_f[k] * W[v][k]))
  * (gamma_f may be NULL) in tiles of 16 rows x 32 channels: element (v, k)
  * at ((v/16 * d/32 + k/32) * 16 + v%16) * 32 + k%32, so the kernel reads
@@ -357,6 +377,21 @@ typedef struct {
   int instantiated;
 } i4d_projection_plan;
 i4d_status i4d_projection_plan_of(const i4d_layer_shape* shape, int stage, int M, i4d_projection_plan* out);
+
+/* The decode step with E4M3 decode weights: as i4d_decode_block_step, with
+ * the layer's four projections packed by i4d_pack_weights_e4m3 (the FP8
+ * decode-weight variant the summary page [P1] reports beside the INT4 path
+ * in "premises and limits"; the INT4 KV cache, the rotation and attention
+ * are the same).  Every M runs one launch per stage; the workspace is the
+ * one i4d_workspace_bytes sizes. */
+i4d_status i4d_decode_block_step_e4m3(const i4d_layer* layer, const i4d_kv_cache* cache, const uint16_t* x_in,
+                                      uint16_t* x_out, const int32_t* ctx_len, int M, int max_ctx_len,
+                                      int num_splits, void* workspace, size_t workspace_bytes, float* attn_f32,
+                                      void* stream);
+
+/* Stage 5 with E4M3 weights (h = x + attn . Wo^T, as i4d_attn_out_proj). */
+i4d_status i4d_attn_out_proj_e4m3(const i4d_layer* layer, const uint16_t* attn_bf16, const uint16_t* x, int M,
+                                  float* h_f32, uint16_t* h_bf16, void* stream);
 
 /* Bytes of the library-owned scratch array of i4d_decode_block_step_noalloc
  * (one per GPU, held until the process ends). */

@@ -80,6 +80,9 @@ _SIGS = {
     "i4d_unpack_weights": (_I, [_I, _VP, _VP, _I, _I, _I, _VP, _VP]),
     "i4d_pack_codes": (_I, [_I, _VP, _VP, _I, _I, _I, _VP, _VP, _I]),
     "i4d_pack_lm_head": (_I, [_VP, _VP, _I, _I, _VP, _I]),
+    "i4d_packed_sizes_e4m3": (_I, [_I, _I, _I, _I, c_size_p, c_size_p]),
+    "i4d_pack_weights_e4m3": (_I, [_I, _VP, _VP, _VP, _I, _I, _I, _VP, _VP, _I]),
+    "i4d_unpack_weights_e4m3": (_I, [_I, _VP, _VP, _I, _I, _I, _VP, _VP]),
     "i4d_kv_cache_bytes": (_I, [_I, _I, ctypes.c_int64, c_size_p, c_size_p, c_size_p, c_size_p]),
     "i4d_kv_append": (_I, [ctypes.POINTER(i4d_kv_cache), _VP, _VP, _VP, _VP, _I, _VP]),
     "i4d_kv_unpack_host": (_I, [ctypes.POINTER(i4d_kv_cache), _VP, _I, _I, _I, _VP, _VP, _VP, _VP]),
@@ -98,6 +101,9 @@ _SIGS = {
     "i4d_decode_step_is_one_launch": (_I, [ctypes.POINTER(i4d_layer_shape), _I, ctypes.POINTER(_I)]),
     "i4d_decode_block_step": (_I, [ctypes.POINTER(i4d_layer), ctypes.POINTER(i4d_kv_cache), _VP, _VP, _VP,
                                    _I, _I, _I, _VP, ctypes.c_size_t, _VP, _VP]),
+    "i4d_decode_block_step_e4m3": (_I, [ctypes.POINTER(i4d_layer), ctypes.POINTER(i4d_kv_cache), _VP, _VP, _VP,
+                                        _I, _I, _I, _VP, ctypes.c_size_t, _VP, _VP]),
+    "i4d_attn_out_proj_e4m3": (_I, [ctypes.POINTER(i4d_layer), _VP, _VP, _I, _VP, _VP, _VP]),
     "i4d_decode_block_step_noalloc": (_I, [ctypes.POINTER(i4d_layer), ctypes.POINTER(i4d_kv_cache), _VP, _VP,
                                            _VP, _I, _I, _I, _VP, _VP]),
     "i4d_lm_head_workspace_bytes": (_I, [_I, _I, c_size_p]),
@@ -219,6 +225,36 @@ def i4d_unpack_weights(kind: int, codes, scales, N: int, K: int, head_dim: int =
     return q, s
 
 
+def i4d_packed_sizes_e4m3(kind: int, N: int, K: int, head_dim: int = 0):
+    cb, sb = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().i4d_packed_sizes_e4m3(kind, N, K, head_dim, ctypes.byref(cb), ctypes.byref(sb)))
+    return cb.value, sb.value
+
+
+def i4d_pack_weights_e4m3(kind: int, W0, W1=None, gamma=None, head_dim: int = 0, threads: int = 0):
+    """fp32 host weights -> (E4M3 codes uint8, fp16 scales uint16) in the device layout."""
+    W0 = np.ascontiguousarray(W0, dtype=np.float32)
+    N, K = W0.shape
+    W1 = None if W1 is None else np.ascontiguousarray(W1, dtype=np.float32)
+    gamma = None if gamma is None else np.ascontiguousarray(gamma, dtype=np.float32)
+    cb, sb = i4d_packed_sizes_e4m3(kind, N, K, head_dim)
+    codes = np.empty(cb, np.uint8)
+    scales = np.empty(sb // 2, np.uint16)
+    _check(lib().i4d_pack_weights_e4m3(kind, ptr(W0), ptr(W1), ptr(gamma), N, K, head_dim,
+                                       ptr(codes), ptr(scales), threads))
+    return codes, scales
+
+
+def i4d_unpack_weights_e4m3(kind: int, codes, scales, N: int, K: int, head_dim: int = 0):
+    rows = 2 * N if kind == I4D_PROJ_GATE_UP else N
+    q = np.empty((rows, K), np.uint8)
+    s = np.empty((rows, K // 128), np.uint16)
+    codes = np.ascontiguousarray(codes)
+    scales = np.ascontiguousarray(scales)
+    _check(lib().i4d_unpack_weights_e4m3(kind, ptr(codes), ptr(scales), N, K, head_dim, ptr(q), ptr(s)))
+    return q, s
+
+
 def i4d_pack_lm_head(W, gamma=None, threads: int = 0):
     """fp32 [V][d] -> bf16 bits in tiles [V/16][d/32][16][32]."""
     W = np.ascontiguousarray(W, dtype=np.float32)
@@ -329,6 +365,19 @@ def i4d_decode_block_step(layer: i4d_layer, cache: i4d_kv_cache, x_in, x_out, ct
     _check(lib().i4d_decode_block_step(ctypes.byref(layer), ctypes.byref(cache), ptr(x_in), ptr(x_out),
                                        ptr(ctx_len), M, max_ctx_len, num_splits, ptr(workspace),
                                        workspace_bytes, ptr(attn_f32), stream_handle(stream)))
+
+
+def i4d_decode_block_step_e4m3(layer: i4d_layer, cache: i4d_kv_cache, x_in, x_out, ctx_len, M: int,
+                               max_ctx_len: int, num_splits: int, workspace, workspace_bytes: int,
+                               attn_f32=None, stream=None):
+    _check(lib().i4d_decode_block_step_e4m3(ctypes.byref(layer), ctypes.byref(cache), ptr(x_in), ptr(x_out),
+                                            ptr(ctx_len), M, max_ctx_len, num_splits, ptr(workspace),
+                                            workspace_bytes, ptr(attn_f32), stream_handle(stream)))
+
+
+def i4d_attn_out_proj_e4m3(layer: i4d_layer, attn_bf16, x, M: int, h_f32, h_bf16, stream=None):
+    _check(lib().i4d_attn_out_proj_e4m3(ctypes.byref(layer), ptr(attn_bf16), ptr(x), M, ptr(h_f32), ptr(h_bf16),
+                                        stream_handle(stream)))
 
 
 def i4d_decode_block_step_noalloc(layer: i4d_layer, cache: i4d_kv_cache, x_in, x_out, ctx_len, M: int,

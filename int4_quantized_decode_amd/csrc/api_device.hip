@@ -217,7 +217,7 @@ i4d_status check_decode_step(const i4d_layer* layer, const i4d_kv_cache* cache, 
 i4d_status run_decode_step(const i4d_layer* layer, const i4d_kv_cache* cache, const uint16_t* x_in,
                            uint16_t* x_out, const int32_t* ctx_len, int M, int max_ctx_len, int num_splits,
                            char* ws, const i4d_workspace_layout& wl, size_t split_part_bytes, float* attn_f32,
-                           hipStream_t st) {
+                           hipStream_t st, int fmt) {
   float* q = (float*)(ws + wl.q);
   uint16_t* k = (uint16_t*)(ws + wl.k);
   uint16_t* v = (uint16_t*)(ws + wl.v);
@@ -227,7 +227,7 @@ i4d_status run_decode_step(const i4d_layer* layer, const i4d_kv_cache* cache, co
   uint16_t* act = (uint16_t*)(ws + wl.a);
   const i4d_layer_shape& s = layer->shape;
 
-  if (M == 1 && step_m1_supported(&s)) {
+  if (fmt == kFmtInt4 && M == 1 && step_m1_supported(&s)) {
     StepInputs in;
     in.layer = layer;
     in.qkv = qkv_args(layer, x_in, ctx_len, 1, q, k, v);
@@ -240,10 +240,12 @@ i4d_status run_decode_step(const i4d_layer* layer, const i4d_kv_cache* cache, co
     return launch_step_m1(in, st);
   }
   // the projections may split K across workgroups through the workspace
+  // (INT4); the weights' format selects the kernels
   auto split = [&](ProjArgs a) {
     a.split_cnt = (unsigned*)(ws + wl.split_cnt);
     a.split_part = (float*)(ws + wl.split_part);
     a.split_bytes = split_part_bytes;
+    a.fmt = fmt;
     return a;
   };
   I4D_TRY(launch_projection(EPI_QKV, split(qkv_args(layer, x_in, ctx_len, M, q, k, v)), st));
@@ -367,7 +369,33 @@ i4d_status i4d_decode_block_step(const i4d_layer* layer, const i4d_kv_cache* cac
   if (workspace_bytes < wl.total)
     return fail(I4D_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, wl.total);
   return run_decode_step(layer, cache, x_in, x_out, ctx_len, M, max_ctx_len, num_splits, (char*)workspace, wl,
-                         wl.sync - wl.split_part, attn_f32, (hipStream_t)stream);
+                         wl.sync - wl.split_part, attn_f32, (hipStream_t)stream, kFmtInt4);
+}
+
+i4d_status i4d_decode_block_step_e4m3(const i4d_layer* layer, const i4d_kv_cache* cache, const uint16_t* x_in,
+                                      uint16_t* x_out, const int32_t* ctx_len, int M, int max_ctx_len,
+                                      int num_splits, void* workspace, size_t workspace_bytes, float* attn_f32,
+                                      void* stream) {
+  i4d_workspace_layout wl;
+  I4D_TRY(check_decode_step(layer, cache, x_in, x_out, ctx_len, M, max_ctx_len, num_splits, attn_f32, &wl));
+  I4D_TRY(need(workspace, "workspace"));
+  if (workspace_bytes < wl.total)
+    return fail(I4D_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, wl.total);
+  return run_decode_step(layer, cache, x_in, x_out, ctx_len, M, max_ctx_len, num_splits, (char*)workspace, wl,
+                         wl.sync - wl.split_part, attn_f32, (hipStream_t)stream, kFmtE4M3);
+}
+
+i4d_status i4d_attn_out_proj_e4m3(const i4d_layer* layer, const uint16_t* attn_bf16, const uint16_t* x, int M,
+                                  float* h_f32, uint16_t* h_bf16, void* stream) {
+  I4D_TRY(check_layer(layer));
+  I4D_TRY(check_rows(M));
+  I4D_TRY(need(attn_bf16, "attn_bf16"));
+  I4D_TRY(need(x, "x"));
+  I4D_TRY(need(h_f32, "h_f32"));
+  I4D_TRY(need(h_bf16, "h_bf16"));
+  ProjArgs a = o_args(layer, attn_bf16, x, M, h_f32, h_bf16);
+  a.fmt = kFmtE4M3;
+  return launch_projection(EPI_O, a, (hipStream_t)stream);
 }
 
 i4d_status i4d_projection_plan_of(const i4d_layer_shape* shape, int stage, int M, i4d_projection_plan* out) {

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 #include <string>
 #include <thread>
 #include <vector>
@@ -147,6 +148,36 @@ static inline uint16_t quantize_group(const float* w, int8_t* q) {
       q[k] = (int8_t)r;
     }
   }
+  return s16;
+}
+
+// E4M3 (OCP FP8: 4 exponent bits, bias 7, 3 mantissa bits, largest finite
+// 448) of a finite fp32 value: nearest, ties to the even mantissa, 448 and
+// above saturating to 448; the sign is kept (also on zero)
+static inline uint8_t e4m3_of(float x) {
+  const uint8_t sign = std::signbit(x) ? 0x80 : 0x00;
+  const double a = fabs((double)x);
+  if (!(a < 448.0)) return sign | 0x7E;
+  if (a < 0.015625) return sign | (uint8_t)nearbyint(a * 512.0);  // 2^-9 steps; 8 -> 2^-6 = 0x08
+  int e;
+  frexp(a, &e);                          // a in [2^(e-1), 2^e)
+  double q = nearbyint(ldexp(a, 4 - e));  // mantissa steps of 2^(e-4): 8..16
+  int E = e - 1;
+  if (q >= 16.0) {
+    q = 8.0;
+    ++E;
+  }
+  const int code = ((E + 7) << 3) | ((int)q - 8);
+  return sign | (uint8_t)std::min(code, 0x7E);
+}
+
+// E4M3 codes of one 128-wide group: scale fp16(absmax / 448)
+static inline uint16_t quantize_group_e4m3(const float* w, uint8_t* q) {
+  float a = 0.f;
+  for (int k = 0; k < kGroup; ++k) a = std::max(a, fabsf(w[k]));
+  const uint16_t s16 = f32_to_f16_sat(a / 448.0f);
+  const float sf = f16_to_f32(s16);
+  for (int k = 0; k < kGroup; ++k) q[k] = sf == 0.f ? 0 : e4m3_of(w[k] / sf);
   return s16;
 }
 
@@ -306,6 +337,69 @@ i4d_status i4d_pack_codes(i4d_proj_kind kind, const int8_t* q, const uint16_t* s
       }
     }
   });
+  return ok();
+}
+
+i4d_status i4d_packed_sizes_e4m3(i4d_proj_kind kind, int N, int K, int head_dim, size_t* code_bytes,
+                                 size_t* scale_bytes) {
+  if (!code_bytes || !scale_bytes) return fail(I4D_ERR_NULL, "output pointer is NULL");
+  i4d_status st = check_pack_args(kind, N, K, head_dim);
+  if (st) return st;
+  const int Np = packed_rows(kind, N);
+  *code_bytes = (size_t)Np * (size_t)K;
+  *scale_bytes = packed_scale_elems(Np, K) * sizeof(uint16_t);
+  return ok();
+}
+
+i4d_status i4d_pack_weights_e4m3(i4d_proj_kind kind, const float* W0, const float* W1, const float* gamma,
+                                 int N, int K, int head_dim, void* codes_out, uint16_t* scales_out,
+                                 int threads) {
+  i4d_status st = check_pack_args(kind, N, K, head_dim);
+  if (st) return st;
+  if (!W0 || !codes_out || !scales_out) return fail(I4D_ERR_NULL, "W0/codes_out/scales_out NULL");
+  if (kind == I4D_PROJ_GATE_UP && !W1) return fail(I4D_ERR_NULL, "gate/up needs W1 (up)");
+  if (kind == I4D_PROJ_PLAIN && gamma)
+    return fail(I4D_ERR_RANGE, "PLAIN projections take no gain (gamma must be NULL)");
+  const int Np = packed_rows(kind, N);
+  const int G = groups_of(K);
+  uint8_t* codes = (uint8_t*)codes_out;
+  parallel_for(Np / kStrip, threads, [&](long t0, long t1) {
+    float w[kGroup];
+    uint8_t q[kGroup];
+    for (long t = t0; t < t1; ++t) {
+      for (int r = 0; r < kStrip; ++r) {
+        int p = (int)t * kStrip + r, mat, row;
+        source_row(kind, p, head_dim, &mat, &row);
+        const float* src = (mat ? W1 : W0) + (size_t)row * K;
+        for (int g = 0; g < G; ++g) {
+          for (int k = 0; k < kGroup; ++k) {
+            const float v = src[g * kGroup + k];
+            w[k] = gamma ? gamma[g * kGroup + k] * v : v;  // one fp32 product
+          }
+          scales_out[((size_t)t * G + g) * kStrip + r] = quantize_group_e4m3(w, q);
+          for (int k = 0; k < kGroup; ++k) codes[e4m3_code_offset(p, g * kGroup + k, K)] = q[k];
+        }
+      }
+    }
+  });
+  return ok();
+}
+
+i4d_status i4d_unpack_weights_e4m3(i4d_proj_kind kind, const void* codes, const uint16_t* scales, int N, int K,
+                                   int head_dim, uint8_t* q_out, uint16_t* s_out) {
+  i4d_status st = check_pack_args(kind, N, K, head_dim);
+  if (st) return st;
+  if (!codes || !scales || !q_out || !s_out) return fail(I4D_ERR_NULL, "NULL pointer");
+  const int Np = packed_rows(kind, N);
+  const int G = groups_of(K);
+  const uint8_t* c = (const uint8_t*)codes;
+  for (int p = 0; p < Np; ++p) {
+    int mat, row;
+    source_row(kind, p, head_dim, &mat, &row);
+    const int out_row = mat * N + row;
+    for (int k = 0; k < K; ++k) q_out[(size_t)out_row * K + k] = c[e4m3_code_offset(p, k, K)];
+    for (int g = 0; g < G; ++g) s_out[(size_t)out_row * G + g] = scales[scale_index(p, g, K)];
+  }
   return ok();
 }
 

@@ -48,6 +48,19 @@ constexpr int kVBlock = 32;
 
 inline constexpr int nibble_slot(int e) { return 4 * (e & 1) + (e >> 1); }
 
+// E4M3 weights (the FP8 decode-weight variant): one byte per weight, the
+// same strips, groups and scales; an atom (strip, group) is 2 KiB: lane
+// l = 16*j + r holds 32 bytes, byte 8*kb + e = the code of row r at
+// k = 128*g + 32*kb + 8*j + e (kb = 0..3, e = 0..7), i.e. the four bf16 MFMA
+// A operands of the group in k order once decoded, two 16-byte loads.
+constexpr int kAtomBytesE4M3 = 2048;
+
+inline size_t e4m3_code_offset(int p, int k, int K) {
+  int t = p / kStrip, r = p % kStrip, g = k / kGroup, kk = k % kGroup;
+  int kb = kk / 32, j = (kk % 32) / 8, e = kk % 8;
+  return (((size_t)t * (K / kGroup) + g) * 64 + 16 * j + r) * 32 + kb * 8 + e;
+}
+
 inline int groups_of(int K) { return K / kGroup; }
 inline int g8_of(int K) { return (K / kGroup + 7) / 8; }
 

@@ -21,6 +21,7 @@
 
 #include "device_common.h"
 #include "i4d_internal.h"
+#include "proj.h"
 #include "step.h"
 
 namespace i4d {
@@ -118,5 +119,5 @@ extern "C" i4d_status i4d_decode_block_step_noalloc(const i4d_layer* layer, cons
     }
   }
   return run_decode_step(layer, cache, x_in, x_out, ctx_len, M, max_ctx_len, num_splits, (char*)base, sl,
-                         split_part_bytes, attn_f32, s);
+                         split_part_bytes, attn_f32, s, kFmtInt4);
 }

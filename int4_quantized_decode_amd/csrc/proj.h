@@ -9,6 +9,10 @@ namespace i4d {
 
 enum Epi { EPI_QKV = 0, EPI_O = 1, EPI_GU = 2, EPI_DOWN = 3 };
 
+// weight formats: INT4 codes (1 KiB atoms) or E4M3 codes (2 KiB atoms), both
+// with fp16 scales per (row, 128-group)
+enum WeightFormat { kFmtInt4 = 0, kFmtE4M3 = 1 };
+
 struct ProjArgs {
   const uint8_t* codes;    // packed atoms [Np/16][K/128][64][16]
   const uint16_t* scales;  // fp16 [Np/16][G][16]
@@ -37,10 +41,13 @@ struct ProjArgs {
   float* split_part;
   unsigned* split_cnt;
   size_t split_bytes;
+  int fmt;  // WeightFormat of codes/scales
 };
 
 
 i4d_status launch_projection(int epi, const ProjArgs& a, hipStream_t st);
+// E4M3 weights (a.fmt == kFmtE4M3), any M in [1, 32]
+i4d_status launch_projection_e4m3(int epi, const ProjArgs& a, hipStream_t st);
 // the launch plan of launch_projection for `a` (host only, nothing launched)
 i4d_status projection_plan_of(int epi, const ProjArgs& a, i4d_projection_plan* out);
 

@@ -634,6 +634,7 @@ static i4d_status projection_fits(const ProjArgs& a, const ProjLaunch& l) {
 
 i4d_status launch_projection(int epi, const ProjArgs& a, hipStream_t st) {
   if (epi < EPI_QKV || epi > EPI_DOWN) return fail(I4D_ERR_RANGE, "bad epilogue %d", epi);
+  if (a.fmt == kFmtE4M3) return launch_projection_e4m3(epi, a, st);
   const bool rho = epi == EPI_QKV || epi == EPI_GU;
   const ProjLaunch l = plan_projection(a, rho);
   const i4d_status fit = projection_fits(a, l);

@@ -31,19 +31,23 @@ def bf16_tensor_to_f32(t: torch.Tensor) -> np.ndarray:
 class DeviceLayer:
     """One layer's packed INT4 weights on the GPU and its i4d_layer struct."""
 
-    def __init__(self, shape: synth.LayerShape, lw: synth.LayerWeights, device="cuda", threads: int = 0):
-        self._upload(shape, self.pack_host(shape, lw, threads), device)
+    def __init__(self, shape: synth.LayerShape, lw: synth.LayerWeights, device="cuda", threads: int = 0,
+                 fmt: str = "int4"):
+        self.fmt = fmt
+        self._upload(shape, self.pack_host(shape, lw, threads, fmt), device)
 
     @staticmethod
-    def pack_host(shape: synth.LayerShape, lw: synth.LayerWeights, threads: int = 0) -> dict:
+    def pack_host(shape: synth.LayerShape, lw: synth.LayerWeights, threads: int = 0, fmt: str = "int4") -> dict:
         """The library's host packer on the four projections of a layer:
-        {name: (codes uint8, scales uint16)} in the device layout."""
+        {name: (codes uint8, scales uint16)} in the device layout; fmt
+        "int4" (i4d_pack_weights) or "e4m3" (i4d_pack_weights_e4m3)."""
+        pack = {"int4": B.i4d_pack_weights, "e4m3": B.i4d_pack_weights_e4m3}[fmt]
         hd = shape.head_dim
         return dict(
-            qkv=B.i4d_pack_weights(B.I4D_PROJ_QKV, lw.w_qkv, None, lw.gamma_attn, hd, threads),
-            o=B.i4d_pack_weights(B.I4D_PROJ_PLAIN, lw.w_o, None, None, 0, threads),
-            gu=B.i4d_pack_weights(B.I4D_PROJ_GATE_UP, lw.w_gate, lw.w_up, lw.gamma_ffn, 0, threads),
-            down=B.i4d_pack_weights(B.I4D_PROJ_PLAIN, lw.w_down, None, None, 0, threads))
+            qkv=pack(B.I4D_PROJ_QKV, lw.w_qkv, None, lw.gamma_attn, hd, threads),
+            o=pack(B.I4D_PROJ_PLAIN, lw.w_o, None, None, 0, threads),
+            gu=pack(B.I4D_PROJ_GATE_UP, lw.w_gate, lw.w_up, lw.gamma_ffn, 0, threads),
+            down=pack(B.I4D_PROJ_PLAIN, lw.w_down, None, None, 0, threads))
 
     @classmethod
     def from_host(cls, shape: synth.LayerShape, host: dict, device="cuda") -> "DeviceLayer":
@@ -71,7 +75,9 @@ class DeviceLayer:
     def clone(self) -> "DeviceLayer":
         """Same bytes at new device addresses (for cache-cold timing)."""
         t = {k: (c.clone(), s.clone()) for k, (c, s) in self.tensors.items()}
-        return DeviceLayer.from_packed(self.shape, t)
+        obj = DeviceLayer.from_packed(self.shape, t)
+        obj.fmt = getattr(self, "fmt", "int4")
+        return obj
 
     def _make_struct(self) -> B.i4d_layer:
         t = self.tensors

@@ -399,3 +399,55 @@ def test_noalloc_step_rejects_a_step_larger_than_its_scratch():
     assert ei.value.status == -5 and "scratch" in str(ei.value)
     # the same step fits a caller's workspace of the reported size
     assert B.i4d_workspace_bytes(shape, 32, 4096, 256) > B.I4D_NOALLOC_SCRATCH_BYTES
+
+
+# ---------------------------------------------------------------------------
+# E4M3 decode-weight packer
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shape", [synth.SHAPE_TINY, synth.SHAPE_SMALL128], ids=["tiny", "small128"])
+def test_e4m3_packer_bit_exact_full_layer(shape):
+    """Codes and fp16 scales of every projection kind equal the oracle's
+    E4M3 encoding (gain folded) after undoing the layout permutation."""
+    lw = synth.make_layer(shape, 9)
+    ql = O.quantize_layer_e4m3(lw)
+    hd, d, F = shape.head_dim, shape.d_model, shape.d_ffn
+    nq = shape.n_q_heads * hd
+    cases = [
+        (B.I4D_PROJ_QKV, lw.w_qkv, None, lw.gamma_attn, hd, [ql.qkv]),
+        (B.I4D_PROJ_PLAIN, lw.w_o, None, None, 0, [ql.o]),
+        (B.I4D_PROJ_GATE_UP, lw.w_gate, lw.w_up, lw.gamma_ffn, 0, [ql.gate, ql.up]),
+        (B.I4D_PROJ_PLAIN, lw.w_down, None, None, 0, [ql.down]),
+    ]
+    for kind, W0, W1, g, h, refs in cases:
+        codes, scales = B.i4d_pack_weights_e4m3(kind, W0, W1, g, h)
+        N, K = W0.shape
+        assert codes.size == (2 if W1 is not None else 1) * N * K
+        q, s = B.i4d_unpack_weights_e4m3(kind, codes, scales, N, K, h)
+        np.testing.assert_array_equal(q, np.concatenate([r[0] for r in refs]))
+        np.testing.assert_array_equal(s, np.concatenate([r[1] for r in refs]).view(np.uint16))
+
+
+def test_e4m3_packer_edge_values_and_layout():
+    """Saturation, subnormals, ties, signed zeros and a zero group, against
+    the oracle; and the documented byte position of (row, k) in an atom."""
+    N, K = 16, 256
+    W = np.zeros((N, K), np.float32)
+    W[0, :128] = np.linspace(-1, 1, 128, dtype=np.float32)
+    W[1, :128] = np.float32(2.0 ** -12) * np.arange(128, dtype=np.float32)  # subnormal codes
+    W[2, :128] = -0.0
+    W[3, :128] = np.float32(448.0)
+    W[3, 5] = np.float32(-448.0)
+    W[4, :128] = np.array([1 + 1 / 16, 1 + 3 / 16] * 64, np.float32) * np.float32(448.0 / 1.25)
+    W[5:, 128:] = np.random.default_rng(4).standard_normal((11, 128)).astype(np.float32)
+    codes, scales = B.i4d_pack_weights_e4m3(B.I4D_PROJ_PLAIN, W)
+    rq, rs, _ = O.quantize_weight_e4m3(W)
+    q, s = B.i4d_unpack_weights_e4m3(B.I4D_PROJ_PLAIN, codes, scales, N, K)
+    np.testing.assert_array_equal(q, rq)
+    np.testing.assert_array_equal(s, rs.view(np.uint16))
+    # byte of (row r, k = 128 g + 32 kb + 8 j + e) at ((g * 64 + 16 j + r) * 32 + 8 kb + e)
+    for r, k in [(0, 0), (3, 5), (7, 127), (15, 200), (9, 128 + 32 * 3 + 8 * 2 + 6)]:
+        g, kk = divmod(k, 128)
+        kb, rem = divmod(kk, 32)
+        j, e = divmod(rem, 8)
+        assert codes[(g * 64 + 16 * j + r) * 32 + 8 * kb + e] == rq[r, k]
