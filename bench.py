@@ -108,6 +108,9 @@ def main():
     ap.add_argument("--splits", type=int, default=-1)
     ap.add_argument("--weights", default="int4", choices=["int4", "e4m3"],
                     help="decode-weight format (e4m3: the FP8 decode-weight variant)")
+    ap.add_argument("--stage", default="step", choices=["step", "attention"],
+                    help="time the whole decode step, or the attention launch alone (i4d_attention on the "
+                         "step's query, no append)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-steps", type=int, default=5)
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -179,6 +182,17 @@ def main():
     # eager check that the step runs, then graphs
     step(0)
     torch.cuda.synchronize()
+    if args.stage == "attention":
+        # the attention launch alone on the query the step left in the
+        # workspace (the caches already hold the step's token: no append)
+        cs = B.make_shape(shape)
+        q = ws.view("q", torch.float32, M * shape.n_q_heads * shape.head_dim)
+        anb = B.i4d_attention_workspace_bytes(cs, M, maxL, max(splits, 0))
+        aws = torch.zeros(anb, dtype=torch.uint8, device="cuda")
+        a16 = torch.empty((M, shape.n_q_heads * shape.head_dim), dtype=torch.int16, device="cuda")
+
+        def step(i):  # noqa: F811
+            B.i4d_attention(caches[i % C].struct, cs, q, ctx, M, maxL, max(splits, 0), aws, anb, None, a16)
 
     def capture(n, fn):
         g = torch.cuda.CUDAGraph()
@@ -202,10 +216,14 @@ def main():
     ms_step = ms_total / args.steps
     us_step = ms_step * 1e3
     total_b, w_b, kv_b = algorithmic_bytes(shape, lengths, args.weights)
+    if args.stage == "attention":
+        total_b, w_b = kv_b, 0
     gbps = total_b / (us_step * 1e-6) / 1e9
 
     one_launch = args.weights == "int4" and B.i4d_decode_step_is_one_launch(B.make_shape(shape), M)
-    if args.weights == "e4m3":
+    if args.stage == "attention":
+        rf_kernel, rf_bytes, rf_us = "attention launch (split partials and combine)", kv_b, us_step
+    elif args.weights == "e4m3":
         # the E4M3 variant's entry is the step as a whole (one launch per
         # stage, no stage-level timing entry point for gate/up)
         rf_kernel, rf_bytes, rf_us = "E4M3 decode step (all stage launches)", total_b, us_step
@@ -234,7 +252,8 @@ def main():
     rf_gbps = rf_bytes / (rf_us * 1e-6) / 1e9
 
     result = {
-        "metric": "us per INT4 decode block step (+ achieved HBM GB/s)",
+        "metric": ("us per INT4 decode block step (+ achieved HBM GB/s)" if args.stage == "step" else
+                   "us per attention launch on the INT4 KV cache (+ achieved HBM GB/s)"),
         "value": round(us_step, 3),
         "unit": "us/step",
         "n_gpus": 1,
@@ -249,7 +268,7 @@ def main():
         "config": {"workload": args.workload, "d_model": shape.d_model, "n_q_heads": shape.n_q_heads,
                    "n_kv_heads": shape.n_kv_heads, "head_dim": shape.head_dim, "d_ffn": shape.d_ffn,
                    "M": M, "ctx_total": int(lengths.sum()), "ctx_max": maxL, "num_splits": splits,
-                   "layer_copies": C, "one_launch_step": one_launch, "weights": args.weights,
+                   "layer_copies": C, "one_launch_step": one_launch, "weights": args.weights, "stage": args.stage,
                    "timing": "hip graph of K steps, events on the launch stream"},
         "hbm_GBps": round(gbps, 1),
         "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
@@ -263,7 +282,7 @@ def main():
         "setup_s": round(setup_s, 1),
     }
 
-    if not args.no_cpu:
+    if not args.no_cpu and args.stage == "step":
         result["cpu_baseline"] = cpu_baseline(shape, lw, lengths, pre, xb, args.cpu_steps, args.workload)
     print(json.dumps(result), flush=True)
 
