@@ -15,7 +15,9 @@ abstract).  Value distributions:
 * cached keys / values N(0, 1) with hd/16 outlier channels per KV head
   (chosen without replacement, independently for K and V, fixed across
   tokens) multiplied by 20, then rounded to bf16;
-* block input x ~ N(0, 1) rounded to bf16.
+* block input x ~ N(0, 1) rounded to bf16;
+* prefill activations N(0, 1) with d/128 outlier channels multiplied by
+  20, rounded to bf16.
 
 Random streams are keyed by (seed, purpose) through numpy's SeedSequence so
 that the weights of a layer do not depend on the batch size or the context
@@ -29,7 +31,7 @@ from typing import List, Optional
 import numpy as np
 
 # purposes of the independent random streams of one (config, layer) seed
-_P_WEIGHTS, _P_CACHE, _P_X, _P_LENGTHS, _P_LMHEAD = 0, 1, 2, 3, 4
+_P_WEIGHTS, _P_CACHE, _P_X, _P_LENGTHS, _P_LMHEAD, _P_PREFILL = 0, 1, 2, 3, 4, 5
 
 
 @dataclasses.dataclass(frozen=True)
@@ -95,6 +97,48 @@ WORKLOADS = {
     "8b_32layer_ctx32768": Workload("8b_32layer_ctx32768", SHAPE_8B, 1, 32768, 4000,
                                     n_layers=32, num_splits=16),
 }
+
+
+@dataclasses.dataclass(frozen=True)
+class PrefillWorkload:
+    """A packed prefill batch: request r has seqlens[r] new tokens at positions
+    starts[r], starts[r] + 1, ... of its cache row."""
+    name: str
+    shape: LayerShape
+    seqlens: tuple
+    starts: tuple
+    seed: int
+
+    @property
+    def T(self) -> int:
+        return int(sum(self.seqlens))
+
+
+PREFILL_WORKLOADS = {
+    # 8B-shape layer, one 2048-token prompt from position 0 (the pages' 8B
+    # prefill shape at S = 2048)
+    "8b_prefill_s2048": PrefillWorkload("8b_prefill_s2048", SHAPE_8B, (2048,), (0,), 5000),
+    # 8B shape, a packed batch of 8: one 2048-token prompt and seven of 128
+    # (the pages' variable-length case, B = 8, S_max = 2048)
+    "8b_prefill_varlen": PrefillWorkload("8b_prefill_varlen", SHAPE_8B, (2048,) + (128,) * 7, (0,) * 8, 5001),
+    # 70B-shape layer, one 2048-token prompt
+    "70b_prefill_s2048": PrefillWorkload("70b_prefill_s2048", SHAPE_70B, (2048,), (0,), 5002),
+}
+
+
+def prefill_offsets(seqlens) -> np.ndarray:
+    """Prefix sums of the request lengths: int32 [R + 1], starting at 0."""
+    return np.concatenate([[0], np.cumsum(np.asarray(seqlens, dtype=np.int64))]).astype(np.int32)
+
+
+def make_prefill_x(shape: LayerShape, T: int, seed: int) -> np.ndarray:
+    """Packed prefill activations, bf16 bits [T, d]: N(0, 1) with d/128
+    outlier channels (fixed across tokens) multiplied by 20."""
+    r = _rng(seed, _P_PREFILL)
+    d = shape.d_model
+    m = np.ones(d, dtype=np.float32)
+    m[r.permutation(d)[: max(1, d // 128)]] = np.float32(20.0)
+    return f32_to_bf16_bits(r.standard_normal((T, d), dtype=np.float32) * m[None])
 
 
 def _rng(seed: int, purpose: int) -> np.random.Generator:

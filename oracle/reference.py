@@ -77,6 +77,21 @@ R12 E4M3 decode-weight variant: the pages report E4M3 decode weights beside
     bits, subnormals m 2^-9, no infinities, largest finite 448); s == 0
     gives zero codes.  The sign of a value that rounds to zero is kept
     (code 0x80 for negative inputs).
+R13 FP8 prefill of the QKV projection, the step that fills the cache the
+    decode step reads [P1 how-it-works: FP8 GEMM whose QKV epilogue writes K
+    and V straight to offset(request, head, position, channel); gain folded,
+    rho in the epilogue; packed prefill by prefix sums, no padding rows;
+    delayed per-tensor scaling: the FP8 output is written in the producing
+    epilogue and the current maximum gives the next call's scale; P3
+    abstract].  Reading: R requests, request r owns tokens [cu[r], cu[r+1])
+    at positions start[r], start[r] + 1, ...; the activations are E4M3 of
+    fp32(x / s_x) with one per-tensor scale s_x (R12 encoding); the weights
+    are the R12 E4M3 QKV weights; y = rho_t (sum_k W_hat[n, k] x_hat[t, k])
+    in fp64 with x_hat = s_x E4M3(x8); RoPE (R4) at the token's position;
+    q is written as E4M3 of fp32(q / s_q) with its own per-tensor scale; k
+    and v are rounded to bf16 (R10) and encoded (R6) at their slot.  The
+    call reports max |x| and max |q|; the next call's scale is max / 448
+    (fp32), a zero maximum keeping the previous scale.
 """
 from __future__ import annotations
 
@@ -573,3 +588,88 @@ def lm_head_argmax(h, W_hat_lm, eps: float) -> tuple[np.ndarray, np.ndarray]:
     rho = rms_factor(h, eps)
     logits = rho[:, None] * (h @ np.asarray(W_hat_lm, dtype=np.float64).T)
     return logits, np.argmax(logits, axis=-1)
+
+
+# ---------------------------------------------------------------------------
+# FP8 prefill of the QKV projection (R13)
+# ---------------------------------------------------------------------------
+
+
+def prefill_token_map(cu_seqlens, start_pos):
+    """Request and position of every packed token: request r owns tokens
+    cu[r] .. cu[r+1]-1 at positions start[r], start[r] + 1, ... (R13)."""
+    rows, pos = [], []
+    for r in range(len(cu_seqlens) - 1):
+        n = int(cu_seqlens[r + 1]) - int(cu_seqlens[r])
+        rows += [r] * n
+        pos += list(range(int(start_pos[r]), int(start_pos[r]) + n))
+    return np.array(rows, dtype=np.int64), np.array(pos, dtype=np.int64)
+
+
+def delayed_scale(amax, prev) -> np.float32:
+    """The next call's per-tensor E4M3 scale: fp32(max) / 448, or the previous
+    scale when the maximum is zero (R13)."""
+    a = np.float32(amax)
+    return np.float32(a / np.float32(E4M3_MAX)) if a > 0 else np.float32(prev)
+
+
+@dataclasses.dataclass
+class PrefillResult:
+    x8: np.ndarray        # [T, d] E4M3 codes of the activations
+    rho: np.ndarray       # [T] RMS factor of each token
+    q: np.ndarray         # [T, n_q, hd] fp64 queries after RoPE
+    q8: np.ndarray        # [T, n_q, hd] E4M3 codes of q / s_q
+    k_new: np.ndarray     # [T, n_kv, hd] bf16-rounded keys after RoPE
+    v_new: np.ndarray
+    k_codes: np.ndarray   # [T, n_kv, hd] cache codes (R6) and scales
+    k_scales: np.ndarray
+    v_codes: np.ndarray
+    v_scales: np.ndarray
+    rows: np.ndarray      # [T] request of each token
+    pos: np.ndarray       # [T] position of each token
+    amax_x: float
+    amax_q: float
+
+
+def fp8_quantize(v, scale) -> np.ndarray:
+    """E4M3 codes of fp32(v) / fp32(scale) (fp32 division, R12 encoding):
+    the FP8 activation or query of the prefill (R13)."""
+    return e4m3_encode(np.asarray(v, np.float32) / np.float32(scale))
+
+
+def fp8_dequantize(codes, scale) -> np.ndarray:
+    """fp64 values scale * E4M3(codes) (R13)."""
+    return e4m3_decode(codes) * np.float64(np.float32(scale))
+
+
+def prefill_qkv(shape, qkv_e4m3, x_bits, cu_seqlens, start_pos, x_scale, q_scale,
+                W_dense: Optional[np.ndarray] = None) -> PrefillResult:
+    """The FP8 prefill of the QKV projection for packed tokens (R13).
+
+    x_bits: bf16 bits [T, d] of the packed tokens; qkv_e4m3: (codes, scales,
+    "e4m3") of the gain-folded QKV weight (R12), or its fp64 dense form in
+    W_dense.  Steps: token map; rho of each token from its bf16 values; x8 =
+    E4M3(x / s_x); y = rho (s_x dec(x8)) W_hat^T; RoPE of q and k at the
+    token's position; q8 = E4M3(q / s_q); k and v rounded to bf16 and encoded
+    for the INT4 cache."""
+    T = int(cu_seqlens[-1])
+    hd, nq, nkv = shape.head_dim, shape.n_q_heads, shape.n_kv_heads
+    x = _bf16_bits_to_values(np.asarray(x_bits).reshape(T, shape.d_model))
+    rows, pos = prefill_token_map(cu_seqlens, start_pos)
+    rho = rms_factor(x.astype(np.float64), shape.rms_eps)
+    x8 = fp8_quantize(x, x_scale)
+    x_hat = fp8_dequantize(x8, x_scale)
+    W = dense(qkv_e4m3) if W_dense is None else W_dense
+    y = rho[:, None] * (x_hat @ W.T)
+    q = y[:, : nq * hd].reshape(T, nq, hd)
+    k = y[:, nq * hd: (nq + nkv) * hd].reshape(T, nkv, hd)
+    v = y[:, (nq + nkv) * hd:].reshape(T, nkv, hd)
+    q = rope(q, pos[:, None], shape.rope_theta)
+    k = rope(k, pos[:, None], shape.rope_theta)
+    q8 = fp8_quantize(q, q_scale)
+    k_b, v_b = round_to_bf16(k), round_to_bf16(v)
+    kq, ks = quantize_kv(k_b)
+    vq, vs = quantize_kv(v_b)
+    amax_x = float(np.max(np.abs(x))) if T else 0.0
+    amax_q = float(np.max(np.abs(q.astype(np.float32)))) if T else 0.0
+    return PrefillResult(x8, rho, q, q8, k_b, v_b, kq, ks, vq, vs, rows, pos, amax_x, amax_q)

@@ -1,0 +1,243 @@
+"""Pins of the oracle's FP8 prefill of the QKV projection (reading R13 of the
+oracle: the summary page's "how it works" section has an FP8 GEMM whose QKV
+epilogue writes K and V straight into the cache at offset(request, head,
+position, channel), a packed prefill tracked by prefix sums, and delayed
+per-tensor scaling with the FP8 output written by the producing epilogue).
+
+Each pin fixes the prefill by something other than the prefill code itself:
+a worked token map, closed forms of the delayed scale, PyTorch's own
+float8_e4m3fn conversion for the activation and query encodings, the
+decode-step oracle (pinned on its own) as the one-token special case,
+invariants (packing, token independence, the scale invariance that rho
+gives), and bit-level properties.  A planted mistake in a prefill step fails
+one of them (test_planted_prefill_mistakes_fail_a_pin).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import oracle.reference as R
+from int4_quantized_decode_amd import synth
+
+SHAPE = synth.SHAPE_SMALL128
+
+
+@pytest.fixture(scope="module")
+def layer():
+    lw = synth.make_layer(SHAPE, 71)
+    ql = O.quantize_layer_e4m3(lw)
+    return ql, O.dense(ql.qkv)
+
+
+def _exact_x(rng, T, scale_pow):
+    """bf16 activations that are exactly s_x * E4M3 values (s_x = 2^scale_pow)."""
+    codes = rng.integers(0, 256, size=(T, SHAPE.d_model)).astype(np.uint8)
+    codes = np.where((codes & 0x7F) == 0x7F, codes ^ 0x01, codes).astype(np.uint8)
+    x = O.e4m3_decode(codes) * 2.0 ** scale_pow
+    return synth.f32_to_bf16_bits(x.astype(np.float32)), codes
+
+
+# ---------------------------------------------------------------------------
+# token map and delayed scale
+# ---------------------------------------------------------------------------
+
+def test_token_map_worked_example():
+    # three requests: 3 tokens from position 5, none, 4 tokens from position 30
+    rows, pos = O.prefill_token_map([0, 3, 3, 7], [5, 0, 30])
+    np.testing.assert_array_equal(rows, [0, 0, 0, 2, 2, 2, 2])
+    np.testing.assert_array_equal(pos, [5, 6, 7, 30, 31, 32, 33])
+    rows, pos = O.prefill_token_map([0], [])
+    assert rows.size == 0 and pos.size == 0
+
+
+def test_delayed_scale_closed_forms():
+    assert O.delayed_scale(448.0, 3.0) == np.float32(1.0)
+    assert O.delayed_scale(896.0, 3.0) == np.float32(2.0)
+    assert O.delayed_scale(0.0, 0.25) == np.float32(0.25)
+    assert O.delayed_scale(1.0, 0.0) == np.float32(1.0) / np.float32(448.0)
+    assert O.delayed_scale(1.0, 0.0).dtype == np.float32
+
+
+# ---------------------------------------------------------------------------
+# encodings against PyTorch's float8_e4m3fn conversion
+# ---------------------------------------------------------------------------
+
+def _torch_e4m3(values_f32, scale):
+    t = torch.from_numpy(np.asarray(values_f32, np.float32)) / torch.tensor(np.float32(scale))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_activation_and_query_codes_match_torch(layer):
+    ql, W = layer
+    T = 37
+    xb = synth.make_prefill_x(SHAPE, T, 3)
+    x = synth.bf16_bits_to_f32(xb)
+    sx = np.float32(np.max(np.abs(x)) / 440.0)   # every |x / s_x| stays below 448
+    cu = synth.prefill_offsets([T])
+    res = O.prefill_qkv(SHAPE, ql.qkv, xb, cu, [11], sx, np.float32(0.05), W_dense=W)
+    np.testing.assert_array_equal(res.x8, _torch_e4m3(x, sx))
+    sq = np.float32(np.max(np.abs(res.q)) / 440.0)
+    res2 = O.prefill_qkv(SHAPE, ql.qkv, xb, cu, [11], sx, sq, W_dense=W)
+    np.testing.assert_array_equal(res2.q8, _torch_e4m3(res2.q.astype(np.float32), sq))
+    # saturation: values beyond 448 s encode to +-448
+    big = O.fp8_quantize(np.array([1000.0, -1000.0, 448.0 * 3], np.float32), np.float32(2.0))
+    np.testing.assert_array_equal(big, [0x7E, 0xFE, 0x7E])
+
+
+def test_amax_and_delayed_scaling_round_trip(layer):
+    ql, W = layer
+    T = 20
+    xb = synth.make_prefill_x(SHAPE, T, 4)
+    x = synth.bf16_bits_to_f32(xb)
+    cu = synth.prefill_offsets([T])
+    first = O.prefill_qkv(SHAPE, ql.qkv, xb, cu, [0], np.float32(1.0), np.float32(1.0), W_dense=W)
+    assert first.amax_x == float(np.max(np.abs(x)))
+    neg = O.prefill_qkv(SHAPE, ql.qkv, xb ^ np.uint16(0x8000), cu, [0], np.float32(1.0), np.float32(1.0), W_dense=W)
+    assert neg.amax_x == first.amax_x and neg.amax_q == first.amax_q
+    assert first.amax_q == float(np.max(np.abs(first.q.astype(np.float32))))
+    sx = O.delayed_scale(first.amax_x, 1.0)
+    sq = O.delayed_scale(first.amax_q, 1.0)
+    second = O.prefill_qkv(SHAPE, ql.qkv, xb, cu, [0], sx, sq, W_dense=W)
+    # with the scale from the same tensor's maximum, the largest element sits
+    # at +-448 and nothing saturates beyond it
+    i = np.unravel_index(np.argmax(np.abs(x)), x.shape)
+    assert second.x8[i] & 0x7F == 0x7E
+    assert np.all(np.abs(O.e4m3_decode(second.x8)) <= 448.0)
+    iq = np.unravel_index(np.argmax(np.abs(second.q)), second.q.shape)
+    assert second.q8[iq] & 0x7F == 0x7E
+
+
+# ---------------------------------------------------------------------------
+# the one-token case is the decode step's QKV stage and append
+# ---------------------------------------------------------------------------
+
+def test_one_token_requests_reduce_to_the_decode_qkv_stage(layer):
+    ql, W = layer
+    rng = np.random.default_rng(5)
+    R_ = 6
+    xb, codes = _exact_x(rng, R_, -3)
+    starts = np.array([0, 1, 31, 32, 500, 4095])
+    cu = synth.prefill_offsets([1] * R_)
+    res = O.prefill_qkv(SHAPE, ql.qkv, xb, cu, starts, np.float32(2.0 ** -3), np.float32(1.0), W_dense=W)
+    # the activation is exact: its codes are the chosen ones
+    np.testing.assert_array_equal(res.x8, codes)
+    x = synth.bf16_bits_to_f32(xb).astype(np.float64)
+    q, k, v = O.qkv_stage(SHAPE, W, x, starts + 1)
+    np.testing.assert_allclose(res.q, q, rtol=1e-13, atol=1e-13)
+    np.testing.assert_array_equal(res.k_new, O.round_to_bf16(k))
+    np.testing.assert_array_equal(res.v_new, O.round_to_bf16(v))
+    kq, ks = O.quantize_kv(O.round_to_bf16(k))
+    vq, vs = O.quantize_kv(O.round_to_bf16(v))
+    np.testing.assert_array_equal(res.k_codes, kq)
+    np.testing.assert_array_equal(res.k_scales, ks)
+    np.testing.assert_array_equal(res.v_codes, vq)
+    np.testing.assert_array_equal(res.v_scales, vs)
+
+
+def test_new_keys_and_values_are_bf16_values(layer):
+    ql, W = layer
+    T = 9
+    xb = synth.make_prefill_x(SHAPE, T, 6)
+    res = O.prefill_qkv(SHAPE, ql.qkv, xb, synth.prefill_offsets([T]), [3], np.float32(0.2), np.float32(0.1),
+                        W_dense=W)
+    for a in (res.k_new, res.v_new):
+        f = a.astype(np.float32)
+        assert np.array_equal(f.astype(np.float64), a)
+        assert np.all((f.view(np.uint32) & 0xFFFF) == 0)
+
+
+# ---------------------------------------------------------------------------
+# invariants
+# ---------------------------------------------------------------------------
+
+def test_packing_and_token_independence(layer):
+    """A packed batch gives, token for token, what separate requests give, and
+    each token what a one-token request at its position gives."""
+    ql, W = layer
+    seqlens, starts = [3, 0, 5, 1], [7, 2, 30, 0]
+    T = sum(seqlens)
+    xb = synth.make_prefill_x(SHAPE, T, 7)
+    sx, sq = np.float32(0.2), np.float32(0.1)
+    cu = synth.prefill_offsets(seqlens)
+    packed = O.prefill_qkv(SHAPE, ql.qkv, xb, cu, starts, sx, sq, W_dense=W)
+    np.testing.assert_array_equal(packed.rows, [0, 0, 0, 2, 2, 2, 2, 2, 3])
+    np.testing.assert_array_equal(packed.pos, [7, 8, 9, 30, 31, 32, 33, 34, 0])
+    for r in range(len(seqlens)):
+        a, b = int(cu[r]), int(cu[r + 1])
+        if a == b:
+            continue
+        one = O.prefill_qkv(SHAPE, ql.qkv, xb[a:b], synth.prefill_offsets([b - a]), [starts[r]], sx, sq,
+                            W_dense=W)
+        np.testing.assert_allclose(packed.q[a:b], one.q, rtol=1e-12, atol=1e-12)
+        np.testing.assert_array_equal(packed.k_codes[a:b], one.k_codes)
+        np.testing.assert_array_equal(packed.v_codes[a:b], one.v_codes)
+        np.testing.assert_array_equal(packed.x8[a:b], one.x8)
+    for t in (0, 4, 8):
+        single = O.prefill_qkv(SHAPE, ql.qkv, xb[t:t + 1], synth.prefill_offsets([1]), [packed.pos[t]], sx, sq,
+                               W_dense=W)
+        np.testing.assert_allclose(packed.q[t], single.q[0], rtol=1e-12, atol=1e-12)
+        np.testing.assert_array_equal(packed.k_scales[t], single.k_scales[0])
+
+
+def test_rho_makes_the_projection_scale_invariant(layer):
+    """Scaling x and s_x by 4 leaves the FP8 codes unchanged; the RMS factor
+    then removes the factor 4 from the output (up to the epsilon term)."""
+    ql, W = layer
+    T = 8
+    xb = synth.make_prefill_x(SHAPE, T, 8)
+    x4 = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(xb) * np.float32(4.0))
+    cu = synth.prefill_offsets([T])
+    a = O.prefill_qkv(SHAPE, ql.qkv, xb, cu, [0], np.float32(0.25), np.float32(1.0), W_dense=W)
+    b = O.prefill_qkv(SHAPE, ql.qkv, x4, cu, [0], np.float32(1.0), np.float32(1.0), W_dense=W)
+    np.testing.assert_array_equal(a.x8, b.x8)
+    np.testing.assert_allclose(b.q, a.q, rtol=1e-4, atol=1e-6)
+    np.testing.assert_allclose(b.rho * 4.0, a.rho, rtol=1e-4)
+
+
+# ---------------------------------------------------------------------------
+# planted mistakes
+# ---------------------------------------------------------------------------
+
+PINS = ["test_token_map_worked_example", "test_activation_and_query_codes_match_torch",
+        "test_amax_and_delayed_scaling_round_trip", "test_one_token_requests_reduce_to_the_decode_qkv_stage",
+        "test_new_keys_and_values_are_bf16_values", "test_packing_and_token_independence",
+        "test_rho_makes_the_projection_scale_invariant"]
+
+
+@pytest.mark.parametrize("mistake", ["map_no_start", "map_token_index", "dequant_no_scale", "no_rho",
+                                     "scale_multiplied", "kv_not_bf16", "amax_before_abs"])
+def test_planted_prefill_mistakes_fail_a_pin(monkeypatch, layer, mistake):
+    if mistake == "map_no_start":
+        orig = R.prefill_token_map
+        monkeypatch.setattr(R, "prefill_token_map", lambda cu, st: orig(cu, np.zeros(len(st), np.int64)))
+    elif mistake == "map_token_index":
+        orig = R.prefill_token_map
+        monkeypatch.setattr(R, "prefill_token_map", lambda cu, st: (orig(cu, st)[0], np.arange(int(cu[-1]))))
+    elif mistake == "dequant_no_scale":
+        monkeypatch.setattr(R, "fp8_dequantize", lambda c, s: R.e4m3_decode(c))
+    elif mistake == "no_rho":
+        monkeypatch.setattr(R, "rms_factor", lambda x, eps: np.ones(np.asarray(x).shape[:-1]))
+    elif mistake == "scale_multiplied":
+        monkeypatch.setattr(R, "fp8_quantize", lambda v, s: R.e4m3_encode(np.asarray(v, np.float32) * np.float32(s)))
+        monkeypatch.setattr(O, "fp8_quantize", R.fp8_quantize)
+    elif mistake == "kv_not_bf16":
+        monkeypatch.setattr(R, "round_to_bf16", lambda x: np.asarray(x, np.float64))
+    elif mistake == "amax_before_abs":
+        orig = R.prefill_qkv
+
+        def wrong(*a, **k):
+            res = orig(*a, **k)
+            res.amax_x = float(np.max(synth.bf16_bits_to_f32(np.asarray(a[2]))))
+            return res
+        monkeypatch.setattr(R, "prefill_qkv", wrong)
+        monkeypatch.setattr(O, "prefill_qkv", wrong)
+    failed = 0
+    for name in PINS:
+        pin = globals()[name]
+        args = [] if name in ("test_token_map_worked_example",) else [layer]
+        try:
+            pin(*args)
+        except AssertionError:
+            failed += 1
+    assert failed >= 1, mistake
