@@ -63,6 +63,7 @@ typedef enum {
 #define I4D_DEVERR_APPEND_POS 1 /* kv_append: pos outside [0, capacity) */
 #define I4D_DEVERR_CTX_LEN 2    /* attention: ctx_len outside [1, capacity] */
 #define I4D_DEVERR_SYNC 4       /* one-launch decode step: a stage wait timed out (results invalid) */
+#define I4D_DEVERR_SCALE 8      /* FP8 prefill: a per-tensor scale is not positive and finite (1 used) */
 
 const char* i4d_last_error(void);
 
@@ -414,6 +415,63 @@ i4d_status i4d_decode_block_step_noalloc(const i4d_layer* layer, const i4d_kv_ca
                                          const uint16_t* x_in, uint16_t* x_out, const int32_t* ctx_len,
                                          int M, int max_ctx_len, int num_splits, float* attn_f32,
                                          void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* FP8 prefill of the QKV projection (fills the cache the decode step reads)  */
+/* ------------------------------------------------------------------------ */
+
+/* Delayed per-tensor scaling state (device memory, 16 bytes).  A prefill
+ * call uses x_scale and q_scale and raises x_amax and q_amax to the largest
+ * |x| and |q| it sees (atomic maximum; they start at 0).
+ * i4d_fp8_scales_update then sets each scale to amax / 448 (a zero maximum
+ * keeps the previous scale) and clears the maxima: the summary page's "how
+ * it works" section, where the maximum seen now gives the next call's
+ * scale.  The first call's scales are the caller's choice. */
+typedef struct {
+  float x_scale;
+  float q_scale;
+  float x_amax;
+  float q_amax;
+} i4d_fp8_scales;
+
+/* Workspace of i4d_prefill_qkv_e4m3 for T packed tokens.  It begins with
+ * the call's FP8 activations (for inspection by tests): T128 = T rounded up
+ * to 128 tokens, layout [T128/16 tiles][d/128 groups][2 halves][64 lanes]
+ * [16 bytes], lane 16j + r holding token 16 * tile + r, byte 8 * b + e of
+ * half h = code of channel 128 * group + 32 * (2h + b) + 8j + e; tokens
+ * from T on hold zeros. */
+i4d_status i4d_prefill_workspace_bytes(const i4d_layer_shape* shape, int T, size_t* bytes);
+
+/* FP8 prefill of the QKV projection for T packed tokens of R requests (the
+ * summary page's "how it works" section: an FP8 GEMM whose QKV epilogue
+ * writes K and V straight to offset(request, head, position, channel) of
+ * the cache; gain folded, rho in the epilogue; packed requests tracked by
+ * prefix sums, no padding rows; FP8 output with delayed scaling).
+ * Request r owns tokens cu_seqlens[r] .. cu_seqlens[r+1]-1 (device int32
+ * [R+1], non-decreasing, cu_seqlens[0] = 0, cu_seqlens[R] = T) at positions
+ * start_pos[r], start_pos[r]+1, ... (device int32 [R]) of cache row r.
+ * x: bf16 device [T][d].  The layer's qkv_codes / qkv_scales hold the QKV
+ * weight packed by i4d_pack_weights_e4m3 (the other projections are not
+ * read and may be NULL).  Per token: rho = 1/sqrt(mean x^2 + eps) from the
+ * bf16 values; x8 = E4M3(fp32(x / x_scale)) (nearest even, saturating at
+ * 448); y = x_scale * rho * sum_g s[n][g] * (E4M3 dot product of group g)
+ * in fp32; RoPE at the token's position on q and k; q_fp8 (device [T][n_q
+ * * 128]) = E4M3(fp32(q / q_scale)); k and v rounded to bf16, rotated and
+ * quantized as i4d_kv_append does and stored at their slot.  k_bf16 /
+ * v_bf16 (device, optional): the bf16 keys and values at the same
+ * placement, element (slot, channel) at slot * 128 + channel, slot as in
+ * i4d_kv_cache.  A position outside [0, capacity) of its row skips that
+ * token's cache writes and sets I4D_DEVERR_APPEND_POS; a scale that is not
+ * positive and finite is replaced by 1 with I4D_DEVERR_SCALE.  head_dim
+ * 128 and an even number of q + k + v heads.  T = 0 enqueues nothing. */
+i4d_status i4d_prefill_qkv_e4m3(const i4d_layer* layer, const i4d_kv_cache* cache, const uint16_t* x, int T,
+                                const int32_t* cu_seqlens, const int32_t* start_pos, int R,
+                                i4d_fp8_scales* scales, uint8_t* q_fp8, uint16_t* k_bf16, uint16_t* v_bf16,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Delayed scaling step on `stream`: scale = amax / 448 (fp32, correctly
+ * rounded) where amax > 0, then amax = 0, for x and for q. */
+i4d_status i4d_fp8_scales_update(i4d_fp8_scales* scales, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Final norm + LM head + greedy argmax (full-model step)                    */

@@ -24,6 +24,7 @@ I4D_MAX_SPLITS = 256
 I4D_DEVERR_APPEND_POS = 1
 I4D_DEVERR_CTX_LEN = 2
 I4D_DEVERR_SYNC = 4
+I4D_DEVERR_SCALE = 8
 I4D_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 STATUS_NAMES = {0: "I4D_OK", -1: "I4D_ERR_NULL", -2: "I4D_ERR_SHAPE", -3: "I4D_ERR_UNSUPPORTED",
@@ -63,6 +64,10 @@ class i4d_projection_plan(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in ("kernel", "waves", "strips_per_workgroup", "k_slices", "depth",
                                             "persistent", "grid")] + \
                [("lds_bytes", ctypes.c_size_t), ("instantiated", ctypes.c_int)]
+
+
+class i4d_fp8_scales(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_float) for n in ("x_scale", "q_scale", "x_amax", "q_amax")]
 
 
 class i4d_workspace_layout(ctypes.Structure):
@@ -106,6 +111,10 @@ _SIGS = {
     "i4d_attn_out_proj_e4m3": (_I, [ctypes.POINTER(i4d_layer), _VP, _VP, _I, _VP, _VP, _VP]),
     "i4d_decode_block_step_noalloc": (_I, [ctypes.POINTER(i4d_layer), ctypes.POINTER(i4d_kv_cache), _VP, _VP,
                                            _VP, _I, _I, _I, _VP, _VP]),
+    "i4d_prefill_workspace_bytes": (_I, [ctypes.POINTER(i4d_layer_shape), _I, c_size_p]),
+    "i4d_prefill_qkv_e4m3": (_I, [ctypes.POINTER(i4d_layer), ctypes.POINTER(i4d_kv_cache), _VP, _I, _VP, _VP, _I,
+                                  _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
+    "i4d_fp8_scales_update": (_I, [_VP, _VP]),
     "i4d_lm_head_workspace_bytes": (_I, [_I, _I, c_size_p]),
     "i4d_lm_head_argmax": (_I, [_VP, _I, _I, _VP, _I, ctypes.c_float, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
 }
@@ -391,3 +400,21 @@ def i4d_lm_head_argmax(w_lm, V: int, d: int, h, M: int, rms_eps: float, logits_o
                        workspace, workspace_bytes: int, stream=None):
     _check(lib().i4d_lm_head_argmax(ptr(w_lm), V, d, ptr(h), M, float(rms_eps), ptr(logits_out),
                                     ptr(token_out), ptr(workspace), workspace_bytes, stream_handle(stream)))
+
+
+def i4d_prefill_workspace_bytes(shape: i4d_layer_shape, T: int) -> int:
+    b = ctypes.c_size_t()
+    _check(lib().i4d_prefill_workspace_bytes(ctypes.byref(shape), T, ctypes.byref(b)))
+    return b.value
+
+
+def i4d_prefill_qkv_e4m3(layer: i4d_layer, cache: i4d_kv_cache, x, T: int, cu_seqlens, start_pos, R: int,
+                         scales, q_fp8, k_bf16, v_bf16, workspace, workspace_bytes: int, stream=None):
+    """scales: device i4d_fp8_scales (e.g. a float32 tensor of 4 elements)."""
+    _check(lib().i4d_prefill_qkv_e4m3(ctypes.byref(layer), ctypes.byref(cache), ptr(x), T, ptr(cu_seqlens),
+                                      ptr(start_pos), R, ptr(scales), ptr(q_fp8), ptr(k_bf16), ptr(v_bf16),
+                                      ptr(workspace), workspace_bytes, stream_handle(stream)))
+
+
+def i4d_fp8_scales_update(scales, stream=None):
+    _check(lib().i4d_fp8_scales_update(ptr(scales), stream_handle(stream)))

@@ -13,7 +13,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libi4d.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api_host.cpp", "api_device.hip", "proj.hip", "attn.hip", "lmhead.hip", "step.hip", "noalloc.hip", "proj_e4m3.hip"]
+SOURCES = ["api_host.cpp", "api_device.hip", "proj.hip", "attn.hip", "lmhead.hip", "step.hip", "noalloc.hip", "proj_e4m3.hip", "prefill.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           "-fno-fast-math", "-ffp-contract=fast-honor-pragmas"]

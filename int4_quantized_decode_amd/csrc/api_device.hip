@@ -12,19 +12,23 @@
 
 using namespace i4d;
 
-namespace {
-
 #define I4D_TRY(expr)                \
   do {                               \
     i4d_status st_ = (expr);         \
     if (st_ != I4D_OK) return st_;   \
   } while (0)
 
+namespace i4d {
+
 i4d_status need(const void* p, const char* what) {
   if (!p) return fail(I4D_ERR_NULL, "%s is NULL", what);
   if (!aligned16(p)) return fail(I4D_ERR_ALIGN, "%s is not 16-byte aligned", what);
   return ok();
 }
+
+}  // namespace i4d
+
+namespace {
 
 i4d_status check_rows(int M) {
   if (M < 1 || M > I4D_MAX_ROWS) return fail(I4D_ERR_RANGE, "M=%d outside [1, %d]", M, I4D_MAX_ROWS);
@@ -44,6 +48,10 @@ i4d_status check_layer(const i4d_layer* L) {
   I4D_TRY(need(L->down_scales, "down_scales"));
   return ok();
 }
+
+}  // namespace
+
+namespace i4d {
 
 i4d_status check_cache(const i4d_kv_cache* c, const i4d_layer_shape* s, int M) {
   if (!c) return fail(I4D_ERR_NULL, "cache is NULL");
@@ -79,6 +87,10 @@ KvArgs kv_args(const i4d_kv_cache* c) {
   k.err_word = c->err_word;
   return k;
 }
+
+}  // namespace i4d
+
+namespace {
 
 ProjArgs proj_args(const void* codes, const uint16_t* scales, const uint16_t* x, int Np, int K,
                    int M, float eps) {

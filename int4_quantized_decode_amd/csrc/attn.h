@@ -42,6 +42,8 @@ struct AttnArgs {
   uint16_t* attn_bf16;     // [M][n_q*hd]
 };
 
+KvArgs kv_args(const i4d_kv_cache* c);
+
 i4d_status launch_kv_append(const AppendArgs& a, hipStream_t st);
 // nwa = waves per workgroup (4, 8 or 16).  With S > 1 the launch writes
 // per-split partials; combine = true adds the kernel that merges them into

@@ -27,6 +27,11 @@ bool aligned16(const void* p);
 // validates a layer shape (returns I4D_OK or the error, message set)
 i4d_status check_shape(const i4d_layer_shape* s);
 
+// a required device pointer: non-NULL and 16-byte aligned
+i4d_status need(const void* p, const char* what);
+// a cache that matches the shape `s` (may be NULL) and holds at least M rows
+i4d_status check_cache(const i4d_kv_cache* c, const i4d_layer_shape* s, int M);
+
 // launch plan of the attention kernel: KV splits per (row, kv head) and
 // waves per workgroup
 struct AttnPlan {

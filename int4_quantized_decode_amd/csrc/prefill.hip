@@ -1,0 +1,677 @@
+// prefill.hip - FP8 (E4M3) prefill of the QKV projection, with the keys and
+// values placed straight into the INT4 cache (gfx950).
+//
+// The "how it works" section of the onedev.kr summary describes the prefill
+// as an FP8 GEMM whose QKV epilogue writes K and V at offset(request, head,
+// position, channel) of the cache (no dense K/V tensor, no scatter kernel),
+// with the RMSNorm gain folded into the weights and rho applied in the
+// epilogue, FP8 outputs written by the producing epilogue under delayed
+// per-tensor scaling (this call's maximum sets the next call's scale), and
+// packed requests tracked by prefix sums instead of padding rows.
+//
+// Launches:
+//   prep   one workgroup per (16-token tile, chunk of 8 weight groups of d):
+//          the token map (request by binary search of the prefix sums,
+//          position), the RoPE rotation of every token, partial sums of
+//          squares for rho, max |x| (atomic max), and x8 = E4M3(x / s_x)
+//          stored in the FP8 MFMA operand order;
+//   gemm   one workgroup per (two heads = 256 output rows, 128 tokens):
+//          v_mfma_scale_f32_16x16x128_f8f6f4 with unit block scales.  A is
+//          the E4M3 weight atom exactly as stored for the decode variant
+//          (lane 16j + r: row r, bytes 8kb + e = k 32kb + 8j + e), B the x8
+//          tile in the same byte order, so the 128-term dot product of a
+//          group comes out of one instruction.  Each group's product is
+//          scaled by its fp16 weight scale and added to the fp32 tile.
+//          Epilogue through LDS per 32 tokens: s_x * rho, RoPE, then q ->
+//          E4M3(q / s_q) (max |q| atomic), k and v -> bf16 -> Hadamard
+//          rotation -> INT4 with one fp16 scale -> cache slot;
+//   update (own entry point) next scale = max / 448, maxima reset.
+//
+// Every (token, head) of the cache is written by exactly one workgroup.
+// A value dword holds 8 tokens of one channel: it is stored whole when its 8
+// tokens are in one workgroup's tile and request, else each token sets its
+// nibble with an atomic and/or (the tile edges and request ends).
+#include <math.h>
+
+#include "attn.h"
+#include "device_common.h"
+#include "gemv.h"
+#include "i4d_internal.h"
+
+namespace i4d {
+
+namespace {
+
+constexpr int kHd = 128;            // head_dim this path takes
+constexpr int kTilesPerWg = 8;      // 16-token tiles per gemm workgroup
+constexpr int kTokPerWg = 16 * kTilesPerWg;
+constexpr int kRowsPerWg = 256;     // two heads
+constexpr int kStripsPerWave = 4;   // 64 rows per wave
+constexpr int kChunkTok = 32;       // epilogue tokens per LDS pass
+constexpr int kYPitch = kHd + 4;    // fp32 words per (head, token) row of the epilogue tile
+constexpr int kPrepGroups = 8;      // weight groups of d per prep workgroup
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+struct PrefillArgs {
+  const uint8_t* codes;  // E4M3 QKV atoms [strip][group][64 lanes][32 B]
+  const uint16_t* scales;
+  int N, K, G;
+  int n_q, n_kv;
+  float eps;
+  double rope_ratio;
+  const uint16_t* x;  // bf16 [T][K]
+  int T, T128, R, nch;
+  const int32_t* cu;     // [R + 1]
+  const int32_t* start;  // [R]
+  i4d_fp8_scales* sc;
+  uint8_t* q8;  // [T][n_q * 128]
+  uint16_t* k_bf16;
+  uint16_t* v_bf16;
+  KvArgs kv;
+  uint8_t* x8;    // [T128 / 16][G][2 halves][64 lanes][16 B]
+  float* sumsq;   // [nch][T128]
+  int2* map;      // [T128] (cache row, position; -1 = no cache write)
+  float2* rope;   // [T128][64] (cos, sin)
+};
+
+// OCP E4M3 code of a finite fp32 value: nearest, ties to even, saturating at
+// +-448, the sign kept on zero.  Normals round the fp32 mantissa to 3 bits
+// (the carry moves into the exponent); below 2^-6 the step is 2^-9.
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  const float a = fminf(fabsf(v), 448.0f);
+  uint32_t mag;
+  if (a < 0.015625f) {
+    mag = (uint32_t)rintf(a * 512.0f);
+  } else {
+    const uint32_t b = __float_as_uint(a);
+    mag = ((b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20) - (120u << 3);
+  }
+  return sign | mag;
+}
+
+// a per-tensor scale the caller supplied: a positive finite value, else 1
+// with I4D_DEVERR_SCALE raised
+__device__ __forceinline__ float checked_scale(float s, int32_t* err, bool report) {
+  if (s > 0.f && s <= 3.4e38f) return s;
+  if (report && err) atomicOr(err, I4D_DEVERR_SCALE);
+  return 1.0f;
+}
+
+__device__ __forceinline__ void atomic_max_pos(float* p, float v) {
+  atomicMax(reinterpret_cast<unsigned int*>(p), __float_as_uint(v));
+}
+
+// workgroup b of n on XCD b % 8 -> a linear index in which each XCD holds a
+// contiguous range (its workgroups share weights in that XCD's L2)
+__device__ __forceinline__ int xcd_linear(int b, int n) {
+  const int q = n / 8, r = n % 8, x = b % 8;
+  return x * q + min(x, r) + b / 8;
+}
+
+// ---------------------------------------------------------------------------
+// prep
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void prefill_prep_kernel(PrefillArgs a) {
+  __shared__ float red_sq[4][16];
+  __shared__ float red_max[4];
+  __shared__ int tok_pos[16];
+  const int tile = blockIdx.x, ch = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 15, j = lane >> 4;
+  const int t = tile * 16 + r;
+  const bool live = t < a.T;
+  const float sx = checked_scale(a.sc->x_scale, a.kv.err_word, tile == 0 && ch == 0 && tid == 0);
+
+  float sq = 0.f, amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int u = tid + 256 * i;
+    const int g = ch * kPrepGroups + (u >> 7), h = (u >> 6) & 1;
+    if (g >= a.G) break;
+    uint32_t out[4];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int k0 = 128 * g + 32 * (2 * h + half) + 8 * j;
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (live) v = load16(a.x + (size_t)t * a.K + k0);
+      uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float f = (e & 1) ? bf16_hi(v[e >> 1]) : bf16_lo(v[e >> 1]);
+        sq = fmaf(f, f, sq);
+        amax = fmaxf(amax, fabsf(f));
+        const uint32_t c = e4m3_code(__fdiv_rn(f, sx));
+        if (e < 4) w0 |= c << (8 * e); else w1 |= c << (8 * (e - 4));
+      }
+      out[2 * half] = w0;
+      out[2 * half + 1] = w1;
+    }
+    const u32x4_t o = {out[0], out[1], out[2], out[3]};
+    *reinterpret_cast<u32x4_t*>(a.x8 + ((((size_t)tile * a.G + g) * 2 + h) * 64 + lane) * 16) = o;
+  }
+  // the thread's token is r in every unit: sum over j (lanes), then waves
+  sq += lane_xor(sq, 16, lane);
+  sq += lane_xor(sq, 32, lane);
+  float m = amax;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, lane_xor(m, o, lane));
+  if (j == 0) red_sq[wave][r] = sq;
+  if (lane == 0) red_max[wave] = m;
+  if (ch == 0 && tid < 16) {
+    // token map: request rr with cu[rr] <= t < cu[rr + 1]
+    const int tt = tile * 16 + tid;
+    int row = 0, cpos = -1, rpos = 0;
+    if (tt < a.T) {
+      int lo = 0, hi = a.R;  // cu[lo] <= tt < cu[hi] when tt is inside the batch
+      if (a.cu[0] <= tt && tt < a.cu[a.R]) {
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (a.cu[mid] <= tt) lo = mid; else hi = mid;
+        }
+        row = lo;
+        rpos = a.start[lo] + (tt - a.cu[lo]);
+        const int64_t cap = a.kv.row_base[lo + 1] - a.kv.row_base[lo];
+        cpos = (rpos >= 0 && rpos < cap) ? rpos : -1;
+      }
+      if (cpos < 0 && a.kv.err_word) atomicOr(a.kv.err_word, I4D_DEVERR_APPEND_POS);
+      rpos = max(rpos, 0);
+    }
+    a.map[tt] = make_int2(row, cpos);
+    tok_pos[tid] = rpos;
+  }
+  __syncthreads();
+  if (tid < 16) {
+    const float s = red_sq[0][tid] + red_sq[1][tid] + red_sq[2][tid] + red_sq[3][tid];
+    a.sumsq[(size_t)ch * a.T128 + tile * 16 + tid] = s;
+  }
+  if (tid == 0) {
+    const float mm = fmaxf(fmaxf(red_max[0], red_max[1]), fmaxf(red_max[2], red_max[3]));
+    if (mm > 0.f) atomic_max_pos(&a.sc->x_amax, mm);
+  }
+  if (ch == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + 256 * i;  // token idx / 64 of the tile, pair c = idx % 64
+      const int tl = idx >> 6, c = idx & 63;
+      float cs, sn;
+      rope_angle(a.rope_ratio, tok_pos[tl], c, cs, sn);
+      a.rope[(size_t)(tile * 16 + tl) * 64 + c] = make_float2(cs, sn);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// gemm + epilogue
+// ---------------------------------------------------------------------------
+
+struct TokInfo {
+  int row, pos;  // cache row, position (-1: no cache write)
+  int lo, hi;    // the token's request as a local token range of this tile
+  float rho;
+};
+
+// LDS: B operands [2 buffers][8 tiles][2 KiB], reused by the epilogue's fp32
+// tile [2 heads][32 tokens][kYPitch]; value codes [128 tokens][2][128];
+// token info [128]
+constexpr size_t kBBytes = 2 * kTilesPerWg * 2048;
+constexpr size_t kYBytes = (size_t)2 * kChunkTok * kYPitch * 4;
+constexpr size_t kRegion0 = kBBytes > kYBytes ? kBBytes : kYBytes;
+constexpr size_t kVcodeBytes = (size_t)kTokPerWg * 2 * kHd;
+constexpr size_t kGemmLds = kRegion0 + kVcodeBytes + kTokPerWg * sizeof(TokInfo);
+
+__device__ __forceinline__ i32x8_t cat8(const u32x4_t& lo, const u32x4_t& hi) {
+  return i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
+__global__ __launch_bounds__(256) void prefill_gemm_kernel(PrefillArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  unsigned char* bbuf = smem;
+  float* ybuf = reinterpret_cast<float*>(smem);
+  uint8_t* vcodes = smem + kRegion0;
+  TokInfo* tinfo = reinterpret_cast<TokInfo*>(smem + kRegion0 + kVcodeBytes);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, j = lane >> 4;
+  const int G = a.G;
+  const int t_tiles = a.T128 / kTokPerWg;
+  const int b = xcd_linear(blockIdx.x, gridDim.x);
+  const int ntile = b / t_tiles, ttile = b % t_tiles;
+  const int strip0 = ntile * (kRowsPerWg / 16) + wave * kStripsPerWave;
+  const int tile16_0 = ttile * kTilesPerWg;
+  const int tok0 = ttile * kTokPerWg;
+
+  // ---- main loop over the weight groups of d ----
+  struct ARegs {
+    u32x4_t w[kStripsPerWave][2];
+    u32x2_t sc[kStripsPerWave];
+  };
+  auto load_a = [&](ARegs& A, int g) {
+#pragma unroll
+    for (int s = 0; s < kStripsPerWave; ++s) {
+      const size_t atom = (size_t)(strip0 + s) * G + g;
+      const uint8_t* p = a.codes + atom * 2048 + lane * 32;
+      A.w[s][0] = load16_stream(p);
+      A.w[s][1] = load16_stream(p + 16);
+      A.sc[s] = *reinterpret_cast<const u32x2_t*>(a.scales + atom * 16 + 4 * j);
+    }
+  };
+  u32x4_t bst[kTilesPerWg / 2];
+  auto load_b = [&](int g) {
+#pragma unroll
+    for (int i = 0; i < kTilesPerWg / 2; ++i) {
+      const int v = tid + 256 * i, tt = v >> 7;
+      bst[i] = load16(a.x8 + ((size_t)(tile16_0 + tt) * G + g) * 2048 + (v & 127) * 16);
+    }
+  };
+  auto store_b = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < kTilesPerWg / 2; ++i) {
+      const int v = tid + 256 * i;
+      *reinterpret_cast<u32x4_t*>(bbuf + (size_t)buf * kTilesPerWg * 2048 + v * 16) = bst[i];
+    }
+  };
+
+  f32x4_t acc[kStripsPerWave][kTilesPerWg];
+#pragma unroll
+  for (int s = 0; s < kStripsPerWave; ++s)
+#pragma unroll
+    for (int t = 0; t < kTilesPerWg; ++t) acc[s][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const ARegs& A, int buf) {
+    float scl[kStripsPerWave][4];
+    i32x8_t av[kStripsPerWave];
+#pragma unroll
+    for (int s = 0; s < kStripsPerWave; ++s) {
+      av[s] = cat8(A.w[s][0], A.w[s][1]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) scl[s][i] = f16_bits_to_f32((uint16_t)(A.sc[s][i >> 1] >> (16 * (i & 1))));
+    }
+    const unsigned char* bb = bbuf + (size_t)buf * kTilesPerWg * 2048;
+    // the products of tile t are issued before the scaled adds of tile t - 1,
+    // so that the MFMA latency is covered by independent work
+    f32x4_t prev[kStripsPerWave];
+#pragma unroll
+    for (int t = 0; t <= kTilesPerWg; ++t) {
+      f32x4_t cur[kStripsPerWave];
+      if (t < kTilesPerWg) {
+        const u32x4_t h0 = *reinterpret_cast<const u32x4_t*>(bb + t * 2048 + lane * 16);
+        const u32x4_t h1 = *reinterpret_cast<const u32x4_t*>(bb + t * 2048 + 1024 + lane * 16);
+        const i32x8_t bv = cat8(h0, h1);
+#pragma unroll
+        for (int s = 0; s < kStripsPerWave; ++s)
+          cur[s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av[s], bv, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0,
+                                                                    0, 127, 0, 127);
+      }
+      if (t > 0) {
+#pragma unroll
+        for (int s = 0; s < kStripsPerWave; ++s)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[s][t - 1][i] = fmaf(scl[s][i], prev[s][i], acc[s][t - 1][i]);
+      }
+      if (t < kTilesPerWg) {
+#pragma unroll
+        for (int s = 0; s < kStripsPerWave; ++s) prev[s] = cur[s];
+      }
+    }
+  };
+
+  ARegs A0, A1;
+  load_a(A0, 0);
+  load_b(0);
+  store_b(0);
+  __syncthreads();
+  for (int g = 0; g < G; g += 2) {
+    if (g + 1 < G) {
+      load_a(A1, g + 1);
+      load_b(g + 1);
+    }
+    compute(A0, 0);
+    if (g + 1 < G) store_b(1);
+    __syncthreads();
+    if (g + 1 >= G) break;
+    if (g + 2 < G) {
+      load_a(A0, g + 2);
+      load_b(g + 2);
+    }
+    compute(A1, 1);
+    if (g + 2 < G) store_b(0);
+    __syncthreads();
+  }
+
+  // ---- epilogue ----
+  const float sx = checked_scale(a.sc->x_scale, nullptr, false);
+  const float sq = checked_scale(a.sc->q_scale, a.kv.err_word, blockIdx.x == 0 && tid == 0);
+  if (tid < kTokPerWg) {
+    const int t = tok0 + tid;
+    float s = 0.f;
+    for (int c = 0; c < a.nch; ++c) s += a.sumsq[(size_t)c * a.T128 + t];
+    TokInfo ti;
+    ti.rho = 1.0f / sqrtf(s / (float)a.K + a.eps);
+    const int2 m = a.map[t];
+    ti.row = m.x;
+    ti.pos = t < a.T ? m.y : -1;
+    ti.lo = 0;
+    ti.hi = 0;
+    if (ti.pos >= 0) {
+      ti.lo = max(a.cu[m.x], tok0) - tok0;
+      ti.hi = min(min(a.cu[m.x + 1], a.T), tok0 + kTokPerWg) - tok0;
+    }
+    tinfo[tid] = ti;
+  }
+  __syncthreads();
+
+  const int head0 = ntile * 2;  // first of the workgroup's two heads (q | k | v order)
+  float qmax = 0.f;
+  const int hl_w = wave >> 1;  // head of this wave's rows
+  const int sp0 = 4 * (wave & 1);
+#pragma unroll
+  for (int c = 0; c < kTilesPerWg / 2; ++c) {
+    // fp32 tile [head][token][channel] of tokens 32c .. 32c + 31 (the loop is
+    // unrolled so that acc is indexed by constants and stays in registers)
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int t = 2 * c + tt;
+      const int tl = 16 * tt + r;
+      const float f = sx * tinfo[16 * t + r].rho;
+#pragma unroll
+      for (int s = 0; s < kStripsPerWave; ++s) {
+        const int sp = sp0 + s;
+        const int ch0 = (j < 2) ? 8 * sp + 4 * j : kHd / 2 + 8 * sp + 4 * (j - 2);
+        const f32x4_t v = {acc[s][t][0] * f, acc[s][t][1] * f, acc[s][t][2] * f, acc[s][t][3] * f};
+        *reinterpret_cast<f32x4_t*>(&ybuf[((size_t)hl_w * kChunkTok + tl) * kYPitch + ch0]) = v;
+      }
+    }
+    __syncthreads();
+    // one (head, token) vector per 16 lanes, 8 channels per lane
+    const int l16 = tid & 15;
+#pragma unroll 1
+    for (int it = 0; it < 4; ++it) {
+      const int vec = it * 16 + (tid >> 4);
+      const int hl = vec >> 5, tl = vec & 31;
+      const int tloc = 32 * c + tl;
+      const int t = tok0 + tloc;
+      const int head = head0 + hl;
+      const bool is_q = head < a.n_q;
+      const bool is_k = !is_q && head < a.n_q + a.n_kv;
+      const TokInfo ti = tinfo[tloc];
+      const float* yr = &ybuf[((size_t)hl * kChunkTok + tl) * kYPitch];
+      float y[8];
+      {
+        const f32x4_t p0 = *reinterpret_cast<const f32x4_t*>(yr + 8 * l16);
+        const f32x4_t p1 = *reinterpret_cast<const f32x4_t*>(yr + 8 * l16 + 4);
+        y[0] = p0.x; y[1] = p0.y; y[2] = p0.z; y[3] = p0.w;
+        y[4] = p1.x; y[5] = p1.y; y[6] = p1.z; y[7] = p1.w;
+      }
+      if (is_q || is_k) {
+        // rotate-half RoPE: channel c pairs with c + 64 (lane l16 ^ 8)
+        const int part = (8 * l16 + kHd / 2) & (kHd - 1);
+        const f32x4_t p0 = *reinterpret_cast<const f32x4_t*>(yr + part);
+        const f32x4_t p1 = *reinterpret_cast<const f32x4_t*>(yr + part + 4);
+        const float o[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+        const float2* rp = a.rope + (size_t)t * 64 + (8 * l16 & 63);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float2 cs = rp[e];
+          y[e] = (l16 < 8) ? y[e] * cs.x - o[e] * cs.y : y[e] * cs.x + o[e] * cs.y;
+        }
+      }
+      if (t >= a.T) continue;
+      if (is_q) {
+        uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          qmax = fmaxf(qmax, fabsf(y[e]));
+          const uint32_t code = e4m3_code(__fdiv_rn(y[e], sq));
+          if (e < 4) w0 |= code << (8 * e); else w1 |= code << (8 * (e - 4));
+        }
+        *reinterpret_cast<u32x2_t*>(a.q8 + ((size_t)t * a.n_q + head) * kHd + 8 * l16) = u32x2_t{w0, w1};
+        continue;
+      }
+      // keys and values: bf16, Hadamard rotation, INT4 with one fp16 scale
+      const int kvh = head - a.n_q - (is_k ? 0 : a.n_kv);
+      const int64_t cap = (ti.pos >= 0) ? a.kv.row_base[ti.row + 1] - a.kv.row_base[ti.row] : 0;
+      const int64_t slot = (ti.pos >= 0) ? a.kv.row_base[ti.row] * a.kv.n_kv + (int64_t)kvh * cap + ti.pos : 0;
+      uint16_t bf[8];
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        bf[e] = f32_to_bf16(y[e]);
+        x[e] = bf16_to_f32(bf[e]);
+      }
+      uint16_t* dense = is_k ? a.k_bf16 : a.v_bf16;
+      if (dense && ti.pos >= 0) {
+        const u32x4_t pk = {bf[0] | ((uint32_t)bf[1] << 16), bf[2] | ((uint32_t)bf[3] << 16),
+                            bf[4] | ((uint32_t)bf[5] << 16), bf[6] | ((uint32_t)bf[7] << 16)};
+        *reinterpret_cast<u32x4_t*>(dense + slot * kHd + 8 * l16) = pk;
+      }
+#pragma unroll
+      for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (!(e & h)) {
+            const float lo = x[e], hi = x[e | h];
+            x[e] = lo + hi;
+            x[e | h] = lo - hi;
+          }
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p = lane_xor(x[e], m, lane);
+          x[e] = (l16 & m) ? (p - x[e]) : (x[e] + p);
+        }
+      float am = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(x[e]));
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1) am = fmaxf(am, lane_xor(am, m, lane));
+      const float q7 = __fdiv_rn(am, 7.0f);
+      _Float16 h16 = (_Float16)q7;
+      uint16_t s16 = bitcast<uint16_t>(h16);
+      if ((s16 & 0x7fffu) == 0x7c00u) s16 = (uint16_t)((s16 & 0x8000u) | 0x7bffu);
+      const float sf = f16_bits_to_f32(s16);
+      uint32_t u[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        u[e] = (sf != 0.f) ? (uint32_t)((int)fminf(7.f, fmaxf(-8.f, rintf(__fdiv_rn(x[e], sf)))) + 8) : 8u;
+      if (ti.pos < 0) continue;
+      if (is_k) {
+        // key slot dword jj * 4 + kb holds channels 32 kb + 8 jj + e: this lane's 8
+        uint32_t word = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) word |= u[e] << (4 * (4 * (e & 1) + (e >> 1)));
+        const int kb = l16 >> 2, jj = l16 & 3;
+        reinterpret_cast<uint32_t*>(a.kv.k_codes + (size_t)slot * (kHd / 2))[jj * 4 + kb] = word;
+        if (l16 == 0) a.kv.k_scales[slot] = s16;
+      } else {
+        uint32_t c0 = 0, c1 = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          c0 |= u[e] << (8 * e);
+          c1 |= u[e + 4] << (8 * e);
+        }
+        *reinterpret_cast<u32x2_t*>(vcodes + ((size_t)tloc * 2 + hl) * kHd + 8 * l16) = u32x2_t{c0, c1};
+        if (l16 == 0) a.kv.v_scales[slot] = s16;
+      }
+    }
+    __syncthreads();
+  }
+
+  // value blocks: a dword holds channel c of tokens w = 4jj + e and 16 + 4jj + e
+  // (e = 0..3) of one 32-token block
+#pragma unroll 1
+  for (int hl = 0; hl < 2; ++hl) {
+    const int head = head0 + hl;
+    if (head < a.n_q + a.n_kv) continue;
+    const int kvh = head - a.n_q - a.n_kv;
+    for (int it = tid; it < kTokPerWg * kHd; it += 256) {
+      const int tloc = it / kHd, ch = it % kHd;
+      const TokInfo ti = tinfo[tloc];
+      if (ti.pos < 0) continue;
+      const int w = ti.pos & 31;
+      const int jj = (w & 15) >> 2;
+      const int e = (w & 3) + (w >= 16 ? 4 : 0);
+      const int off = (w & 3) + (w >= 16 ? 16 : 0);  // distance from the dword's first token
+      const int lead = tloc - off;
+      const bool whole = lead >= ti.lo && lead + 19 < ti.hi;
+      const int64_t cap = a.kv.row_base[ti.row + 1] - a.kv.row_base[ti.row];
+      const int64_t region = a.kv.row_base[ti.row] * a.kv.n_kv + (int64_t)kvh * cap;
+      uint32_t* dw = a.kv.v_codes + (size_t)(region / 32 + ti.pos / 32) * 4 * kHd + jj * kHd + (ch % 16) * (kHd / 16) +
+                     ch / 16;
+      if (whole) {
+        if (off != 0) continue;
+        uint32_t word = 0;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int o = (q < 4) ? q : 12 + q;
+          const uint32_t code = vcodes[((size_t)(tloc + o) * 2 + hl) * kHd + ch];
+          word |= code << (4 * (4 * (q & 1) + (q >> 1)));
+        }
+        *dw = word;
+      } else {
+        const int sh = 4 * (4 * (e & 1) + (e >> 1));
+        const uint32_t code = vcodes[((size_t)tloc * 2 + hl) * kHd + ch];
+        atomicAnd(dw, ~(0xFu << sh));
+        atomicOr(dw, code << sh);
+      }
+    }
+  }
+
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) qmax = fmaxf(qmax, lane_xor(qmax, o, lane));
+  if (lane == 0 && qmax > 0.f) atomic_max_pos(&a.sc->q_amax, qmax);
+}
+
+__global__ void fp8_scales_update_kernel(i4d_fp8_scales* s) {
+  if (threadIdx.x != 0) return;
+  const float ax = s->x_amax, aq = s->q_amax;
+  if (ax > 0.f) s->x_scale = __fdiv_rn(ax, 448.0f);
+  if (aq > 0.f) s->q_scale = __fdiv_rn(aq, 448.0f);
+  s->x_amax = 0.f;
+  s->q_amax = 0.f;
+}
+
+struct PrefillWs {
+  size_t x8, sumsq, map, rope, total;
+  int T128, nch;
+};
+
+PrefillWs prefill_ws(const i4d_layer_shape& s, int T) {
+  PrefillWs w;
+  w.T128 = ((T + kTokPerWg - 1) / kTokPerWg) * kTokPerWg;
+  w.nch = (groups_of(s.d_model) + kPrepGroups - 1) / kPrepGroups;
+  size_t o = 0;
+  w.x8 = o;
+  o = align256(o + (size_t)w.T128 * s.d_model);
+  w.sumsq = o;
+  o = align256(o + (size_t)w.nch * w.T128 * sizeof(float));
+  w.map = o;
+  o = align256(o + (size_t)w.T128 * sizeof(int2));
+  w.rope = o;
+  o = align256(o + (size_t)w.T128 * 64 * sizeof(float2));
+  w.total = o;
+  return w;
+}
+
+i4d_status check_prefill_shape(const i4d_layer_shape* s) {
+  if (!s) return fail(I4D_ERR_NULL, "shape is NULL");
+  i4d_status st = check_shape(s);
+  if (st != I4D_OK) return st;
+  if (s->head_dim != kHd) return fail(I4D_ERR_UNSUPPORTED, "the FP8 prefill takes head_dim 128 (got %d)", s->head_dim);
+  if ((s->n_q_heads + 2 * s->n_kv_heads) % 2)
+    return fail(I4D_ERR_UNSUPPORTED, "the FP8 prefill needs an even number of q + k + v heads (%d)",
+                s->n_q_heads + 2 * s->n_kv_heads);
+  return ok();
+}
+
+}  // namespace
+
+}  // namespace i4d
+
+using namespace i4d;
+
+extern "C" i4d_status i4d_prefill_workspace_bytes(const i4d_layer_shape* shape, int T, size_t* bytes) {
+  i4d_status st = check_prefill_shape(shape);
+  if (st != I4D_OK) return st;
+  if (T < 0) return fail(I4D_ERR_RANGE, "T=%d", T);
+  if (!bytes) return fail(I4D_ERR_NULL, "bytes is NULL");
+  *bytes = prefill_ws(*shape, T).total;
+  return ok();
+}
+
+extern "C" i4d_status i4d_prefill_qkv_e4m3(const i4d_layer* layer, const i4d_kv_cache* cache, const uint16_t* x,
+                                           int T, const int32_t* cu_seqlens, const int32_t* start_pos, int R,
+                                           i4d_fp8_scales* scales, uint8_t* q_fp8, uint16_t* k_bf16,
+                                           uint16_t* v_bf16, void* workspace, size_t workspace_bytes,
+                                           void* stream) {
+  if (!layer) return fail(I4D_ERR_NULL, "layer is NULL");
+  const i4d_layer_shape& s = layer->shape;
+  i4d_status st = check_prefill_shape(&s);
+  if (st != I4D_OK) return st;
+  if ((st = need(layer->qkv_codes, "qkv_codes")) != I4D_OK) return st;
+  if ((st = need(layer->qkv_scales, "qkv_scales")) != I4D_OK) return st;
+  if (T < 0) return fail(I4D_ERR_RANGE, "T=%d", T);
+  if (R < 1) return fail(I4D_ERR_RANGE, "R=%d requests", R);
+  if ((st = check_cache(cache, &s, R)) != I4D_OK) return st;
+  if (!cu_seqlens || !start_pos) return fail(I4D_ERR_NULL, "cu_seqlens / start_pos is NULL");
+  if (!scales) return fail(I4D_ERR_NULL, "scales is NULL");
+  if (T == 0) return ok();
+  if ((st = need(x, "x")) != I4D_OK) return st;
+  if ((st = need(q_fp8, "q_fp8")) != I4D_OK) return st;
+  if (k_bf16 && !aligned16(k_bf16)) return fail(I4D_ERR_ALIGN, "k_bf16 is not 16-byte aligned");
+  if (v_bf16 && !aligned16(v_bf16)) return fail(I4D_ERR_ALIGN, "v_bf16 is not 16-byte aligned");
+  if ((st = need(workspace, "workspace")) != I4D_OK) return st;
+  const PrefillWs w = prefill_ws(s, T);
+  if (workspace_bytes < w.total)
+    return fail(I4D_ERR_WORKSPACE, "prefill workspace %zu bytes < %zu", workspace_bytes, w.total);
+
+  PrefillArgs a = {};
+  a.codes = (const uint8_t*)layer->qkv_codes;
+  a.scales = layer->qkv_scales;
+  a.N = (s.n_q_heads + 2 * s.n_kv_heads) * kHd;
+  a.K = s.d_model;
+  a.G = groups_of(s.d_model);
+  a.n_q = s.n_q_heads;
+  a.n_kv = s.n_kv_heads;
+  a.eps = s.rms_eps;
+  a.rope_ratio = pow((double)s.rope_theta, -2.0 / (double)s.head_dim);
+  a.x = x;
+  a.T = T;
+  a.T128 = w.T128;
+  a.R = R;
+  a.nch = w.nch;
+  a.cu = cu_seqlens;
+  a.start = start_pos;
+  a.sc = scales;
+  a.q8 = q_fp8;
+  a.k_bf16 = k_bf16;
+  a.v_bf16 = v_bf16;
+  a.kv = kv_args(cache);
+  char* ws = (char*)workspace;
+  a.x8 = (uint8_t*)(ws + w.x8);
+  a.sumsq = (float*)(ws + w.sumsq);
+  a.map = (int2*)(ws + w.map);
+  a.rope = (float2*)(ws + w.rope);
+
+  hipStream_t hs = (hipStream_t)stream;
+  hipLaunchKernelGGL(prefill_prep_kernel, dim3(w.T128 / 16, w.nch), dim3(256), 0, hs, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(I4D_ERR_HIP, "prefill prep launch: %s", hipGetErrorString(e));
+  const int grid = (a.N / kRowsPerWg) * (w.T128 / kTokPerWg);
+  hipLaunchKernelGGL(prefill_gemm_kernel, dim3(grid), dim3(256), kGemmLds, hs, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return fail(I4D_ERR_HIP, "prefill gemm launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+extern "C" i4d_status i4d_fp8_scales_update(i4d_fp8_scales* scales, void* stream) {
+  if (!scales) return fail(I4D_ERR_NULL, "scales is NULL");
+  hipLaunchKernelGGL(fp8_scales_update_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, scales);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(I4D_ERR_HIP, "scale update launch: %s", hipGetErrorString(e));
+  return ok();
+}
