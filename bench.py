@@ -2,6 +2,9 @@
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--M m]
 
+(a prefill workload name, e.g. 8b_prefill_s2048, times the FP8 prefill of
+the QKV projection instead: see prefill_bench)
+
 One step = one decode_block_step (QKV + rho1 + RoPE, KV append through the
 Hadamard rotation, split-KV GQA attention + combine + inverse rotation, O +
 residual, gate/up + SwiGLU, down + residual) for one batch of decode rows.
@@ -29,6 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0  # dense fp8 MFMA, MI355X
 
 # HBM traffic of the dominant kernel per launch, from two rocprofv3 --pmc
 # runs (FETCH_SIZE, then WRITE_SIZE) scaled by the same counters on a plain
@@ -141,6 +145,8 @@ def main():
         print(json.dumps({"copy_bytes": n, "launches": 3}), flush=True)
         return
     B.lib()
+    if args.workload in synth.PREFILL_WORKLOADS:
+        return prefill_bench(args, synth.PREFILL_WORKLOADS[args.workload], torch, B, D, synth)
     wl = synth.WORKLOADS[args.workload]
     if wl.n_layers > 1:
         return full_model(args, wl, torch, B, D, synth)
@@ -362,6 +368,129 @@ def full_model(args, wl, torch, B, D, synth):
         "setup_s": round(setup_s, 1),
     }
     print(json.dumps(result), flush=True)
+
+
+def prefill_bench(args, pw, torch, B, D, synth):
+    """The FP8 prefill of the QKV projection on a packed batch: one step =
+    i4d_prefill_qkv_e4m3 (prep launch + FP8 GEMM launch with the q / INT4
+    cache epilogue) + i4d_fp8_scales_update, inputs resident in HBM, K steps
+    in one captured HIP graph between two events.  The roofline entry is the
+    GEMM launch alone (i4d_prefill_project replayed over the prepared
+    workspace), priced against the dense fp8 MFMA peak with the algorithmic
+    2 T N d flops of the projection."""
+    shape, T, R = pw.shape, pw.T, len(pw.seqlens)
+    t0 = time.time()
+    lw = synth.make_layer(shape, pw.seed)
+    layer = D.DeviceLayer(shape, lw, fmt="e4m3")
+    caps = [s + n for s, n in zip(pw.starts, pw.seqlens)]
+    cache = D.DeviceCache(shape, caps)
+    xb = synth.make_prefill_x(shape, T, pw.seed)
+    x_d = D.to_device_u16(xb)
+    cu = torch.from_numpy(synth.prefill_offsets(pw.seqlens)).cuda()
+    st = torch.tensor(pw.starts, dtype=torch.int32, device="cuda")
+    sx0 = float(np.max(np.abs(synth.bf16_bits_to_f32(xb)))) / 448.0
+    scales = torch.tensor([sx0, 1.0, 0.0, 0.0], dtype=torch.float32, device="cuda")
+    cs = B.make_shape(shape)
+    nbytes = B.i4d_prefill_workspace_bytes(cs, T)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    q8 = torch.empty((T, shape.n_q_heads * shape.head_dim), dtype=torch.uint8, device="cuda")
+    setup_s = time.time() - t0
+    stream = torch.cuda.current_stream()
+
+    def step(_):
+        B.i4d_prefill_qkv_e4m3(layer.struct, cache.struct, x_d, T, cu, st, R, scales, q8, None, None, ws, nbytes)
+        B.i4d_fp8_scales_update(scales)
+
+    def project(_):
+        B.i4d_prefill_project(layer.struct, cache.struct, T, cu, st, R, scales, q8, None, None, ws, nbytes)
+
+    step(0)  # the delayed scales of this input: the timed steps run with them
+    torch.cuda.synchronize()
+    require_clean([cache], "prefill warm-up")
+
+    def capture(n, fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                fn(i)
+        return g
+
+    def timed(fn, n):
+        g_w = capture(max(args.warmup, 1), fn)
+        g = capture(n, fn)
+        g_w.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+
+    us_step = timed(step, args.steps)
+    us_gemm = timed(project, args.steps)
+    require_clean([cache], "timed prefill steps")
+    N = shape.n_qkv
+    flops = 2.0 * T * N * shape.d_model
+    tflops_gemm = flops / (us_gemm * 1e-6) / 1e12
+    result = {
+        "metric": "us per FP8 prefill QKV projection step (prep + FP8 GEMM with q / INT4 cache epilogue + "
+                  "scale update)",
+        "value": round(us_step, 3),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": max(args.warmup, 1),
+        "ms_per_step": round(us_step / 1e3, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e4m3 x e4m3 -> f32",
+        "data": "synthetic",
+        "config": {"workload": pw.name, "d_model": shape.d_model, "n_q_heads": shape.n_q_heads,
+                   "n_kv_heads": shape.n_kv_heads, "head_dim": shape.head_dim, "T": T, "requests": R,
+                   "seqlens": list(pw.seqlens), "stage": "prefill",
+                   "timing": "hip graph of K steps, events on the launch stream"},
+        "tflops_step": round(flops / (us_step * 1e-6) / 1e12, 1),
+        "flops_per_step": flops,
+        "roofline": {"kernel": "prefill_gemm_kernel (FP8 MFMA GEMM + epilogue)", "bound": "mfma",
+                     "achieved": round(tflops_gemm, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops_gemm / FP8_PEAK_TFLOPS, 4),
+                     "traffic": traffic_of(pw.name, "prefill_gemm_kernel (FP8 MFMA GEMM + epilogue)"),
+                     "avg_launch_us": round(us_gemm, 3), "flops_per_launch": flops},
+        "device_errors": device_errors([cache]),
+        "pages_context": "the pages time a whole 8B-shape prefill at S = 2048 on one H100 (804.2 us), not this "
+                         "projection alone, so there is no like-for-like baseline",
+        "setup_s": round(setup_s, 1),
+    }
+    if not args.no_cpu:
+        result["cpu_baseline"] = prefill_cpu_baseline(shape, lw, xb, pw, args.cpu_steps)
+    print(json.dumps(result), flush=True)
+
+
+def prefill_cpu_baseline(shape, lw, xb, pw, n_reps, sample=512):
+    """The oracle's prefill_qkv on the first `sample` tokens of the batch
+    (one request from position 0; the dense weight computed beforehand),
+    median of n_reps, scaled to the batch's T tokens (the projection is
+    linear in T)."""
+    import oracle as O
+    from threadpoolctl import threadpool_info
+    blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    model, nproc = host_cpu()
+    qkv = O.quantize_weight_e4m3(lw.w_qkv, lw.gamma_attn)
+    W = O.dense(qkv)
+    n = min(sample, pw.T)
+    times = []
+    for _ in range(max(1, n_reps)):
+        t = time.time()
+        O.prefill_qkv(shape, qkv, xb[:n], np.array([0, n], np.int32), [0], np.float32(0.1), np.float32(0.1),
+                      W_dense=W)
+        times.append(time.time() - t)
+    us = float(np.median(times)) * 1e6 * pw.T / n
+    return {"value": round(us, 1), "unit": "us/step", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"prefill_qkv on {n} of the {pw.T} tokens of {pw.name} (median of {max(1, n_reps)}; fp64 "
+                      f"numpy), scaled by {pw.T}/{n}",
+            "host_cpu": model, "nproc": int(nproc)}
 
 
 def host_cpu():

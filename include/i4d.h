@@ -469,6 +469,24 @@ i4d_status i4d_prefill_qkv_e4m3(const i4d_layer* layer, const i4d_kv_cache* cach
                                 i4d_fp8_scales* scales, uint8_t* q_fp8, uint16_t* k_bf16, uint16_t* v_bf16,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* The two launches of i4d_prefill_qkv_e4m3 as separate calls (same
+ * arguments, the workspace carrying the first call's results to the
+ * second): i4d_prefill_prepare reads x and writes the FP8 activations,
+ * the token map, the RoPE rotations and the sums of squares of rho into the
+ * workspace and raises x_amax; it stands in for the producing epilogue of
+ * the layer before, which on the pages hands the projection its FP8 input.
+ * i4d_prefill_project runs the FP8 GEMM and its epilogue (q_fp8, the cache,
+ * k_bf16 / v_bf16, q_amax) from a workspace i4d_prefill_prepare filled
+ * for the same tokens, requests and scales; it only reads the workspace, so
+ * it may be repeated on it. */
+i4d_status i4d_prefill_prepare(const i4d_layer* layer, const i4d_kv_cache* cache, const uint16_t* x, int T,
+                               const int32_t* cu_seqlens, const int32_t* start_pos, int R, i4d_fp8_scales* scales,
+                               void* workspace, size_t workspace_bytes, void* stream);
+i4d_status i4d_prefill_project(const i4d_layer* layer, const i4d_kv_cache* cache, int T, const int32_t* cu_seqlens,
+                               const int32_t* start_pos, int R, i4d_fp8_scales* scales, uint8_t* q_fp8,
+                               uint16_t* k_bf16, uint16_t* v_bf16, const void* workspace, size_t workspace_bytes,
+                               void* stream);
+
 /* Delayed scaling step on `stream`: scale = amax / 448 (fp32, correctly
  * rounded) where amax > 0, then amax = 0, for x and for q. */
 i4d_status i4d_fp8_scales_update(i4d_fp8_scales* scales, void* stream);

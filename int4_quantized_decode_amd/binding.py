@@ -114,6 +114,10 @@ _SIGS = {
     "i4d_prefill_workspace_bytes": (_I, [ctypes.POINTER(i4d_layer_shape), _I, c_size_p]),
     "i4d_prefill_qkv_e4m3": (_I, [ctypes.POINTER(i4d_layer), ctypes.POINTER(i4d_kv_cache), _VP, _I, _VP, _VP, _I,
                                   _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
+    "i4d_prefill_prepare": (_I, [ctypes.POINTER(i4d_layer), ctypes.POINTER(i4d_kv_cache), _VP, _I, _VP, _VP, _I,
+                                 _VP, _VP, ctypes.c_size_t, _VP]),
+    "i4d_prefill_project": (_I, [ctypes.POINTER(i4d_layer), ctypes.POINTER(i4d_kv_cache), _I, _VP, _VP, _I,
+                                 _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
     "i4d_fp8_scales_update": (_I, [_VP, _VP]),
     "i4d_lm_head_workspace_bytes": (_I, [_I, _I, c_size_p]),
     "i4d_lm_head_argmax": (_I, [_VP, _I, _I, _VP, _I, ctypes.c_float, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
@@ -414,6 +418,20 @@ def i4d_prefill_qkv_e4m3(layer: i4d_layer, cache: i4d_kv_cache, x, T: int, cu_se
     _check(lib().i4d_prefill_qkv_e4m3(ctypes.byref(layer), ctypes.byref(cache), ptr(x), T, ptr(cu_seqlens),
                                       ptr(start_pos), R, ptr(scales), ptr(q_fp8), ptr(k_bf16), ptr(v_bf16),
                                       ptr(workspace), workspace_bytes, stream_handle(stream)))
+
+
+def i4d_prefill_prepare(layer: i4d_layer, cache: i4d_kv_cache, x, T: int, cu_seqlens, start_pos, R: int, scales,
+                        workspace, workspace_bytes: int, stream=None):
+    _check(lib().i4d_prefill_prepare(ctypes.byref(layer), ctypes.byref(cache), ptr(x), T, ptr(cu_seqlens),
+                                     ptr(start_pos), R, ptr(scales), ptr(workspace), workspace_bytes,
+                                     stream_handle(stream)))
+
+
+def i4d_prefill_project(layer: i4d_layer, cache: i4d_kv_cache, T: int, cu_seqlens, start_pos, R: int, scales,
+                        q_fp8, k_bf16, v_bf16, workspace, workspace_bytes: int, stream=None):
+    _check(lib().i4d_prefill_project(ctypes.byref(layer), ctypes.byref(cache), T, ptr(cu_seqlens), ptr(start_pos),
+                                     R, ptr(scales), ptr(q_fp8), ptr(k_bf16), ptr(v_bf16), ptr(workspace),
+                                     workspace_bytes, stream_handle(stream)))
 
 
 def i4d_fp8_scales_update(scales, stream=None):

@@ -18,6 +18,10 @@ SOURCES = ["api_host.cpp", "api_device.hip", "proj.hip", "attn.hip", "lmhead.hip
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           "-fno-fast-math", "-ffp-contract=fast-honor-pragmas"]
 DEVICE = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# per-file flags: the prefill GEMM keeps its MFMA results in VGPRs, where the
+# group-scale FMAs read them without accumulator-register copies (measured
+# faster there; the decode kernels are left to the default)
+EXTRA = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def build(verbose: bool = False) -> str:
@@ -28,7 +32,7 @@ def build(verbose: bool = False) -> str:
     for src in SOURCES:
         path = os.path.join(CSRC, src)
         obj = os.path.join(objdir, src + ".o")
-        cmd = [HIPCC] + COMMON + DEVICE + ["-c", path, "-o", obj]
+        cmd = [HIPCC] + COMMON + DEVICE + EXTRA.get(src, []) + ["-c", path, "-o", obj]
         if src.endswith(".cpp"):
             # host-only translation unit: no fp contraction so the packer's
             # products and divisions are single IEEE operations

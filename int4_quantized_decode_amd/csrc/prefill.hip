@@ -91,6 +91,18 @@ __device__ __forceinline__ uint32_t e4m3_code(float v) {
   return sign | mag;
 }
 
+// rint(x / s) clamped to [-8, 7], plus 8, where x / s is the correctly
+// rounded fp32 quotient: q = x * (1/s) with one residual correction is
+// within one ulp of it, which decides the same integer except next to a
+// half-integer, where the quotient is recomputed with the rounded division
+__device__ __forceinline__ uint32_t int4_code(float x, float s, float rs) {
+  const float q0 = x * rs;
+  float q = fmaf(fmaf(-q0, s, x), rs, q0);
+  const float fr = fabsf(q - truncf(q));
+  if (fabsf(fr - 0.5f) < 1.0e-5f) q = __fdiv_rn(x, s);
+  return (uint32_t)((int)fminf(7.f, fmaxf(-8.f, rintf(q))) + 8);
+}
+
 // a per-tensor scale the caller supplied: a positive finite value, else 1
 // with I4D_DEVERR_SCALE raised
 __device__ __forceinline__ float checked_scale(float s, int32_t* err, bool report) {
@@ -101,13 +113,6 @@ __device__ __forceinline__ float checked_scale(float s, int32_t* err, bool repor
 
 __device__ __forceinline__ void atomic_max_pos(float* p, float v) {
   atomicMax(reinterpret_cast<unsigned int*>(p), __float_as_uint(v));
-}
-
-// workgroup b of n on XCD b % 8 -> a linear index in which each XCD holds a
-// contiguous range (its workgroups share weights in that XCD's L2)
-__device__ __forceinline__ int xcd_linear(int b, int n) {
-  const int q = n / 8, r = n % 8, x = b % 8;
-  return x * q + min(x, r) + b / 8;
 }
 
 // ---------------------------------------------------------------------------
@@ -208,70 +213,107 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrefillArgs a) {
 // ---------------------------------------------------------------------------
 
 struct TokInfo {
+  int64_t base;  // first slot of the token's cache row (row_base * n_kv)
+  int cap;       // capacity of that row
   int row, pos;  // cache row, position (-1: no cache write)
   int lo, hi;    // the token's request as a local token range of this tile
   float rho;
 };
 
-// LDS: B operands [2 buffers][8 tiles][2 KiB], reused by the epilogue's fp32
-// tile [2 heads][32 tokens][kYPitch]; value codes [128 tokens][2][128];
-// token info [128]
-constexpr size_t kBBytes = 2 * kTilesPerWg * 2048;
+// LDS.  Main loop: a ring of kStages stages, each holding one weight group's
+// A operands [16 strips][2 halves][64 lanes][16 B], the B operands of the
+// workgroup's tokens [8 tiles][2 halves][64 lanes][16 B] and the group
+// scales [4 waves][4 strips][16 rows] fp16.  Epilogue (after the loop, over
+// the same bytes): fp32 tile [2 heads][32 tokens][kYPitch], RoPE rotations
+// [128 tokens][kRopePitch] (cos, sin), value codes [128 tokens][2 heads]
+// [128].  Token info [128] sits after both.
+constexpr int kStages = 3;
+constexpr size_t kStageA = 16 * 2048;
+constexpr size_t kStageB = kTilesPerWg * 2048;
+constexpr size_t kStageS = 4 * 4 * 32;
+constexpr size_t kStageBytes = kStageA + kStageB + kStageS;
+constexpr size_t kRingBytes = kStages * kStageBytes;
 constexpr size_t kYBytes = (size_t)2 * kChunkTok * kYPitch * 4;
-constexpr size_t kRegion0 = kBBytes > kYBytes ? kBBytes : kYBytes;
+constexpr int kRopePitch = 72;  // float2 per token row: 64 pairs + 64 B so that 4 rows read at once hit distinct banks
+constexpr size_t kRopeBytes = (size_t)kTokPerWg * kRopePitch * 8;
 constexpr size_t kVcodeBytes = (size_t)kTokPerWg * 2 * kHd;
-constexpr size_t kGemmLds = kRegion0 + kVcodeBytes + kTokPerWg * sizeof(TokInfo);
+constexpr size_t kEpiBytes = kYBytes + kRopeBytes + kVcodeBytes;
+constexpr size_t kShared = kRingBytes > kEpiBytes ? kRingBytes : kEpiBytes;
+constexpr size_t kGemmLds = kShared + kTokPerWg * sizeof(TokInfo);  // token info after the shared region
+static_assert(kGemmLds <= 160 * 1024, "LDS");
+// DMA instructions per wave and stage: A 8, B (2 per token tile over 4 waves), scales 1
+constexpr int kDmaB = kTilesPerWg / 2;
+constexpr int kDmaPerStage = 8 + kDmaB + 1;
 
 __device__ __forceinline__ i32x8_t cat8(const u32x4_t& lo, const u32x4_t& hi) {
   return i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// 16 bytes per active lane from global memory straight into LDS at
+// lds + 16 * lane.  Issued from asm (M0 saved and restored) so that the
+// compiler does not drain it before every LDS read; the ring waits for it
+// with explicit vmcnt counts (every vector-memory instruction of the main
+// loop is one of these, so the counts are exact).
+__device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(gptr), "s"(lds)
+      : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  // vmcnt <= N; expcnt and lgkmcnt left at their maxima (no wait)
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
 __global__ __launch_bounds__(256) void prefill_gemm_kernel(PrefillArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
-  unsigned char* bbuf = smem;
-  float* ybuf = reinterpret_cast<float*>(smem);
-  uint8_t* vcodes = smem + kRegion0;
-  TokInfo* tinfo = reinterpret_cast<TokInfo*>(smem + kRegion0 + kVcodeBytes);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, j = lane >> 4;
   const int G = a.G;
   const int t_tiles = a.T128 / kTokPerWg;
-  const int b = xcd_linear(blockIdx.x, gridDim.x);
+  // consecutive workgroups share the weight tile (measured faster than
+  // grouping whole weight tiles per XCD)
+  const int b = blockIdx.x;
   const int ntile = b / t_tiles, ttile = b % t_tiles;
-  const int strip0 = ntile * (kRowsPerWg / 16) + wave * kStripsPerWave;
+  const int wstrip0 = ntile * (kRowsPerWg / 16) + wave * kStripsPerWave;  // the wave's first strip
   const int tile16_0 = ttile * kTilesPerWg;
   const int tok0 = ttile * kTokPerWg;
+  const uint32_t lds0 = lds_offset(smem);
 
-  // ---- main loop over the weight groups of d ----
-  struct ARegs {
-    u32x4_t w[kStripsPerWave][2];
-    u32x2_t sc[kStripsPerWave];
-  };
-  auto load_a = [&](ARegs& A, int g) {
+  // ---- main loop: a ring of kStages weight groups in LDS ----
+  auto issue = [&](int g, int stage) {
+    const uint32_t sa = lds0 + stage * (uint32_t)kStageBytes;
+    const uint32_t sb = sa + (uint32_t)kStageA;
+    const uint32_t ss = sb + (uint32_t)kStageB;
 #pragma unroll
-    for (int s = 0; s < kStripsPerWave; ++s) {
-      const size_t atom = (size_t)(strip0 + s) * G + g;
-      const uint8_t* p = a.codes + atom * 2048 + lane * 32;
-      A.w[s][0] = load16_stream(p);
-      A.w[s][1] = load16_stream(p + 16);
-      A.sc[s] = *reinterpret_cast<const u32x2_t*>(a.scales + atom * 16 + 4 * j);
+    for (int i = 0; i < 8; ++i) {  // the wave's 4 strips x 2 halves
+      const int s = i >> 1, h = i & 1;
+      const uint8_t* src = a.codes + ((size_t)(wstrip0 + s) * G + g) * 2048 + lane * 32 + h * 16;
+      lds_dma16(src, sa + (uint32_t)(((wave * kStripsPerWave + s) * 2 + h) * 1024));
     }
-  };
-  u32x4_t bst[kTilesPerWg / 2];
-  auto load_b = [&](int g) {
 #pragma unroll
-    for (int i = 0; i < kTilesPerWg / 2; ++i) {
-      const int v = tid + 256 * i, tt = v >> 7;
-      bst[i] = load16(a.x8 + ((size_t)(tile16_0 + tt) * G + g) * 2048 + (v & 127) * 16);
+    for (int i = 0; i < kDmaB; ++i) {  // a quarter of the tokens' tiles x 2 halves
+      const int p = wave * kDmaB + i, tt = p >> 1, h = p & 1;
+      const uint8_t* src = a.x8 + ((size_t)(tile16_0 + tt) * G + g) * 2048 + h * 1024 + lane * 16;
+      lds_dma16(src, sb + (uint32_t)(p * 1024));
     }
-  };
-  auto store_b = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < kTilesPerWg / 2; ++i) {
-      const int v = tid + 256 * i;
-      *reinterpret_cast<u32x4_t*>(bbuf + (size_t)buf * kTilesPerWg * 2048 + v * 16) = bst[i];
+    {  // the wave's 4 strips' scales: 8 lanes x 16 B
+      const int l8 = lane & 7;
+      const uint16_t* src = a.scales + ((size_t)(wstrip0 + (l8 >> 1)) * G + g) * 16 + (l8 & 1) * 8;
+      if (lane < 8) lds_dma16(src, ss + (uint32_t)(wave * 128));
     }
   };
 
@@ -281,93 +323,99 @@ __global__ __launch_bounds__(256) void prefill_gemm_kernel(PrefillArgs a) {
 #pragma unroll
     for (int t = 0; t < kTilesPerWg; ++t) acc[s][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const ARegs& A, int buf) {
-    float scl[kStripsPerWave][4];
+  auto compute = [&](int stage) {
+    const unsigned char* sa = smem + (size_t)stage * kStageBytes;
+    const unsigned char* sb = sa + kStageA;
+    const unsigned char* ss = sb + kStageB;
     i32x8_t av[kStripsPerWave];
+    u32x2_t sc[kStripsPerWave];
 #pragma unroll
     for (int s = 0; s < kStripsPerWave; ++s) {
-      av[s] = cat8(A.w[s][0], A.w[s][1]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) scl[s][i] = f16_bits_to_f32((uint16_t)(A.sc[s][i >> 1] >> (16 * (i & 1))));
+      const unsigned char* pa = sa + ((wave * kStripsPerWave + s) * 2) * 1024 + lane * 16;
+      av[s] = cat8(*reinterpret_cast<const u32x4_t*>(pa), *reinterpret_cast<const u32x4_t*>(pa + 1024));
+      sc[s] = *reinterpret_cast<const u32x2_t*>(ss + wave * 128 + s * 32 + j * 8);
     }
-    const unsigned char* bb = bbuf + (size_t)buf * kTilesPerWg * 2048;
-    // the products of tile t are issued before the scaled adds of tile t - 1,
-    // so that the MFMA latency is covered by independent work
-    f32x4_t prev[kStripsPerWave];
 #pragma unroll
-    for (int t = 0; t <= kTilesPerWg; ++t) {
-      f32x4_t cur[kStripsPerWave];
-      if (t < kTilesPerWg) {
-        const u32x4_t h0 = *reinterpret_cast<const u32x4_t*>(bb + t * 2048 + lane * 16);
-        const u32x4_t h1 = *reinterpret_cast<const u32x4_t*>(bb + t * 2048 + 1024 + lane * 16);
-        const i32x8_t bv = cat8(h0, h1);
+    for (int t = 0; t < kTilesPerWg; ++t) {
+      const unsigned char* pb = sb + (t * 2) * 1024 + lane * 16;
+      const i32x8_t bv = cat8(*reinterpret_cast<const u32x4_t*>(pb), *reinterpret_cast<const u32x4_t*>(pb + 1024));
+      f32x4_t pr[kStripsPerWave];
 #pragma unroll
-        for (int s = 0; s < kStripsPerWave; ++s)
-          cur[s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av[s], bv, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0,
-                                                                    0, 127, 0, 127);
-      }
-      if (t > 0) {
+      for (int s = 0; s < kStripsPerWave; ++s)
+        pr[s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av[s], bv, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0,
+                                                                 127, 0, 127);
 #pragma unroll
-        for (int s = 0; s < kStripsPerWave; ++s)
+      for (int s = 0; s < kStripsPerWave; ++s)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[s][t - 1][i] = fmaf(scl[s][i], prev[s][i], acc[s][t - 1][i]);
-      }
-      if (t < kTilesPerWg) {
-#pragma unroll
-        for (int s = 0; s < kStripsPerWave; ++s) prev[s] = cur[s];
-      }
+        for (int i = 0; i < 4; ++i) {
+          const float scl = f16_bits_to_f32((uint16_t)(sc[s][i >> 1] >> (16 * (i & 1))));
+          acc[s][t][i] = fmaf(scl, pr[s][i], acc[s][t][i]);
+        }
     }
   };
 
-  ARegs A0, A1;
-  load_a(A0, 0);
-  load_b(0);
-  store_b(0);
-  __syncthreads();
-  for (int g = 0; g < G; g += 2) {
-    if (g + 1 < G) {
-      load_a(A1, g + 1);
-      load_b(g + 1);
-    }
-    compute(A0, 0);
-    if (g + 1 < G) store_b(1);
-    __syncthreads();
-    if (g + 1 >= G) break;
-    if (g + 2 < G) {
-      load_a(A0, g + 2);
-      load_b(g + 2);
-    }
-    compute(A1, 1);
-    if (g + 2 < G) store_b(0);
-    __syncthreads();
-  }
+  // prologue: groups 0 and 1 in flight
+  issue(0, 0);
+  if (G > 1) issue(1, 1);
 
-  // ---- epilogue ----
-  const float sx = checked_scale(a.sc->x_scale, nullptr, false);
-  const float sq = checked_scale(a.sc->q_scale, a.kv.err_word, blockIdx.x == 0 && tid == 0);
+  // token info for the epilogue, read while the first groups load
+  TokInfo* tinfo = reinterpret_cast<TokInfo*>(smem + kShared);
   if (tid < kTokPerWg) {
     const int t = tok0 + tid;
-    float s = 0.f;
-    for (int c = 0; c < a.nch; ++c) s += a.sumsq[(size_t)c * a.T128 + t];
+    float ssum = 0.f;
+    for (int c = 0; c < a.nch; ++c) ssum += a.sumsq[(size_t)c * a.T128 + t];
     TokInfo ti;
-    ti.rho = 1.0f / sqrtf(s / (float)a.K + a.eps);
+    ti.rho = 1.0f / sqrtf(ssum / (float)a.K + a.eps);
     const int2 m = a.map[t];
     ti.row = m.x;
     ti.pos = t < a.T ? m.y : -1;
     ti.lo = 0;
     ti.hi = 0;
+    ti.cap = 0;
+    ti.base = 0;
     if (ti.pos >= 0) {
       ti.lo = max(a.cu[m.x], tok0) - tok0;
       ti.hi = min(min(a.cu[m.x + 1], a.T), tok0 + kTokPerWg) - tok0;
+      const int64_t rb = a.kv.row_base[m.x];
+      ti.cap = (int)(a.kv.row_base[m.x + 1] - rb);
+      ti.base = rb * a.kv.n_kv;
     }
     tinfo[tid] = ti;
   }
-  __syncthreads();
 
+  for (int g = 0; g < G; ++g) {
+    const int stage = g % kStages;
+    // group g landed (group g + 1 may still be in flight), for every wave
+    if (g + 1 < G) wait_vm<kDmaPerStage>(); else wait_vm<0>();
+    lds_barrier();
+    // the stage of group g - 1 is free again: group g + 2 goes there
+    if (g + 2 < G) issue(g + 2, (g + 2) % kStages);
+    compute(stage);
+  }
+  lds_barrier();  // every wave is done with the ring; the epilogue reuses it
+
+  // ---- epilogue ----
+  float* ybuf = reinterpret_cast<float*>(smem);
+  float2* rope_s = reinterpret_cast<float2*>(smem + kYBytes);
+  uint8_t* vcodes = smem + kYBytes + kRopeBytes;
   const int head0 = ntile * 2;  // first of the workgroup's two heads (q | k | v order)
+  const bool has_rope = head0 < a.n_q + a.n_kv;
+  if (has_rope) {
+    // the tile's RoPE rotations from the prep's table, 512 B per token row
+    // (32 lanes), in flight while the first chunk is staged
+    const uint32_t rb = lds_offset(rope_s);
+    for (int tl = wave; tl < kTokPerWg; tl += 4) {
+      const float2* src = a.rope + (size_t)(tok0 + tl) * 64 + 2 * (lane & 31);
+      if (lane < 32) lds_dma16(src, rb + (uint32_t)(tl * kRopePitch * 8));
+    }
+  }
+  const float sx = checked_scale(a.sc->x_scale, nullptr, false);
+  const float sq = checked_scale(a.sc->q_scale, a.kv.err_word, blockIdx.x == 0 && tid == 0);
+  const float rsq = __fdiv_rn(1.0f, sq);
   float qmax = 0.f;
   const int hl_w = wave >> 1;  // head of this wave's rows
   const int sp0 = 4 * (wave & 1);
+  const int l16 = tid & 15;
 #pragma unroll
   for (int c = 0; c < kTilesPerWg / 2; ++c) {
     // fp32 tile [head][token][channel] of tokens 32c .. 32c + 31 (the loop is
@@ -385,9 +433,9 @@ __global__ __launch_bounds__(256) void prefill_gemm_kernel(PrefillArgs a) {
         *reinterpret_cast<f32x4_t*>(&ybuf[((size_t)hl_w * kChunkTok + tl) * kYPitch + ch0]) = v;
       }
     }
+    if (c == 0) wait_vm<0>();  // the RoPE rows (every wave's own DMAs)
     __syncthreads();
     // one (head, token) vector per 16 lanes, 8 channels per lane
-    const int l16 = tid & 15;
 #pragma unroll 1
     for (int it = 0; it < 4; ++it) {
       const int vec = it * 16 + (tid >> 4);
@@ -397,6 +445,7 @@ __global__ __launch_bounds__(256) void prefill_gemm_kernel(PrefillArgs a) {
       const int head = head0 + hl;
       const bool is_q = head < a.n_q;
       const bool is_k = !is_q && head < a.n_q + a.n_kv;
+      if (t >= a.T) continue;
       const TokInfo ti = tinfo[tloc];
       const float* yr = &ybuf[((size_t)hl * kChunkTok + tl) * kYPitch];
       float y[8];
@@ -412,20 +461,19 @@ __global__ __launch_bounds__(256) void prefill_gemm_kernel(PrefillArgs a) {
         const f32x4_t p0 = *reinterpret_cast<const f32x4_t*>(yr + part);
         const f32x4_t p1 = *reinterpret_cast<const f32x4_t*>(yr + part + 4);
         const float o[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-        const float2* rp = a.rope + (size_t)t * 64 + (8 * l16 & 63);
+        const float2* rp = rope_s + tloc * kRopePitch + (8 * l16 & 63);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float2 cs = rp[e];
           y[e] = (l16 < 8) ? y[e] * cs.x - o[e] * cs.y : y[e] * cs.x + o[e] * cs.y;
         }
       }
-      if (t >= a.T) continue;
       if (is_q) {
         uint32_t w0 = 0, w1 = 0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           qmax = fmaxf(qmax, fabsf(y[e]));
-          const uint32_t code = e4m3_code(__fdiv_rn(y[e], sq));
+          const uint32_t code = e4m3_code(y[e] * rsq);
           if (e < 4) w0 |= code << (8 * e); else w1 |= code << (8 * (e - 4));
         }
         *reinterpret_cast<u32x2_t*>(a.q8 + ((size_t)t * a.n_q + head) * kHd + 8 * l16) = u32x2_t{w0, w1};
@@ -433,8 +481,7 @@ __global__ __launch_bounds__(256) void prefill_gemm_kernel(PrefillArgs a) {
       }
       // keys and values: bf16, Hadamard rotation, INT4 with one fp16 scale
       const int kvh = head - a.n_q - (is_k ? 0 : a.n_kv);
-      const int64_t cap = (ti.pos >= 0) ? a.kv.row_base[ti.row + 1] - a.kv.row_base[ti.row] : 0;
-      const int64_t slot = (ti.pos >= 0) ? a.kv.row_base[ti.row] * a.kv.n_kv + (int64_t)kvh * cap + ti.pos : 0;
+      const int64_t slot = ti.base + (int64_t)kvh * ti.cap + ti.pos;
       uint16_t bf[8];
       float x[8];
 #pragma unroll
@@ -461,8 +508,8 @@ __global__ __launch_bounds__(256) void prefill_gemm_kernel(PrefillArgs a) {
       for (int m = 1; m < 16; m <<= 1)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float p = lane_xor(x[e], m, lane);
-          x[e] = (l16 & m) ? (p - x[e]) : (x[e] + p);
+          const float pv = lane_xor(x[e], m, lane);
+          x[e] = (l16 & m) ? (pv - x[e]) : (x[e] + pv);
         }
       float am = 0.f;
 #pragma unroll
@@ -474,10 +521,10 @@ __global__ __launch_bounds__(256) void prefill_gemm_kernel(PrefillArgs a) {
       uint16_t s16 = bitcast<uint16_t>(h16);
       if ((s16 & 0x7fffu) == 0x7c00u) s16 = (uint16_t)((s16 & 0x8000u) | 0x7bffu);
       const float sf = f16_bits_to_f32(s16);
+      const float rsf = (sf != 0.f) ? __fdiv_rn(1.0f, sf) : 0.f;
       uint32_t u[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        u[e] = (sf != 0.f) ? (uint32_t)((int)fminf(7.f, fmaxf(-8.f, rintf(__fdiv_rn(x[e], sf)))) + 8) : 8u;
+      for (int e = 0; e < 8; ++e) u[e] = (sf != 0.f) ? int4_code(x[e], sf, rsf) : 8u;
       if (ti.pos < 0) continue;
       if (is_k) {
         // key slot dword jj * 4 + kb holds channels 32 kb + 8 jj + e: this lane's 8
@@ -502,41 +549,42 @@ __global__ __launch_bounds__(256) void prefill_gemm_kernel(PrefillArgs a) {
   }
 
   // value blocks: a dword holds channel c of tokens w = 4jj + e and 16 + 4jj + e
-  // (e = 0..3) of one 32-token block
-#pragma unroll 1
-  for (int hl = 0; hl < 2; ++hl) {
+  // (e = 0..3) of one 32-token block.  Thread: head tid / 128, channel
+  // tid % 128; the token loop is uniform across the wave.
+  {
+    const int hl = tid >> 7, ch = tid & 127;
     const int head = head0 + hl;
-    if (head < a.n_q + a.n_kv) continue;
-    const int kvh = head - a.n_q - a.n_kv;
-    for (int it = tid; it < kTokPerWg * kHd; it += 256) {
-      const int tloc = it / kHd, ch = it % kHd;
-      const TokInfo ti = tinfo[tloc];
-      if (ti.pos < 0) continue;
-      const int w = ti.pos & 31;
-      const int jj = (w & 15) >> 2;
-      const int e = (w & 3) + (w >= 16 ? 4 : 0);
-      const int off = (w & 3) + (w >= 16 ? 16 : 0);  // distance from the dword's first token
-      const int lead = tloc - off;
-      const bool whole = lead >= ti.lo && lead + 19 < ti.hi;
-      const int64_t cap = a.kv.row_base[ti.row + 1] - a.kv.row_base[ti.row];
-      const int64_t region = a.kv.row_base[ti.row] * a.kv.n_kv + (int64_t)kvh * cap;
-      uint32_t* dw = a.kv.v_codes + (size_t)(region / 32 + ti.pos / 32) * 4 * kHd + jj * kHd + (ch % 16) * (kHd / 16) +
-                     ch / 16;
-      if (whole) {
-        if (off != 0) continue;
-        uint32_t word = 0;
+    if (head >= a.n_q + a.n_kv) {
+      const int kvh = head - a.n_q - a.n_kv;
+      const int dw_in = (ch % 16) * (kHd / 16) + ch / 16;
+#pragma unroll 1
+      for (int tloc = 0; tloc < kTokPerWg; ++tloc) {
+        const TokInfo ti = tinfo[tloc];
+        if (ti.pos < 0) continue;
+        const int w = ti.pos & 31;
+        const int jj = (w & 15) >> 2;
+        const int e = (w & 3) + (w >= 16 ? 4 : 0);
+        const int off = (w & 3) + (w >= 16 ? 16 : 0);  // distance from the dword's first token
+        const int lead = tloc - off;
+        const bool whole = lead >= ti.lo && lead + 19 < ti.hi;
+        if (whole && off != 0) continue;
+        const int64_t region = ti.base + (int64_t)kvh * ti.cap;
+        uint32_t* dw = a.kv.v_codes + (size_t)(region / 32 + ti.pos / 32) * 4 * kHd + jj * kHd + dw_in;
+        if (whole) {
+          uint32_t word = 0;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const int o = (q < 4) ? q : 12 + q;
-          const uint32_t code = vcodes[((size_t)(tloc + o) * 2 + hl) * kHd + ch];
-          word |= code << (4 * (4 * (q & 1) + (q >> 1)));
+          for (int q = 0; q < 8; ++q) {
+            const int o = (q < 4) ? q : 12 + q;
+            const uint32_t code = vcodes[((size_t)(tloc + o) * 2 + hl) * kHd + ch];
+            word |= code << (4 * (4 * (q & 1) + (q >> 1)));
+          }
+          *dw = word;
+        } else {
+          const int sh = 4 * (4 * (e & 1) + (e >> 1));
+          const uint32_t code = vcodes[((size_t)tloc * 2 + hl) * kHd + ch];
+          atomicAnd(dw, ~(0xFu << sh));
+          atomicOr(dw, code << sh);
         }
-        *dw = word;
-      } else {
-        const int sh = 4 * (4 * (e & 1) + (e >> 1));
-        const uint32_t code = vcodes[((size_t)tloc * 2 + hl) * kHd + ch];
-        atomicAnd(dw, ~(0xFu << sh));
-        atomicOr(dw, code << sh);
       }
     }
   }
@@ -603,11 +651,14 @@ extern "C" i4d_status i4d_prefill_workspace_bytes(const i4d_layer_shape* shape, 
   return ok();
 }
 
-extern "C" i4d_status i4d_prefill_qkv_e4m3(const i4d_layer* layer, const i4d_kv_cache* cache, const uint16_t* x,
-                                           int T, const int32_t* cu_seqlens, const int32_t* start_pos, int R,
-                                           i4d_fp8_scales* scales, uint8_t* q_fp8, uint16_t* k_bf16,
-                                           uint16_t* v_bf16, void* workspace, size_t workspace_bytes,
-                                           void* stream) {
+namespace i4d {
+namespace {
+
+// host checks shared by the three entry points; fills `a` (workspace
+// pointers included) and the workspace layout
+i4d_status prefill_args(const i4d_layer* layer, const i4d_kv_cache* cache, const uint16_t* x, int T,
+                        const int32_t* cu_seqlens, const int32_t* start_pos, int R, i4d_fp8_scales* scales,
+                        void* workspace, size_t workspace_bytes, bool need_x, PrefillArgs* a, PrefillWs* w) {
   if (!layer) return fail(I4D_ERR_NULL, "layer is NULL");
   const i4d_layer_shape& s = layer->shape;
   i4d_status st = check_prefill_shape(&s);
@@ -619,53 +670,108 @@ extern "C" i4d_status i4d_prefill_qkv_e4m3(const i4d_layer* layer, const i4d_kv_
   if ((st = check_cache(cache, &s, R)) != I4D_OK) return st;
   if (!cu_seqlens || !start_pos) return fail(I4D_ERR_NULL, "cu_seqlens / start_pos is NULL");
   if (!scales) return fail(I4D_ERR_NULL, "scales is NULL");
-  if (T == 0) return ok();
-  if ((st = need(x, "x")) != I4D_OK) return st;
-  if ((st = need(q_fp8, "q_fp8")) != I4D_OK) return st;
+  if (need_x && T > 0 && (st = need(x, "x")) != I4D_OK) return st;
+  *w = prefill_ws(s, T);
+  if (T > 0) {
+    if ((st = need(workspace, "workspace")) != I4D_OK) return st;
+    if (workspace_bytes < w->total)
+      return fail(I4D_ERR_WORKSPACE, "prefill workspace %zu bytes < %zu", workspace_bytes, w->total);
+  }
+  *a = PrefillArgs{};
+  a->codes = (const uint8_t*)layer->qkv_codes;
+  a->scales = layer->qkv_scales;
+  a->N = (s.n_q_heads + 2 * s.n_kv_heads) * kHd;
+  a->K = s.d_model;
+  a->G = groups_of(s.d_model);
+  a->n_q = s.n_q_heads;
+  a->n_kv = s.n_kv_heads;
+  a->eps = s.rms_eps;
+  a->rope_ratio = pow((double)s.rope_theta, -2.0 / (double)s.head_dim);
+  a->x = x;
+  a->T = T;
+  a->T128 = w->T128;
+  a->R = R;
+  a->nch = w->nch;
+  a->cu = cu_seqlens;
+  a->start = start_pos;
+  a->sc = scales;
+  a->kv = kv_args(cache);
+  char* ws = (char*)workspace;
+  a->x8 = (uint8_t*)(ws + w->x8);
+  a->sumsq = (float*)(ws + w->sumsq);
+  a->map = (int2*)(ws + w->map);
+  a->rope = (float2*)(ws + w->rope);
+  return ok();
+}
+
+i4d_status launch_prep(const PrefillArgs& a, const PrefillWs& w, hipStream_t hs) {
+  hipLaunchKernelGGL(prefill_prep_kernel, dim3(w.T128 / 16, w.nch), dim3(256), 0, hs, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(I4D_ERR_HIP, "prefill prep launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+i4d_status launch_gemm(PrefillArgs a, const PrefillWs& w, uint8_t* q_fp8, uint16_t* k_bf16, uint16_t* v_bf16,
+                       hipStream_t hs) {
+  i4d_status st = need(q_fp8, "q_fp8");
+  if (st != I4D_OK) return st;
   if (k_bf16 && !aligned16(k_bf16)) return fail(I4D_ERR_ALIGN, "k_bf16 is not 16-byte aligned");
   if (v_bf16 && !aligned16(v_bf16)) return fail(I4D_ERR_ALIGN, "v_bf16 is not 16-byte aligned");
-  if ((st = need(workspace, "workspace")) != I4D_OK) return st;
-  const PrefillWs w = prefill_ws(s, T);
-  if (workspace_bytes < w.total)
-    return fail(I4D_ERR_WORKSPACE, "prefill workspace %zu bytes < %zu", workspace_bytes, w.total);
-
-  PrefillArgs a = {};
-  a.codes = (const uint8_t*)layer->qkv_codes;
-  a.scales = layer->qkv_scales;
-  a.N = (s.n_q_heads + 2 * s.n_kv_heads) * kHd;
-  a.K = s.d_model;
-  a.G = groups_of(s.d_model);
-  a.n_q = s.n_q_heads;
-  a.n_kv = s.n_kv_heads;
-  a.eps = s.rms_eps;
-  a.rope_ratio = pow((double)s.rope_theta, -2.0 / (double)s.head_dim);
-  a.x = x;
-  a.T = T;
-  a.T128 = w.T128;
-  a.R = R;
-  a.nch = w.nch;
-  a.cu = cu_seqlens;
-  a.start = start_pos;
-  a.sc = scales;
   a.q8 = q_fp8;
   a.k_bf16 = k_bf16;
   a.v_bf16 = v_bf16;
-  a.kv = kv_args(cache);
-  char* ws = (char*)workspace;
-  a.x8 = (uint8_t*)(ws + w.x8);
-  a.sumsq = (float*)(ws + w.sumsq);
-  a.map = (int2*)(ws + w.map);
-  a.rope = (float2*)(ws + w.rope);
-
-  hipStream_t hs = (hipStream_t)stream;
-  hipLaunchKernelGGL(prefill_prep_kernel, dim3(w.T128 / 16, w.nch), dim3(256), 0, hs, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(I4D_ERR_HIP, "prefill prep launch: %s", hipGetErrorString(e));
   const int grid = (a.N / kRowsPerWg) * (w.T128 / kTokPerWg);
   hipLaunchKernelGGL(prefill_gemm_kernel, dim3(grid), dim3(256), kGemmLds, hs, a);
-  e = hipGetLastError();
+  const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(I4D_ERR_HIP, "prefill gemm launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+}  // namespace i4d
+
+extern "C" i4d_status i4d_prefill_prepare(const i4d_layer* layer, const i4d_kv_cache* cache, const uint16_t* x, int T,
+                                          const int32_t* cu_seqlens, const int32_t* start_pos, int R,
+                                          i4d_fp8_scales* scales, void* workspace, size_t workspace_bytes,
+                                          void* stream) {
+  PrefillArgs a;
+  PrefillWs w;
+  i4d_status st = prefill_args(layer, cache, x, T, cu_seqlens, start_pos, R, scales, workspace, workspace_bytes,
+                               true, &a, &w);
+  if (st != I4D_OK || T == 0) return st;
+  return launch_prep(a, w, (hipStream_t)stream);
+}
+
+extern "C" i4d_status i4d_prefill_project(const i4d_layer* layer, const i4d_kv_cache* cache, int T,
+                                          const int32_t* cu_seqlens, const int32_t* start_pos, int R,
+                                          i4d_fp8_scales* scales, uint8_t* q_fp8, uint16_t* k_bf16,
+                                          uint16_t* v_bf16, const void* workspace, size_t workspace_bytes,
+                                          void* stream) {
+  PrefillArgs a;
+  PrefillWs w;
+  i4d_status st = prefill_args(layer, cache, nullptr, T, cu_seqlens, start_pos, R, scales, (void*)workspace,
+                               workspace_bytes, false, &a, &w);
+  if (st != I4D_OK || T == 0) return st;
+  return launch_gemm(a, w, q_fp8, k_bf16, v_bf16, (hipStream_t)stream);
+}
+
+extern "C" i4d_status i4d_prefill_qkv_e4m3(const i4d_layer* layer, const i4d_kv_cache* cache, const uint16_t* x,
+                                           int T, const int32_t* cu_seqlens, const int32_t* start_pos, int R,
+                                           i4d_fp8_scales* scales, uint8_t* q_fp8, uint16_t* k_bf16,
+                                           uint16_t* v_bf16, void* workspace, size_t workspace_bytes,
+                                           void* stream) {
+  PrefillArgs a;
+  PrefillWs w;
+  i4d_status st = prefill_args(layer, cache, x, T, cu_seqlens, start_pos, R, scales, workspace, workspace_bytes,
+                               true, &a, &w);
+  if (st != I4D_OK || T == 0) return st;
+  // the output pointers are checked before anything is enqueued
+  if ((st = need(q_fp8, "q_fp8")) != I4D_OK) return st;
+  if (k_bf16 && !aligned16(k_bf16)) return fail(I4D_ERR_ALIGN, "k_bf16 is not 16-byte aligned");
+  if (v_bf16 && !aligned16(v_bf16)) return fail(I4D_ERR_ALIGN, "v_bf16 is not 16-byte aligned");
+  hipStream_t hs = (hipStream_t)stream;
+  if ((st = launch_prep(a, w, hs)) != I4D_OK) return st;
+  return launch_gemm(a, w, q_fp8, k_bf16, v_bf16, hs);
 }
 
 extern "C" i4d_status i4d_fp8_scales_update(i4d_fp8_scales* scales, void* stream) {

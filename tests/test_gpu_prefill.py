@@ -319,3 +319,28 @@ def test_decode_step_reads_the_prefilled_cache(gpu):
     e_att = norm_maxabs(attn.cpu().numpy(), ref.attn)
     say(f"  decode after prefill: out rel-RMS {e_out:.2e}  attn {e_att:.2e}")
     assert e_out <= 1e-2 and e_att <= 2e-2
+
+
+def test_prepare_then_project_equals_the_fused_call(gpu):
+    """The two-call form gives the fused call's results bit for bit, and a
+    repeated projection over the same workspace changes nothing."""
+    torch, B, D = gpu
+    seqlens, starts = [70, 129, 1], [3, 40, 0]
+    run = run_prefill(gpu, SMALL, 37, seqlens, starts)
+    cache2 = D.DeviceCache(SMALL, run.caps)
+    scales2 = torch.tensor([run.sx, run.sq, 0.0, 0.0], dtype=torch.float32, device="cuda")
+    ws2 = torch.zeros_like(run.ws)
+    q2 = torch.zeros_like(run.q8)
+    kd2, vd2 = torch.zeros_like(run.kd), torch.zeros_like(run.vd)
+    cu = torch.from_numpy(run.cu).cuda()
+    st = torch.tensor(starts, dtype=torch.int32, device="cuda")
+    B.i4d_prefill_prepare(run.layer.struct, cache2.struct, D.to_device_u16(run.xb), run.T, cu, st, run.R, scales2,
+                          ws2, ws2.numel())
+    for _ in range(2):
+        B.i4d_prefill_project(run.layer.struct, cache2.struct, run.T, cu, st, run.R, scales2, q2, kd2, vd2, ws2,
+                              ws2.numel())
+    torch.cuda.synchronize()
+    for a, b in ((run.q8, q2), (run.kd, kd2), (run.vd, vd2), (run.scales, scales2), (run.ws, ws2),
+                 (run.cache.k_codes, cache2.k_codes), (run.cache.v_codes, cache2.v_codes),
+                 (run.cache.k_scales, cache2.k_scales), (run.cache.v_scales, cache2.v_scales)):
+        assert torch.equal(a, b)
