@@ -41,10 +41,15 @@ FP8_PEAK_TFLOPS = 5000.0  # dense fp8 MFMA, MI355X
 # reports null.
 STEP_M1_SOURCES = ("step.hip", "step.h", "gemv.h", "attn_core.h", "attn.h", "coherent.h", "device_common.h",
                    "proj.h", "i4d_internal.h", "i4d_layout.h", "api_device.hip", "api_host.cpp")
+PREFILL_SOURCES = ("prefill.hip", "gemv.h", "attn.h", "coherent.h", "device_common.h", "proj.h", "i4d_internal.h",
+                   "i4d_layout.h", "../build.py")
 TRAFFIC = {
     "8b_m1_ctx4096": {"kernel": "step_m1_kernel (one-launch decode step)", "sources": STEP_M1_SOURCES,
-                      "sha256": "2c788a405efba1c9920cd4f92b7ebb040041773626a6aa1504c856102805acf8",
-                      "fetch_bytes": 118782464, "write_bytes": 751104},
+                      "sha256": "dd736fd30ba2815ed0a2343aa8f313573a3de8027da8205a94c62c4b5e5c4b0b",
+                      "fetch_bytes": 118803584, "write_bytes": 751104},
+    "8b_prefill_s2048": {"kernel": "prefill_gemm_kernel (FP8 MFMA GEMM + epilogue)", "sources": PREFILL_SOURCES,
+                         "sha256": "b0b167718cd5dcdf7d5d55047d58fc80b683b625177d3f810e651e5e220e2d0a",
+                         "fetch_bytes": 223922176, "write_bytes": 10584064},
 }
 
 
