@@ -128,8 +128,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build runs on one GPU only; --gpus must be 1 (the multi-GPU layout is "
-              "described in DESIGN.md, not built)", file=sys.stderr)
+        print("bench.py: the library runs on one GPU; --gpus must be 1 (tensor- and sequence-parallel "
+              "sharding of the step is not implemented)", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -50,7 +50,7 @@ typedef enum {
   I4D_OK = 0,
   I4D_ERR_NULL = -1,        /* a required pointer is NULL */
   I4D_ERR_SHAPE = -2,       /* inconsistent or unsupported dimensions */
-  I4D_ERR_UNSUPPORTED = -3, /* valid request this build does not implement */
+  I4D_ERR_UNSUPPORTED = -3, /* valid request the library does not implement */
   I4D_ERR_ALIGN = -4,       /* device pointer not 16-byte aligned */
   I4D_ERR_WORKSPACE = -5,   /* workspace smaller than i4d_workspace_bytes() */
   I4D_ERR_RANGE = -6,       /* scalar argument out of range */
@@ -188,8 +188,8 @@ i4d_status i4d_pack_lm_head(const float* W, const float* gamma, int V, int d,
  *   e = row_base[r] * n_kv_heads + j * cap_r + t
  * (the direct placement offset(request, head, position, channel) of "how it
  * works").  Per slot the cache stores head_dim INT4 codes of H k (resp. H v)
- * and one fp16 scale; see the DESIGN notes in the source for the nibble
- * order inside a slot (keys) and a 32-token block (values).
+ * and one fp16 scale; csrc/i4d_layout.h gives the nibble order inside a
+ * slot (keys) and a 32-token block (values).
  *   k_codes, v_codes : device, total_capacity * n_kv_heads * head_dim / 2 bytes
  *   k_scales, v_scales : device, total_capacity * n_kv_heads fp16
  *   row_base : device int64 [n_rows + 1], row_base[0] = 0, multiples of 32
