@@ -434,7 +434,8 @@ __global__ __launch_bounds__(256) void prefill_gemm_kernel(PrefillArgs a) {
       }
     }
     if (c == 0) wait_vm<0>();  // the RoPE rows (every wave's own DMAs)
-    __syncthreads();
+    // LDS-only barriers: the chunk's global stores need not complete here
+    lds_barrier();
     // one (head, token) vector per 16 lanes, 8 channels per lane
 #pragma unroll 1
     for (int it = 0; it < 4; ++it) {
@@ -545,46 +546,81 @@ __global__ __launch_bounds__(256) void prefill_gemm_kernel(PrefillArgs a) {
         if (l16 == 0) a.kv.v_scales[slot] = s16;
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
 
-  // value blocks: a dword holds channel c of tokens w = 4jj + e and 16 + 4jj + e
-  // (e = 0..3) of one 32-token block.  Thread: head tid / 128, channel
-  // tid % 128; the token loop is uniform across the wave.
-  {
-    const int hl = tid >> 7, ch = tid & 127;
-    const int head = head0 + hl;
-    if (head >= a.n_q + a.n_kv) {
-      const int kvh = head - a.n_q - a.n_kv;
-      const int dw_in = (ch % 16) * (kHd / 16) + ch / 16;
-#pragma unroll 1
-      for (int tloc = 0; tloc < kTokPerWg; ++tloc) {
+  // Value blocks: a dword holds one channel of the 8 tokens w = 4jj + e and
+  // 16 + 4jj + e (e = 0..3) of a 32-token block.  Wave 0 lists one
+  // representative token per such group present in the tile (the group's
+  // first token here) with the mask of its members present in the tile and
+  // request; then every thread builds dwords of (representative, channel)
+  // items independently: stored whole when all 8 members are present, else
+  // merged nibble-wise with an atomic and/or.
+  const int nvh = (head0 + 1 >= a.n_q + a.n_kv) ? ((head0 >= a.n_q + a.n_kv) ? 2 : 1) : 0;  // v heads in the tile
+  int* rep_list = reinterpret_cast<int*>(ybuf);  // [kTokPerWg] (tloc | mask << 8), then the count
+  if (nvh > 0) {
+    if (wave == 0) {
+      int base = 0;
+#pragma unroll
+      for (int half = 0; half < kTokPerWg / 64; ++half) {
+        const int tloc = half * 64 + lane;
         const TokInfo ti = tinfo[tloc];
-        if (ti.pos < 0) continue;
-        const int w = ti.pos & 31;
-        const int jj = (w & 15) >> 2;
-        const int e = (w & 3) + (w >= 16 ? 4 : 0);
-        const int off = (w & 3) + (w >= 16 ? 16 : 0);  // distance from the dword's first token
-        const int lead = tloc - off;
-        const bool whole = lead >= ti.lo && lead + 19 < ti.hi;
-        if (whole && off != 0) continue;
-        const int64_t region = ti.base + (int64_t)kvh * ti.cap;
-        uint32_t* dw = a.kv.v_codes + (size_t)(region / 32 + ti.pos / 32) * 4 * kHd + jj * kHd + dw_in;
-        if (whole) {
-          uint32_t word = 0;
+        int entry = -1;
+        if (ti.pos >= 0) {
+          const int w = ti.pos & 31;
+          const int off = (w & 3) + (w >= 16 ? 16 : 0);  // distance from the group's first position
+          const int t0 = tloc - off;
+          int mask = 0, first = -1;
 #pragma unroll
           for (int q = 0; q < 8; ++q) {
             const int o = (q < 4) ? q : 12 + q;
-            const uint32_t code = vcodes[((size_t)(tloc + o) * 2 + hl) * kHd + ch];
-            word |= code << (4 * (4 * (q & 1) + (q >> 1)));
+            const bool present = t0 + o >= ti.lo && t0 + o < ti.hi;
+            mask |= present ? (1 << q) : 0;
+            if (present && first < 0) first = o;
           }
-          *dw = word;
-        } else {
-          const int sh = 4 * (4 * (e & 1) + (e >> 1));
-          const uint32_t code = vcodes[((size_t)tloc * 2 + hl) * kHd + ch];
-          atomicAnd(dw, ~(0xFu << sh));
-          atomicOr(dw, code << sh);
+          if (first == off) entry = tloc | (mask << 8);
         }
+        const uint64_t bal = __ballot(entry >= 0);
+        const int idx = base + __popcll(bal & ((1ull << lane) - 1ull));
+        if (entry >= 0) rep_list[idx] = entry;
+        base += __popcll(bal);
+      }
+      if (lane == 0) rep_list[kTokPerWg] = base;
+    }
+    lds_barrier();
+    const int nrep = rep_list[kTokPerWg];
+    const int nitems = nrep * kHd * nvh;
+#pragma unroll 4
+    for (int item = tid; item < nitems; item += 256) {
+      const int ch = item % kHd;
+      const int rh = item / kHd;
+      const int hl = 2 - nvh + rh % nvh;
+      const int entry = rep_list[rh / nvh];
+      const int tloc = entry & 0xFF, mask = entry >> 8;
+      const TokInfo ti = tinfo[tloc];
+      const int w = ti.pos & 31;
+      const int jj = (w & 15) >> 2;
+      const int t0 = tloc - ((w & 3) + (w >= 16 ? 16 : 0));
+      const int kvh = head0 + hl - a.n_q - a.n_kv;
+      const int64_t region = ti.base + (int64_t)kvh * ti.cap;
+      uint32_t* dw = a.kv.v_codes + (size_t)(region / 32 + ti.pos / 32) * 4 * kHd + jj * kHd + (ch % 16) * (kHd / 16) +
+                     ch / 16;
+      uint32_t word = 0, keep = 0;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int o = (q < 4) ? q : 12 + q;
+        const int sh = 4 * (4 * (q & 1) + (q >> 1));
+        if (mask & (1 << q)) {
+          word |= (uint32_t)vcodes[((size_t)(t0 + o) * 2 + hl) * kHd + ch] << sh;
+        } else {
+          keep |= 0xFu << sh;
+        }
+      }
+      if (mask == 0xFF) {
+        *dw = word;
+      } else {
+        atomicAnd(dw, keep);
+        atomicOr(dw, word);
       }
     }
   }
