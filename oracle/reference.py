@@ -86,7 +86,11 @@ R13 FP8 prefill of the QKV projection, the step that fills the cache the
     abstract].  Reading: R requests, request r owns tokens [cu[r], cu[r+1])
     at positions start[r], start[r] + 1, ...; the activations are E4M3 of
     fp32(x / s_x) with one per-tensor scale s_x (R12 encoding); the weights
-    are the R12 E4M3 QKV weights; y = rho_t (sum_k W_hat[n, k] x_hat[t, k])
+    are E4M3 codes of the gain-folded QKV weight with one power-of-two scale
+    per (row, 128-group) (the pages give no scale form for the prefill
+    weights; a power of two is the E8M0 scale gfx950's FP8 MFMA applies in
+    the instruction, OCP MX style): e = the smallest integer with absmax <=
+    448 2^e, codes = E4M3(fp32(w 2^-e)); y = rho_t (sum_k W_hat[n, k] x_hat[t, k])
     in fp64 with x_hat = s_x E4M3(x8); RoPE (R4) at the token's position;
     q is written as E4M3 of fp32(q / s_q) with its own per-tensor scale; k
     and v are rounded to bf16 (R10) and encoded (R6) at their slot.  The
@@ -256,6 +260,44 @@ def quantize_weight_e4m3(W, gamma=None) -> tuple[np.ndarray, np.ndarray, str]:
         r = g / sf
     codes = e4m3_encode(np.where(sf == 0, np.float32(0.0), r))
     return codes.reshape(N, K), s, "e4m3"
+
+
+def mx_exponent(absmax) -> np.ndarray:
+    """The smallest integer e with absmax <= 448 * 2^e (exact: with
+    absmax = m 2^x, 0.5 <= m < 1, and 448 = 0.875 2^9, e = x - 9 when
+    m <= 0.875, else x - 8), clamped to the E8M0 range [-127, 127]; an
+    all-zero group takes -127.  [R13]"""
+    a = np.asarray(absmax, dtype=np.float64)
+    m, x = np.frexp(a)
+    e = np.where(m <= 0.875, x - 9, x - 8)
+    e = np.where(a == 0, -127, e)
+    return np.clip(e, -127, 127).astype(np.int64)
+
+
+def quantize_weight_e4m3_mx(W, gamma=None) -> tuple[np.ndarray, np.ndarray, str]:
+    """Group-128 E4M3 codes with one power-of-two scale per (row, group), the
+    scale form gfx950's FP8 MFMA applies by itself (an E8M0 byte, exponent
+    + 127, as in the OCP MX formats): gain folded first (R3); e =
+    mx_exponent(absmax); codes = E4M3(fp32(w * 2^-e)) (the scaling is exact,
+    and no code saturates since |w| 2^-e <= 448).  Returns (codes uint8
+    [N, K], E8M0 bytes uint8 [N, K/128], "e4m3mx").  [R13]"""
+    Wp = fold_gain(W, gamma)
+    N, K = Wp.shape
+    if K % GROUP:
+        raise ValueError("K must be a multiple of 128")
+    g = Wp.reshape(N, K // GROUP, GROUP)
+    e = mx_exponent(np.max(np.abs(g), axis=-1))
+    r = np.ldexp(g.astype(np.float64), -e[..., None]).astype(np.float32)
+    codes = e4m3_encode(r)
+    return codes.reshape(N, K), (e + 127).astype(np.uint8), "e4m3mx"
+
+
+def dequantize_weight_e4m3_mx(codes, e8m0) -> np.ndarray:
+    """W_hat[n, k] = 2^(e8m0[n, k // 128] - 127) * E4M3 value of code[n, k]."""
+    c = np.asarray(codes)
+    N, K = c.shape
+    e = np.asarray(e8m0, dtype=np.int64) - 127
+    return np.ldexp(e4m3_decode(c).reshape(N, K // GROUP, GROUP), e[:, :, None]).reshape(N, K)
 
 
 def dequantize_weight_e4m3(codes, s) -> np.ndarray:
@@ -454,6 +496,8 @@ def dense(ql_part) -> np.ndarray:
     (codes, scales, "e4m3")."""
     if len(ql_part) == 3 and ql_part[2] == "e4m3":
         return dequantize_weight_e4m3(ql_part[0], ql_part[1])
+    if len(ql_part) == 3 and ql_part[2] == "e4m3mx":
+        return dequantize_weight_e4m3_mx(ql_part[0], ql_part[1])
     return dequantize_weight(*ql_part)
 
 
@@ -646,9 +690,10 @@ def prefill_qkv(shape, qkv_e4m3, x_bits, cu_seqlens, start_pos, x_scale, q_scale
                 W_dense: Optional[np.ndarray] = None) -> PrefillResult:
     """The FP8 prefill of the QKV projection for packed tokens (R13).
 
-    x_bits: bf16 bits [T, d] of the packed tokens; qkv_e4m3: (codes, scales,
-    "e4m3") of the gain-folded QKV weight (R12), or its fp64 dense form in
-    W_dense.  Steps: token map; rho of each token from its bf16 values; x8 =
+    x_bits: bf16 bits [T, d] of the packed tokens; qkv_e4m3: (codes, E8M0
+    bytes, "e4m3mx") of the gain-folded QKV weight from
+    quantize_weight_e4m3_mx (any encoded form dense() takes), or its fp64
+    dense form in W_dense.  Steps: token map; rho of each token from its bf16 values; x8 =
     E4M3(x / s_x); y = rho (s_x dec(x8)) W_hat^T; RoPE of q and k at the
     token's position; q8 = E4M3(q / s_q); k and v rounded to bf16 and encoded
     for the INT4 cache."""

@@ -23,11 +23,16 @@ from int4_quantized_decode_amd import synth
 SHAPE = synth.SHAPE_SMALL128
 
 
+class _QL:
+    def __init__(self, qkv):
+        self.qkv = qkv
+
+
 @pytest.fixture(scope="module")
 def layer():
     lw = synth.make_layer(SHAPE, 71)
-    ql = O.quantize_layer_e4m3(lw)
-    return ql, O.dense(ql.qkv)
+    qkv = O.quantize_weight_e4m3_mx(lw.w_qkv, lw.gamma_attn)
+    return _QL(qkv), O.dense(qkv)
 
 
 def _exact_x(rng, T, scale_pow):
@@ -36,6 +41,65 @@ def _exact_x(rng, T, scale_pow):
     codes = np.where((codes & 0x7F) == 0x7F, codes ^ 0x01, codes).astype(np.uint8)
     x = O.e4m3_decode(codes) * 2.0 ** scale_pow
     return synth.f32_to_bf16_bits(x.astype(np.float32)), codes
+
+
+# ---------------------------------------------------------------------------
+# the prefill weights: E4M3 codes, one power-of-two scale per (row, group)
+# ---------------------------------------------------------------------------
+
+def test_mx_exponent_closed_forms():
+    # smallest e with absmax <= 448 * 2^e
+    cases = [(448.0, 0), (448.5, 1), (224.0, -1), (224.5, 0), (1.0, -8), (1.75, -8), (1.76, -7), (896.0, 1),
+             (0.0, -127), (3.4e38, 120)]
+    got = O.mx_exponent(np.array([a for a, _ in cases]))
+    np.testing.assert_array_equal(got, [e for _, e in cases])
+    # brute force: the definition over many magnitudes
+    a = np.abs(np.random.default_rng(3).standard_normal(5000)) * np.exp2(np.random.default_rng(4).integers(-40, 40, 5000))
+    a = a.astype(np.float32).astype(np.float64)
+    e = O.mx_exponent(a)
+    assert np.all(a <= 448.0 * np.exp2(e.astype(np.float64)))
+    assert np.all(a > 448.0 * np.exp2(e.astype(np.float64) - 1))
+
+
+def test_mx_quantizer_codes_scales_and_round_trip():
+    rng = np.random.default_rng(8)
+    W = (rng.standard_normal((48, 384)) * 0.02).astype(np.float32)
+    W[3, 128:256] = 0.0
+    W[7, 0:128] *= np.float32(1e3)
+    q, e8, fmt = O.quantize_weight_e4m3_mx(W)
+    assert fmt == "e4m3mx" and q.dtype == np.uint8 and e8.dtype == np.uint8 and e8.shape == (48, 3)
+    assert e8[3, 1] == 0 and np.all(q[3, 128:256] == 0)
+    e = e8.astype(np.int64) - 127
+    # codes: PyTorch's E4M3 conversion of w * 2^-e (exact scaling)
+    r = np.ldexp(W.reshape(48, 3, 128).astype(np.float64), -e[..., None]).astype(np.float32).reshape(48, 384)
+    np.testing.assert_array_equal(q, torch.from_numpy(r).to(torch.float8_e4m3fn).view(torch.uint8).numpy())
+    # no saturation, and the group maximum lands in the top binade [224, 448]
+    dec = np.abs(O.e4m3_decode(q)).reshape(48, 3, 128)
+    live = e8 > 0
+    assert np.all(dec <= 448.0)
+    assert np.all(dec.max(axis=-1)[live] >= 224.0)
+    # dequantized weights re-encode to the same codes under the same
+    # exponents; derived again, an exponent drops by one exactly when the
+    # group's maximum was rounded down to 224 * 2^e
+    W_hat = O.dense((q, e8, fmt))
+    r2 = np.ldexp(W_hat.reshape(48, 3, 128), -e[..., None]).astype(np.float32).reshape(48, 384)
+    np.testing.assert_array_equal(O.e4m3_encode(r2), q)
+    _, e82, _ = O.quantize_weight_e4m3_mx(W_hat.astype(np.float32))
+    dropped = e82.astype(np.int64) != e8.astype(np.int64)
+    np.testing.assert_array_equal(e82[dropped].astype(np.int64), e8[dropped].astype(np.int64) - 1)
+    np.testing.assert_array_equal(dropped & live, (dec.max(axis=-1) == 224.0) & live)
+    # half a step of error per element
+    err = np.abs(W_hat - W.astype(np.float64)).reshape(48, 3, 128)
+    bound = np.maximum(np.abs(W.astype(np.float64)).reshape(48, 3, 128) * 2.0 ** -4, 2.0 ** -10 * np.exp2(e)[..., None])
+    assert np.all(err <= bound + 1e-30)
+
+
+def test_mx_gain_fold():
+    lw = synth.make_layer(SHAPE, 5)
+    a = O.quantize_weight_e4m3_mx(lw.w_qkv, lw.gamma_attn)
+    b = O.quantize_weight_e4m3_mx(lw.w_qkv * lw.gamma_attn[None, :])
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
 
 
 # ---------------------------------------------------------------------------
@@ -199,14 +263,15 @@ def test_rho_makes_the_projection_scale_invariant(layer):
 # planted mistakes
 # ---------------------------------------------------------------------------
 
-PINS = ["test_token_map_worked_example", "test_activation_and_query_codes_match_torch",
+PINS = ["test_mx_exponent_closed_forms", "test_token_map_worked_example", "test_activation_and_query_codes_match_torch",
         "test_amax_and_delayed_scaling_round_trip", "test_one_token_requests_reduce_to_the_decode_qkv_stage",
         "test_new_keys_and_values_are_bf16_values", "test_packing_and_token_independence",
         "test_rho_makes_the_projection_scale_invariant"]
 
 
 @pytest.mark.parametrize("mistake", ["map_no_start", "map_token_index", "dequant_no_scale", "no_rho",
-                                     "scale_multiplied", "kv_not_bf16", "amax_before_abs"])
+                                     "scale_multiplied", "kv_not_bf16", "amax_before_abs", "mx_floor",
+                                     "mx_off_by_one"])
 def test_planted_prefill_mistakes_fail_a_pin(monkeypatch, layer, mistake):
     if mistake == "map_no_start":
         orig = R.prefill_token_map
@@ -223,6 +288,16 @@ def test_planted_prefill_mistakes_fail_a_pin(monkeypatch, layer, mistake):
         monkeypatch.setattr(O, "fp8_quantize", R.fp8_quantize)
     elif mistake == "kv_not_bf16":
         monkeypatch.setattr(R, "round_to_bf16", lambda x: np.asarray(x, np.float64))
+    elif mistake == "mx_floor":  # the OCP rounding of the shared exponent (floor(log2 max) - 8): saturates
+        def wrong_e(a):
+            a = np.asarray(a, dtype=np.float64)
+            return np.where(a == 0, -127, np.floor(np.log2(np.where(a == 0, 1.0, a))) - 8).astype(np.int64)
+        monkeypatch.setattr(R, "mx_exponent", wrong_e)
+        monkeypatch.setattr(O, "mx_exponent", wrong_e)
+    elif mistake == "mx_off_by_one":
+        orig_e = R.mx_exponent
+        monkeypatch.setattr(R, "mx_exponent", lambda a: orig_e(a) + 1)
+        monkeypatch.setattr(O, "mx_exponent", R.mx_exponent)
     elif mistake == "amax_before_abs":
         orig = R.prefill_qkv
 
@@ -235,7 +310,7 @@ def test_planted_prefill_mistakes_fail_a_pin(monkeypatch, layer, mistake):
     failed = 0
     for name in PINS:
         pin = globals()[name]
-        args = [] if name in ("test_token_map_worked_example",) else [layer]
+        args = [] if name in ("test_token_map_worked_example", "test_mx_exponent_closed_forms") else [layer]
         try:
             pin(*args)
         except AssertionError:
