@@ -386,7 +386,7 @@ def prefill_bench(args, pw, torch, B, D, synth):
     shape, T, R = pw.shape, pw.T, len(pw.seqlens)
     t0 = time.time()
     lw = synth.make_layer(shape, pw.seed)
-    layer = D.DeviceLayer(shape, lw, fmt="e4m3")
+    layer = D.PrefillWeights(shape, lw)
     caps = [s + n for s, n in zip(pw.starts, pw.seqlens)]
     cache = D.DeviceCache(shape, caps)
     xb = synth.make_prefill_x(shape, T, pw.seed)
@@ -482,7 +482,7 @@ def prefill_cpu_baseline(shape, lw, xb, pw, n_reps, sample=512):
     from threadpoolctl import threadpool_info
     blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     model, nproc = host_cpu()
-    qkv = O.quantize_weight_e4m3(lw.w_qkv, lw.gamma_attn)
+    qkv = O.quantize_weight_e4m3_mx(lw.w_qkv, lw.gamma_attn)
     W = O.dense(qkv)
     n = min(sample, pw.T)
     times = []

@@ -171,6 +171,24 @@ i4d_status i4d_pack_weights_e4m3(i4d_proj_kind kind, const float* W0, const floa
 i4d_status i4d_unpack_weights_e4m3(i4d_proj_kind kind, const void* codes, const uint16_t* scales, int N, int K,
                                    int head_dim, uint8_t* q_out, uint16_t* s_out);
 
+/* FP8 prefill weights: E4M3 codes with one power-of-two scale per (row,
+ * 128-group), stored as an E8M0 byte (exponent + 127), the scale form the
+ * gfx950 FP8 MFMA applies in the instruction (OCP MX style).  e is the
+ * smallest integer with absmax <= 448 * 2^e (so no code saturates; an
+ * all-zero group takes e = -127), codes = E4M3 of w * 2^-e (exact scaling,
+ * nearest even).  The pages give the prefill an FP8 GEMM ("how it works")
+ * but no weight scale form.  Same kinds, gain fold, strip order and 2 KiB
+ * atoms as i4d_pack_weights_e4m3; scales one byte per (strip, group, row).
+ * Host memory. */
+i4d_status i4d_packed_sizes_mx(i4d_proj_kind kind, int N, int K, int head_dim, size_t* code_bytes,
+                               size_t* scale_bytes);
+i4d_status i4d_pack_weights_mx(i4d_proj_kind kind, const float* W0, const float* W1, const float* gamma, int N,
+                               int K, int head_dim, void* codes_out, uint8_t* scales_out, int threads);
+/* Inverse of the layout permutation: codes q_out [rows][K] and E8M0 bytes
+ * s_out [rows][K/128], rows as for i4d_unpack_weights.  Host. */
+i4d_status i4d_unpack_weights_mx(i4d_proj_kind kind, const void* codes, const uint8_t* scales, int N, int K,
+                                 int head_dim, uint8_t* q_out, uint8_t* s_out);
+
 /* LM head (full-model step only): bf16 weight = bf16(fp32(gamma_f[k] * W[v][k]))
  * (gamma_f may be NULL) in tiles of 16 rows x 32 channels: element (v, k)
  * at ((v/16 * d/32 + k/32) * 16 + v%16) * 32 + k%32, so the kernel reads
@@ -434,9 +452,17 @@ typedef struct {
   float q_amax;
 } i4d_fp8_scales;
 
+/* The prefill's weights (device): the gain-folded QKV weight packed by
+ * i4d_pack_weights_mx (kind QKV): E4M3 atoms and E8M0 scale bytes. */
+typedef struct {
+  i4d_layer_shape shape;
+  const void* qkv_codes;
+  const uint8_t* qkv_scales;
+} i4d_prefill_weights;
+
 /* Workspace of i4d_prefill_qkv_e4m3 for T packed tokens.  It begins with
- * the call's FP8 activations (for inspection by tests): T128 = T rounded up
- * to 128 tokens, layout [T128/16 tiles][d/128 groups][2 halves][64 lanes]
+ * the call's FP8 activations (for inspection by tests): Tpad = T rounded up
+ * to 256 tokens, layout [Tpad/16 tiles][d/128 groups][2 halves][64 lanes]
  * [16 bytes], lane 16j + r holding token 16 * tile + r, byte 8 * b + e of
  * half h = code of channel 128 * group + 32 * (2h + b) + 8j + e; tokens
  * from T on hold zeros. */
@@ -450,21 +476,21 @@ i4d_status i4d_prefill_workspace_bytes(const i4d_layer_shape* shape, int T, size
  * Request r owns tokens cu_seqlens[r] .. cu_seqlens[r+1]-1 (device int32
  * [R+1], non-decreasing, cu_seqlens[0] = 0, cu_seqlens[R] = T) at positions
  * start_pos[r], start_pos[r]+1, ... (device int32 [R]) of cache row r.
- * x: bf16 device [T][d].  The layer's qkv_codes / qkv_scales hold the QKV
- * weight packed by i4d_pack_weights_e4m3 (the other projections are not
- * read and may be NULL).  Per token: rho = 1/sqrt(mean x^2 + eps) from the
+ * x: bf16 device [T][d].  Per token: rho = 1/sqrt(mean x^2 + eps) from the
  * bf16 values; x8 = E4M3(fp32(x / x_scale)) (nearest even, saturating at
- * 448); y = x_scale * rho * sum_g s[n][g] * (E4M3 dot product of group g)
- * in fp32; RoPE at the token's position on q and k; q_fp8 (device [T][n_q
- * * 128]) = E4M3(fp32(q / q_scale)); k and v rounded to bf16, rotated and
- * quantized as i4d_kv_append does and stored at their slot.  k_bf16 /
+ * 448); y = x_scale * rho * sum_g 2^e[n][g] * (E4M3 dot product of group
+ * g) accumulated in fp32 by the FP8 MFMA (which applies the E8M0 group
+ * scales itself); RoPE at the token's position on q and k; q_fp8 (device
+ * [T][n_q * 128]) = E4M3 of q times the rounded reciprocal of q_scale;
+ * k and v rounded to bf16, rotated and quantized as i4d_kv_append does
+ * and stored at their slot.  k_bf16 /
  * v_bf16 (device, optional): the bf16 keys and values at the same
  * placement, element (slot, channel) at slot * 128 + channel, slot as in
  * i4d_kv_cache.  A position outside [0, capacity) of its row skips that
  * token's cache writes and sets I4D_DEVERR_APPEND_POS; a scale that is not
  * positive and finite is replaced by 1 with I4D_DEVERR_SCALE.  head_dim
  * 128 and an even number of q + k + v heads.  T = 0 enqueues nothing. */
-i4d_status i4d_prefill_qkv_e4m3(const i4d_layer* layer, const i4d_kv_cache* cache, const uint16_t* x, int T,
+i4d_status i4d_prefill_qkv_e4m3(const i4d_prefill_weights* weights, const i4d_kv_cache* cache, const uint16_t* x, int T,
                                 const int32_t* cu_seqlens, const int32_t* start_pos, int R,
                                 i4d_fp8_scales* scales, uint8_t* q_fp8, uint16_t* k_bf16, uint16_t* v_bf16,
                                 void* workspace, size_t workspace_bytes, void* stream);
@@ -479,10 +505,10 @@ i4d_status i4d_prefill_qkv_e4m3(const i4d_layer* layer, const i4d_kv_cache* cach
  * k_bf16 / v_bf16, q_amax) from a workspace i4d_prefill_prepare filled
  * for the same tokens, requests and scales; it only reads the workspace, so
  * it may be repeated on it. */
-i4d_status i4d_prefill_prepare(const i4d_layer* layer, const i4d_kv_cache* cache, const uint16_t* x, int T,
+i4d_status i4d_prefill_prepare(const i4d_prefill_weights* weights, const i4d_kv_cache* cache, const uint16_t* x, int T,
                                const int32_t* cu_seqlens, const int32_t* start_pos, int R, i4d_fp8_scales* scales,
                                void* workspace, size_t workspace_bytes, void* stream);
-i4d_status i4d_prefill_project(const i4d_layer* layer, const i4d_kv_cache* cache, int T, const int32_t* cu_seqlens,
+i4d_status i4d_prefill_project(const i4d_prefill_weights* weights, const i4d_kv_cache* cache, int T, const int32_t* cu_seqlens,
                                const int32_t* start_pos, int R, i4d_fp8_scales* scales, uint8_t* q_fp8,
                                uint16_t* k_bf16, uint16_t* v_bf16, const void* workspace, size_t workspace_bytes,
                                void* stream);

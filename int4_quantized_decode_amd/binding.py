@@ -66,6 +66,10 @@ class i4d_projection_plan(ctypes.Structure):
                [("lds_bytes", ctypes.c_size_t), ("instantiated", ctypes.c_int)]
 
 
+class i4d_prefill_weights(ctypes.Structure):
+    _fields_ = [("shape", i4d_layer_shape), ("qkv_codes", ctypes.c_void_p), ("qkv_scales", ctypes.c_void_p)]
+
+
 class i4d_fp8_scales(ctypes.Structure):
     _fields_ = [(n, ctypes.c_float) for n in ("x_scale", "q_scale", "x_amax", "q_amax")]
 
@@ -88,6 +92,9 @@ _SIGS = {
     "i4d_packed_sizes_e4m3": (_I, [_I, _I, _I, _I, c_size_p, c_size_p]),
     "i4d_pack_weights_e4m3": (_I, [_I, _VP, _VP, _VP, _I, _I, _I, _VP, _VP, _I]),
     "i4d_unpack_weights_e4m3": (_I, [_I, _VP, _VP, _I, _I, _I, _VP, _VP]),
+    "i4d_packed_sizes_mx": (_I, [_I, _I, _I, _I, c_size_p, c_size_p]),
+    "i4d_pack_weights_mx": (_I, [_I, _VP, _VP, _VP, _I, _I, _I, _VP, _VP, _I]),
+    "i4d_unpack_weights_mx": (_I, [_I, _VP, _VP, _I, _I, _I, _VP, _VP]),
     "i4d_kv_cache_bytes": (_I, [_I, _I, ctypes.c_int64, c_size_p, c_size_p, c_size_p, c_size_p]),
     "i4d_kv_append": (_I, [ctypes.POINTER(i4d_kv_cache), _VP, _VP, _VP, _VP, _I, _VP]),
     "i4d_kv_unpack_host": (_I, [ctypes.POINTER(i4d_kv_cache), _VP, _I, _I, _I, _VP, _VP, _VP, _VP]),
@@ -112,11 +119,11 @@ _SIGS = {
     "i4d_decode_block_step_noalloc": (_I, [ctypes.POINTER(i4d_layer), ctypes.POINTER(i4d_kv_cache), _VP, _VP,
                                            _VP, _I, _I, _I, _VP, _VP]),
     "i4d_prefill_workspace_bytes": (_I, [ctypes.POINTER(i4d_layer_shape), _I, c_size_p]),
-    "i4d_prefill_qkv_e4m3": (_I, [ctypes.POINTER(i4d_layer), ctypes.POINTER(i4d_kv_cache), _VP, _I, _VP, _VP, _I,
+    "i4d_prefill_qkv_e4m3": (_I, [ctypes.POINTER(i4d_prefill_weights), ctypes.POINTER(i4d_kv_cache), _VP, _I, _VP, _VP, _I,
                                   _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
-    "i4d_prefill_prepare": (_I, [ctypes.POINTER(i4d_layer), ctypes.POINTER(i4d_kv_cache), _VP, _I, _VP, _VP, _I,
+    "i4d_prefill_prepare": (_I, [ctypes.POINTER(i4d_prefill_weights), ctypes.POINTER(i4d_kv_cache), _VP, _I, _VP, _VP, _I,
                                  _VP, _VP, ctypes.c_size_t, _VP]),
-    "i4d_prefill_project": (_I, [ctypes.POINTER(i4d_layer), ctypes.POINTER(i4d_kv_cache), _I, _VP, _VP, _I,
+    "i4d_prefill_project": (_I, [ctypes.POINTER(i4d_prefill_weights), ctypes.POINTER(i4d_kv_cache), _I, _VP, _VP, _I,
                                  _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
     "i4d_fp8_scales_update": (_I, [_VP, _VP]),
     "i4d_lm_head_workspace_bytes": (_I, [_I, _I, c_size_p]),
@@ -268,6 +275,36 @@ def i4d_unpack_weights_e4m3(kind: int, codes, scales, N: int, K: int, head_dim: 
     return q, s
 
 
+def i4d_packed_sizes_mx(kind: int, N: int, K: int, head_dim: int = 0):
+    cb, sb = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().i4d_packed_sizes_mx(kind, N, K, head_dim, ctypes.byref(cb), ctypes.byref(sb)))
+    return cb.value, sb.value
+
+
+def i4d_pack_weights_mx(kind: int, W0, W1=None, gamma=None, head_dim: int = 0, threads: int = 0):
+    """fp32 host weights -> (E4M3 codes uint8, E8M0 scale bytes uint8) in the device layout."""
+    W0 = np.ascontiguousarray(W0, dtype=np.float32)
+    N, K = W0.shape
+    W1 = None if W1 is None else np.ascontiguousarray(W1, dtype=np.float32)
+    gamma = None if gamma is None else np.ascontiguousarray(gamma, dtype=np.float32)
+    cb, sb = i4d_packed_sizes_mx(kind, N, K, head_dim)
+    codes = np.empty(cb, np.uint8)
+    scales = np.empty(sb, np.uint8)
+    _check(lib().i4d_pack_weights_mx(kind, ptr(W0), ptr(W1), ptr(gamma), N, K, head_dim, ptr(codes), ptr(scales),
+                                     threads))
+    return codes, scales
+
+
+def i4d_unpack_weights_mx(kind: int, codes, scales, N: int, K: int, head_dim: int = 0):
+    rows = 2 * N if kind == I4D_PROJ_GATE_UP else N
+    q = np.empty((rows, K), np.uint8)
+    s = np.empty((rows, K // 128), np.uint8)
+    codes = np.ascontiguousarray(codes)
+    scales = np.ascontiguousarray(scales)
+    _check(lib().i4d_unpack_weights_mx(kind, ptr(codes), ptr(scales), N, K, head_dim, ptr(q), ptr(s)))
+    return q, s
+
+
 def i4d_pack_lm_head(W, gamma=None, threads: int = 0):
     """fp32 [V][d] -> bf16 bits in tiles [V/16][d/32][16][32]."""
     W = np.ascontiguousarray(W, dtype=np.float32)
@@ -412,7 +449,7 @@ def i4d_prefill_workspace_bytes(shape: i4d_layer_shape, T: int) -> int:
     return b.value
 
 
-def i4d_prefill_qkv_e4m3(layer: i4d_layer, cache: i4d_kv_cache, x, T: int, cu_seqlens, start_pos, R: int,
+def i4d_prefill_qkv_e4m3(layer: i4d_prefill_weights, cache: i4d_kv_cache, x, T: int, cu_seqlens, start_pos, R: int,
                          scales, q_fp8, k_bf16, v_bf16, workspace, workspace_bytes: int, stream=None):
     """scales: device i4d_fp8_scales (e.g. a float32 tensor of 4 elements)."""
     _check(lib().i4d_prefill_qkv_e4m3(ctypes.byref(layer), ctypes.byref(cache), ptr(x), T, ptr(cu_seqlens),
@@ -420,14 +457,14 @@ def i4d_prefill_qkv_e4m3(layer: i4d_layer, cache: i4d_kv_cache, x, T: int, cu_se
                                       ptr(workspace), workspace_bytes, stream_handle(stream)))
 
 
-def i4d_prefill_prepare(layer: i4d_layer, cache: i4d_kv_cache, x, T: int, cu_seqlens, start_pos, R: int, scales,
+def i4d_prefill_prepare(layer: i4d_prefill_weights, cache: i4d_kv_cache, x, T: int, cu_seqlens, start_pos, R: int, scales,
                         workspace, workspace_bytes: int, stream=None):
     _check(lib().i4d_prefill_prepare(ctypes.byref(layer), ctypes.byref(cache), ptr(x), T, ptr(cu_seqlens),
                                      ptr(start_pos), R, ptr(scales), ptr(workspace), workspace_bytes,
                                      stream_handle(stream)))
 
 
-def i4d_prefill_project(layer: i4d_layer, cache: i4d_kv_cache, T: int, cu_seqlens, start_pos, R: int, scales,
+def i4d_prefill_project(layer: i4d_prefill_weights, cache: i4d_kv_cache, T: int, cu_seqlens, start_pos, R: int, scales,
                         q_fp8, k_bf16, v_bf16, workspace, workspace_bytes: int, stream=None):
     _check(lib().i4d_prefill_project(ctypes.byref(layer), ctypes.byref(cache), T, ptr(cu_seqlens), ptr(start_pos),
                                      R, ptr(scales), ptr(q_fp8), ptr(k_bf16), ptr(v_bf16), ptr(workspace),

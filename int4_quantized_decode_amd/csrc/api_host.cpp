@@ -181,6 +181,27 @@ static inline uint16_t quantize_group_e4m3(const float* w, uint8_t* q) {
   return s16;
 }
 
+// the smallest e with absmax <= 448 * 2^e: with absmax = m 2^x (0.5 <= m < 1)
+// and 448 = 0.875 2^9 that is x - 9 when m <= 0.875, else x - 8; clamped to
+// the E8M0 range [-127, 127]; an all-zero group takes -127
+static inline int mx_exponent_of(float a) {
+  if (a == 0.f) return -127;
+  int x;
+  const double m = frexp((double)a, &x);
+  const int e = (m <= 0.875) ? x - 9 : x - 8;
+  return std::min(127, std::max(-127, e));
+}
+
+// E4M3 codes of one 128-wide group with a power-of-two scale 2^e: codes of
+// w * 2^-e (exact scaling, no saturation); returns the E8M0 byte e + 127
+static inline uint8_t quantize_group_mx(const float* w, uint8_t* q) {
+  float a = 0.f;
+  for (int k = 0; k < kGroup; ++k) a = std::max(a, fabsf(w[k]));
+  const int e = mx_exponent_of(a);
+  for (int k = 0; k < kGroup; ++k) q[k] = e4m3_of((float)ldexp((double)w[k], -e));
+  return (uint8_t)(e + 127);
+}
+
 template <typename F>
 static void parallel_for(long n, int threads, F&& fn) {
   if (threads <= 0) threads = (int)std::max(1u, std::thread::hardware_concurrency());
@@ -237,6 +258,60 @@ static inline void source_row(i4d_proj_kind kind, int p, int head_dim, int* mat,
 }  // namespace i4d
 
 using namespace i4d;
+
+// E4M3 atoms with one scale per (row, group) of type S from quantize_group
+template <typename S, typename QG>
+static i4d_status pack_e4m3_atoms(i4d_proj_kind kind, const float* W0, const float* W1, const float* gamma, int N,
+                                  int K, int head_dim, void* codes_out, S* scales_out, int threads, QG quantize_group) {
+  i4d_status st = check_pack_args(kind, N, K, head_dim);
+  if (st) return st;
+  if (!W0 || !codes_out || !scales_out) return fail(I4D_ERR_NULL, "W0/codes_out/scales_out NULL");
+  if (kind == I4D_PROJ_GATE_UP && !W1) return fail(I4D_ERR_NULL, "gate/up needs W1 (up)");
+  if (kind == I4D_PROJ_PLAIN && gamma)
+    return fail(I4D_ERR_RANGE, "PLAIN projections take no gain (gamma must be NULL)");
+  const int Np = packed_rows(kind, N);
+  const int G = groups_of(K);
+  uint8_t* codes = (uint8_t*)codes_out;
+  parallel_for(Np / kStrip, threads, [&](long t0, long t1) {
+    float w[kGroup];
+    uint8_t q[kGroup];
+    for (long t = t0; t < t1; ++t) {
+      for (int r = 0; r < kStrip; ++r) {
+        int p = (int)t * kStrip + r, mat, row;
+        source_row(kind, p, head_dim, &mat, &row);
+        const float* src = (mat ? W1 : W0) + (size_t)row * K;
+        for (int g = 0; g < G; ++g) {
+          for (int k = 0; k < kGroup; ++k) {
+            const float v = src[g * kGroup + k];
+            w[k] = gamma ? gamma[g * kGroup + k] * v : v;  // one fp32 product
+          }
+          scales_out[((size_t)t * G + g) * kStrip + r] = quantize_group(w, q);
+          for (int k = 0; k < kGroup; ++k) codes[e4m3_code_offset(p, g * kGroup + k, K)] = q[k];
+        }
+      }
+    }
+  });
+  return ok();
+}
+
+template <typename S>
+static i4d_status unpack_e4m3_atoms(i4d_proj_kind kind, const void* codes, const S* scales, int N, int K,
+                                    int head_dim, uint8_t* q_out, S* s_out) {
+  i4d_status st = check_pack_args(kind, N, K, head_dim);
+  if (st) return st;
+  if (!codes || !scales || !q_out || !s_out) return fail(I4D_ERR_NULL, "NULL pointer");
+  const int Np = packed_rows(kind, N);
+  const int G = groups_of(K);
+  const uint8_t* c = (const uint8_t*)codes;
+  for (int p = 0; p < Np; ++p) {
+    int mat, row;
+    source_row(kind, p, head_dim, &mat, &row);
+    const int out_row = mat * N + row;
+    for (int k = 0; k < K; ++k) q_out[(size_t)out_row * K + k] = c[e4m3_code_offset(p, k, K)];
+    for (int g = 0; g < G; ++g) s_out[(size_t)out_row * G + g] = scales[scale_index(p, g, K)];
+  }
+  return ok();
+}
 
 extern "C" {
 
@@ -354,53 +429,33 @@ i4d_status i4d_packed_sizes_e4m3(i4d_proj_kind kind, int N, int K, int head_dim,
 i4d_status i4d_pack_weights_e4m3(i4d_proj_kind kind, const float* W0, const float* W1, const float* gamma,
                                  int N, int K, int head_dim, void* codes_out, uint16_t* scales_out,
                                  int threads) {
+  return pack_e4m3_atoms(kind, W0, W1, gamma, N, K, head_dim, codes_out, scales_out, threads, quantize_group_e4m3);
+}
+
+i4d_status i4d_packed_sizes_mx(i4d_proj_kind kind, int N, int K, int head_dim, size_t* code_bytes,
+                               size_t* scale_bytes) {
+  if (!code_bytes || !scale_bytes) return fail(I4D_ERR_NULL, "output pointer is NULL");
   i4d_status st = check_pack_args(kind, N, K, head_dim);
   if (st) return st;
-  if (!W0 || !codes_out || !scales_out) return fail(I4D_ERR_NULL, "W0/codes_out/scales_out NULL");
-  if (kind == I4D_PROJ_GATE_UP && !W1) return fail(I4D_ERR_NULL, "gate/up needs W1 (up)");
-  if (kind == I4D_PROJ_PLAIN && gamma)
-    return fail(I4D_ERR_RANGE, "PLAIN projections take no gain (gamma must be NULL)");
   const int Np = packed_rows(kind, N);
-  const int G = groups_of(K);
-  uint8_t* codes = (uint8_t*)codes_out;
-  parallel_for(Np / kStrip, threads, [&](long t0, long t1) {
-    float w[kGroup];
-    uint8_t q[kGroup];
-    for (long t = t0; t < t1; ++t) {
-      for (int r = 0; r < kStrip; ++r) {
-        int p = (int)t * kStrip + r, mat, row;
-        source_row(kind, p, head_dim, &mat, &row);
-        const float* src = (mat ? W1 : W0) + (size_t)row * K;
-        for (int g = 0; g < G; ++g) {
-          for (int k = 0; k < kGroup; ++k) {
-            const float v = src[g * kGroup + k];
-            w[k] = gamma ? gamma[g * kGroup + k] * v : v;  // one fp32 product
-          }
-          scales_out[((size_t)t * G + g) * kStrip + r] = quantize_group_e4m3(w, q);
-          for (int k = 0; k < kGroup; ++k) codes[e4m3_code_offset(p, g * kGroup + k, K)] = q[k];
-        }
-      }
-    }
-  });
+  *code_bytes = (size_t)Np * (size_t)K;
+  *scale_bytes = packed_scale_elems(Np, K);
   return ok();
+}
+
+i4d_status i4d_pack_weights_mx(i4d_proj_kind kind, const float* W0, const float* W1, const float* gamma, int N,
+                               int K, int head_dim, void* codes_out, uint8_t* scales_out, int threads) {
+  return pack_e4m3_atoms(kind, W0, W1, gamma, N, K, head_dim, codes_out, scales_out, threads, quantize_group_mx);
+}
+
+i4d_status i4d_unpack_weights_mx(i4d_proj_kind kind, const void* codes, const uint8_t* scales, int N, int K,
+                                 int head_dim, uint8_t* q_out, uint8_t* s_out) {
+  return unpack_e4m3_atoms(kind, codes, scales, N, K, head_dim, q_out, s_out);
 }
 
 i4d_status i4d_unpack_weights_e4m3(i4d_proj_kind kind, const void* codes, const uint16_t* scales, int N, int K,
                                    int head_dim, uint8_t* q_out, uint16_t* s_out) {
-  i4d_status st = check_pack_args(kind, N, K, head_dim);
-  if (st) return st;
-  if (!codes || !scales || !q_out || !s_out) return fail(I4D_ERR_NULL, "NULL pointer");
-  const int Np = packed_rows(kind, N);
-  const int G = groups_of(K);
-  const uint8_t* c = (const uint8_t*)codes;
-  for (int p = 0; p < Np; ++p) {
-    int mat, row;
-    source_row(kind, p, head_dim, &mat, &row);
-    const int out_row = mat * N + row;
-    for (int k = 0; k < K; ++k) q_out[(size_t)out_row * K + k] = c[e4m3_code_offset(p, k, K)];
-    for (int g = 0; g < G; ++g) s_out[(size_t)out_row * G + g] = scales[scale_index(p, g, K)];
-  }
-  return ok();
+  return unpack_e4m3_atoms(kind, codes, scales, N, K, head_dim, q_out, s_out);
 }
 
 i4d_status i4d_unpack_weights(i4d_proj_kind kind, const void* codes, const uint16_t* scales, int N,

@@ -43,8 +43,11 @@ namespace i4d {
 namespace {
 
 constexpr int kHd = 128;            // head_dim this path takes
-constexpr int kTilesPerWg = 8;      // 16-token tiles per gemm workgroup
+constexpr int kWaves = 8;           // gemm workgroup: 4 row quarters x 2 token halves
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTilesPerWg = 16;     // 16-token tiles per gemm workgroup
 constexpr int kTokPerWg = 16 * kTilesPerWg;
+constexpr int kTilesPerWave = 8;    // a wave's token half
 constexpr int kRowsPerWg = 256;     // two heads
 constexpr int kStripsPerWave = 4;   // 64 rows per wave
 constexpr int kChunkTok = 32;       // epilogue tokens per LDS pass
@@ -54,14 +57,14 @@ constexpr int kPrepGroups = 8;      // weight groups of d per prep workgroup
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
 struct PrefillArgs {
-  const uint8_t* codes;  // E4M3 QKV atoms [strip][group][64 lanes][32 B]
-  const uint16_t* scales;
+  const uint8_t* codes;   // E4M3 QKV atoms [strip][group][64 lanes][32 B]
+  const uint8_t* scales;  // E8M0 bytes [strip][group][16 rows]
   int N, K, G;
   int n_q, n_kv;
   float eps;
   double rope_ratio;
   const uint16_t* x;  // bf16 [T][K]
-  int T, T128, R, nch;
+  int T, Tpad, R, nch;
   const int32_t* cu;     // [R + 1]
   const int32_t* start;  // [R]
   i4d_fp8_scales* sc;
@@ -69,10 +72,10 @@ struct PrefillArgs {
   uint16_t* k_bf16;
   uint16_t* v_bf16;
   KvArgs kv;
-  uint8_t* x8;    // [T128 / 16][G][2 halves][64 lanes][16 B]
-  float* sumsq;   // [nch][T128]
-  int2* map;      // [T128] (cache row, position; -1 = no cache write)
-  float2* rope;   // [T128][64] (cos, sin)
+  uint8_t* x8;    // [Tpad / 16][G][2 halves][64 lanes][16 B]
+  float* sumsq;   // [nch][Tpad]
+  int2* map;      // [Tpad] (cache row, position; -1 = no cache write)
+  float2* rope;   // [Tpad][64] (cos, sin)
 };
 
 // OCP E4M3 code of a finite fp32 value: nearest, ties to even, saturating at
@@ -190,7 +193,7 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrefillArgs a) {
   __syncthreads();
   if (tid < 16) {
     const float s = red_sq[0][tid] + red_sq[1][tid] + red_sq[2][tid] + red_sq[3][tid];
-    a.sumsq[(size_t)ch * a.T128 + tile * 16 + tid] = s;
+    a.sumsq[(size_t)ch * a.Tpad + tile * 16 + tid] = s;
   }
   if (tid == 0) {
     const float mm = fmaxf(fmaxf(red_max[0], red_max[1]), fmaxf(red_max[2], red_max[3]));
@@ -220,30 +223,32 @@ struct TokInfo {
   float rho;
 };
 
-// LDS.  Main loop: a ring of kStages stages, each holding one weight group's
-// A operands [16 strips][2 halves][64 lanes][16 B], the B operands of the
-// workgroup's tokens [8 tiles][2 halves][64 lanes][16 B] and the group
-// scales [4 waves][4 strips][16 rows] fp16.  Epilogue (after the loop, over
-// the same bytes): fp32 tile [2 heads][32 tokens][kYPitch], RoPE rotations
-// [128 tokens][kRopePitch] (cos, sin), value codes [128 tokens][2 heads]
-// [128].  Token info [128] sits after both.
-constexpr int kStages = 3;
+// LDS.  Main loop: a ring of two stages, each holding one weight group's A
+// operands [16 strips][2 halves][64 lanes][16 B], the B operands of the
+// workgroup's tokens [16 tiles][2 halves][64 lanes][16 B] and the group
+// scales [16 strips][16 rows] (E8M0 bytes).  Epilogue (after the loop, over
+// the same bytes): fp32 tile [2 heads][32 tokens][kYPitch] and one region
+// that holds either the RoPE rotations of half the tile's tokens [128]
+// [kRopePitch] (q and k tiles) or the value codes [256 tokens][2 heads]
+// [128] (v tiles; a tile is one or the other when n_q and n_kv are even).
+// Token info [256] sits after both.
+constexpr int kStages = 2;
 constexpr size_t kStageA = 16 * 2048;
 constexpr size_t kStageB = kTilesPerWg * 2048;
-constexpr size_t kStageS = 4 * 4 * 32;
+constexpr size_t kStageS = 16 * 16;
 constexpr size_t kStageBytes = kStageA + kStageB + kStageS;
 constexpr size_t kRingBytes = kStages * kStageBytes;
 constexpr size_t kYBytes = (size_t)2 * kChunkTok * kYPitch * 4;
 constexpr int kRopePitch = 72;  // float2 per token row: 64 pairs + 64 B so that 4 rows read at once hit distinct banks
-constexpr size_t kRopeBytes = (size_t)kTokPerWg * kRopePitch * 8;
+constexpr int kRopeTok = 128;   // tokens whose rotations are in LDS at a time
+constexpr size_t kRopeBytes = (size_t)kRopeTok * kRopePitch * 8;
 constexpr size_t kVcodeBytes = (size_t)kTokPerWg * 2 * kHd;
-constexpr size_t kEpiBytes = kYBytes + kRopeBytes + kVcodeBytes;
+constexpr size_t kRegionBytes = kRopeBytes > kVcodeBytes ? kRopeBytes : kVcodeBytes;
+constexpr size_t kEpiBytes = kYBytes + kRegionBytes;
 constexpr size_t kShared = kRingBytes > kEpiBytes ? kRingBytes : kEpiBytes;
 constexpr size_t kGemmLds = kShared + kTokPerWg * sizeof(TokInfo);  // token info after the shared region
 static_assert(kGemmLds <= 160 * 1024, "LDS");
-// DMA instructions per wave and stage: A 8, B (2 per token tile over 4 waves), scales 1
-constexpr int kDmaB = kTilesPerWg / 2;
-constexpr int kDmaPerStage = 8 + kDmaB + 1;
+static_assert(kTokPerWg <= 256, "representative entries keep the token in 8 bits");
 
 __device__ __forceinline__ i32x8_t cat8(const u32x4_t& lo, const u32x4_t& hi) {
   return i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
@@ -256,8 +261,7 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
 // 16 bytes per active lane from global memory straight into LDS at
 // lds + 16 * lane.  Issued from asm (M0 saved and restored) so that the
 // compiler does not drain it before every LDS read; the ring waits for it
-// with explicit vmcnt counts (every vector-memory instruction of the main
-// loop is one of these, so the counts are exact).
+// with an explicit vmcnt.  lds must be wave-uniform.
 __device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds) {
   uint32_t saved;
   asm volatile(
@@ -270,100 +274,91 @@ __device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds) {
       : "memory");
 }
 
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  // vmcnt <= N; expcnt and lgkmcnt left at their maxima (no wait)
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
+// every vector-memory operation of the wave has completed
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xF << 8)); }
 
-__global__ __launch_bounds__(256) void prefill_gemm_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kThreads) void prefill_gemm_kernel(PrefillArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave & 3, wt = wave >> 2;  // row quarter (4 strips), token half (8 tiles)
   const int r = lane & 15, j = lane >> 4;
   const int G = a.G;
-  const int t_tiles = a.T128 / kTokPerWg;
+  const int t_tiles = a.Tpad / kTokPerWg;
   // consecutive workgroups share the weight tile (measured faster than
   // grouping whole weight tiles per XCD)
   const int b = blockIdx.x;
   const int ntile = b / t_tiles, ttile = b % t_tiles;
-  const int wstrip0 = ntile * (kRowsPerWg / 16) + wave * kStripsPerWave;  // the wave's first strip
+  const int strip0 = ntile * (kRowsPerWg / 16);  // the workgroup's first strip
   const int tile16_0 = ttile * kTilesPerWg;
   const int tok0 = ttile * kTokPerWg;
   const uint32_t lds0 = lds_offset(smem);
 
-  // ---- main loop: a ring of kStages weight groups in LDS ----
+  // ---- main loop: the weight groups of d through a two-stage LDS ring ----
+  // per stage and wave: 4 of the 32 A halves, 4 of the 32 B halves, and (in
+  // the first token half) the scales of the wave's 4 strips
   auto issue = [&](int g, int stage) {
     const uint32_t sa = lds0 + stage * (uint32_t)kStageBytes;
     const uint32_t sb = sa + (uint32_t)kStageA;
     const uint32_t ss = sb + (uint32_t)kStageB;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {  // the wave's 4 strips x 2 halves
-      const int s = i >> 1, h = i & 1;
-      const uint8_t* src = a.codes + ((size_t)(wstrip0 + s) * G + g) * 2048 + lane * 32 + h * 16;
-      lds_dma16(src, sa + (uint32_t)(((wave * kStripsPerWave + s) * 2 + h) * 1024));
+    for (int i = 0; i < 4; ++i) {
+      const int p = wt * 4 + i, s = 4 * wn + (p >> 1), h = p & 1;
+      const uint8_t* src = a.codes + ((size_t)(strip0 + s) * G + g) * 2048 + lane * 32 + h * 16;
+      lds_dma16(src, sa + (uint32_t)((s * 2 + h) * 1024));
     }
 #pragma unroll
-    for (int i = 0; i < kDmaB; ++i) {  // a quarter of the tokens' tiles x 2 halves
-      const int p = wave * kDmaB + i, tt = p >> 1, h = p & 1;
+    for (int i = 0; i < 4; ++i) {
+      const int p = wave * 4 + i, tt = p >> 1, h = p & 1;
       const uint8_t* src = a.x8 + ((size_t)(tile16_0 + tt) * G + g) * 2048 + h * 1024 + lane * 16;
       lds_dma16(src, sb + (uint32_t)(p * 1024));
     }
-    {  // the wave's 4 strips' scales: 8 lanes x 16 B
-      const int l8 = lane & 7;
-      const uint16_t* src = a.scales + ((size_t)(wstrip0 + (l8 >> 1)) * G + g) * 16 + (l8 & 1) * 8;
-      if (lane < 8) lds_dma16(src, ss + (uint32_t)(wave * 128));
+    {
+      const uint8_t* src = a.scales + ((size_t)(strip0 + 4 * wn + (lane & 3)) * G + g) * 16;
+      if (wt == 0 && lane < 4) lds_dma16(src, ss + (uint32_t)(wn * 64));
     }
   };
 
-  f32x4_t acc[kStripsPerWave][kTilesPerWg];
+  f32x4_t acc[kStripsPerWave][kTilesPerWave];
 #pragma unroll
   for (int s = 0; s < kStripsPerWave; ++s)
 #pragma unroll
-    for (int t = 0; t < kTilesPerWg; ++t) acc[s][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < kTilesPerWave; ++t) acc[s][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   auto compute = [&](int stage) {
     const unsigned char* sa = smem + (size_t)stage * kStageBytes;
     const unsigned char* sb = sa + kStageA;
     const unsigned char* ss = sb + kStageB;
     i32x8_t av[kStripsPerWave];
-    u32x2_t sc[kStripsPerWave];
+    int sc[kStripsPerWave];
 #pragma unroll
     for (int s = 0; s < kStripsPerWave; ++s) {
-      const unsigned char* pa = sa + ((wave * kStripsPerWave + s) * 2) * 1024 + lane * 16;
+      const unsigned char* pa = sa + ((4 * wn + s) * 2) * 1024 + lane * 16;
       av[s] = cat8(*reinterpret_cast<const u32x4_t*>(pa), *reinterpret_cast<const u32x4_t*>(pa + 1024));
-      sc[s] = *reinterpret_cast<const u32x2_t*>(ss + wave * 128 + s * 32 + j * 8);
+      // the E8M0 scale of the lane's row (row r of the strip, whatever j)
+      sc[s] = ss[wn * 64 + s * 16 + r];
     }
+    // the group scales enter the instruction (E8M0 per row), so the
+    // accumulators chain across groups with no VALU work
 #pragma unroll
-    for (int t = 0; t < kTilesPerWg; ++t) {
-      const unsigned char* pb = sb + (t * 2) * 1024 + lane * 16;
+    for (int t = 0; t < kTilesPerWave; ++t) {
+      const unsigned char* pb = sb + ((kTilesPerWave * wt + t) * 2) * 1024 + lane * 16;
       const i32x8_t bv = cat8(*reinterpret_cast<const u32x4_t*>(pb), *reinterpret_cast<const u32x4_t*>(pb + 1024));
-      f32x4_t pr[kStripsPerWave];
 #pragma unroll
       for (int s = 0; s < kStripsPerWave; ++s)
-        pr[s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av[s], bv, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0,
-                                                                 127, 0, 127);
-#pragma unroll
-      for (int s = 0; s < kStripsPerWave; ++s)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float scl = f16_bits_to_f32((uint16_t)(sc[s][i >> 1] >> (16 * (i & 1))));
-          acc[s][t][i] = fmaf(scl, pr[s][i], acc[s][t][i]);
-        }
+        acc[s][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av[s], bv, acc[s][t], 0, 0, 0, sc[s], 0, 127);
     }
   };
 
-  // prologue: groups 0 and 1 in flight
   issue(0, 0);
-  if (G > 1) issue(1, 1);
 
-  // token info for the epilogue, read while the first groups load
+  // token info for the epilogue, read while the first group loads
   TokInfo* tinfo = reinterpret_cast<TokInfo*>(smem + kShared);
   if (tid < kTokPerWg) {
     const int t = tok0 + tid;
     float ssum = 0.f;
-    for (int c = 0; c < a.nch; ++c) ssum += a.sumsq[(size_t)c * a.T128 + t];
+    for (int c = 0; c < a.nch; ++c) ssum += a.sumsq[(size_t)c * a.Tpad + t];
     TokInfo ti;
     ti.rho = 1.0f / sqrtf(ssum / (float)a.K + a.eps);
     const int2 m = a.map[t];
@@ -384,62 +379,68 @@ __global__ __launch_bounds__(256) void prefill_gemm_kernel(PrefillArgs a) {
   }
 
   for (int g = 0; g < G; ++g) {
-    const int stage = g % kStages;
-    // group g landed (group g + 1 may still be in flight), for every wave
-    if (g + 1 < G) wait_vm<kDmaPerStage>(); else wait_vm<0>();
+    // group g landed (nothing else is in flight), for every wave
+    wait_vm0();
     lds_barrier();
-    // the stage of group g - 1 is free again: group g + 2 goes there
-    if (g + 2 < G) issue(g + 2, (g + 2) % kStages);
-    compute(stage);
+    // the stage of group g - 1 is free again: group g + 1 goes there
+    if (g + 1 < G) issue(g + 1, (g + 1) % kStages);
+    compute(g % kStages);
   }
   lds_barrier();  // every wave is done with the ring; the epilogue reuses it
 
   // ---- epilogue ----
   float* ybuf = reinterpret_cast<float*>(smem);
-  float2* rope_s = reinterpret_cast<float2*>(smem + kYBytes);
-  uint8_t* vcodes = smem + kYBytes + kRopeBytes;
+  unsigned char* region = smem + kYBytes;
+  float2* rope_s = reinterpret_cast<float2*>(region);
+  uint8_t* vcodes = region;
   const int head0 = ntile * 2;  // first of the workgroup's two heads (q | k | v order)
   const bool has_rope = head0 < a.n_q + a.n_kv;
-  if (has_rope) {
-    // the tile's RoPE rotations from the prep's table, 512 B per token row
-    // (32 lanes), in flight while the first chunk is staged
+  // the RoPE rows of tokens [128 h, 128 h + 128) of the tile (q and k tiles)
+  auto load_rope = [&](int h) {
     const uint32_t rb = lds_offset(rope_s);
-    for (int tl = wave; tl < kTokPerWg; tl += 4) {
-      const float2* src = a.rope + (size_t)(tok0 + tl) * 64 + 2 * (lane & 31);
+    for (int tl = wave; tl < kRopeTok; tl += kWaves) {
+      const float2* src = a.rope + (size_t)(tok0 + kRopeTok * h + tl) * 64 + 2 * (lane & 31);
       if (lane < 32) lds_dma16(src, rb + (uint32_t)(tl * kRopePitch * 8));
     }
-  }
+  };
+  if (has_rope) load_rope(0);
   const float sx = checked_scale(a.sc->x_scale, nullptr, false);
   const float sq = checked_scale(a.sc->q_scale, a.kv.err_word, blockIdx.x == 0 && tid == 0);
   const float rsq = __fdiv_rn(1.0f, sq);
   float qmax = 0.f;
-  const int hl_w = wave >> 1;  // head of this wave's rows
-  const int sp0 = 4 * (wave & 1);
+  const int hl_w = wn >> 1;  // head of this wave's rows
+  const int sp0 = 4 * (wn & 1);
   const int l16 = tid & 15;
 #pragma unroll
   for (int c = 0; c < kTilesPerWg / 2; ++c) {
-    // fp32 tile [head][token][channel] of tokens 32c .. 32c + 31 (the loop is
-    // unrolled so that acc is indexed by constants and stays in registers)
+    // fp32 tile [head][token][channel] of tokens 32c .. 32c + 31, from the
+    // waves of that token half (the loop is unrolled so that acc is indexed
+    // by constants and stays in registers)
+    if (wt == c / 4) {
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const int t = 2 * c + tt;
-      const int tl = 16 * tt + r;
-      const float f = sx * tinfo[16 * t + r].rho;
+      for (int tt = 0; tt < 2; ++tt) {
+        const int t = 2 * (c % 4) + tt;  // the wave's tile
+        const int tl = 16 * tt + r;
+        const float f = sx * tinfo[32 * c + tl].rho;
 #pragma unroll
-      for (int s = 0; s < kStripsPerWave; ++s) {
-        const int sp = sp0 + s;
-        const int ch0 = (j < 2) ? 8 * sp + 4 * j : kHd / 2 + 8 * sp + 4 * (j - 2);
-        const f32x4_t v = {acc[s][t][0] * f, acc[s][t][1] * f, acc[s][t][2] * f, acc[s][t][3] * f};
-        *reinterpret_cast<f32x4_t*>(&ybuf[((size_t)hl_w * kChunkTok + tl) * kYPitch + ch0]) = v;
+        for (int s = 0; s < kStripsPerWave; ++s) {
+          const int sp = sp0 + s;
+          const int ch0 = (j < 2) ? 8 * sp + 4 * j : kHd / 2 + 8 * sp + 4 * (j - 2);
+          const f32x4_t v = {acc[s][t][0] * f, acc[s][t][1] * f, acc[s][t][2] * f, acc[s][t][3] * f};
+          *reinterpret_cast<f32x4_t*>(&ybuf[((size_t)hl_w * kChunkTok + tl) * kYPitch + ch0]) = v;
+        }
       }
     }
-    if (c == 0) wait_vm<0>();  // the RoPE rows (every wave's own DMAs)
+    if (has_rope && c % 4 == 0) {
+      if (c > 0) load_rope(c / 4);
+      wait_vm0();  // the RoPE rows (every wave's own DMAs)
+    }
     // LDS-only barriers: the chunk's global stores need not complete here
     lds_barrier();
     // one (head, token) vector per 16 lanes, 8 channels per lane
 #pragma unroll 1
-    for (int it = 0; it < 4; ++it) {
-      const int vec = it * 16 + (tid >> 4);
+    for (int it = 0; it < 2 * kChunkTok / (kThreads / 16); ++it) {
+      const int vec = it * (kThreads / 16) + (tid >> 4);
       const int hl = vec >> 5, tl = vec & 31;
       const int tloc = 32 * c + tl;
       const int t = tok0 + tloc;
@@ -462,7 +463,7 @@ __global__ __launch_bounds__(256) void prefill_gemm_kernel(PrefillArgs a) {
         const f32x4_t p0 = *reinterpret_cast<const f32x4_t*>(yr + part);
         const f32x4_t p1 = *reinterpret_cast<const f32x4_t*>(yr + part + 4);
         const float o[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-        const float2* rp = rope_s + tloc * kRopePitch + (8 * l16 & 63);
+        const float2* rp = rope_s + (tloc % kRopeTok) * kRopePitch + (8 * l16 & 63);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float2 cs = rp[e];
@@ -556,7 +557,7 @@ __global__ __launch_bounds__(256) void prefill_gemm_kernel(PrefillArgs a) {
   // request; then every thread builds dwords of (representative, channel)
   // items independently: stored whole when all 8 members are present, else
   // merged nibble-wise with an atomic and/or.
-  const int nvh = (head0 + 1 >= a.n_q + a.n_kv) ? ((head0 >= a.n_q + a.n_kv) ? 2 : 1) : 0;  // v heads in the tile
+  const int nvh = has_rope ? 0 : 2;  // v heads in the tile
   int* rep_list = reinterpret_cast<int*>(ybuf);  // [kTokPerWg] (tloc | mask << 8), then the count
   if (nvh > 0) {
     if (wave == 0) {
@@ -591,7 +592,7 @@ __global__ __launch_bounds__(256) void prefill_gemm_kernel(PrefillArgs a) {
     const int nrep = rep_list[kTokPerWg];
     const int nitems = nrep * kHd * nvh;
 #pragma unroll 4
-    for (int item = tid; item < nitems; item += 256) {
+    for (int item = tid; item < nitems; item += kThreads) {
       const int ch = item % kHd;
       const int rh = item / kHd;
       const int hl = 2 - nvh + rh % nvh;
@@ -602,8 +603,8 @@ __global__ __launch_bounds__(256) void prefill_gemm_kernel(PrefillArgs a) {
       const int jj = (w & 15) >> 2;
       const int t0 = tloc - ((w & 3) + (w >= 16 ? 16 : 0));
       const int kvh = head0 + hl - a.n_q - a.n_kv;
-      const int64_t region = ti.base + (int64_t)kvh * ti.cap;
-      uint32_t* dw = a.kv.v_codes + (size_t)(region / 32 + ti.pos / 32) * 4 * kHd + jj * kHd + (ch % 16) * (kHd / 16) +
+      const int64_t reg = ti.base + (int64_t)kvh * ti.cap;
+      uint32_t* dw = a.kv.v_codes + (size_t)(reg / 32 + ti.pos / 32) * 4 * kHd + jj * kHd + (ch % 16) * (kHd / 16) +
                      ch / 16;
       uint32_t word = 0, keep = 0;
 #pragma unroll
@@ -641,22 +642,22 @@ __global__ void fp8_scales_update_kernel(i4d_fp8_scales* s) {
 
 struct PrefillWs {
   size_t x8, sumsq, map, rope, total;
-  int T128, nch;
+  int Tpad, nch;
 };
 
 PrefillWs prefill_ws(const i4d_layer_shape& s, int T) {
   PrefillWs w;
-  w.T128 = ((T + kTokPerWg - 1) / kTokPerWg) * kTokPerWg;
+  w.Tpad = ((T + kTokPerWg - 1) / kTokPerWg) * kTokPerWg;
   w.nch = (groups_of(s.d_model) + kPrepGroups - 1) / kPrepGroups;
   size_t o = 0;
   w.x8 = o;
-  o = align256(o + (size_t)w.T128 * s.d_model);
+  o = align256(o + (size_t)w.Tpad * s.d_model);
   w.sumsq = o;
-  o = align256(o + (size_t)w.nch * w.T128 * sizeof(float));
+  o = align256(o + (size_t)w.nch * w.Tpad * sizeof(float));
   w.map = o;
-  o = align256(o + (size_t)w.T128 * sizeof(int2));
+  o = align256(o + (size_t)w.Tpad * sizeof(int2));
   w.rope = o;
-  o = align256(o + (size_t)w.T128 * 64 * sizeof(float2));
+  o = align256(o + (size_t)w.Tpad * 64 * sizeof(float2));
   w.total = o;
   return w;
 }
@@ -666,9 +667,9 @@ i4d_status check_prefill_shape(const i4d_layer_shape* s) {
   i4d_status st = check_shape(s);
   if (st != I4D_OK) return st;
   if (s->head_dim != kHd) return fail(I4D_ERR_UNSUPPORTED, "the FP8 prefill takes head_dim 128 (got %d)", s->head_dim);
-  if ((s->n_q_heads + 2 * s->n_kv_heads) % 2)
-    return fail(I4D_ERR_UNSUPPORTED, "the FP8 prefill needs an even number of q + k + v heads (%d)",
-                s->n_q_heads + 2 * s->n_kv_heads);
+  if (s->n_q_heads % 2 || s->n_kv_heads % 2)
+    return fail(I4D_ERR_UNSUPPORTED, "the FP8 prefill takes even numbers of q and kv heads (%d, %d)", s->n_q_heads,
+                s->n_kv_heads);
   return ok();
 }
 
@@ -692,7 +693,7 @@ namespace {
 
 // host checks shared by the three entry points; fills `a` (workspace
 // pointers included) and the workspace layout
-i4d_status prefill_args(const i4d_layer* layer, const i4d_kv_cache* cache, const uint16_t* x, int T,
+i4d_status prefill_args(const i4d_prefill_weights* layer, const i4d_kv_cache* cache, const uint16_t* x, int T,
                         const int32_t* cu_seqlens, const int32_t* start_pos, int R, i4d_fp8_scales* scales,
                         void* workspace, size_t workspace_bytes, bool need_x, PrefillArgs* a, PrefillWs* w) {
   if (!layer) return fail(I4D_ERR_NULL, "layer is NULL");
@@ -725,7 +726,7 @@ i4d_status prefill_args(const i4d_layer* layer, const i4d_kv_cache* cache, const
   a->rope_ratio = pow((double)s.rope_theta, -2.0 / (double)s.head_dim);
   a->x = x;
   a->T = T;
-  a->T128 = w->T128;
+  a->Tpad = w->Tpad;
   a->R = R;
   a->nch = w->nch;
   a->cu = cu_seqlens;
@@ -741,7 +742,7 @@ i4d_status prefill_args(const i4d_layer* layer, const i4d_kv_cache* cache, const
 }
 
 i4d_status launch_prep(const PrefillArgs& a, const PrefillWs& w, hipStream_t hs) {
-  hipLaunchKernelGGL(prefill_prep_kernel, dim3(w.T128 / 16, w.nch), dim3(256), 0, hs, a);
+  hipLaunchKernelGGL(prefill_prep_kernel, dim3(w.Tpad / 16, w.nch), dim3(256), 0, hs, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(I4D_ERR_HIP, "prefill prep launch: %s", hipGetErrorString(e));
   return ok();
@@ -756,8 +757,8 @@ i4d_status launch_gemm(PrefillArgs a, const PrefillWs& w, uint8_t* q_fp8, uint16
   a.q8 = q_fp8;
   a.k_bf16 = k_bf16;
   a.v_bf16 = v_bf16;
-  const int grid = (a.N / kRowsPerWg) * (w.T128 / kTokPerWg);
-  hipLaunchKernelGGL(prefill_gemm_kernel, dim3(grid), dim3(256), kGemmLds, hs, a);
+  const int grid = (a.N / kRowsPerWg) * (w.Tpad / kTokPerWg);
+  hipLaunchKernelGGL(prefill_gemm_kernel, dim3(grid), dim3(kThreads), kGemmLds, hs, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(I4D_ERR_HIP, "prefill gemm launch: %s", hipGetErrorString(e));
   return ok();
@@ -766,7 +767,7 @@ i4d_status launch_gemm(PrefillArgs a, const PrefillWs& w, uint8_t* q_fp8, uint16
 }  // namespace
 }  // namespace i4d
 
-extern "C" i4d_status i4d_prefill_prepare(const i4d_layer* layer, const i4d_kv_cache* cache, const uint16_t* x, int T,
+extern "C" i4d_status i4d_prefill_prepare(const i4d_prefill_weights* layer, const i4d_kv_cache* cache, const uint16_t* x, int T,
                                           const int32_t* cu_seqlens, const int32_t* start_pos, int R,
                                           i4d_fp8_scales* scales, void* workspace, size_t workspace_bytes,
                                           void* stream) {
@@ -778,7 +779,7 @@ extern "C" i4d_status i4d_prefill_prepare(const i4d_layer* layer, const i4d_kv_c
   return launch_prep(a, w, (hipStream_t)stream);
 }
 
-extern "C" i4d_status i4d_prefill_project(const i4d_layer* layer, const i4d_kv_cache* cache, int T,
+extern "C" i4d_status i4d_prefill_project(const i4d_prefill_weights* layer, const i4d_kv_cache* cache, int T,
                                           const int32_t* cu_seqlens, const int32_t* start_pos, int R,
                                           i4d_fp8_scales* scales, uint8_t* q_fp8, uint16_t* k_bf16,
                                           uint16_t* v_bf16, const void* workspace, size_t workspace_bytes,
@@ -791,7 +792,7 @@ extern "C" i4d_status i4d_prefill_project(const i4d_layer* layer, const i4d_kv_c
   return launch_gemm(a, w, q_fp8, k_bf16, v_bf16, (hipStream_t)stream);
 }
 
-extern "C" i4d_status i4d_prefill_qkv_e4m3(const i4d_layer* layer, const i4d_kv_cache* cache, const uint16_t* x,
+extern "C" i4d_status i4d_prefill_qkv_e4m3(const i4d_prefill_weights* layer, const i4d_kv_cache* cache, const uint16_t* x,
                                            int T, const int32_t* cu_seqlens, const int32_t* start_pos, int R,
                                            i4d_fp8_scales* scales, uint8_t* q_fp8, uint16_t* k_bf16,
                                            uint16_t* v_bf16, void* workspace, size_t workspace_bytes,

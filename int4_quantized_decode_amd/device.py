@@ -92,6 +92,18 @@ class DeviceLayer:
         return sum(c.numel() + 2 * s.numel() for c, s in self.tensors.values())
 
 
+class PrefillWeights:
+    """The FP8 prefill's QKV weight on the device: E4M3 atoms with E8M0 group
+    scales (i4d_pack_weights_mx, attention gain folded)."""
+
+    def __init__(self, shape: synth.LayerShape, lw: synth.LayerWeights, device="cuda", threads: int = 0):
+        codes, scales = B.i4d_pack_weights_mx(B.I4D_PROJ_QKV, lw.w_qkv, None, lw.gamma_attn, shape.head_dim, threads)
+        self.shape = shape
+        self.codes = torch.from_numpy(codes).to(device)
+        self.scales = torch.from_numpy(scales).to(device)
+        self.struct = B.i4d_prefill_weights(B.make_shape(shape), self.codes.data_ptr(), self.scales.data_ptr())
+
+
 class DeviceCache:
     """Paged INT4 KV cache: one row per decode row, capacity rounded up to 32."""
 

@@ -428,6 +428,43 @@ def test_e4m3_packer_bit_exact_full_layer(shape):
         np.testing.assert_array_equal(s, np.concatenate([r[1] for r in refs]).view(np.uint16))
 
 
+@pytest.mark.parametrize("shape", [synth.SHAPE_TINY, synth.SHAPE_SMALL128])
+def test_mx_packer_bit_exact(shape):
+    """Codes and E8M0 scale bytes of the prefill weight format equal the
+    oracle's encoding on every projection kind, and the edge cases: a zero
+    group, tiny and huge magnitudes, exact powers of two at 448 * 2^e."""
+    lw = synth.make_layer(shape, 11)
+    hd = shape.head_dim
+    W = lw.w_qkv.copy()
+    W[0, :128] = 0.0
+    W[1, :128] *= np.float32(1e-30)
+    W[2, :128] *= np.float32(1e30)
+    W[3, :128] = np.float32(448.0 * 2.0 ** -5)
+    W[4, 128:256] = -np.float32(2.0 ** -20)
+    cases = [
+        (B.I4D_PROJ_QKV, W, None, lw.gamma_attn, hd),
+        (B.I4D_PROJ_QKV, W, None, None, hd),
+        (B.I4D_PROJ_PLAIN, lw.w_o, None, None, 0),
+        (B.I4D_PROJ_GATE_UP, lw.w_gate, lw.w_up, lw.gamma_ffn, 0),
+    ]
+    for kind, W0, W1, g, h in cases:
+        codes, scales = B.i4d_pack_weights_mx(kind, W0, W1, g, h)
+        N, K = W0.shape
+        q, s = B.i4d_unpack_weights_mx(kind, codes, scales, N, K, h)
+        refs = [O.quantize_weight_e4m3_mx(W0, g)] + ([O.quantize_weight_e4m3_mx(W1, g)] if W1 is not None else [])
+        np.testing.assert_array_equal(q, np.concatenate([r[0] for r in refs]))
+        np.testing.assert_array_equal(s, np.concatenate([r[1] for r in refs]))
+    # the layout is the E4M3 atom layout: same code bytes as the E4M3 packer would place
+    codes, _ = B.i4d_pack_weights_mx(B.I4D_PROJ_PLAIN, lw.w_o, None, None, 0)
+    q_ref = O.quantize_weight_e4m3_mx(lw.w_o)[0]
+    N, K = lw.w_o.shape
+    for (n, k) in [(0, 0), (5, 131), (17, 255), (N - 1, K - 1)]:
+        t, r, gi, kk = n // 16, n % 16, k // 128, k % 128
+        kb, j, e = kk // 32, (kk % 32) // 8, kk % 8
+        off = ((t * (K // 128) + gi) * 64 + 16 * j + r) * 32 + kb * 8 + e
+        assert codes[off] == q_ref[n, k]
+
+
 def test_e4m3_packer_edge_values_and_layout():
     """Saturation, subnormals, ties, signed zeros and a zero group, against
     the oracle; and the documented byte position of (row, k) in an atom."""

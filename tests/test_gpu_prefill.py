@@ -51,11 +51,11 @@ def _layer(gpu, shape, seed):
     torch, B, D = gpu
     key = (shape, seed)
     if key not in _LAYERS:
-        say(f"packing E4M3 layer d={shape.d_model} seed={seed}")
+        say(f"packing the prefill weights d={shape.d_model} seed={seed}")
         lw = synth.make_layer(shape, seed)
-        qkv = O.quantize_weight_e4m3(lw.w_qkv, lw.gamma_attn)
+        qkv = O.quantize_weight_e4m3_mx(lw.w_qkv, lw.gamma_attn)
         _LAYERS.clear()
-        _LAYERS[key] = (lw, D.DeviceLayer(shape, lw, fmt="e4m3"), qkv, O.dense(qkv))
+        _LAYERS[key] = (lw, D.PrefillWeights(shape, lw), qkv, O.dense(qkv))
     return _LAYERS[key]
 
 
