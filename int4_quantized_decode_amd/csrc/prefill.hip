@@ -78,20 +78,18 @@ struct PrefillArgs {
   float2* rope;   // [Tpad][64] (cos, sin)
 };
 
-// OCP E4M3 code of a finite fp32 value: nearest, ties to even, saturating at
-// +-448, the sign kept on zero.  Normals round the fp32 mantissa to 3 bits
-// (the carry moves into the exponent); below 2^-6 the step is 2^-9.
-__device__ __forceinline__ uint32_t e4m3_code(float v) {
-  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
-  const float a = fminf(fabsf(v), 448.0f);
-  uint32_t mag;
-  if (a < 0.015625f) {
-    mag = (uint32_t)rintf(a * 512.0f);
-  } else {
-    const uint32_t b = __float_as_uint(a);
-    mag = ((b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20) - (120u << 3);
-  }
-  return sign | mag;
+// OCP E4M3 codes of four finite fp32 values (nearest, ties to even, the sign
+// kept on zero), bytes 0..3 of the result: gfx950's v_cvt_pk_fp8_f32 on
+// inputs clamped to +-448, which gives the saturating encoding (checked
+// against the format's definition on every fp16 value, on random values
+// and on every midpoint between neighbouring codes and its neighbours)
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  a = fminf(fmaxf(a, -448.0f), 448.0f);
+  b = fminf(fmaxf(b, -448.0f), 448.0f);
+  c = fminf(fmaxf(c, -448.0f), 448.0f);
+  d = fminf(fmaxf(d, -448.0f), 448.0f);
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 
 // rint(x / s) clamped to [-8, 7], plus 8, where x / s is the correctly
@@ -145,17 +143,16 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrefillArgs a) {
       const int k0 = 128 * g + 32 * (2 * h + half) + 8 * j;
       u32x4_t v = {0u, 0u, 0u, 0u};
       if (live) v = load16(a.x + (size_t)t * a.K + k0);
-      uint32_t w0 = 0, w1 = 0;
+      float q[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float f = (e & 1) ? bf16_hi(v[e >> 1]) : bf16_lo(v[e >> 1]);
         sq = fmaf(f, f, sq);
         amax = fmaxf(amax, fabsf(f));
-        const uint32_t c = e4m3_code(__fdiv_rn(f, sx));
-        if (e < 4) w0 |= c << (8 * e); else w1 |= c << (8 * (e - 4));
+        q[e] = __fdiv_rn(f, sx);
       }
-      out[2 * half] = w0;
-      out[2 * half + 1] = w1;
+      out[2 * half] = e4m3x4(q[0], q[1], q[2], q[3]);
+      out[2 * half + 1] = e4m3x4(q[4], q[5], q[6], q[7]);
     }
     const u32x4_t o = {out[0], out[1], out[2], out[3]};
     *reinterpret_cast<u32x4_t*>(a.x8 + ((((size_t)tile * a.G + g) * 2 + h) * 64 + lane) * 16) = o;
@@ -471,13 +468,10 @@ __global__ __launch_bounds__(kThreads) void prefill_gemm_kernel(PrefillArgs a) {
         }
       }
       if (is_q) {
-        uint32_t w0 = 0, w1 = 0;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          qmax = fmaxf(qmax, fabsf(y[e]));
-          const uint32_t code = e4m3_code(y[e] * rsq);
-          if (e < 4) w0 |= code << (8 * e); else w1 |= code << (8 * (e - 4));
-        }
+        for (int e = 0; e < 8; ++e) qmax = fmaxf(qmax, fabsf(y[e]));
+        const uint32_t w0 = e4m3x4(y[0] * rsq, y[1] * rsq, y[2] * rsq, y[3] * rsq);
+        const uint32_t w1 = e4m3x4(y[4] * rsq, y[5] * rsq, y[6] * rsq, y[7] * rsq);
         *reinterpret_cast<u32x2_t*>(a.q8 + ((size_t)t * a.n_q + head) * kHd + 8 * l16) = u32x2_t{w0, w1};
         continue;
       }
@@ -506,13 +500,14 @@ __global__ __launch_bounds__(kThreads) void prefill_gemm_kernel(PrefillArgs a) {
             x[e] = lo + hi;
             x[e | h] = lo - hi;
           }
+      // stages h = 8 .. 64 across lanes: x' = x + p (lower lane) or p - x
+      // (upper lane), both one rounded operation as fma(+-1, x, p)
 #pragma unroll
-      for (int m = 1; m < 16; m <<= 1)
+      for (int m = 1; m < 16; m <<= 1) {
+        const float sgn = (l16 & m) ? -1.0f : 1.0f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float pv = lane_xor(x[e], m, lane);
-          x[e] = (l16 & m) ? (pv - x[e]) : (x[e] + pv);
-        }
+        for (int e = 0; e < 8; ++e) x[e] = fmaf(sgn, x[e], lane_xor(x[e], m, lane));
+      }
       float am = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(x[e]));
