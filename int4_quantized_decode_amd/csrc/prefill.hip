@@ -226,9 +226,9 @@ struct TokInfo {
 // scales [16 strips][16 rows] (E8M0 bytes).  Epilogue (after the loop, over
 // the same bytes): fp32 tile [2 heads][32 tokens][kYPitch] and one region
 // that holds either the RoPE rotations of half the tile's tokens [128]
-// [kRopePitch] (q and k tiles) or the value codes [256 tokens][2 heads]
-// [128] (v tiles; a tile is one or the other when n_q and n_kv are even).
-// Token info [256] sits after both.
+// [kRopePitch] (tiles with a q or k head) and after them the value codes
+// [256 tokens][v heads][128] (tiles with a v head).  Token info [256] sits
+// after both.
 constexpr int kStages = 2;
 constexpr size_t kStageA = 16 * 2048;
 constexpr size_t kStageB = kTilesPerWg * 2048;
@@ -240,7 +240,9 @@ constexpr int kRopePitch = 72;  // float2 per token row: 64 pairs + 64 B so that
 constexpr int kRopeTok = 128;   // tokens whose rotations are in LDS at a time
 constexpr size_t kRopeBytes = (size_t)kRopeTok * kRopePitch * 8;
 constexpr size_t kVcodeBytes = (size_t)kTokPerWg * 2 * kHd;
-constexpr size_t kRegionBytes = kRopeBytes > kVcodeBytes ? kRopeBytes : kVcodeBytes;
+// a tile has RoPE rows and one v head's codes, or two v heads' codes
+constexpr size_t kRegionBytes =
+    kRopeBytes + kVcodeBytes / 2 > kVcodeBytes ? kRopeBytes + kVcodeBytes / 2 : kVcodeBytes;
 constexpr size_t kEpiBytes = kYBytes + kRegionBytes;
 constexpr size_t kShared = kRingBytes > kEpiBytes ? kRingBytes : kEpiBytes;
 constexpr size_t kGemmLds = kShared + kTokPerWg * sizeof(TokInfo);  // token info after the shared region
@@ -271,6 +273,20 @@ __device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds) {
       : "memory");
 }
 
+// The two heads of gemm tile n: the q heads paired with the k and v heads
+// first (q_i with kv head i, kv heads in k | v order), then the remaining
+// heads two by two, so that the tiles with the heavier k / v epilogue also
+// hold a q head and the epilogues even out.  Heads are numbered in the
+// packed QKV order (q | k | v), head h owns strips 8h .. 8h + 7.
+__device__ __forceinline__ int2 tile_heads(int n, int n_q, int n_kv) {
+  const int P = min(n_q, 2 * n_kv);
+  if (n < P) return make_int2(n, n_q + n);
+  // the rest in order: q heads P .. n_q - 1, then kv heads P .. 2 n_kv - 1
+  const int i = 2 * (n - P);
+  auto rest = [&](int k) { return k < n_q - P ? P + k : n_q + P + (k - (n_q - P)); };
+  return make_int2(rest(i), rest(i + 1));
+}
+
 // every vector-memory operation of the wave has completed
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xF << 8)); }
 
@@ -287,7 +303,9 @@ __global__ __launch_bounds__(kThreads) void prefill_gemm_kernel(PrefillArgs a) {
   // grouping whole weight tiles per XCD)
   const int b = blockIdx.x;
   const int ntile = b / t_tiles, ttile = b % t_tiles;
-  const int strip0 = ntile * (kRowsPerWg / 16);  // the workgroup's first strip
+  const int2 heads = tile_heads(ntile, a.n_q, a.n_kv);
+  // global strip of the tile's strip s (0..7: first head, 8..15: second)
+  auto gstrip = [&](int s) { return (s < 8 ? heads.x * 8 : heads.y * 8 - 8) + s; };
   const int tile16_0 = ttile * kTilesPerWg;
   const int tok0 = ttile * kTokPerWg;
   const uint32_t lds0 = lds_offset(smem);
@@ -302,7 +320,7 @@ __global__ __launch_bounds__(kThreads) void prefill_gemm_kernel(PrefillArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int p = wt * 4 + i, s = 4 * wn + (p >> 1), h = p & 1;
-      const uint8_t* src = a.codes + ((size_t)(strip0 + s) * G + g) * 2048 + lane * 32 + h * 16;
+      const uint8_t* src = a.codes + ((size_t)gstrip(s) * G + g) * 2048 + lane * 32 + h * 16;
       lds_dma16(src, sa + (uint32_t)((s * 2 + h) * 1024));
     }
 #pragma unroll
@@ -312,7 +330,7 @@ __global__ __launch_bounds__(kThreads) void prefill_gemm_kernel(PrefillArgs a) {
       lds_dma16(src, sb + (uint32_t)(p * 1024));
     }
     {
-      const uint8_t* src = a.scales + ((size_t)(strip0 + 4 * wn + (lane & 3)) * G + g) * 16;
+      const uint8_t* src = a.scales + ((size_t)gstrip(4 * wn + (lane & 3)) * G + g) * 16;
       if (wt == 0 && lane < 4) lds_dma16(src, ss + (uint32_t)(wn * 64));
     }
   };
@@ -389,9 +407,12 @@ __global__ __launch_bounds__(kThreads) void prefill_gemm_kernel(PrefillArgs a) {
   float* ybuf = reinterpret_cast<float*>(smem);
   unsigned char* region = smem + kYBytes;
   float2* rope_s = reinterpret_cast<float2*>(region);
-  uint8_t* vcodes = region;
-  const int head0 = ntile * 2;  // first of the workgroup's two heads (q | k | v order)
-  const bool has_rope = head0 < a.n_q + a.n_kv;
+  const int hv0 = heads.x >= a.n_q + a.n_kv, hv1 = heads.y >= a.n_q + a.n_kv;  // v heads
+  const int nvh = hv0 + hv1;
+  const bool has_rope = nvh < 2;  // a q or k head
+  uint8_t* vcodes = region + (has_rope ? kRopeBytes : 0);  // [token][v slot][128]
+  // the v slot of head hl (0 for the tile's only v head)
+  auto vslot = [&](int hl) { return nvh == 2 ? hl : 0; };
   // the RoPE rows of tokens [128 h, 128 h + 128) of the tile (q and k tiles)
   auto load_rope = [&](int h) {
     const uint32_t rb = lds_offset(rope_s);
@@ -441,7 +462,7 @@ __global__ __launch_bounds__(kThreads) void prefill_gemm_kernel(PrefillArgs a) {
       const int hl = vec >> 5, tl = vec & 31;
       const int tloc = 32 * c + tl;
       const int t = tok0 + tloc;
-      const int head = head0 + hl;
+      const int head = hl ? heads.y : heads.x;
       const bool is_q = head < a.n_q;
       const bool is_k = !is_q && head < a.n_q + a.n_kv;
       if (t >= a.T) continue;
@@ -538,7 +559,7 @@ __global__ __launch_bounds__(kThreads) void prefill_gemm_kernel(PrefillArgs a) {
           c0 |= u[e] << (8 * e);
           c1 |= u[e + 4] << (8 * e);
         }
-        *reinterpret_cast<u32x2_t*>(vcodes + ((size_t)tloc * 2 + hl) * kHd + 8 * l16) = u32x2_t{c0, c1};
+        *reinterpret_cast<u32x2_t*>(vcodes + ((size_t)tloc * nvh + vslot(hl)) * kHd + 8 * l16) = u32x2_t{c0, c1};
         if (l16 == 0) a.kv.v_scales[slot] = s16;
       }
     }
@@ -552,7 +573,6 @@ __global__ __launch_bounds__(kThreads) void prefill_gemm_kernel(PrefillArgs a) {
   // request; then every thread builds dwords of (representative, channel)
   // items independently: stored whole when all 8 members are present, else
   // merged nibble-wise with an atomic and/or.
-  const int nvh = has_rope ? 0 : 2;  // v heads in the tile
   int* rep_list = reinterpret_cast<int*>(ybuf);  // [kTokPerWg] (tloc | mask << 8), then the count
   if (nvh > 0) {
     if (wave == 0) {
@@ -590,14 +610,14 @@ __global__ __launch_bounds__(kThreads) void prefill_gemm_kernel(PrefillArgs a) {
     for (int item = tid; item < nitems; item += kThreads) {
       const int ch = item % kHd;
       const int rh = item / kHd;
-      const int hl = 2 - nvh + rh % nvh;
+      const int hl = nvh == 2 ? rh % 2 : hv1;  // the v head
       const int entry = rep_list[rh / nvh];
       const int tloc = entry & 0xFF, mask = entry >> 8;
       const TokInfo ti = tinfo[tloc];
       const int w = ti.pos & 31;
       const int jj = (w & 15) >> 2;
       const int t0 = tloc - ((w & 3) + (w >= 16 ? 16 : 0));
-      const int kvh = head0 + hl - a.n_q - a.n_kv;
+      const int kvh = (hl ? heads.y : heads.x) - a.n_q - a.n_kv;
       const int64_t reg = ti.base + (int64_t)kvh * ti.cap;
       uint32_t* dw = a.kv.v_codes + (size_t)(reg / 32 + ti.pos / 32) * 4 * kHd + jj * kHd + (ch % 16) * (kHd / 16) +
                      ch / 16;
@@ -607,7 +627,7 @@ __global__ __launch_bounds__(kThreads) void prefill_gemm_kernel(PrefillArgs a) {
         const int o = (q < 4) ? q : 12 + q;
         const int sh = 4 * (4 * (q & 1) + (q >> 1));
         if (mask & (1 << q)) {
-          word |= (uint32_t)vcodes[((size_t)(t0 + o) * 2 + hl) * kHd + ch] << sh;
+          word |= (uint32_t)vcodes[((size_t)(t0 + o) * nvh + vslot(hl)) * kHd + ch] << sh;
         } else {
           keep |= 0xFu << sh;
         }
