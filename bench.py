@@ -48,8 +48,8 @@ TRAFFIC = {
                       "sha256": "dd736fd30ba2815ed0a2343aa8f313573a3de8027da8205a94c62c4b5e5c4b0b",
                       "fetch_bytes": 118803584, "write_bytes": 751104},
     "8b_prefill_s2048": {"kernel": "prefill_gemm_kernel (FP8 MFMA GEMM + epilogue)", "sources": PREFILL_SOURCES,
-                         "sha256": "b0b167718cd5dcdf7d5d55047d58fc80b683b625177d3f810e651e5e220e2d0a",
-                         "fetch_bytes": 223922176, "write_bytes": 10584064},
+                         "sha256": "35f798cd3a2ade5426a57f6cf53b5e692e8fa57c248eca09256b9aab8b5d5c69",
+                         "fetch_bytes": 213150720, "write_bytes": 10600448},
 }
 
 
