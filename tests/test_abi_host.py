@@ -378,6 +378,17 @@ def test_every_projection_plan_has_a_kernel(shape):
                 assert p.waves == 8 and p.strips_per_workgroup in (1, 2, 3, 4, 5, 7)
 
 
+def test_one_launch_coverage():
+    """The M = 1 step of the 8B shape runs as one launch, more rows do not;
+    the 70B shape (FFN 28672, beyond the one-launch x staging of 16384) and
+    more than 16 kv heads keep one launch per stage."""
+    cs8 = B.make_shape(synth.SHAPE_8B)
+    assert B.i4d_decode_step_is_one_launch(cs8, 1) == 1
+    assert B.i4d_decode_step_is_one_launch(cs8, 2) == 0
+    for shape in (synth.SHAPE_70B, synth.LayerShape(4096, 32, 32, 128, 2048)):
+        assert B.i4d_decode_step_is_one_launch(B.make_shape(shape), 1) == 0
+
+
 def test_projection_plan_splits_large_k_only_with_many_rows():
     cs = B.make_shape(synth.SHAPE_8B)
     # down projection (K = 14336): unsplit at 16 rows, split at 32
