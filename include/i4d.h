@@ -379,7 +379,9 @@ i4d_status i4d_decode_block_step(const i4d_layer* layer, const i4d_kv_cache* cac
 
 /* Launch plan of one projection stage as i4d_decode_block_step runs it at M
  * rows (host only; diagnostics and tests).  stage: 0 QKV, 1 O, 2 gate/up,
- * 3 down.  kernel 0 = the M = 1 GEMV, 1 = the skinny MFMA kernel;
+ * 3 down.  kernel 0 = the M = 1 GEMV, 1 = the skinny MFMA kernel, 2 = the
+ * multi-row GEMV (M = 2..8: the M = 1 weight stream with the rows of x in the
+ * MFMA operand's rows, where its x staging fits);
  * instantiated = 1 when the library holds a kernel for the plan (a step
  * whose plan has none fails with I4D_ERR_UNSUPPORTED instead of launching
  * nothing).  I4D_ERR_UNSUPPORTED when the shape exceeds the kernels' limits

@@ -8,7 +8,9 @@
 //   as exact fp16 subnormals (the B operand of four f16 MFMA 16x16x32, one
 //   per 32 k) against range-scaled fp16 x, staged in LDS and broadcast to
 //   every row of the A operand, so each lane gets the dot of its atom row.
-// M = 2..32: skinny GEMM on bf16 MFMA 16x16x32, computed as
+// M = 2..8 (when x fits the kernel's staging): the same stream with rows
+//   0..M-1 of x in rows 0..M-1 of the A operand (gemv_rows.h).
+// Otherwise (M <= 32): skinny GEMM on bf16 MFMA 16x16x32, computed as
 //   sum_g s[n][g] * (A[n][g] - 136 * X[m][g]) where A accumulates
 //   (128 + u) * x from the bf16 magic-exponent decode of each nibble and X
 //   is the group sum of x (one more MFMA against ones); the scale and the
@@ -28,6 +30,7 @@
 
 #include "device_common.h"
 #include "gemv.h"
+#include "gemv_rows.h"
 #include "i4d_internal.h"
 #include "proj.h"
 
@@ -45,6 +48,15 @@ __global__ __launch_bounds__(NW * 64) void proj_gemv_kernel(ProjArgs a, GemvPlan
   const int nstrips = a.Np / kStrip;
   const int strip0 = blockIdx.x * pl.SP;
   gemv_body<EPI, NW, U, GPW, false>(a, pl, strip0, min(pl.SP, nstrips - strip0), smem, NoWait());
+}
+
+// M = 2..8: the M = 1 stream with x rows in the A operand's rows
+template <int EPI, int NW, int U, int GPW, int XMAX>
+__global__ __launch_bounds__(NW * 64) void proj_gemv_rows_kernel(ProjArgs a, GemvPlan pl) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int nstrips = a.Np / kStrip;
+  const int strip0 = blockIdx.x * pl.SP;
+  gemv_rows_body<EPI, NW, U, GPW, XMAX>(a, pl, strip0, min(pl.SP, nstrips - strip0), smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -511,6 +523,18 @@ static GemvPlan gemv_plan(int nstrips, int G) {
 }
 
 template <int EPI, int NW>
+static void launch_gemv_rows(const ProjArgs& a, const GemvPlan& p, size_t lds, int grid, hipStream_t st) {
+  constexpr int X = kRowsXMax;
+  switch (gemv_reg_groups(p, a.G)) {
+    case 1: hipLaunchKernelGGL((proj_gemv_rows_kernel<EPI, NW, 8, 1, X>), dim3(grid), dim3(NW * 64), lds, st, a, p); break;
+    case 2: hipLaunchKernelGGL((proj_gemv_rows_kernel<EPI, NW, 8, 2, X>), dim3(grid), dim3(NW * 64), lds, st, a, p); break;
+    case 4: hipLaunchKernelGGL((proj_gemv_rows_kernel<EPI, NW, 4, 4, X>), dim3(grid), dim3(NW * 64), lds, st, a, p); break;
+    default:
+      hipLaunchKernelGGL((proj_gemv_rows_kernel<EPI, NW, 8, 0, kRowsXMax>), dim3(grid), dim3(NW * 64), lds, st, a, p);
+  }
+}
+
+template <int EPI, int NW>
 static void launch_gemv(const ProjArgs& a, const GemvPlan& p, size_t lds, int grid, hipStream_t st) {
   // x in registers (GPW > 0) needs every wave to own exactly GPW groups
   if (a.G % NW != 0)
@@ -536,10 +560,11 @@ static size_t split_bytes_of(const ProjArgs& a) {
   return a.split_bytes;
 }
 
-// The launch shape of one projection: the M = 1 GEMV or the skinny MFMA
-// kernel, with its plan, LDS bytes and grid.
+// The launch shape of one projection: the M = 1 GEMV, the multi-row GEMV
+// (rows) or the skinny MFMA kernel, with its plan, LDS bytes and grid.
 struct ProjLaunch {
   bool gemv;
+  bool rows;  // gemv with 2..8 rows of x
   GemvPlan g;
   SkinnyPlan s;
   int T;         // 16-row x tiles (skinny)
@@ -556,7 +581,29 @@ static ProjLaunch plan_projection(const ProjArgs& a, bool rho) {
     l.g = gemv_plan(nstrips, a.G);
     l.lds = gemv_lds_bytes(a.K, l.g);
     l.grid = (nstrips + l.g.SP - 1) / l.g.SP;
-  } else {
+    return l;
+  }
+  // the multi-row GEMV for M <= 4, and up to 8 rows at K >= 8192, when
+  // its x staging fits (the scaled x of all rows in LDS, within kRowsXMax
+  // 16-byte chunks per thread).  Its staging grows with M * K per
+  // workgroup against a weight stream that grows with K: against the
+  // skinny kernel it measured faster at every M <= 8 on the 70B-shape
+  // layer (K 8192), and at M <= 4 only on the 8B shape (K 4096).
+  if (a.M <= 4 || (a.M <= kRowsMax && a.K >= 8192)) {
+    const GemvPlan g = gemv_plan(nstrips, a.G);
+    const int gpw_t = gemv_reg_groups(g, a.G);
+    const size_t lds = gemv_rows_lds_bytes(a.K, a.M, g, gpw_t);
+    const int xn = (a.M * (a.K / 8) + g.NW * 64 - 1) / (g.NW * 64);
+    if (lds <= (size_t)kMaxLdsBytes && xn <= kRowsXMax) {
+      l.gemv = true;
+      l.rows = true;
+      l.g = g;
+      l.lds = lds;
+      l.grid = (nstrips + g.SP - 1) / g.SP;
+      return l;
+    }
+  }
+  {
     l.T = a.M <= 16 ? 1 : 2;
     l.s = skinny_plan(nstrips, a.G, l.T, !rho, split_bytes_of(a));
     l.lds = l.s.SP ? skinny_lds_bytes(l.s.GPW, l.s.SP, l.T) : 0;
@@ -599,7 +646,16 @@ template <int EPI>
 static bool launch_epi(const ProjArgs& a, hipStream_t st, bool launch) {
   const ProjLaunch l = plan_projection(a, needs_rho<EPI>());
   if (l.gemv) {
-    if (!launch) return true;  // launch_gemv has a kernel for every plan
+    if (!launch) return true;  // launch_gemv(_rows) has a kernel for every plan
+    if (l.rows) {
+      if (l.g.NW == 16)
+        launch_gemv_rows<EPI, 16>(a, l.g, l.lds, l.grid, st);
+      else if (l.g.NW == 8)
+        launch_gemv_rows<EPI, 8>(a, l.g, l.lds, l.grid, st);
+      else
+        launch_gemv_rows<EPI, 4>(a, l.g, l.lds, l.grid, st);
+      return true;
+    }
     if (l.g.NW == 16)
       launch_gemv<EPI, 16>(a, l.g, l.lds, l.grid, st);
     else if (l.g.NW == 8)
@@ -624,7 +680,8 @@ static bool dispatch_epi(int epi, const ProjArgs& a, hipStream_t st, bool launch
 // shape limits of the kernels (message set when unsupported)
 static i4d_status projection_fits(const ProjArgs& a, const ProjLaunch& l) {
   if (l.gemv) {
-    if (l.lds > (size_t)kMaxLdsBytes || a.K > 4 * 8 * l.g.NW * 64)
+    // the multi-row plan is only chosen where its staging fits
+    if (!l.rows && (l.lds > (size_t)kMaxLdsBytes || a.K > 4 * 8 * l.g.NW * 64))
       return fail(I4D_ERR_UNSUPPORTED, "K=%d too large for the M=1 kernel (LDS %zu bytes)", a.K, l.lds);
   } else if (l.s.SP == 0) {
     return fail(I4D_ERR_UNSUPPORTED, "K=%d too large for the M>1 kernel", a.K);
@@ -651,7 +708,7 @@ i4d_status projection_plan_of(int epi, const ProjArgs& a, i4d_projection_plan* o
   const bool rho = epi == EPI_QKV || epi == EPI_GU;
   const ProjLaunch l = plan_projection(a, rho);
   *out = i4d_projection_plan{};
-  out->kernel = l.gemv ? 0 : 1;
+  out->kernel = l.gemv ? (l.rows ? 2 : 0) : 1;
   out->waves = l.gemv ? l.g.NW : kSkinnyWaves;
   out->strips_per_workgroup = l.gemv ? l.g.SP : l.s.SP;
   out->k_slices = l.gemv ? 1 : l.s.KS;

@@ -372,9 +372,9 @@ def test_every_projection_plan_has_a_kernel(shape):
         for stage in range(4):
             p = B.i4d_projection_plan_of(cs, stage, M)
             assert p.instantiated == 1, (M, stage, p.strips_per_workgroup, p.k_slices, p.depth, p.persistent)
-            assert p.kernel == (0 if M == 1 else 1)
+            assert p.kernel == 0 if M == 1 else (p.kernel in (1, 2) and (p.kernel == 1 or M <= 8))
             assert 0 < p.lds_bytes <= 160 * 1024 and p.grid >= 1
-            if M > 1:
+            if p.kernel == 1:
                 assert p.waves == 8 and p.strips_per_workgroup in (1, 2, 3, 4, 5, 7)
 
 
@@ -387,6 +387,23 @@ def test_one_launch_coverage():
     assert B.i4d_decode_step_is_one_launch(cs8, 2) == 0
     for shape in (synth.SHAPE_70B, synth.LayerShape(4096, 32, 32, 128, 2048)):
         assert B.i4d_decode_step_is_one_launch(B.make_shape(shape), 1) == 0
+
+
+def test_multi_row_gemv_plans():
+    """The multi-row GEMV runs at M = 2..4, and up to M = 8 where K >= 8192,
+    wherever its x staging fits: the 70B stages with K = 8192 at every M up
+    to 8, the 8B ones (K = 4096) to M = 4, and the down projections while
+    M x K fp16 fits the staging: 8B (K = 14336) to M = 4, 70B (K = 28672) at
+    M = 2 only."""
+    cs8, cs70 = B.make_shape(synth.SHAPE_8B), B.make_shape(synth.SHAPE_70B)
+    for M in range(2, 9):
+        for stage in range(3):
+            assert B.i4d_projection_plan_of(cs8, stage, M).kernel == (2 if M <= 4 else 1)
+            assert B.i4d_projection_plan_of(cs70, stage, M).kernel == 2
+        assert B.i4d_projection_plan_of(cs8, 3, M).kernel == (2 if M <= 4 else 1)
+        assert B.i4d_projection_plan_of(cs70, 3, M).kernel == (2 if M == 2 else 1)
+    for M in (9, 16, 32):
+        assert all(B.i4d_projection_plan_of(cs8, st, M).kernel == 1 for st in range(4))
 
 
 def test_projection_plan_splits_large_k_only_with_many_rows():

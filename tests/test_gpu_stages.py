@@ -192,8 +192,11 @@ def layers(gpu):
 
 
 @pytest.mark.parametrize("name", list(SHAPES))
-@pytest.mark.parametrize("M", [1, 2, 5, 16, 17, 32])
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 8, 16, 17, 32])
 def test_projection_stages(gpu, layers, name, M):
+    """Every projection stage against the oracle: M = 1 GEMV, the multi-row
+    GEMV (M = 2..8, x in registers or in LDS), the skinny kernel (M >= 9, and
+    where the multi-row staging does not fit)."""
     torch, B, D = gpu
     shape, layer, W = layers[name]
     rng = np.random.default_rng(M)
