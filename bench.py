@@ -45,8 +45,8 @@ PREFILL_SOURCES = ("prefill.hip", "gemv.h", "attn.h", "coherent.h", "device_comm
                    "i4d_layout.h", "../build.py")
 TRAFFIC = {
     "8b_m1_ctx4096": {"kernel": "step_m1_kernel (one-launch decode step)", "sources": STEP_M1_SOURCES,
-                      "sha256": "dd736fd30ba2815ed0a2343aa8f313573a3de8027da8205a94c62c4b5e5c4b0b",
-                      "fetch_bytes": 118803584, "write_bytes": 751104},
+                      "sha256": "b1e8c4671745dcf52aec3fd847949a3bd1396d0781bc9d25c0d39d99d6e2da4e",
+                      "fetch_bytes": 118799744, "write_bytes": 751104},
     "8b_prefill_s2048": {"kernel": "prefill_gemm_kernel (FP8 MFMA GEMM + epilogue)", "sources": PREFILL_SOURCES,
                          "sha256": "35f798cd3a2ade5426a57f6cf53b5e692e8fa57c248eca09256b9aab8b5d5c69",
                          "fetch_bytes": 213150720, "write_bytes": 10600448},
