@@ -45,8 +45,8 @@ PREFILL_SOURCES = ("prefill.hip", "gemv.h", "attn.h", "coherent.h", "device_comm
                    "i4d_layout.h", "../build.py")
 TRAFFIC = {
     "8b_m1_ctx4096": {"kernel": "step_m1_kernel (one-launch decode step)", "sources": STEP_M1_SOURCES,
-                      "sha256": "b1e8c4671745dcf52aec3fd847949a3bd1396d0781bc9d25c0d39d99d6e2da4e",
-                      "fetch_bytes": 118799744, "write_bytes": 751104},
+                      "sha256": "fa6ab10f4235d32a8aeef1bd3d57352cf54129e6fa09d10c6c433ca3df98e894",
+                      "fetch_bytes": 118826368, "write_bytes": 751104},
     "8b_prefill_s2048": {"kernel": "prefill_gemm_kernel (FP8 MFMA GEMM + epilogue)", "sources": PREFILL_SOURCES,
                          "sha256": "35f798cd3a2ade5426a57f6cf53b5e692e8fa57c248eca09256b9aab8b5d5c69",
                          "fetch_bytes": 213150720, "write_bytes": 10600448},
@@ -106,6 +106,47 @@ def gate_up_bytes(shape):
     return n // 2 + (n // 128) * 2
 
 
+TIMELINE_SLOTS = ["entry", "QKV strips stored", "attention units done", "attention outputs seen by O",
+                  "O strips stored", "barrier after O passed", "gate/up strips stored",
+                  "barrier after gate/up passed", "down strips stored"]
+
+
+def timeline(args, shape, M, layers, caches, x_in, x_out, ctx, maxL, splits, ws, step, torch, B):
+    """Per-stage timestamps of the one-launch step: each workgroup's readings
+    of the 100 MHz real-time counter, relative to the first workgroup's
+    entry in the same step; medians (and 90th percentiles) over steps and
+    workgroups.  Eager launches, so the gaps between steps are not those of
+    the timed graph."""
+    if args.weights != "int4" or not B.i4d_decode_step_is_one_launch(B.make_shape(shape), M):
+        print("bench.py --timeline: the workload does not run as the one-launch step", file=sys.stderr)
+        sys.exit(2)
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    per = ncu * B.I4D_STEP_STAMPS
+    n = max(args.steps, 1)
+    stamps = torch.zeros((n, per), dtype=torch.int64, device="cuda")
+    for i in range(args.warmup):
+        step(i)
+    C = len(layers)
+    for i in range(n):
+        B.i4d_decode_block_step_timeline(layers[i % C].struct, caches[i % C].struct, x_in, x_out, ctx, M, maxL,
+                                         splits, ws.buf, ws.nbytes, stamps[i], per)
+    torch.cuda.synchronize()
+    require_clean(caches, "timeline steps")
+    t = stamps.cpu().numpy().reshape(n, ncu, B.I4D_STEP_STAMPS)[:, :, :len(TIMELINE_SLOTS)].astype(np.int64)
+    rel = (t - t[:, :, :1].min(axis=1, keepdims=True)) * 0.01  # 100 MHz ticks -> us
+    med = np.median(rel.reshape(-1, len(TIMELINE_SLOTS)), axis=0)
+    p90 = np.percentile(rel.reshape(-1, len(TIMELINE_SLOTS)), 90, axis=0)
+    span = np.median(rel[:, :, -1].max(axis=1))
+    print("%-32s %10s %10s" % ("workgroup event", "median us", "p90 us"))
+    for name, a, b in zip(TIMELINE_SLOTS, med, p90):
+        print("%-32s %10.2f %10.2f" % (name, a, b))
+    print("%-32s %10.2f" % ("last workgroup done (median)", span))
+    print(json.dumps({"timeline": {k: round(float(v), 3) for k, v in zip(TIMELINE_SLOTS, med)},
+                      "timeline_p90": {k: round(float(v), 3) for k, v in zip(TIMELINE_SLOTS, p90)},
+                      "last_done_us": round(float(span), 3), "steps": n, "workgroups": ncu,
+                      "workload": args.workload}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -122,6 +163,9 @@ def main():
                          "step's query, no append)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-steps", type=int, default=5)
+    ap.add_argument("--timeline", action="store_true",
+                    help="instead of timing: per-stage timestamps of the one-launch step (M = 1) over --steps "
+                         "eager steps (i4d_decode_block_step_timeline), medians over steps and workgroups")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (the reference "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -193,6 +237,8 @@ def main():
     # eager check that the step runs, then graphs
     step(0)
     torch.cuda.synchronize()
+    if args.timeline:
+        return timeline(args, shape, M, layers, caches, x_in, x_out, ctx, maxL, splits, ws, step, torch, B)
     if args.stage == "attention":
         # the attention launch alone on the query the step left in the
         # workspace (the caches already hold the step's token: no append)

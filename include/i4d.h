@@ -377,6 +377,25 @@ i4d_status i4d_decode_block_step(const i4d_layer* layer, const i4d_kv_cache* cac
                                  int M, int max_ctx_len, int num_splits, void* workspace,
                                  size_t workspace_bytes, float* attn_f32, void* stream);
 
+/* The one-launch decode step (M = 1) with a timeline: as
+ * i4d_decode_block_step, and each of its workgroups (one per compute unit,
+ * n_cu of them) stores I4D_STEP_STAMPS readings of the device's 100 MHz
+ * real-time counter into stamps[workgroup][slot] (device uint64, at least
+ * n_cu * I4D_STEP_STAMPS values; n_cu is the device's compute-unit count):
+ * 0 entry, 1 its QKV strips stored and counted, 2 its attention units done,
+ * 3 the wait for every head's attention output passed, 4 its O strips
+ * stored, 5 the barrier after O passed, 6 its gate/up strips stored, 7 the
+ * barrier after gate/up passed, 8 its down strips stored; slot 9 is unused.
+ * For diagnostics: the stamps add a few stores and one workgroup barrier.
+ * I4D_ERR_UNSUPPORTED for M > 1 or shapes the one-launch step does not
+ * cover. */
+#define I4D_STEP_STAMPS 10
+i4d_status i4d_decode_block_step_timeline(const i4d_layer* layer, const i4d_kv_cache* cache,
+                                          const uint16_t* x_in, uint16_t* x_out, const int32_t* ctx_len,
+                                          int M, int max_ctx_len, int num_splits, void* workspace,
+                                          size_t workspace_bytes, float* attn_f32, uint64_t* stamps,
+                                          size_t stamps_count, void* stream);
+
 /* Launch plan of one projection stage as i4d_decode_block_step runs it at M
  * rows (host only; diagnostics and tests).  stage: 0 QKV, 1 O, 2 gate/up,
  * 3 down.  kernel 0 = the M = 1 GEMV, 1 = the skinny MFMA kernel, 2 = the

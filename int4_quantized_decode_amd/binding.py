@@ -26,6 +26,7 @@ I4D_DEVERR_CTX_LEN = 2
 I4D_DEVERR_SYNC = 4
 I4D_DEVERR_SCALE = 8
 I4D_NOALLOC_SCRATCH_BYTES = 16 << 20
+I4D_STEP_STAMPS = 10
 
 STATUS_NAMES = {0: "I4D_OK", -1: "I4D_ERR_NULL", -2: "I4D_ERR_SHAPE", -3: "I4D_ERR_UNSUPPORTED",
                 -4: "I4D_ERR_ALIGN", -5: "I4D_ERR_WORKSPACE", -6: "I4D_ERR_RANGE", -7: "I4D_ERR_HIP"}
@@ -115,6 +116,9 @@ _SIGS = {
                                    _I, _I, _I, _VP, ctypes.c_size_t, _VP, _VP]),
     "i4d_decode_block_step_e4m3": (_I, [ctypes.POINTER(i4d_layer), ctypes.POINTER(i4d_kv_cache), _VP, _VP, _VP,
                                         _I, _I, _I, _VP, ctypes.c_size_t, _VP, _VP]),
+    "i4d_decode_block_step_timeline": (_I, [ctypes.POINTER(i4d_layer), ctypes.POINTER(i4d_kv_cache), _VP, _VP,
+                                            _VP, _I, _I, _I, _VP, ctypes.c_size_t, _VP, _VP, ctypes.c_size_t,
+                                            _VP]),
     "i4d_attn_out_proj_e4m3": (_I, [ctypes.POINTER(i4d_layer), _VP, _VP, _I, _VP, _VP, _VP]),
     "i4d_decode_block_step_noalloc": (_I, [ctypes.POINTER(i4d_layer), ctypes.POINTER(i4d_kv_cache), _VP, _VP,
                                            _VP, _I, _I, _I, _VP, _VP]),
@@ -415,6 +419,15 @@ def i4d_decode_block_step(layer: i4d_layer, cache: i4d_kv_cache, x_in, x_out, ct
     _check(lib().i4d_decode_block_step(ctypes.byref(layer), ctypes.byref(cache), ptr(x_in), ptr(x_out),
                                        ptr(ctx_len), M, max_ctx_len, num_splits, ptr(workspace),
                                        workspace_bytes, ptr(attn_f32), stream_handle(stream)))
+
+
+def i4d_decode_block_step_timeline(layer: i4d_layer, cache: i4d_kv_cache, x_in, x_out, ctx_len, M: int,
+                                   max_ctx_len: int, num_splits: int, workspace, workspace_bytes: int, stamps,
+                                   stamps_count: int, attn_f32=None, stream=None):
+    _check(lib().i4d_decode_block_step_timeline(ctypes.byref(layer), ctypes.byref(cache), ptr(x_in), ptr(x_out),
+                                                ptr(ctx_len), M, max_ctx_len, num_splits, ptr(workspace),
+                                                workspace_bytes, ptr(attn_f32), ptr(stamps), stamps_count,
+                                                stream_handle(stream)))
 
 
 def i4d_decode_block_step_e4m3(layer: i4d_layer, cache: i4d_kv_cache, x_in, x_out, ctx_len, M: int,

@@ -229,7 +229,7 @@ i4d_status check_decode_step(const i4d_layer* layer, const i4d_kv_cache* cache, 
 i4d_status run_decode_step(const i4d_layer* layer, const i4d_kv_cache* cache, const uint16_t* x_in,
                            uint16_t* x_out, const int32_t* ctx_len, int M, int max_ctx_len, int num_splits,
                            char* ws, const i4d_workspace_layout& wl, size_t split_part_bytes, float* attn_f32,
-                           hipStream_t st, int fmt) {
+                           hipStream_t st, int fmt, uint64_t* stamps) {
   float* q = (float*)(ws + wl.q);
   uint16_t* k = (uint16_t*)(ws + wl.k);
   uint16_t* v = (uint16_t*)(ws + wl.v);
@@ -249,6 +249,7 @@ i4d_status run_decode_step(const i4d_layer* layer, const i4d_kv_cache* cache, co
     in.attn = attention_args(cache, s, q, ctx_len, 1, max_ctx_len, step_m1_splits(&s, max_ctx_len, num_splits),
                              ws + wl.attn_ws, attn_f32, attn, k, v);
     in.sync = (unsigned*)(ws + wl.sync);
+    in.stamps = stamps;
     return launch_step_m1(in, st);
   }
   // the projections may split K across workgroups through the workspace
@@ -382,6 +383,29 @@ i4d_status i4d_decode_block_step(const i4d_layer* layer, const i4d_kv_cache* cac
     return fail(I4D_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, wl.total);
   return run_decode_step(layer, cache, x_in, x_out, ctx_len, M, max_ctx_len, num_splits, (char*)workspace, wl,
                          wl.sync - wl.split_part, attn_f32, (hipStream_t)stream, kFmtInt4);
+}
+
+i4d_status i4d_decode_block_step_timeline(const i4d_layer* layer, const i4d_kv_cache* cache, const uint16_t* x_in,
+                                          uint16_t* x_out, const int32_t* ctx_len, int M, int max_ctx_len,
+                                          int num_splits, void* workspace, size_t workspace_bytes, float* attn_f32,
+                                          uint64_t* stamps, size_t stamps_count, void* stream) {
+  i4d_workspace_layout wl;
+  I4D_TRY(check_decode_step(layer, cache, x_in, x_out, ctx_len, M, max_ctx_len, num_splits, attn_f32, &wl));
+  I4D_TRY(need(workspace, "workspace"));
+  if (workspace_bytes < wl.total)
+    return fail(I4D_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, wl.total);
+  if (M != 1 || !step_m1_supported(&layer->shape))
+    return fail(I4D_ERR_UNSUPPORTED, "the timeline covers the one-launch step (M = 1, a shape it supports)");
+  I4D_TRY(need(stamps, "stamps"));
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return fail(I4D_ERR_HIP, "device query failed");
+  if (stamps_count < (size_t)cus * I4D_STEP_STAMPS)
+    return fail(I4D_ERR_RANGE, "stamps holds %zu values, the step needs %d x %d", stamps_count, cus,
+                I4D_STEP_STAMPS);
+  return run_decode_step(layer, cache, x_in, x_out, ctx_len, M, max_ctx_len, num_splits, (char*)workspace, wl,
+                         wl.sync - wl.split_part, attn_f32, (hipStream_t)stream, kFmtInt4, stamps);
 }
 
 i4d_status i4d_decode_block_step_e4m3(const i4d_layer* layer, const i4d_kv_cache* cache, const uint16_t* x_in,

@@ -53,11 +53,23 @@ constexpr int kSyncErr = 52 * kLine;      // sticky timeout flag (not cleared)
 // waves per workgroup: 8 (one workgroup per CU, 256 registers per lane)
 constexpr int kStepWaves = 8;
 
+// Timeline of a workgroup (optional): the 100 MHz real-time counter at
+// entry, QKV stored and counted, attention units done, O's wait passed, O
+// stored, gate/up's wait passed, gate/up stored, down's wait passed, down
+// stored; read by thread 0 (in the wait hooks after their barrier), stored
+// by a vector store.
+static_assert(kStepStamps == 10, "stamp slots");
+__device__ __forceinline__ void stamp(uint64_t* stamps, int slot) {
+  if (stamps && threadIdx.x == 0)
+    stamps[(size_t)blockIdx.x * kStepStamps + slot] = __builtin_amdgcn_s_memrealtime();
+}
+
 struct StepArgs {
   ProjArgs qkv, o, gu, down;
   GemvPlan pq, po, pg, pd;
   AttnArgs at;
   unsigned* sync;
+  uint64_t* stamps;  // optional: kStepStamps timestamps per workgroup
   int32_t* err_word;  // optional (the cache's)
   int n_kv, G, hd, Sf;
 };
@@ -118,6 +130,7 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_m1_kernel(StepArgs sa) {
   constexpr int UD = 4;
   const int tid = threadIdx.x;
   const int wg = blockIdx.x, nwg = gridDim.x;
+  stamp(sa.stamps, 0);
   // the attention units' row metadata (one row), read now so that its
   // latency overlaps the QKV stage
   RowMeta meta;
@@ -141,6 +154,7 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_m1_kernel(StepArgs sa) {
         for (int t = s0; t < s0 + ns; ++t)
           atomic_add_agent(&sync[kSyncQkv + kLine * strip_kv_head(t, hd, pa.n_q, n_kv, G)], 1u);
     }
+    stamp(A->stamps, 1);
   }
 
   // ---- 2. attention units (kv head j, split s), head-interleaved
@@ -181,6 +195,7 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_m1_kernel(StepArgs sa) {
         atomic_add_agent(&sync[kSyncAttnDone], 1u);
       }
     }
+    stamp(A->stamps, 2);
   }
 
   // ---- 3. O + residual (waits for every kv head's attention output)
@@ -197,6 +212,7 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_m1_kernel(StepArgs sa) {
       if (tid == (NW - 1) * 64 && !spin_geq(&sync[kSyncAttnDone], (unsigned)n_kv, &sync[kSyncErr], 1u))
         flag_error(sync, err_word);
       lds_barrier();
+      stamp(A->stamps, 3);
     };
     __syncthreads();
     // the first ring of atoms (with one strip per workgroup, the whole O
@@ -204,6 +220,7 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_m1_kernel(StepArgs sa) {
     if (ns > 0) gemv_body<EPI_O, NW, UO, GQ, true, true>(pa, pl, s0, ns, smem, wait_attn);
     stores_done();
     if (tid == 0) bar_arrive(&sync[kSyncBar1], wg);
+    stamp(A->stamps, 4);
   }
 
   // ---- 4. gate/up + SwiGLU (after every O strip)
@@ -218,11 +235,13 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_m1_kernel(StepArgs sa) {
     auto wait_o = [&] {
       if (tid == (NW - 1) * 64 && !bar_wait(&sync[kSyncBar1], nwg, &sync[kSyncErr])) flag_error(sync, err_word);
       lds_barrier();
+      stamp(A->stamps, 5);
     };
     __syncthreads();
     if (ns > 0) gemv_body<EPI_GU, NW, UQ, GQ, true>(pa, pl, s0, ns, smem, wait_o);
     stores_done();
     if (tid == 0) bar_arrive(&sync[kSyncBar2], wg);
+    stamp(A->stamps, 6);
   }
 
   // ---- 5. down + residual (after every gate/up strip)
@@ -237,6 +256,7 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_m1_kernel(StepArgs sa) {
     auto wait_gu = [&] {
       if (tid == (NW - 1) * 64 && !bar_wait(&sync[kSyncBar2], nwg, &sync[kSyncErr])) flag_error(sync, err_word);
       lds_barrier();
+      stamp(A->stamps, 7);
     };
     __syncthreads();
     // the first ring of atoms is requested before the barrier: gate/up
@@ -245,6 +265,10 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_m1_kernel(StepArgs sa) {
     // arrived when the wait ends (on the gate/up stage the same measured
     // slower: its wait is short)
     if (ns > 0) gemv_body<EPI_DOWN, NW, UD, GD, true, true>(pa, pl, s0, ns, smem, wait_gu);
+    if (A->stamps) {  // timeline only: every wave's down strips stored
+      __syncthreads();
+      stamp(A->stamps, 8);
+    }
   }
 
   // ---- exit: the last workgroup clears the counters for the next launch
@@ -344,6 +368,7 @@ i4d_status launch_step_m1(const StepInputs& in, hipStream_t st) {
   sa.down = in.down;
   sa.at = in.attn;
   sa.sync = in.sync;
+  sa.stamps = in.stamps;
   sa.err_word = in.attn.kv.err_word;
   sa.n_kv = s.n_kv_heads;
   sa.G = s.n_q_heads / s.n_kv_heads;

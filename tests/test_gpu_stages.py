@@ -382,6 +382,40 @@ def test_block_m1_one_launch(gpu, shape, L):
     assert torch.equal(first, res["x_out"])
 
 
+def test_block_m1_timeline(gpu):
+    """The one-launch step with its timeline writes the same outputs as
+    without; every workgroup stamps entry, its QKV, attention, O, gate/up
+    and down ends in order (the waits' stamps, taken only by workgroups
+    with strips in that stage, fall between their neighbours); M > 1 is
+    refused."""
+    torch, B, D = gpu
+    shape = ONE_LAUNCH_SHAPES[0]
+    res = run_block(gpu, shape, 23, [300])
+    first = res["x_out"].clone()
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    per = ncu * B.I4D_STEP_STAMPS
+    stamps = torch.zeros(per, dtype=torch.int64, device="cuda")
+    say("one-launch step with timeline")
+    B.i4d_decode_block_step_timeline(res["layer"].struct, res["cache"].struct, res["x_in"], res["x_out"],
+                                     res["ctx"], 1, 300, 0, res["ws"].buf, res["ws"].nbytes, stamps, per)
+    torch.cuda.synchronize()
+    assert res["cache"].errors() == 0
+    assert torch.equal(first, res["x_out"])
+    t = stamps.cpu().numpy().reshape(ncu, B.I4D_STEP_STAMPS)
+    always = t[:, [0, 1, 2, 4, 6, 8]]
+    assert (always > 0).all()
+    assert (np.diff(always, axis=1) >= 0).all()
+    for w, lo, hi in ((3, 2, 4), (5, 4, 6), (7, 6, 8)):
+        seen = t[:, w] > 0
+        assert ((t[seen, w] >= t[seen, lo]) & (t[seen, w] <= t[seen, hi])).all()
+    with pytest.raises(B.I4DError):
+        B.i4d_decode_block_step_timeline(res["layer"].struct, res["cache"].struct, res["x_in"], res["x_out"],
+                                         res["ctx"], 2, 300, 0, res["ws"].buf, res["ws"].nbytes, stamps, per)
+    with pytest.raises(B.I4DError):
+        B.i4d_decode_block_step_timeline(res["layer"].struct, res["cache"].struct, res["x_in"], res["x_out"],
+                                         res["ctx"], 1, 300, 0, res["ws"].buf, res["ws"].nbytes, stamps, per - 1)
+
+
 # d_ffn 16384: at M >= 17 each unsplit down workgroup would read more than
 # 512 KiB of the activation, so the down projection splits K across
 # workgroups through the workspace (partial tiles + arrival counters)
