@@ -132,10 +132,13 @@ def timeline(args, shape, M, layers, caches, x_in, x_out, ctx, maxL, splits, ws,
                                          splits, ws.buf, ws.nbytes, stamps[i], per)
     torch.cuda.synchronize()
     require_clean(caches, "timeline steps")
-    t = stamps.cpu().numpy().reshape(n, ncu, B.I4D_STEP_STAMPS)[:, :, :len(TIMELINE_SLOTS)].astype(np.int64)
+    t_all = stamps.cpu().numpy().reshape(n, ncu, B.I4D_STEP_STAMPS).astype(np.int64)
+    t = t_all[:, :, :len(TIMELINE_SLOTS)]
     rel = (t - t[:, :, :1].min(axis=1, keepdims=True)) * 0.01  # 100 MHz ticks -> us
     med = np.median(rel.reshape(-1, len(TIMELINE_SLOTS)), axis=0)
     p90 = np.percentile(rel.reshape(-1, len(TIMELINE_SLOTS)), 90, axis=0)
+    if args.timeline_out:
+        np.save(args.timeline_out, (t_all - t[:, :, :1].min(axis=1, keepdims=True)) * 0.01)
     span = np.median(rel[:, :, -1].max(axis=1))
     print("%-32s %10s %10s" % ("workgroup event", "median us", "p90 us"))
     for name, a, b in zip(TIMELINE_SLOTS, med, p90):
@@ -166,6 +169,9 @@ def main():
     ap.add_argument("--timeline", action="store_true",
                     help="instead of timing: per-stage timestamps of the one-launch step (M = 1) over --steps "
                          "eager steps (i4d_decode_block_step_timeline), medians over steps and workgroups")
+    ap.add_argument("--timeline-out", default="",
+                    help="with --timeline: also save every stamp (us from the step's first entry, "
+                         "[steps][workgroups][slots]; a slot never stamped reads negative) to this .npy file")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (the reference "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
