@@ -45,7 +45,7 @@ AttnPlan attn_plan(const i4d_layer_shape* s, int M, int max_ctx_len, int num_spl
 int step_m1_splits(const i4d_layer_shape* s, int max_ctx_len, int num_splits);
 
 // size of the sync region of the decode-step workspace (zero before first use)
-constexpr size_t kStepSyncBytes = 8192;
+constexpr size_t kStepSyncBytes = 16384;
 
 struct AttnWs {
   size_t ml;      // fp32 [M][n_q][S][2]   (running max in log2 units, sum)

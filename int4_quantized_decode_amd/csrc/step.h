@@ -12,7 +12,7 @@ struct StepInputs {
   const i4d_layer* layer;
   ProjArgs qkv, o, gu, down;  // as for the stage kernels (M = 1)
   AttnArgs attn;              // S = step_m1_splits(...)
-  unsigned* sync;             // kStepSyncBytes, zero on entry; left zero on exit
+  unsigned* sync;             // kStepSyncBytes, zero before the first launch (the step keeps it usable)
   uint64_t* stamps = nullptr;  // optional timeline, kStepStamps per workgroup
 };
 

@@ -24,7 +24,9 @@
 //   3. O strips (+ residual): wait for all kv heads; then a grid barrier.
 //   4. gate/up strips (+ rho2, SwiGLU): after the barrier; barrier again.
 //   5. down strips (+ residual) -> x_out.
-// The last workgroup to finish clears the counters for the next launch.
+// The counters sit in one of two banks that alternate between launches; the
+// first workgroup clears the other bank and, at its end, advances the epoch
+// that selects the bank.
 // Every wait is bounded: a timeout sets I4D_DEVERR_SYNC and the step runs
 // on (with wrong results) instead of hanging.
 #include <math.h>
@@ -39,16 +41,22 @@
 
 namespace i4d {
 
-// word offsets in the sync region (one 128-byte line per counter)
+// word offsets in the sync region (one 128-byte line per counter).  The
+// counters come in two banks used by alternate launches (the launch's
+// epoch selects one): the first workgroup clears the other bank, which the
+// previous launch has finished with, while this launch runs, so no launch
+// ends with a barrier of all its workgroups to clear its own counters.
 constexpr int kLine = 32;
 constexpr int kSyncQkv = 0;               // [n_kv] finished QKV strips per kv head
 constexpr int kSyncAttn = 16 * kLine;     // [n_kv] finished attention splits per kv head
 constexpr int kSyncAttnDone = 32 * kLine; // kv heads whose attention output is written
 constexpr int kSyncBar1 = 33 * kLine;     // 8 group counters (after O)
 constexpr int kSyncBar2 = 42 * kLine;     // 8 group counters (after gate/up)
-constexpr int kSyncExit = 51 * kLine;
-constexpr int kSyncWords = 52 * kLine;    // cleared at exit
-constexpr int kSyncErr = 52 * kLine;      // sticky timeout flag (not cleared)
+constexpr int kBankLines = 51;            // counter lines of one bank
+constexpr int kBankWords = 52 * kLine;    // bank stride
+constexpr int kSyncErr = 2 * kBankWords;          // sticky timeout flag (never cleared)
+constexpr int kSyncEpoch = 2 * kBankWords + kLine; // completed launches (selects the bank)
+static_assert((kSyncEpoch + 1) * 4 <= (int)kStepSyncBytes, "sync region");
 
 // waves per workgroup: 8 (one workgroup per CU, 256 registers per lane)
 constexpr int kStepWaves = 8;
@@ -87,8 +95,8 @@ __device__ __forceinline__ int strip_kv_head(int t, int hd, int n_q, int n_kv, i
   return head - n_q - n_kv;
 }
 
-__device__ __forceinline__ void flag_error(unsigned* sync, int32_t* err_word) {
-  atomicOr(&sync[kSyncErr], 1u);
+__device__ __forceinline__ void flag_error(unsigned* err, int32_t* err_word) {
+  atomicOr(err, 1u);
   if (err_word) atomicOr(err_word, I4D_DEVERR_SYNC);
 }
 
@@ -131,6 +139,11 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_m1_kernel(StepArgs sa) {
   const int tid = threadIdx.x;
   const int wg = blockIdx.x, nwg = gridDim.x;
   stamp(sa.stamps, 0);
+  // this launch's counter bank; the first workgroup clears the other one
+  const unsigned epoch = ld_coh(&sa.sync[kSyncEpoch]);
+  unsigned* const bank = sa.sync + (epoch & 1u) * kBankWords;
+  unsigned* const err = sa.sync + kSyncErr;
+  if (wg == 0 && tid < kBankLines) st_coh(&sa.sync[((epoch & 1u) ^ 1u) * kBankWords + tid * kLine], 0u);
   // the attention units' row metadata (one row), read now so that its
   // latency overlaps the QKV stage
   RowMeta meta;
@@ -143,7 +156,7 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_m1_kernel(StepArgs sa) {
     const StepArgs* A = &sa;
     const ProjArgs pa = A->qkv;
     const GemvPlan pl = A->pq;
-    unsigned* sync = A->sync;
+    unsigned* sync = bank;
     const int hd = A->hd, n_kv = A->n_kv, G = A->G;
     int s0, ns;
     strip_range(pa.Np / kStrip, wg, nwg, s0, ns);
@@ -161,7 +174,7 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_m1_kernel(StepArgs sa) {
   {
     const StepArgs* A = &sa;
     const AttnArgs at = A->at;
-    unsigned* sync = A->sync;
+    unsigned* sync = bank;
     int32_t* err_word = A->err_word;
     const int n_kv = A->n_kv, G = A->G, Sf = A->Sf;
     const int units = n_kv * Sf;
@@ -170,8 +183,8 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_m1_kernel(StepArgs sa) {
       const int j = u % n_kv, s = u / n_kv;
       __syncthreads();  // LDS reuse
       auto wait_qkv = [&] {
-        if (tid == 0 && !spin_geq(&sync[kSyncQkv + kLine * j], need, &sync[kSyncErr], 1u))
-          flag_error(sync, err_word);
+        if (tid == 0 && !spin_geq(&sync[kSyncQkv + kLine * j], need, err, 1u))
+          flag_error(err, err_word);
         lds_barrier();
       };
       attn_body<HD, NW, true>(at, 0, j, s, reinterpret_cast<float*>(smem), wait_qkv, &meta);
@@ -203,14 +216,14 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_m1_kernel(StepArgs sa) {
     const StepArgs* A = &sa;
     const ProjArgs pa = A->o;
     const GemvPlan pl = A->po;
-    unsigned* sync = A->sync;
+    unsigned* sync = bank;
     int32_t* err_word = A->err_word;
     const int n_kv = A->n_kv;
     int s0, ns;
     strip_range(pa.Np / kStrip, wg, nwg, s0, ns);
     auto wait_attn = [&] {
-      if (tid == (NW - 1) * 64 && !spin_geq(&sync[kSyncAttnDone], (unsigned)n_kv, &sync[kSyncErr], 1u))
-        flag_error(sync, err_word);
+      if (tid == (NW - 1) * 64 && !spin_geq(&sync[kSyncAttnDone], (unsigned)n_kv, err, 1u))
+        flag_error(err, err_word);
       lds_barrier();
       stamp(A->stamps, 3);
     };
@@ -228,12 +241,12 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_m1_kernel(StepArgs sa) {
     const StepArgs* A = &sa;
     const ProjArgs pa = A->gu;
     const GemvPlan pl = A->pg;
-    unsigned* sync = A->sync;
+    unsigned* sync = bank;
     int32_t* err_word = A->err_word;
     int s0, ns;
     strip_range(pa.Np / kStrip, wg, nwg, s0, ns);
     auto wait_o = [&] {
-      if (tid == (NW - 1) * 64 && !bar_wait(&sync[kSyncBar1], nwg, &sync[kSyncErr])) flag_error(sync, err_word);
+      if (tid == (NW - 1) * 64 && !bar_wait(&sync[kSyncBar1], nwg, err)) flag_error(err, err_word);
       lds_barrier();
       stamp(A->stamps, 5);
     };
@@ -249,12 +262,12 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_m1_kernel(StepArgs sa) {
     const StepArgs* A = &sa;
     const ProjArgs pa = A->down;
     const GemvPlan pl = A->pd;
-    unsigned* sync = A->sync;
+    unsigned* sync = bank;
     int32_t* err_word = A->err_word;
     int s0, ns;
     strip_range(pa.Np / kStrip, wg, nwg, s0, ns);
     auto wait_gu = [&] {
-      if (tid == (NW - 1) * 64 && !bar_wait(&sync[kSyncBar2], nwg, &sync[kSyncErr])) flag_error(sync, err_word);
+      if (tid == (NW - 1) * 64 && !bar_wait(&sync[kSyncBar2], nwg, err)) flag_error(err, err_word);
       lds_barrier();
       stamp(A->stamps, 7);
     };
@@ -271,14 +284,9 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_m1_kernel(StepArgs sa) {
     }
   }
 
-  // ---- exit: the last workgroup clears the counters for the next launch
-  // (word 0 of every counter line; one line per thread)
-  {
-    __shared__ int last_out;
-    if (tid == 0) last_out = atomic_add_agent(&sa.sync[kSyncExit], 1u) == (unsigned)(nwg - 1);
-    __syncthreads();
-    if (last_out && tid < kSyncWords / kLine) st_coh(&sa.sync[tid * kLine], 0u);
-  }
+  // ---- exit: the first workgroup advances the epoch (every workgroup read
+  // it at entry, before the barrier after O that this one has passed)
+  if (wg == 0 && tid == 0) st_coh(&sa.sync[kSyncEpoch], epoch + 1u);
 }
 
 // ---------------------------------------------------------------------------
