@@ -45,8 +45,8 @@ PREFILL_SOURCES = ("prefill.hip", "gemv.h", "attn.h", "coherent.h", "device_comm
                    "i4d_layout.h", "../build.py")
 TRAFFIC = {
     "8b_m1_ctx4096": {"kernel": "step_m1_kernel (one-launch decode step)", "sources": STEP_M1_SOURCES,
-                      "sha256": "7550df47cb8c6c21a78034bcd426506fc793143befd3547e37cbbc168e2f1b71",
-                      "fetch_bytes": 118789504, "write_bytes": 742912},
+                      "sha256": "49d175f0c0730d4af6ebda474410b1125e7eb4b58470c2f700f97693d32a0d50",
+                      "fetch_bytes": 118836352, "write_bytes": 742912},
     "8b_prefill_s2048": {"kernel": "prefill_gemm_kernel (FP8 MFMA GEMM + epilogue)", "sources": PREFILL_SOURCES,
                          "sha256": "86591cb1162dc3aced545e0ee1aa56b1ec9b32c19dec6fde5329fd0d881421cb",
                          "fetch_bytes": 213150720, "write_bytes": 10600448},

@@ -139,24 +139,33 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_m1_kernel(StepArgs sa) {
   const int tid = threadIdx.x;
   const int wg = blockIdx.x, nwg = gridDim.x;
   stamp(sa.stamps, 0);
-  // this launch's counter bank; the first workgroup clears the other one
-  const unsigned epoch = ld_coh(&sa.sync[kSyncEpoch]);
-  unsigned* const bank = sa.sync + (epoch & 1u) * kBankWords;
+  // The epoch (which selects this launch's counter bank) is read by one
+  // thread per workgroup into LDS: every wave of every workgroup reading
+  // the one word would queue 2048 requests on it at the start, and a
+  // wave's loads complete in order, so its first x loads would wait behind
+  // them.  Other threads read it after a workgroup barrier; thread 0 uses
+  // its own copy.
+  __shared__ unsigned epoch_s;
+  if (tid == 0) epoch_s = ld_coh(&sa.sync[kSyncEpoch]);
+  auto bank_of = [&]() { return sa.sync + (epoch_s & 1u) * kBankWords; };
   unsigned* const err = sa.sync + kSyncErr;
-  if (wg == 0 && tid < kBankLines) st_coh(&sa.sync[((epoch & 1u) ^ 1u) * kBankWords + tid * kLine], 0u);
   // the attention units' row metadata (one row), read now so that its
-  // latency overlaps the QKV stage
-  RowMeta meta;
-  meta.base = sa.at.kv.row_base[0];
-  meta.cap = sa.at.kv.row_base[1] - meta.base;
-  meta.L = sa.at.ctx_len[0];
+  // latency overlaps the QKV stage, by one thread (as the epoch) into LDS;
+  // the attention stage reads it after its first workgroup barrier
+  __shared__ RowMeta meta;
+  if (tid == 0) {
+    const int64_t b0 = sa.at.kv.row_base[0];
+    meta.base = b0;
+    meta.cap = sa.at.kv.row_base[1] - b0;
+    meta.L = sa.at.ctx_len[0];
+  }
 
   // ---- 1. QKV
   {
     const StepArgs* A = &sa;
     const ProjArgs pa = A->qkv;
     const GemvPlan pl = A->pq;
-    unsigned* sync = bank;
+    unsigned* sync = bank_of();  // thread 0 only (its own read)
     const int hd = A->hd, n_kv = A->n_kv, G = A->G;
     int s0, ns;
     strip_range(pa.Np / kStrip, wg, nwg, s0, ns);
@@ -174,7 +183,7 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_m1_kernel(StepArgs sa) {
   {
     const StepArgs* A = &sa;
     const AttnArgs at = A->at;
-    unsigned* sync = bank;
+    unsigned* sync = bank_of();  // thread 0 only (its own read)
     int32_t* err_word = A->err_word;
     const int n_kv = A->n_kv, G = A->G, Sf = A->Sf;
     const int units = n_kv * Sf;
@@ -216,23 +225,25 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_m1_kernel(StepArgs sa) {
     const StepArgs* A = &sa;
     const ProjArgs pa = A->o;
     const GemvPlan pl = A->po;
-    unsigned* sync = bank;
     int32_t* err_word = A->err_word;
     const int n_kv = A->n_kv;
     int s0, ns;
     strip_range(pa.Np / kStrip, wg, nwg, s0, ns);
     auto wait_attn = [&] {
-      if (tid == (NW - 1) * 64 && !spin_geq(&sync[kSyncAttnDone], (unsigned)n_kv, err, 1u))
+      if (tid == (NW - 1) * 64 && !spin_geq(&bank_of()[kSyncAttnDone], (unsigned)n_kv, err, 1u))
         flag_error(err, err_word);
       lds_barrier();
       stamp(A->stamps, 3);
     };
     __syncthreads();
+    // (every thread reads epoch_s only after this barrier) the first
+    // workgroup clears the other bank, which the previous launch used
+    if (wg == 0 && tid < kBankLines) st_coh(&sa.sync[((epoch_s & 1u) ^ 1u) * kBankWords + tid * kLine], 0u);
     // the first ring of atoms (with one strip per workgroup, the whole O
     // stream) is requested before the wait for the attention heads
     if (ns > 0) gemv_body<EPI_O, NW, UO, GQ, true, true>(pa, pl, s0, ns, smem, wait_attn);
     stores_done();
-    if (tid == 0) bar_arrive(&sync[kSyncBar1], wg);
+    if (tid == 0) bar_arrive(&bank_of()[kSyncBar1], wg);
     stamp(A->stamps, 4);
   }
 
@@ -241,19 +252,18 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_m1_kernel(StepArgs sa) {
     const StepArgs* A = &sa;
     const ProjArgs pa = A->gu;
     const GemvPlan pl = A->pg;
-    unsigned* sync = bank;
     int32_t* err_word = A->err_word;
     int s0, ns;
     strip_range(pa.Np / kStrip, wg, nwg, s0, ns);
     auto wait_o = [&] {
-      if (tid == (NW - 1) * 64 && !bar_wait(&sync[kSyncBar1], nwg, err)) flag_error(err, err_word);
+      if (tid == (NW - 1) * 64 && !bar_wait(&bank_of()[kSyncBar1], nwg, err)) flag_error(err, err_word);
       lds_barrier();
       stamp(A->stamps, 5);
     };
     __syncthreads();
     if (ns > 0) gemv_body<EPI_GU, NW, UQ, GQ, true>(pa, pl, s0, ns, smem, wait_o);
     stores_done();
-    if (tid == 0) bar_arrive(&sync[kSyncBar2], wg);
+    if (tid == 0) bar_arrive(&bank_of()[kSyncBar2], wg);
     stamp(A->stamps, 6);
   }
 
@@ -262,12 +272,11 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_m1_kernel(StepArgs sa) {
     const StepArgs* A = &sa;
     const ProjArgs pa = A->down;
     const GemvPlan pl = A->pd;
-    unsigned* sync = bank;
     int32_t* err_word = A->err_word;
     int s0, ns;
     strip_range(pa.Np / kStrip, wg, nwg, s0, ns);
     auto wait_gu = [&] {
-      if (tid == (NW - 1) * 64 && !bar_wait(&sync[kSyncBar2], nwg, err)) flag_error(err, err_word);
+      if (tid == (NW - 1) * 64 && !bar_wait(&bank_of()[kSyncBar2], nwg, err)) flag_error(err, err_word);
       lds_barrier();
       stamp(A->stamps, 7);
     };
@@ -286,7 +295,7 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_m1_kernel(StepArgs sa) {
 
   // ---- exit: the first workgroup advances the epoch (every workgroup read
   // it at entry, before the barrier after O that this one has passed)
-  if (wg == 0 && tid == 0) st_coh(&sa.sync[kSyncEpoch], epoch + 1u);
+  if (wg == 0 && tid == 0) st_coh(&sa.sync[kSyncEpoch], epoch_s + 1u);
 }
 
 // ---------------------------------------------------------------------------
