@@ -45,10 +45,10 @@ PREFILL_SOURCES = ("prefill.hip", "gemv.h", "attn.h", "coherent.h", "device_comm
                    "i4d_layout.h", "../build.py")
 TRAFFIC = {
     "8b_m1_ctx4096": {"kernel": "step_m1_kernel (one-launch decode step)", "sources": STEP_M1_SOURCES,
-                      "sha256": "49d175f0c0730d4af6ebda474410b1125e7eb4b58470c2f700f97693d32a0d50",
-                      "fetch_bytes": 118836352, "write_bytes": 742912},
+                      "sha256": "ce0c9ab6082373c2a9f7aee835d9506e1d9984358ee3b2bdcdb768abe335fb5f",
+                      "fetch_bytes": 118852736, "write_bytes": 779264},
     "8b_prefill_s2048": {"kernel": "prefill_gemm_kernel (FP8 MFMA GEMM + epilogue)", "sources": PREFILL_SOURCES,
-                         "sha256": "86591cb1162dc3aced545e0ee1aa56b1ec9b32c19dec6fde5329fd0d881421cb",
+                         "sha256": "6b0eed38cb105675cf3580ceb2dbd259bfe41d8dffd2a9c5c32a93d26c49ac5a",
                          "fetch_bytes": 213150720, "write_bytes": 10600448},
 }
 

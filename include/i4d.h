@@ -327,7 +327,11 @@ i4d_status i4d_ffn_down(const i4d_layer* layer, const uint16_t* a, const float* 
 /* Workspace of i4d_decode_block_step.  The workspace must be zero-filled
  * (or passed to i4d_workspace_init) once before its first use; every step
  * leaves it ready for the next (its counters at zero, or, in the one-launch
- * step, cleared one launch ahead), so later steps need nothing. */
+ * step, cleared one launch ahead), so later steps need nothing.  The
+ * one-launch step (M = 1) keeps a launch count in it and passes the query,
+ * key and value between its workgroups as words tagged with that count;
+ * zero-filling the workspace again restarts the count and clears the
+ * tagged words with it, so no step reads a word an earlier step left. */
 i4d_status i4d_workspace_bytes(const i4d_layer_shape* shape, int M, int max_ctx_len,
                                int num_splits, size_t* bytes);
 
@@ -445,9 +449,9 @@ i4d_status i4d_attn_out_proj_e4m3(const i4d_layer* layer, const uint16_t* attn_b
  * each GPU (I4D_NOALLOC_SCRATCH_BYTES, enough for every shape here at the
  * automatic split count; a step that needs more returns I4D_ERR_WORKSPACE
  * before anything is enqueued).  Nothing is allocated: the first call on a
- * device looks the array up (hipGetSymbolAddress) and clears its counters
- * with a kernel on `stream`; every completed step leaves them ready for
- * the next.
+ * device looks the array up (hipGetSymbolAddress) and clears all of it
+ * with a kernel on `stream`; every completed step leaves its counters
+ * ready for the next.
  * The caller still owns every input and output.  All calls on one GPU share
  * its array, so calls that overlap on one GPU (other streams, other
  * threads) race and must be serialised by the caller.  Arguments, results

@@ -132,7 +132,7 @@ i4d_status do_qkv(const i4d_layer* L, const uint16_t* x, const int32_t* ctx_len,
 AttnArgs attention_args(const i4d_kv_cache* c, const i4d_layer_shape& s, const float* q,
                         const int32_t* ctx_len, int M, int max_ctx_len, int S, void* ws, float* attn_f32,
                         uint16_t* attn_bf16, const uint16_t* k_new, const uint16_t* v_new) {
-  AttnArgs a;
+  AttnArgs a = {};
   a.kv = kv_args(c);
   a.q = q;
   a.ctx_len = ctx_len;
@@ -246,8 +246,17 @@ i4d_status run_decode_step(const i4d_layer* layer, const i4d_kv_cache* cache, co
     in.o = o_args(layer, attn, x_in, 1, h, hb);
     in.gu = gu_args(layer, hb, 1, act);
     in.down = down_args(layer, act, h, 1, x_out);
-    in.attn = attention_args(cache, s, q, ctx_len, 1, max_ctx_len, step_m1_splits(&s, max_ctx_len, num_splits),
-                             ws + wl.attn_ws, attn_f32, attn, k, v);
+    const int S1 = step_m1_splits(&s, max_ctx_len, num_splits);
+    in.attn = attention_args(cache, s, q, ctx_len, 1, max_ctx_len, S1, ws + wl.attn_ws, attn_f32, attn, k, v);
+    // the flagged exchange words follow the attention partials
+    char* llb = ws + wl.attn_ws + attn_ws_layout(&s, 1, S1).total;
+    const StepLl ll = step_ll_layout(&s);
+    in.qkv.q_ll = (uint64_t*)(llb + ll.q);
+    in.qkv.k_ll = (uint64_t*)(llb + ll.k);
+    in.qkv.v_ll = (uint64_t*)(llb + ll.v);
+    in.attn.q_ll = in.qkv.q_ll;
+    in.attn.k_ll = in.qkv.k_ll;
+    in.attn.v_ll = in.qkv.v_ll;
     in.sync = (unsigned*)(ws + wl.sync);
     in.stamps = stamps;
     return launch_step_m1(in, st);

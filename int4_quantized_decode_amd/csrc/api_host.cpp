@@ -97,6 +97,17 @@ AttnWs attn_ws_layout(const i4d_layer_shape* s, int M, int S) {
   return w;
 }
 
+StepLl step_ll_layout(const i4d_layer_shape* s) {
+  StepLl w;
+  const size_t nq = (size_t)s->n_q_heads * s->head_dim, nk = (size_t)s->n_kv_heads * s->head_dim;
+  size_t off = 0;
+  w.q = off;    off += align256(nq * 8);
+  w.k = off;    off += align256(nk * 8);
+  w.v = off;    off += align256(nk * 8);
+  w.total = off;
+  return w;
+}
+
 LmWs lm_ws_layout(int V, int M) {
   LmWs w;
   int strips = V / kStrip;
@@ -568,8 +579,9 @@ i4d_status i4d_workspace_layout_of(const i4d_layer_shape* s, int M, int max_ctx_
   size_t attn_bytes;
   i4d_status st = i4d_attention_workspace_bytes(s, M, max_ctx_len, num_splits, &attn_bytes);
   if (st) return st;
-  if (M == 1)  // the one-launch step may use another split count
-    attn_bytes = std::max(attn_bytes, attn_ws_layout(s, 1, step_m1_splits(s, max_ctx_len, num_splits)).total);
+  if (M == 1)  // the one-launch step may use another split count, and adds its flagged words
+    attn_bytes = std::max(attn_bytes, attn_ws_layout(s, 1, step_m1_splits(s, max_ctx_len, num_splits)).total +
+                                          step_ll_layout(s).total);
   size_t nq = (size_t)M * s->n_q_heads * s->head_dim;
   size_t nk = (size_t)M * s->n_kv_heads * s->head_dim;
   size_t off = 0;

@@ -40,6 +40,14 @@ struct AttnArgs {
   float* part_o;           // [M][n_q][S][hd]
   float* attn_f32;         // optional [M][n_q*hd]
   uint16_t* attn_bf16;     // [M][n_q*hd]
+  // Inside the one-launch step (M = 1) the query [n_q][hd] (fp32 bits) and
+  // the new key and value [n_kv][hd] (bf16 bits) arrive as flagged words
+  // (coherent.h) with flag `flag`.
+  const uint64_t* q_ll;
+  const uint64_t* k_ll;
+  const uint64_t* v_ll;
+  uint32_t flag;
+  unsigned* sync_err;  // set (with I4D_DEVERR_SYNC in kv.err_word) by a poll that times out
 };
 
 KvArgs kv_args(const i4d_kv_cache* c);

@@ -63,11 +63,43 @@ struct NewToken {
   uint16_t ks, vs;  // fp16 scales
 };
 
+// poll the flagged words p[lane] and p[lane + 64] (HD = 128) until both hold
+// `flag`; their low 32 bits into d0, d1
+template <int HD>
+__device__ __forceinline__ void poll_pair(const uint64_t* p, int lane, uint32_t flag, unsigned* sync_err,
+                                          int32_t* err_word, uint32_t& d0, uint32_t& d1) {
+  uint64_t w0 = 0, w1 = 0;
+  for (int it = 0;; ++it) {
+    // both loads in flight before either is tested (no branch between)
+    w0 = ld_flag(&p[lane]);
+    w1 = (HD == 128) ? ld_flag(&p[lane + 64]) : ((uint64_t)flag << 32);
+    if (__all(flag_is(w0, flag) & flag_is(w1, flag))) break;
+    if (it == kPollLimit) {
+      poll_timeout(sync_err, err_word);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  d0 = (uint32_t)w0;
+  d1 = (uint32_t)w1;
+}
+
+// COH (one-launch step): the vector comes from the flagged words src_ll
+// [HD] (bf16 bits) instead of src
 template <int HD, bool COH = false>
 __device__ void append_vector(const KvArgs& kv, const uint16_t* src, int64_t region, int pos,
-                              int kind, int lane, NewToken* nt = nullptr) {
-  float x0 = bf16_to_f32(COH ? ld_coh(&src[lane]) : src[lane]);
-  float x1 = (HD == 128) ? bf16_to_f32(COH ? ld_coh(&src[lane + 64]) : src[lane + 64]) : 0.f;
+                              int kind, int lane, NewToken* nt = nullptr, const uint64_t* src_ll = nullptr,
+                              uint32_t flag = 0, unsigned* sync_err = nullptr) {
+  float x0, x1;
+  if (COH) {
+    uint32_t d0, d1;
+    poll_pair<HD>(src_ll, lane, flag, sync_err, kv.err_word, d0, d1);
+    x0 = bf16_to_f32((uint16_t)d0);
+    x1 = (HD == 128) ? bf16_to_f32((uint16_t)d1) : 0.f;
+  } else {
+    x0 = bf16_to_f32(src[lane]);
+    x1 = (HD == 128) ? bf16_to_f32(src[lane + 64]) : 0.f;
+  }
   // FWHT, stages h = 1 .. 32 across lanes, then h = 64 inside the lane
 #pragma unroll
   for (int h = 1; h < 64 && h < HD; h <<= 1) {
@@ -307,8 +339,9 @@ __device__ __forceinline__ void fwht_wave(float& x0, float& x1, int lane) {
 // interleaved 32-token blocks of the split.  `wait_input` runs after the
 // first cache loads are issued and before the query is read.  LDS: wm, wl
 // [NWA][8], wo [NWA][8][HD], then the query operand (attn_lds_floats).
-// COH: the query, the new key/value and the partials are exchanged with
-// other workgroups of the same launch (agent-coherent loads and stores).
+// COH: the query and the new key/value come from other workgroups of the
+// same launch as flagged words (polled loads); the partials are exchanged
+// with agent-coherent stores and loads.
 // Row metadata of a unit read ahead of time (the one-launch step reads it
 // at its start, so that the read is not on the attention critical path).
 struct RowMeta {
@@ -399,9 +432,17 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int m, const 
   // the sum of 8 (128 at the 1/16 slots) times its values (the code offset
   // term)
   for (int g = wave; g < G; g += NWA) {
-    const float* src = a.q + ((size_t)m * a.n_q + (size_t)j * G + g) * HD;
-    float x0 = COH ? ld_coh(&src[lane]) : src[lane];
-    float x1 = (HD == 128) ? (COH ? ld_coh(&src[lane + 64]) : src[lane + 64]) : 0.f;
+    float x0, x1;
+    if (COH) {
+      uint32_t d0, d1;
+      poll_pair<HD>(a.q_ll + ((size_t)j * G + g) * HD, lane, a.flag, a.sync_err, kv.err_word, d0, d1);
+      x0 = __uint_as_float(d0);
+      x1 = (HD == 128) ? __uint_as_float(d1) : 0.f;
+    } else {
+      const float* src = a.q + ((size_t)m * a.n_q + (size_t)j * G + g) * HD;
+      x0 = src[lane];
+      x1 = (HD == 128) ? src[lane + 64] : 0.f;
+    }
     fwht_wave<HD>(x0, x1, lane);
     float sh = 0.f, sl = 0.f;
     auto put = [&](const float x, const int ch) {
@@ -430,7 +471,8 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int m, const 
   const int aw = (G + 2 <= NWA) ? G : 0;
   if (appending && wave >= aw && wave < aw + 2) {
     const uint16_t* src = (wave - aw ? a.v_new : a.k_new) + ((size_t)m * kv.n_kv + j) * HD;
-    append_vector<HD, COH>(kv, src, region, L - 1, wave - aw, lane, nt);
+    append_vector<HD, COH>(kv, src, region, L - 1, wave - aw, lane, nt,
+                           COH ? (wave - aw ? a.v_ll : a.k_ll) + (size_t)j * HD : nullptr, a.flag, a.sync_err);
     // the new codes are in memory before a block read of this workgroup
     // after the first (two) per wave, if one of those is the block appended to
     if (last_blk >= b0 + (TWO ? 2 : 1) * NWA) wait_vmem();

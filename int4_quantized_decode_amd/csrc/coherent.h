@@ -15,6 +15,7 @@
 #include <stdint.h>
 
 #include "device_common.h"
+#include "i4d_internal.h"
 
 namespace i4d {
 
@@ -50,6 +51,29 @@ __device__ __forceinline__ u32x4_t ld_coh16(const void* base, uint32_t off, uint
 __device__ __forceinline__ void st_coh16(void* base, uint32_t off, uint32_t bytes, u32x4_t v) {
   const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, 0, bytes, 0x00020000);
   __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 16 /* sc1 */);
+}
+
+// Flagged words: 8 bytes holding 4 bytes of data and the flag of the launch
+// that wrote them, stored and loaded as one 64-bit access (single-copy
+// atomic).  A reader that sees its launch's flag has that launch's data,
+// so the hand-off needs neither a counter nor the producer's wait for its
+// stores: the consumer polls the data itself.  The flag is the launch's
+// epoch + 1, so words of an earlier launch, and zeroed memory, never match.
+__device__ __forceinline__ void st_flag(uint64_t* p, uint32_t data, uint32_t flag) {
+  __hip_atomic_store(p, ((uint64_t)flag << 32) | data, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_flag(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool flag_is(uint64_t w, uint32_t flag) { return (uint32_t)(w >> 32) == flag; }
+// polls of flagged words before a wait counts as timed out
+constexpr int kPollLimit = 1 << 20;
+// a timed-out poll: the sticky word of the launch and the cache's error word
+__device__ __forceinline__ void poll_timeout(unsigned* sync_err, int32_t* err_word) {
+  if ((threadIdx.x & 63) == 0) {
+    if (sync_err) atomicOr(sync_err, 1u);
+    if (err_word) atomicOr(err_word, I4D_DEVERR_SYNC);
+  }
 }
 
 // wait until this wave's stores (and loads) have completed

@@ -96,18 +96,29 @@ __device__ void run_epilogue(const ProjArgs& a, int strip0, int S, const float* 
           y0 = r0;
           y1 = r1;
         }
+        // COH (one-launch step, M = 1): the attention units read the
+        // flagged copies; the plain ones are the step's visible outputs
         if (head < a.n_q) {
           float* q = a.q_out + ((size_t)m * a.n_q + head) * a.hd;
           st_out<COH>(&q[c0], y0);
           st_out<COH>(&q[c1], y1);
-        } else if (head < a.n_q + a.n_kv) {
-          uint16_t* k = a.k_out + ((size_t)m * a.n_kv + (head - a.n_q)) * a.hd;
-          st_out<COH>(&k[c0], f32_to_bf16(y0));
-          st_out<COH>(&k[c1], f32_to_bf16(y1));
+          if (COH) {
+            uint64_t* ql = a.q_ll + (size_t)head * a.hd;
+            st_flag(&ql[c0], __float_as_uint(y0), *a.epoch + 1u);
+            st_flag(&ql[c1], __float_as_uint(y1), *a.epoch + 1u);
+          }
         } else {
-          uint16_t* v = a.v_out + ((size_t)m * a.n_kv + (head - a.n_q - a.n_kv)) * a.hd;
-          st_out<COH>(&v[c0], f32_to_bf16(y0));
-          st_out<COH>(&v[c1], f32_to_bf16(y1));
+          const bool is_k = head < a.n_q + a.n_kv;
+          const int kvh = head - a.n_q - (is_k ? 0 : a.n_kv);
+          uint16_t* kv = (is_k ? a.k_out : a.v_out) + ((size_t)m * a.n_kv + kvh) * a.hd;
+          const uint16_t b0 = f32_to_bf16(y0), b1 = f32_to_bf16(y1);
+          st_out<COH>(&kv[c0], b0);
+          st_out<COH>(&kv[c1], b1);
+          if (COH) {
+            uint64_t* kl = (is_k ? a.k_ll : a.v_ll) + (size_t)kvh * a.hd;
+            st_flag(&kl[c0], b0, *a.epoch + 1u);
+            st_flag(&kl[c1], b1, *a.epoch + 1u);
+          }
         }
       }
     }

@@ -54,6 +54,14 @@ struct AttnWs {
 };
 AttnWs attn_ws_layout(const i4d_layer_shape* s, int M, int S);
 
+// Flagged exchange words (8 bytes each) of the one-launch step (M = 1),
+// byte offsets from the end of the step's attention partials in the
+// attention workspace: query [n_q][hd], new key and value [n_kv][hd].
+struct StepLl {
+  size_t q, k, v, total;
+};
+StepLl step_ll_layout(const i4d_layer_shape* s);
+
 struct LmWs {
   size_t val;   // fp32 [nwaves][M]
   size_t idx;   // int32 [nwaves][M]

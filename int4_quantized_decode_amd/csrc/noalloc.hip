@@ -108,10 +108,11 @@ extern "C" i4d_status i4d_decode_block_step_noalloc(const i4d_layer* layer, cons
   st = scratch_of(dev, &base, &first);
   if (st != I4D_OK) return st;
   hipStream_t s = (hipStream_t)stream;
-  // the counters start at zero on this device (a fill kernel on the
-  // caller's stream, ordered before the step)
+  // the counters start at zero on this device, and so do the one-launch
+  // step's flagged exchange words (a fill kernel on the caller's stream,
+  // ordered before the step)
   if (first) {
-    st = launch_zero_fill(base, kScratchHeader, s);
+    st = launch_zero_fill(base, kScratchBytes, s);
     if (st != I4D_OK) {
       std::lock_guard<std::mutex> lock(g_mu);
       g_cleared[dev] = false;

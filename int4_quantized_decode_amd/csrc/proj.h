@@ -42,6 +42,13 @@ struct ProjArgs {
   unsigned* split_cnt;
   size_t split_bytes;
   int fmt;  // WeightFormat of codes/scales
+  // one-launch step (M = 1): the QKV epilogue also writes q, k, v as
+  // flagged words (coherent.h) whose flag is *epoch + 1 (the launch's
+  // epoch, read from LDS once the workgroup has passed a barrier)
+  uint64_t* q_ll;
+  uint64_t* k_ll;
+  uint64_t* v_ll;
+  const unsigned* epoch;
 };
 
 

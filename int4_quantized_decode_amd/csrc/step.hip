@@ -14,12 +14,15 @@
 // a grid barrier after the gate/up stream) wait long enough: they request
 // their first atoms before the wait.
 //
-// Stages and hand-offs (counters in the zeroed sync region of the
-// workspace; data exchanged with agent-coherent stores and loads):
-//   1. QKV strips (+ rho1, RoPE): each finished strip counts for its kv head.
-//   2. Attention unit (kv head j, split s): waits for the strips of head j's
-//      query heads, key and value; appends the new key/value (the unit that
-//      owns position L-1); writes a partial; the last unit of kv head j
+// Stages and hand-offs (counters in the sync region of the workspace; data
+// exchanged with agent-coherent stores and loads, except the query, key and
+// value, which travel as flagged words (coherent.h) tagged with the
+// launch's epoch + 1: the attention units poll them directly, so the QKV
+// workgroups neither wait for their stores nor count them):
+//   1. QKV strips (+ rho1, RoPE): q, k, v stored as flagged words.
+//   2. Attention unit (kv head j, split s): polls its query heads (and, in
+//      the unit that owns position L-1, the new key and value, which it
+//      appends); writes a partial; the last unit of kv head j
 //      merges the splits, undoes the rotation and counts head j done.
 //   3. O strips (+ residual): wait for all kv heads; then a grid barrier.
 //   4. gate/up strips (+ rho2, SwiGLU): after the barrier; barrier again.
@@ -47,13 +50,12 @@ namespace i4d {
 // previous launch has finished with, while this launch runs, so no launch
 // ends with a barrier of all its workgroups to clear its own counters.
 constexpr int kLine = 32;
-constexpr int kSyncQkv = 0;               // [n_kv] finished QKV strips per kv head
-constexpr int kSyncAttn = 16 * kLine;     // [n_kv] finished attention splits per kv head
-constexpr int kSyncAttnDone = 32 * kLine; // kv heads whose attention output is written
-constexpr int kSyncBar1 = 33 * kLine;     // 8 group counters (after O)
-constexpr int kSyncBar2 = 42 * kLine;     // 8 group counters (after gate/up)
-constexpr int kBankLines = 51;            // counter lines of one bank
-constexpr int kBankWords = 52 * kLine;    // bank stride
+constexpr int kSyncAttn = 0;              // [n_kv] finished attention splits per kv head
+constexpr int kSyncAttnDone = 16 * kLine; // kv heads whose attention output is written
+constexpr int kSyncBar1 = 17 * kLine;     // 8 group counters (after O)
+constexpr int kSyncBar2 = 26 * kLine;     // 8 group counters (after gate/up)
+constexpr int kBankLines = 35;            // counter lines of one bank
+constexpr int kBankWords = 36 * kLine;    // bank stride
 constexpr int kSyncErr = 2 * kBankWords;          // sticky timeout flag (never cleared)
 constexpr int kSyncEpoch = 2 * kBankWords + kLine; // completed launches (selects the bank)
 static_assert((kSyncEpoch + 1) * 4 <= (int)kStepSyncBytes, "sync region");
@@ -85,14 +87,6 @@ struct StepArgs {
 __device__ __forceinline__ void strip_range(int N, int wg, int nwg, int& s0, int& ns) {
   s0 = (int)((long)wg * N / nwg);
   ns = (int)((long)(wg + 1) * N / nwg) - s0;
-}
-
-// QKV strip t -> kv head whose attention needs it
-__device__ __forceinline__ int strip_kv_head(int t, int hd, int n_q, int n_kv, int G) {
-  const int head = t / (hd / kStrip);
-  if (head < n_q) return head / G;
-  if (head < n_q + n_kv) return head - n_q;
-  return head - n_q - n_kv;
 }
 
 __device__ __forceinline__ void flag_error(unsigned* err, int32_t* err_word) {
@@ -163,40 +157,29 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_m1_kernel(StepArgs sa) {
   // ---- 1. QKV
   {
     const StepArgs* A = &sa;
-    const ProjArgs pa = A->qkv;
+    ProjArgs pa = A->qkv;
+    pa.epoch = &epoch_s;  // read by the epilogue, after the staging barrier
     const GemvPlan pl = A->pq;
-    unsigned* sync = bank_of();  // thread 0 only (its own read)
-    const int hd = A->hd, n_kv = A->n_kv, G = A->G;
     int s0, ns;
     strip_range(pa.Np / kStrip, wg, nwg, s0, ns);
-    if (ns > 0) {
-      gemv_body<EPI_QKV, NW, 4, GQ, true>(pa, pl, s0, ns, smem, NoWait());
-      stores_done();
-      if (tid == 0)
-        for (int t = s0; t < s0 + ns; ++t)
-          atomic_add_agent(&sync[kSyncQkv + kLine * strip_kv_head(t, hd, pa.n_q, n_kv, G)], 1u);
-    }
+    if (ns > 0) gemv_body<EPI_QKV, NW, 4, GQ, true>(pa, pl, s0, ns, smem, NoWait());
     stamp(A->stamps, 1);
   }
 
   // ---- 2. attention units (kv head j, split s), head-interleaved
   {
     const StepArgs* A = &sa;
-    const AttnArgs at = A->at;
+    AttnArgs at = A->at;
+    at.sync_err = err;
     unsigned* sync = bank_of();  // thread 0 only (its own read)
-    int32_t* err_word = A->err_word;
     const int n_kv = A->n_kv, G = A->G, Sf = A->Sf;
     const int units = n_kv * Sf;
-    const unsigned need = (unsigned)((G + 2) * (A->hd / kStrip));
     for (int u = wg; u < units; u += nwg) {
       const int j = u % n_kv, s = u / n_kv;
-      __syncthreads();  // LDS reuse
-      auto wait_qkv = [&] {
-        if (tid == 0 && !spin_geq(&sync[kSyncQkv + kLine * j], need, err, 1u))
-          flag_error(err, err_word);
-        lds_barrier();
-      };
-      attn_body<HD, NW, true>(at, 0, j, s, reinterpret_cast<float*>(smem), wait_qkv, &meta);
+      __syncthreads();  // LDS reuse (and epoch_s is visible to every thread)
+      at.flag = epoch_s + 1u;
+      // the unit polls its query heads (and the new key and value) itself
+      attn_body<HD, NW, true>(at, 0, j, s, reinterpret_cast<float*>(smem), NoWait(), &meta);
       stores_done();
       if (Sf > 1) {
         __shared__ int last;
