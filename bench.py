@@ -45,7 +45,7 @@ PREFILL_SOURCES = ("prefill.hip", "gemv.h", "attn.h", "coherent.h", "device_comm
                    "i4d_layout.h", "../build.py")
 TRAFFIC = {
     "8b_m1_ctx4096": {"kernel": "step_m1_kernel (one-launch decode step)", "sources": STEP_M1_SOURCES,
-                      "sha256": "ce0c9ab6082373c2a9f7aee835d9506e1d9984358ee3b2bdcdb768abe335fb5f",
+                      "sha256": "d17c5bb8a738f95686da55945aa5cd060b34afae60ef0c7cd59f725f4d2d0317",
                       "fetch_bytes": 118852736, "write_bytes": 779264},
     "8b_prefill_s2048": {"kernel": "prefill_gemm_kernel (FP8 MFMA GEMM + epilogue)", "sources": PREFILL_SOURCES,
                          "sha256": "6b0eed38cb105675cf3580ceb2dbd259bfe41d8dffd2a9c5c32a93d26c49ac5a",

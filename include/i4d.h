@@ -387,7 +387,7 @@ i4d_status i4d_decode_block_step(const i4d_layer* layer, const i4d_kv_cache* cac
  * n_cu of them) stores I4D_STEP_STAMPS readings of the device's 100 MHz
  * real-time counter into stamps[workgroup][slot] (device uint64, at least
  * n_cu * I4D_STEP_STAMPS values; n_cu is the device's compute-unit count):
- * 0 entry, 1 its QKV strips stored and counted, 2 its attention units done,
+ * 0 entry, 1 its QKV strips stored, 2 its attention units done,
  * 3 the wait for every head's attention output passed, 4 its O strips
  * stored, 5 the barrier after O passed, 6 its gate/up strips stored, 7 the
  * barrier after gate/up passed, 8 its down strips stored; slot 9 is unused.

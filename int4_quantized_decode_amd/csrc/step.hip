@@ -64,7 +64,7 @@ static_assert((kSyncEpoch + 1) * 4 <= (int)kStepSyncBytes, "sync region");
 constexpr int kStepWaves = 8;
 
 // Timeline of a workgroup (optional): the 100 MHz real-time counter at
-// entry, QKV stored and counted, attention units done, O's wait passed, O
+// entry, QKV stored, attention units done, O's wait passed, O
 // stored, gate/up's wait passed, gate/up stored, down's wait passed, down
 // stored; read by thread 0 (in the wait hooks after their barrier), stored
 // by a vector store.
