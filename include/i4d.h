@@ -344,7 +344,10 @@ i4d_status i4d_decode_step_is_one_launch(const i4d_layer_shape* shape, int M, in
 i4d_status i4d_workspace_init(void* workspace, size_t bytes, void* stream);
 
 /* Byte offsets of the intermediates inside the decode-step workspace (for
- * inspection by tests; all 256-byte aligned). */
+ * inspection by tests; all 256-byte aligned).  The two counter regions,
+ * sync and split_cnt, come first, at the same offsets for every shape, M
+ * and split count, so one zero-filled workspace may serve steps of
+ * different shapes and batch sizes in turn. */
 typedef struct {
   size_t q;     /* fp32 [M][n_q][hd] */
   size_t k;     /* bf16 [M][n_kv][hd] */

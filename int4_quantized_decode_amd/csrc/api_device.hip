@@ -391,7 +391,7 @@ i4d_status i4d_decode_block_step(const i4d_layer* layer, const i4d_kv_cache* cac
   if (workspace_bytes < wl.total)
     return fail(I4D_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, wl.total);
   return run_decode_step(layer, cache, x_in, x_out, ctx_len, M, max_ctx_len, num_splits, (char*)workspace, wl,
-                         wl.sync - wl.split_part, attn_f32, (hipStream_t)stream, kFmtInt4);
+                         wl.total - wl.split_part, attn_f32, (hipStream_t)stream, kFmtInt4);
 }
 
 i4d_status i4d_decode_block_step_timeline(const i4d_layer* layer, const i4d_kv_cache* cache, const uint16_t* x_in,
@@ -414,7 +414,7 @@ i4d_status i4d_decode_block_step_timeline(const i4d_layer* layer, const i4d_kv_c
     return fail(I4D_ERR_RANGE, "stamps holds %zu values, the step needs %d x %d", stamps_count, cus,
                 I4D_STEP_STAMPS);
   return run_decode_step(layer, cache, x_in, x_out, ctx_len, M, max_ctx_len, num_splits, (char*)workspace, wl,
-                         wl.sync - wl.split_part, attn_f32, (hipStream_t)stream, kFmtInt4, stamps);
+                         wl.total - wl.split_part, attn_f32, (hipStream_t)stream, kFmtInt4, stamps);
 }
 
 i4d_status i4d_decode_block_step_e4m3(const i4d_layer* layer, const i4d_kv_cache* cache, const uint16_t* x_in,
@@ -427,7 +427,7 @@ i4d_status i4d_decode_block_step_e4m3(const i4d_layer* layer, const i4d_kv_cache
   if (workspace_bytes < wl.total)
     return fail(I4D_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, wl.total);
   return run_decode_step(layer, cache, x_in, x_out, ctx_len, M, max_ctx_len, num_splits, (char*)workspace, wl,
-                         wl.sync - wl.split_part, attn_f32, (hipStream_t)stream, kFmtE4M3);
+                         wl.total - wl.split_part, attn_f32, (hipStream_t)stream, kFmtE4M3);
 }
 
 i4d_status i4d_attn_out_proj_e4m3(const i4d_layer* layer, const uint16_t* attn_bf16, const uint16_t* x, int M,
@@ -467,7 +467,7 @@ i4d_status i4d_projection_plan_of(const i4d_layer_shape* shape, int stage, int M
   if (M > 1) {
     a.split_cnt = reinterpret_cast<unsigned*>(wl.split_cnt + 256);
     a.split_part = reinterpret_cast<float*>(wl.split_part + 256);
-    a.split_bytes = wl.sync - wl.split_part;
+    a.split_bytes = wl.total - wl.split_part;
   }
   return projection_plan_of(epi, a, out);
 }

@@ -584,15 +584,6 @@ i4d_status i4d_workspace_layout_of(const i4d_layer_shape* s, int M, int max_ctx_
                                           step_ll_layout(s).total);
   size_t nq = (size_t)M * s->n_q_heads * s->head_dim;
   size_t nk = (size_t)M * s->n_kv_heads * s->head_dim;
-  size_t off = 0;
-  out->q = off;       off += align256(nq * 4);
-  out->k = off;       off += align256(nk * 2);
-  out->v = off;       off += align256(nk * 2);
-  out->attn = off;    off += align256(nq * 2);
-  out->h = off;       off += align256((size_t)M * s->d_model * 4);
-  out->h_bf16 = off;  off += align256((size_t)M * s->d_model * 2);
-  out->a = off;       off += align256((size_t)M * s->d_ffn * 2);
-  out->attn_ws = off; off += align256(attn_bytes);
   // the four projections run one after another and leave their counters
   // at zero, so they share one split buffer
   const int nqkv = (s->n_q_heads + 2 * s->n_kv_heads) * s->head_dim;
@@ -605,9 +596,23 @@ i4d_status i4d_workspace_layout_of(const i4d_layer_shape* s, int M, int max_ctx_
     cnt = std::max(cnt, n.counters);
     part = std::max(part, n.part_bytes);
   }
-  out->split_cnt = off;  off += align256(cnt * sizeof(unsigned));
+  if (cnt * sizeof(unsigned) > kSplitCntBytes)
+    return fail(I4D_ERR_UNSUPPORTED, "K split needs %zu arrival counters (at most %zu)", cnt,
+                kSplitCntBytes / sizeof(unsigned));
+  // counters first, at fixed offsets (see kSplitCntBytes); the split
+  // partial tiles last
+  size_t off = 0;
+  out->sync = off;       off += align256(kStepSyncBytes);
+  out->split_cnt = off;  off += align256(kSplitCntBytes);
+  out->q = off;       off += align256(nq * 4);
+  out->k = off;       off += align256(nk * 2);
+  out->v = off;       off += align256(nk * 2);
+  out->attn = off;    off += align256(nq * 2);
+  out->h = off;       off += align256((size_t)M * s->d_model * 4);
+  out->h_bf16 = off;  off += align256((size_t)M * s->d_model * 2);
+  out->a = off;       off += align256((size_t)M * s->d_ffn * 2);
+  out->attn_ws = off; off += align256(attn_bytes);
   out->split_part = off; off += align256(part);
-  out->sync = off;    off += align256(kStepSyncBytes);
   out->total = off;
   return ok();
 }

@@ -46,6 +46,13 @@ int step_m1_splits(const i4d_layer_shape* s, int max_ctx_len, int num_splits);
 
 // size of the sync region of the decode-step workspace (zero before first use)
 constexpr size_t kStepSyncBytes = 16384;
+// The decode-step workspace starts with the counters, at the same offsets
+// for every shape, M and split count: the one-launch step's sync region
+// (kStepSyncBytes), then the projections' K-split arrival counters
+// (kSplitCntBytes).  One zero-filled workspace can then serve steps of any
+// shape: counters a step relies on are never where another layout keeps
+// its data.
+constexpr size_t kSplitCntBytes = 8192;
 
 struct AttnWs {
   size_t ml;      // fp32 [M][n_q][S][2]   (running max in log2 units, sum)

@@ -8,13 +8,14 @@
 // passes the array's name to a kernel or a copy: its device address is
 // looked up once per device with hipGetSymbolAddress and kept.
 //
-// Layout of the array: the step's counters at fixed offsets at the start
-// (the one-launch step's sync region, then the projections' K-split arrival
-// counters), the step's other intermediates after them.  Every completed
-// step leaves its counters at zero, and they sit at the same addresses
-// whatever the shape and M of a call, so a call never sees another call's
-// stale counters; the intermediates are always written before they are
-// read.  The counters are cleared once, at the first call on a device.
+// Layout of the array: the step's workspace layout (i4d_workspace_layout_of),
+// whose counters sit at fixed offsets at its start (the one-launch step's
+// sync region, then the projections' K-split arrival counters) whatever
+// the shape and M of a call, with the other intermediates after them.
+// Every completed step leaves its counters ready for the next call, so a
+// call never sees another call's stale counters; the intermediates are
+// written before they are read.  The array is cleared once, at the first
+// call on a device.
 // Calls that overlap on one GPU (two streams, or two threads) race on the
 // array.
 #include <mutex>
@@ -28,10 +29,6 @@ namespace i4d {
 namespace {
 
 constexpr size_t kScratchBytes = (size_t)16 << 20;         // I4D_NOALLOC_SCRATCH_BYTES
-constexpr size_t kScratchSyncOff = 0;                       // the one-launch step's sync region
-constexpr size_t kScratchSplitCntOff = kStepSyncBytes;      // K-split arrival counters
-constexpr size_t kScratchSplitCntBytes = 8192;
-constexpr size_t kScratchHeader = kScratchSplitCntOff + kScratchSplitCntBytes;
 
 static_assert(kScratchBytes == I4D_NOALLOC_SCRATCH_BYTES, "header and library disagree on the scratch size");
 
@@ -75,30 +72,15 @@ extern "C" i4d_status i4d_decode_block_step_noalloc(const i4d_layer* layer, cons
   i4d_status st =
       check_decode_step(layer, cache, x_in, x_out, ctx_len, M, max_ctx_len, num_splits, attn_f32, &wl);
   if (st != I4D_OK) return st;
-  // The caller's layout moved behind the fixed counter header: every
-  // intermediate keeps its offset plus kScratchHeader, the two counter
-  // regions go to their fixed places.
-  const size_t cnt_bytes = wl.split_part - wl.split_cnt;
-  const size_t need = kScratchHeader + wl.total;
-  if (need > kScratchBytes || cnt_bytes > kScratchSplitCntBytes)
+  // The scratch holds the step's workspace layout as it is: its counters
+  // sit at the start (fixed offsets for every shape), so they keep their
+  // places from one call to the next whatever the shapes.
+  if (wl.total > kScratchBytes)
     return fail(I4D_ERR_WORKSPACE,
-                "this step needs %zu bytes of scratch (%zu of split counters); the no-allocation entry point "
-                "holds %zu (%zu): use i4d_decode_block_step with a workspace",
-                need, cnt_bytes, kScratchBytes, kScratchSplitCntBytes);
-  const size_t split_part_bytes = wl.sync - wl.split_part;
-  i4d_workspace_layout sl = wl;
-  sl.q += kScratchHeader;
-  sl.k += kScratchHeader;
-  sl.v += kScratchHeader;
-  sl.attn += kScratchHeader;
-  sl.h += kScratchHeader;
-  sl.h_bf16 += kScratchHeader;
-  sl.a += kScratchHeader;
-  sl.attn_ws += kScratchHeader;
-  sl.split_part += kScratchHeader;
-  sl.split_cnt = kScratchSplitCntOff;
-  sl.sync = kScratchSyncOff;
-  sl.total = need;
+                "this step needs %zu bytes of scratch; the no-allocation entry point holds %zu: use "
+                "i4d_decode_block_step with a workspace",
+                wl.total, kScratchBytes);
+  const size_t split_part_bytes = wl.total - wl.split_part;
 
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
@@ -119,6 +101,6 @@ extern "C" i4d_status i4d_decode_block_step_noalloc(const i4d_layer* layer, cons
       return st;
     }
   }
-  return run_decode_step(layer, cache, x_in, x_out, ctx_len, M, max_ctx_len, num_splits, (char*)base, sl,
+  return run_decode_step(layer, cache, x_in, x_out, ctx_len, M, max_ctx_len, num_splits, (char*)base, wl,
                          split_part_bytes, attn_f32, s, kFmtInt4);
 }

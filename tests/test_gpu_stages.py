@@ -340,11 +340,12 @@ def test_block_dirty_workspace_forced_splits(gpu):
     cache.prefill(pre)
     ws = D.Workspace(shape, M, maxL, 6)
     ws.buf.fill_(0xA5)
-    # the arrival counters must be zero before first use (the library
-    # leaves them at zero); everything else may hold garbage
+    # the counters (the two regions at the start of the workspace, before
+    # q) must be zero before first use (the library leaves them ready);
+    # everything else may hold garbage
     lay = ws.layout
-    ws.buf[lay.split_cnt:lay.split_part].zero_()
-    ws.buf[lay.sync:lay.total].zero_()
+    assert lay.sync == 0 and lay.sync < lay.split_cnt < lay.q
+    ws.buf[:lay.q].zero_()
     x_in = D.to_device_u16(xb)
     x_out = torch.empty_like(x_in)
     ctx = torch.from_numpy(lengths).cuda()
@@ -380,6 +381,45 @@ def test_block_m1_one_launch(gpu, shape, L):
     torch.cuda.synchronize()
     assert res["cache"].errors() == 0
     assert torch.equal(first, res["x_out"])
+
+
+def test_block_m1_shapes_share_workspace(gpu):
+    """Steps of two shapes (different kv heads, head size and split count)
+    and of two batch sizes (one-launch M = 1, and M = 3 in one launch per
+    stage) take turns on one workspace with new inputs every step: each
+    one-launch step finds its counters ready and matches no tagged word
+    that an earlier step left, whatever that step's layout, and every step
+    matches the oracle."""
+    torch, B, D = gpu
+    shapes = ONE_LAUNCH_SHAPES[:2]
+    plan = [(0, [700]), (1, [300]), (0, [500, 40, 900]), (1, [300]), (0, [700]), (1, [33])]
+    wss = [D.Workspace(shapes[k], len(L), max(L)) for k, L in plan]
+    shared = torch.zeros(max(w.nbytes for w in wss), dtype=torch.uint8, device="cuda")
+    for w in wss:
+        w.buf = shared[:w.nbytes]
+    setups = []
+    for i, shape in enumerate(shapes):
+        lw = synth.make_layer(shape, 31 + i)
+        setups.append((O.quantize_layer(lw), D.DeviceLayer(shape, lw)))
+    for it, ((k, L), ws) in enumerate(zip(plan, wss)):
+        shape = shapes[k]
+        ql, layer = setups[k]
+        lengths = np.array(L, np.int32)
+        M, maxL = len(L), int(lengths.max())
+        pre = synth.make_cache_prefill(shape, lengths, 31 + k)
+        cache = D.DeviceCache(shape, lengths)
+        cache.prefill(pre)
+        xb = synth.make_x(shape, M, 100 + it)
+        x_in = D.to_device_u16(xb)
+        x_out = torch.empty_like(x_in)
+        ctx = torch.from_numpy(lengths).cuda()
+        attn = torch.empty((M, shape.n_q_heads * shape.head_dim), dtype=torch.float32, device="cuda")
+        say(f"shared workspace step {it}: hd={shape.head_dim} n_kv={shape.n_kv_heads} lengths={L}")
+        B.i4d_decode_block_step(layer.struct, cache.struct, x_in, x_out, ctx, M, maxL, 0, ws.buf, ws.nbytes, attn)
+        torch.cuda.synchronize()
+        ref = O.decode_block(shape, ql, O.build_cache(shape, lengths, pre), xb, lengths)
+        check_block(dict(out=D.bf16_tensor_to_f32(x_out), attn=attn.cpu().numpy(), ref=ref, cache=cache, ws=ws,
+                         lengths=lengths, shape=shape), f"shared workspace step {it}")
 
 
 def test_block_m1_timeline(gpu):
@@ -437,8 +477,8 @@ def test_block_split_k(gpu, M):
     torch.cuda.synchronize()
     assert res["cache"].errors() == 0
     assert torch.equal(first, res["x_out"])
-    cnt = res["ws"].buf[res["ws"].layout.split_cnt:res["ws"].layout.split_part]
-    assert res["ws"].layout.split_part > res["ws"].layout.split_cnt and int(cnt.count_nonzero()) == 0
+    cnt = res["ws"].buf[res["ws"].layout.split_cnt:res["ws"].layout.q]
+    assert res["ws"].layout.q > res["ws"].layout.split_cnt and int(cnt.count_nonzero()) == 0
 
 
 def test_block_deterministic(gpu):
