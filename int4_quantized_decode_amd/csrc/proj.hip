@@ -289,8 +289,10 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void proj_skinny_kernel(ProjArgs
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[s][t][i] = fmaf(scl[i], ag[i], acc[s][t][i]);
       }
-      // one atom's decoded operands live at a time
-      __builtin_amdgcn_sched_barrier(0);
+      // one atom's decoded operands live at a time where registers are
+      // short (5 or more strips at two x tiles, the persistent variants);
+      // elsewhere the next atom's decode may overlap this one's MFMAs
+      if constexpr ((SP >= 5 && T == 2) || P) __builtin_amdgcn_sched_barrier(0);
     }
     // every read of this group's x is done before the next group's x loads
     // (into the same registers) are issued
