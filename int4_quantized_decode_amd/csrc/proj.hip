@@ -290,9 +290,9 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void proj_skinny_kernel(ProjArgs
         for (int i = 0; i < 4; ++i) acc[s][t][i] = fmaf(scl[i], ag[i], acc[s][t][i]);
       }
       // one atom's decoded operands live at a time where registers are
-      // short (5 or more strips at two x tiles, the persistent variants);
-      // elsewhere the next atom's decode may overlap this one's MFMAs
-      if constexpr ((SP >= 5 && T == 2) || P) __builtin_amdgcn_sched_barrier(0);
+      // short (the persistent variants); elsewhere the next atom's decode
+      // may overlap this one's MFMAs
+      if constexpr (P) __builtin_amdgcn_sched_barrier(0);
     }
     // every read of this group's x is done before the next group's x loads
     // (into the same registers) are issued
@@ -477,8 +477,15 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void proj_skinny_kernel(ProjArgs
 // plan takes the (SP, KS) that keeps the most CUs busy over the rounds of
 // workgroups (ties to more strips), with KS > 1 only when `split_bytes` of
 // split buffer are at hand and each wave gets at least one group.  D groups
-// of atoms are in flight per wave (about 8 atoms; `deep` allows D = 8 at
-// one strip, for the epilogues without RMSNorm).
+// of atoms are in flight per wave: one group from four strips up (from two
+// at two x tiles), else 2 to 4 atoms at one x tile and two groups at one
+// strip and two x tiles; 4 (or 8 with `deep`, the epilogues without
+// RMSNorm) at one strip and one x tile.  The registers a deeper ring would
+// hold go to overlapping consecutive atoms (the decode of the next during
+// the MFMAs of this one): alternating on one box, the step at 32 rows took
+// 81 us against 86 (8B) and 165 against 169 (70B) with the former D = 2
+// (4 at one strip), and at 16 rows 121 against 133 (70B) and 67 against
+// 69 (8B) with the former D = 2 (4 at two or three strips).
 static SkinnyPlan skinny_plan(int nstrips, int G, int T, bool deep, size_t split_bytes) {
   SkinnyPlan best{};
   double best_score = -1.0;
@@ -501,10 +508,10 @@ static SkinnyPlan skinny_plan(int nstrips, int G, int T, bool deep, size_t split
       best.GPW = gw;
     }
   }
-  if (best.SP >= 4)
+  if (best.SP >= 4 || (T == 2 && best.SP >= 2))
+    best.D = 1;
+  else if (best.SP >= 2 || T == 2)
     best.D = 2;
-  else if (best.SP >= 2)
-    best.D = T == 1 ? 4 : 2;
   else
     best.D = (deep && best.GPW > 4) ? 8 : 4;
   return best;
@@ -632,13 +639,13 @@ static bool skinny_dispatch(const ProjArgs& a, const ProjLaunch& l, hipStream_t 
                          st, a, p);                                                                             \
     return true;                                                                                                \
   }
-  I4D_SKINNY(7, 1, 2, true)
-  I4D_SKINNY(1, 1, 4, false) I4D_SKINNY(2, 1, 4, false) I4D_SKINNY(3, 1, 4, false) I4D_SKINNY(4, 1, 2, false)
-  I4D_SKINNY(5, 1, 2, false) I4D_SKINNY(7, 1, 2, false)
-  I4D_SKINNY(1, 2, 4, false) I4D_SKINNY(2, 2, 2, false) I4D_SKINNY(3, 2, 2, false) I4D_SKINNY(4, 2, 2, false)
-  I4D_SKINNY(5, 2, 2, false) I4D_SKINNY(7, 2, 2, false)
+  I4D_SKINNY(7, 1, 1, true)
+  I4D_SKINNY(1, 1, 4, false) I4D_SKINNY(2, 1, 2, false) I4D_SKINNY(3, 1, 2, false) I4D_SKINNY(4, 1, 1, false)
+  I4D_SKINNY(5, 1, 1, false) I4D_SKINNY(7, 1, 1, false)
+  I4D_SKINNY(1, 2, 2, false) I4D_SKINNY(2, 2, 1, false) I4D_SKINNY(3, 2, 1, false) I4D_SKINNY(4, 2, 1, false)
+  I4D_SKINNY(5, 2, 1, false) I4D_SKINNY(7, 2, 1, false)
   if constexpr (!needs_rho<EPI>()) {
-    I4D_SKINNY(1, 1, 8, false) I4D_SKINNY(1, 2, 8, false)
+    I4D_SKINNY(1, 1, 8, false)
   }
 #undef I4D_SKINNY
   return false;
