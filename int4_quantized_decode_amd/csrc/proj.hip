@@ -478,15 +478,15 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void proj_skinny_kernel(ProjArgs
 // workgroups (ties to more strips), with KS > 1 only when `split_bytes` of
 // split buffer are at hand and each wave gets at least one group.  D groups
 // of atoms are in flight per wave: one group from four strips up (from two
-// at two x tiles), else 2 to 4 atoms at one x tile and two groups at one
-// strip and two x tiles; 4 (or 8 with `deep`, the epilogues without
-// RMSNorm) at one strip and one x tile.  The registers a deeper ring would
-// hold go to overlapping consecutive atoms (the decode of the next during
-// the MFMAs of this one): alternating on one box, the step at 32 rows took
-// 81 us against 86 (8B) and 165 against 169 (70B) with the former D = 2
-// (4 at one strip), and at 16 rows 121 against 133 (70B) and 67 against
-// 69 (8B) with the former D = 2 (4 at two or three strips).
-static SkinnyPlan skinny_plan(int nstrips, int G, int T, bool deep, size_t split_bytes) {
+// at two x tiles), else two groups.  The registers a deeper ring would hold
+// go to overlapping consecutive atoms (the decode of the next during the
+// MFMAs of this one): alternating on one box, the step at 32 rows took 81
+// us against 86 (8B) and 165 against 169 (70B) with the former D = 2 (4 at
+// one strip), at 16 rows 121 against 133 (70B) and 67 against 69 (8B) with
+// the former D = 2 (4 at two or three strips), and at 8 and 16 rows on the
+// 8B shape 1.5 us less with two groups at one strip than with the former
+// 4 (8 for the down projection).
+static SkinnyPlan skinny_plan(int nstrips, int G, int T, size_t split_bytes) {
   SkinnyPlan best{};
   double best_score = -1.0;
   for (int SP : {7, 5, 4, 3, 2, 1}) {
@@ -508,12 +508,7 @@ static SkinnyPlan skinny_plan(int nstrips, int G, int T, bool deep, size_t split
       best.GPW = gw;
     }
   }
-  if (best.SP >= 4 || (T == 2 && best.SP >= 2))
-    best.D = 1;
-  else if (best.SP >= 2 || T == 2)
-    best.D = 2;
-  else
-    best.D = (deep && best.GPW > 4) ? 8 : 4;
+  best.D = (best.SP >= 4 || (T == 2 && best.SP >= 2)) ? 1 : 2;
   return best;
 }
 
@@ -582,7 +577,7 @@ struct ProjLaunch {
   int grid;
 };
 
-static ProjLaunch plan_projection(const ProjArgs& a, bool rho) {
+static ProjLaunch plan_projection(const ProjArgs& a) {
   ProjLaunch l{};
   const int nstrips = a.Np / kStrip;
   if (a.M == 1) {
@@ -614,7 +609,7 @@ static ProjLaunch plan_projection(const ProjArgs& a, bool rho) {
   }
   {
     l.T = a.M <= 16 ? 1 : 2;
-    l.s = skinny_plan(nstrips, a.G, l.T, !rho, split_bytes_of(a));
+    l.s = skinny_plan(nstrips, a.G, l.T, split_bytes_of(a));
     l.lds = l.s.SP ? skinny_lds_bytes(l.s.GPW, l.s.SP, l.T) : 0;
     const int ntiles = l.s.SP ? (nstrips + l.s.SP - 1) / l.s.SP * l.s.KS : 0;
     // more tiles than CUs at seven strips and one x tile: persistent
@@ -640,20 +635,17 @@ static bool skinny_dispatch(const ProjArgs& a, const ProjLaunch& l, hipStream_t 
     return true;                                                                                                \
   }
   I4D_SKINNY(7, 1, 1, true)
-  I4D_SKINNY(1, 1, 4, false) I4D_SKINNY(2, 1, 2, false) I4D_SKINNY(3, 1, 2, false) I4D_SKINNY(4, 1, 1, false)
+  I4D_SKINNY(1, 1, 2, false) I4D_SKINNY(2, 1, 2, false) I4D_SKINNY(3, 1, 2, false) I4D_SKINNY(4, 1, 1, false)
   I4D_SKINNY(5, 1, 1, false) I4D_SKINNY(7, 1, 1, false)
   I4D_SKINNY(1, 2, 2, false) I4D_SKINNY(2, 2, 1, false) I4D_SKINNY(3, 2, 1, false) I4D_SKINNY(4, 2, 1, false)
   I4D_SKINNY(5, 2, 1, false) I4D_SKINNY(7, 2, 1, false)
-  if constexpr (!needs_rho<EPI>()) {
-    I4D_SKINNY(1, 1, 8, false)
-  }
 #undef I4D_SKINNY
   return false;
 }
 
 template <int EPI>
 static bool launch_epi(const ProjArgs& a, hipStream_t st, bool launch) {
-  const ProjLaunch l = plan_projection(a, needs_rho<EPI>());
+  const ProjLaunch l = plan_projection(a);
   if (l.gemv) {
     if (!launch) return true;  // launch_gemv(_rows) has a kernel for every plan
     if (l.rows) {
@@ -701,8 +693,7 @@ static i4d_status projection_fits(const ProjArgs& a, const ProjLaunch& l) {
 i4d_status launch_projection(int epi, const ProjArgs& a, hipStream_t st) {
   if (epi < EPI_QKV || epi > EPI_DOWN) return fail(I4D_ERR_RANGE, "bad epilogue %d", epi);
   if (a.fmt == kFmtE4M3) return launch_projection_e4m3(epi, a, st);
-  const bool rho = epi == EPI_QKV || epi == EPI_GU;
-  const ProjLaunch l = plan_projection(a, rho);
+  const ProjLaunch l = plan_projection(a);
   const i4d_status fit = projection_fits(a, l);
   if (fit != I4D_OK) return fit;
   if (!dispatch_epi(epi, a, st, true))
@@ -714,8 +705,7 @@ i4d_status launch_projection(int epi, const ProjArgs& a, hipStream_t st) {
 }
 
 i4d_status projection_plan_of(int epi, const ProjArgs& a, i4d_projection_plan* out) {
-  const bool rho = epi == EPI_QKV || epi == EPI_GU;
-  const ProjLaunch l = plan_projection(a, rho);
+  const ProjLaunch l = plan_projection(a);
   *out = i4d_projection_plan{};
   out->kernel = l.gemv ? (l.rows ? 2 : 0) : 1;
   out->waves = l.gemv ? l.g.NW : kSkinnyWaves;
@@ -736,7 +726,7 @@ SplitNeed projection_split_need(int Np, int K, int M) {
   if (M <= 1) return n;
   const int nstrips = Np / kStrip, G = K / kGroup;
   if ((size_t)M * K * 2 <= kSplitMinXBytes) return n;
-  const SkinnyPlan p = skinny_plan(nstrips, G, M <= 16 ? 1 : 2, true, (size_t)-1);
+  const SkinnyPlan p = skinny_plan(nstrips, G, M <= 16 ? 1 : 2, (size_t)-1);
   if (p.KS > 1) {
     const size_t nsets = (size_t)(nstrips + p.SP - 1) / p.SP;
     n.part_bytes = nsets * p.KS * split_block_floats(p.SP) * sizeof(float);
