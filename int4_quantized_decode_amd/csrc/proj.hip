@@ -182,10 +182,6 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void proj_skinny_kernel(ProjArgs
   };
   load_scales(cur);
 
-  u32x4_t ring[U];
-#pragma unroll
-  for (int k = 0; k < U; ++k) ring[k] = load16_stream(atom_ptr(k / SP, k % SP));
-
   // x rows of one group as B operands: lane (col r, quarter j) holds row
   // 16 t + r, k = 128 g + 32 kb + 8 j .. +7.  Columns past M re-read row
   // M - 1 (unconditional loads keep the wait counts exact); their outputs
@@ -212,8 +208,16 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void proj_skinny_kernel(ProjArgs
       for (int kb = 0; kb < 4; ++kb)
         bx[t][kb] = *reinterpret_cast<const u32x4_t*>(xw + (16 * t + r) * kXRow + 64 * kb + 16 * j);
   };
+  // The first group's x is requested before the first atoms, the order in
+  // which the loop requests them (x one group ahead, then the refills):
+  // the wait counts the compiler derives at the loop head hold for both
+  // ways in, so the head waits for x only and not for the refills issued
+  // behind it (with the atoms first, every group began by draining them).
   u32x4_t xs[4 * T];
   load_xs(xs, 0);
+  u32x4_t ring[U];
+#pragma unroll
+  for (int k = 0; k < U; ++k) ring[k] = load16_stream(atom_ptr(k / SP, k % SP));
 
   constexpr int RS = T * 16 + 4;
   uint16_t* scw = sc + (size_t)wave * (SP * GW + 1) * kStrip;  // this wave's [SP][GW][16] + a zero row
@@ -344,9 +348,9 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void proj_skinny_kernel(ProjArgs
       tail(std::integral_constant<int, 2>());
     } else {
       // no groups in this tile for this wave: request the next tile directly
+      load_xs_t(nx, xs, 0);
 #pragma unroll
       for (int k = 0; k < U; ++k) ring[k] = load16_stream(atom_ptr_t(nx, k / SP, k % SP));
-      load_xs_t(nx, xs, 0);
     }
     load_scales(nx);
   } else if (ngr > 0) {
