@@ -390,17 +390,16 @@ def test_one_launch_coverage():
 
 
 def test_multi_row_gemv_plans():
-    """The multi-row GEMV runs at M = 2..4, and up to M = 8 where K >= 8192,
-    wherever its x staging fits: the 70B stages with K = 8192 at every M up
-    to 8, the 8B ones (K = 4096) to M = 4, and the down projections while
-    M x K fp16 fits the staging: 8B (K = 14336) to M = 4, 70B (K = 28672) at
-    M = 2 only."""
+    """The multi-row GEMV runs at M = 2, and M = 3 where K >= 8192, wherever
+    its x staging fits: the 8B stages with K = 4096 at M = 2, the 70B ones
+    (K = 8192) and the 8B down projection (K = 14336) to M = 3, the 70B down
+    projection (K = 28672) at M = 2 only (M x K fp16 beyond the staging)."""
     cs8, cs70 = B.make_shape(synth.SHAPE_8B), B.make_shape(synth.SHAPE_70B)
     for M in range(2, 9):
         for stage in range(3):
-            assert B.i4d_projection_plan_of(cs8, stage, M).kernel == (2 if M <= 4 else 1)
-            assert B.i4d_projection_plan_of(cs70, stage, M).kernel == 2
-        assert B.i4d_projection_plan_of(cs8, 3, M).kernel == (2 if M <= 4 else 1)
+            assert B.i4d_projection_plan_of(cs8, stage, M).kernel == (2 if M <= 2 else 1)
+            assert B.i4d_projection_plan_of(cs70, stage, M).kernel == (2 if M <= 3 else 1)
+        assert B.i4d_projection_plan_of(cs8, 3, M).kernel == (2 if M <= 3 else 1)
         assert B.i4d_projection_plan_of(cs70, 3, M).kernel == (2 if M == 2 else 1)
     for M in (9, 16, 32):
         assert all(B.i4d_projection_plan_of(cs8, st, M).kernel == 1 for st in range(4))

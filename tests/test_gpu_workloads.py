@@ -47,7 +47,7 @@ def layer70(gpu):
     return wl, lw, {}, {}
 
 
-@pytest.mark.parametrize("M", [1, 2, 4, 8, 16, 32])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 8, 16, 32])
 def test_70b_layer_ctx4096(gpu, layer70, M):
     wl, lw, dense, memo = layer70
     lengths = synth.make_lengths(wl, M)
