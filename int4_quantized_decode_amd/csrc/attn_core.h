@@ -539,7 +539,9 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int m, const 
         // high part (column c) + low part (column c + 8, rotated in by DPP)
         const float part = fmaf(acc[i], accf, -cq);
         const float full = part + dpp_row_ror8(part);
-        float v = full * f16_half(cur.ks[tile], i);
+        // scale products as FMAs with the fp16 scale as a mixed-precision
+        // operand (one v_fma_mix instead of a conversion and a multiply)
+        float v = fmaf(full, f16_half(cur.ks[tile], i), 0.0f);
         if (LAST) v = (t0 + 16 * tile + 4 * jj + i < L) ? v : -INFINITY;
         sc[tile * 4 + i] = v;
       }
@@ -566,7 +568,8 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int m, const 
       const int tile = e >> 2, i = e & 3;
       const float p = __builtin_amdgcn_exp2f(sc[e] - m_new);  // 0 for masked tokens
       l_run += p;
-      float pv = p * (f16_half(cur.vs[tile], i) * (slot16(e) ? 0.0625f : 1.0f));
+      float pv = fmaf(p, f16_half(cur.vs[tile], i), 0.0f);
+      if (slot16(e)) pv *= 0.0625f;
       if (LAST) pv = (p > 0.f) ? pv : 0.f;
       const _Float16 ph = (_Float16)pv;
       pb[e] = ph;
