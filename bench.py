@@ -45,8 +45,8 @@ PREFILL_SOURCES = ("prefill.hip", "gemv.h", "attn.h", "coherent.h", "device_comm
                    "i4d_layout.h", "../build.py")
 TRAFFIC = {
     "8b_m1_ctx4096": {"kernel": "step_m1_kernel (one-launch decode step)", "sources": STEP_M1_SOURCES,
-                      "sha256": "afb9ef99d193c6199be2f9c6b228f2abe7cf2f109a606f4ec0663c88a05ca277",
-                      "fetch_bytes": 118855168, "write_bytes": 779264},
+                      "sha256": "c57f91ada34c7b9159e7d5f7801c10b290868761df4fe36b08805109e154c547",
+                      "fetch_bytes": 118858112, "write_bytes": 779264},
     "8b_prefill_s2048": {"kernel": "prefill_gemm_kernel (FP8 MFMA GEMM + epilogue)", "sources": PREFILL_SOURCES,
                          "sha256": "be92b6769706595a517fb0e6321dc7a53801b020f67ca35e6923e5082aa4bc13",
                          "fetch_bytes": 213150720, "write_bytes": 10600448},
