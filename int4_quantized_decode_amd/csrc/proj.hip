@@ -562,8 +562,8 @@ static void launch_gemv(const ProjArgs& a, const GemvPlan& p, size_t lds, int gr
     hipLaunchKernelGGL((proj_gemv_kernel<EPI, NW, 8, 2>), dim3(grid), dim3(NW * 64), lds, st, a, p);
   else if (p.GPW == 4)
     hipLaunchKernelGGL((proj_gemv_kernel<EPI, NW, 4, 4>), dim3(grid), dim3(NW * 64), lds, st, a, p);
-  else
-    hipLaunchKernelGGL((proj_gemv_kernel<EPI, NW, 8, 0>), dim3(grid), dim3(NW * 64), lds, st, a, p);
+  else  // other group counts: x from LDS, 4 atoms in flight (70B down, 224 groups: step 91.8 -> 91.1 us against 8)
+    hipLaunchKernelGGL((proj_gemv_kernel<EPI, NW, 4, 0>), dim3(grid), dim3(NW * 64), lds, st, a, p);
 }
 
 // split buffer bytes usable by a projection (0: no split of K)
