@@ -539,15 +539,18 @@ static GemvPlan gemv_plan(int nstrips, int G) {
   return p;
 }
 
+// The multi-row GEMV keeps 4 atoms per wave in flight at every group count
+// (8 at one or two groups per wave and with x from LDS measured slower:
+// 8B-shape step at M = 2 49.3 against 45.4 us, alternating on one box).
 template <int EPI, int NW>
 static void launch_gemv_rows(const ProjArgs& a, const GemvPlan& p, size_t lds, int grid, hipStream_t st) {
   constexpr int X = kRowsXMax;
   switch (gemv_reg_groups(p, a.G)) {
-    case 1: hipLaunchKernelGGL((proj_gemv_rows_kernel<EPI, NW, 8, 1, X>), dim3(grid), dim3(NW * 64), lds, st, a, p); break;
-    case 2: hipLaunchKernelGGL((proj_gemv_rows_kernel<EPI, NW, 8, 2, X>), dim3(grid), dim3(NW * 64), lds, st, a, p); break;
+    case 1: hipLaunchKernelGGL((proj_gemv_rows_kernel<EPI, NW, 4, 1, X>), dim3(grid), dim3(NW * 64), lds, st, a, p); break;
+    case 2: hipLaunchKernelGGL((proj_gemv_rows_kernel<EPI, NW, 4, 2, X>), dim3(grid), dim3(NW * 64), lds, st, a, p); break;
     case 4: hipLaunchKernelGGL((proj_gemv_rows_kernel<EPI, NW, 4, 4, X>), dim3(grid), dim3(NW * 64), lds, st, a, p); break;
     default:
-      hipLaunchKernelGGL((proj_gemv_rows_kernel<EPI, NW, 8, 0, kRowsXMax>), dim3(grid), dim3(NW * 64), lds, st, a, p);
+      hipLaunchKernelGGL((proj_gemv_rows_kernel<EPI, NW, 4, 0, kRowsXMax>), dim3(grid), dim3(NW * 64), lds, st, a, p);
   }
 }
 
