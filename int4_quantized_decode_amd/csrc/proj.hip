@@ -603,14 +603,16 @@ static ProjLaunch plan_projection(const ProjArgs& a) {
     l.grid = (nstrips + l.g.SP - 1) / l.g.SP;
     return l;
   }
-  // the multi-row GEMV for M = 2, and M = 3 at K >= 8192, when its x
-  // staging fits (the scaled x of all rows in LDS, within kRowsXMax 16-byte
-  // chunks per thread).  Against the skinny kernel (one group of atoms in
-  // flight, consecutive atoms overlapping) the whole 70B-shape step took
-  // 103.5 / 106 / 107.8 / 121 / 122 us at M = 2 / 3 / 4 / 6 / 8 with it
-  // and 106 / 108.7 / 108 / 115 / 112 without; the 8B-shape step 49.5 /
-  // 55 / 56.4 at M = 2 / 3 / 4 with it, 50 / 52 / 51.9 without.
-  if (a.M <= 2 || (a.M <= 3 && a.K >= 8192)) {
+  // the multi-row GEMV for M = 2 and 3, when its x staging fits (the
+  // scaled x of all rows in LDS, within kRowsXMax 16-byte chunks per
+  // thread).  Against the skinny kernel (one group of atoms in flight,
+  // consecutive atoms overlapping) the whole 70B-shape step took 103.5 /
+  // 106 / 121 / 122 us at M = 2 / 3 / 6 / 8 with it and 106 / 108.7 / 115 /
+  // 112 without; with 4 atoms per wave in flight the 8B-shape step took
+  // 45.4 / 49.9 / 51.8 us at M = 2 / 3 / 4 with it against 49.3 (M = 2, the
+  // former 8) / 51.1 / 51.5 without, the 70B-shape step at M = 4 106.5
+  // against 106.9 (alternating on one box).
+  if (a.M <= 3) {
     const GemvPlan g = gemv_plan(nstrips, a.G);
     const int gpw_t = gemv_reg_groups(g, a.G);
     const size_t lds = gemv_rows_lds_bytes(a.K, a.M, g, gpw_t);

@@ -390,14 +390,13 @@ def test_one_launch_coverage():
 
 
 def test_multi_row_gemv_plans():
-    """The multi-row GEMV runs at M = 2, and M = 3 where K >= 8192, wherever
-    its x staging fits: the 8B stages with K = 4096 at M = 2, the 70B ones
-    (K = 8192) and the 8B down projection (K = 14336) to M = 3, the 70B down
+    """The multi-row GEMV runs at M = 2 and 3 wherever its x staging fits:
+    every 8B stage and the 70B ones with K = 8192 to M = 3, the 70B down
     projection (K = 28672) at M = 2 only (M x K fp16 beyond the staging)."""
     cs8, cs70 = B.make_shape(synth.SHAPE_8B), B.make_shape(synth.SHAPE_70B)
     for M in range(2, 9):
         for stage in range(3):
-            assert B.i4d_projection_plan_of(cs8, stage, M).kernel == (2 if M <= 2 else 1)
+            assert B.i4d_projection_plan_of(cs8, stage, M).kernel == (2 if M <= 3 else 1)
             assert B.i4d_projection_plan_of(cs70, stage, M).kernel == (2 if M <= 3 else 1)
         assert B.i4d_projection_plan_of(cs8, 3, M).kernel == (2 if M <= 3 else 1)
         assert B.i4d_projection_plan_of(cs70, 3, M).kernel == (2 if M == 2 else 1)
