@@ -407,8 +407,9 @@ i4d_status i4d_decode_block_step_timeline(const i4d_layer* layer, const i4d_kv_c
 /* Launch plan of one projection stage as i4d_decode_block_step runs it at M
  * rows (host only; diagnostics and tests).  stage: 0 QKV, 1 O, 2 gate/up,
  * 3 down.  kernel 0 = the M = 1 GEMV, 1 = the skinny MFMA kernel, 2 = the
- * multi-row GEMV (M = 2..8: the M = 1 weight stream with the rows of x in the
- * MFMA operand's rows, where its x staging fits);
+ * multi-row GEMV (M = 2 and 3: the M = 1 weight stream with the rows of x in
+ * the MFMA operand's rows, where its x staging fits; the kernel itself takes
+ * up to 8 rows);
  * instantiated = 1 when the library holds a kernel for the plan (a step
  * whose plan has none fails with I4D_ERR_UNSUPPORTED instead of launching
  * nothing).  I4D_ERR_UNSUPPORTED when the shape exceeds the kernels' limits

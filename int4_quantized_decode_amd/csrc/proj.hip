@@ -8,8 +8,9 @@
 //   as exact fp16 subnormals (the B operand of four f16 MFMA 16x16x32, one
 //   per 32 k) against range-scaled fp16 x, staged in LDS and broadcast to
 //   every row of the A operand, so each lane gets the dot of its atom row.
-// M = 2..8 (when x fits the kernel's staging): the same stream with rows
-//   0..M-1 of x in rows 0..M-1 of the A operand (gemv_rows.h).
+// M = 2..3 (when x fits the kernel's staging; the kernel takes up to 8):
+//   the same stream with rows 0..M-1 of x in rows 0..M-1 of the A operand
+//   (gemv_rows.h).
 // Otherwise (M <= 32): skinny GEMM on bf16 MFMA 16x16x32, computed as
 //   sum_g s[n][g] * (A[n][g] - 136 * X[m][g]) where A accumulates
 //   (128 + u) * x from the bf16 magic-exponent decode of each nibble and X
@@ -50,7 +51,7 @@ __global__ __launch_bounds__(NW * 64) void proj_gemv_kernel(ProjArgs a, GemvPlan
   gemv_body<EPI, NW, U, GPW, false>(a, pl, strip0, min(pl.SP, nstrips - strip0), smem, NoWait());
 }
 
-// M = 2..8: the M = 1 stream with x rows in the A operand's rows
+// M = 2..8 rows: the M = 1 stream with x rows in the A operand's rows
 template <int EPI, int NW, int U, int GPW, int XMAX>
 __global__ __launch_bounds__(NW * 64) void proj_gemv_rows_kernel(ProjArgs a, GemvPlan pl) {
   extern __shared__ __align__(16) unsigned char smem[];
