@@ -45,11 +45,11 @@ PREFILL_SOURCES = ("prefill.hip", "gemv.h", "attn.h", "coherent.h", "device_comm
                    "i4d_layout.h", "../build.py")
 TRAFFIC = {
     "8b_m1_ctx4096": {"kernel": "step_m1_kernel (one-launch decode step)", "sources": STEP_M1_SOURCES,
-                      "sha256": "c57f91ada34c7b9159e7d5f7801c10b290868761df4fe36b08805109e154c547",
-                      "fetch_bytes": 118858112, "write_bytes": 779264},
+                      "sha256": "3d63810bae1de70c5c98abcd3cc30dedfffd382c7aa137a3a52809458fc4f664",
+                      "fetch_bytes": 118785280, "write_bytes": 779264},
     "8b_prefill_s2048": {"kernel": "prefill_gemm_kernel (FP8 MFMA GEMM + epilogue)", "sources": PREFILL_SOURCES,
-                         "sha256": "be92b6769706595a517fb0e6321dc7a53801b020f67ca35e6923e5082aa4bc13",
-                         "fetch_bytes": 213150720, "write_bytes": 10600448},
+                         "sha256": "a2c449ad7e57c9686148c4b487afd42cff405953cbeeff9541df647627809ae8",
+                         "fetch_bytes": 213150848, "write_bytes": 10600448},
 }
 
 
